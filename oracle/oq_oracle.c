@@ -1,0 +1,351 @@
+/*
+ * oq_oracle.c -- plain fp64 CPU oracle for the OrbitQuant online
+ * quantized-linear path.  TEST INFRASTRUCTURE ONLY: the test-suite, the
+ * smoke check and the benchmark's CPU-baseline leg are the only callers.
+ * The product library never links, loads or calls this file, and this file
+ * shares no code, header, table or constant generator with it.
+ *
+ * Every step is written the slow, obvious way, in double precision, in the
+ * order the method states it.  Sources (page title; section / figure):
+ *
+ *  - "OrbitQuant: Data-Agnostic Quantization for Image and Video Diffusion
+ *    Transformers" (paper.gecl.asia close-reading notes), section Method,
+ *    items 1-4: keep the per-token L2 norm, quantize only the unit
+ *    direction; fold the rotation into the weight rows (W Pi^T) and apply
+ *    Pi x online; Lloyd-Max codebook on the dimension marginal
+ *    f_d ~ N(0, 1/d); RPBH = random permutation then block Hadamard.
+ *  - hotpaper.ai page, abstract: the same quantizer is applied to the weight
+ *    rows offline.
+ *  - pith.science page, Figure 2 caption: f_d ~ N(0,1/d) and one codebook
+ *    C_{d,b} per dimension and bit width; Supplementary A (proof-sketch
+ *    setup): d = k h, y = P_pi x, z^(j) = H_h D_j y^(j), (H_h)_{li} =
+ *    +-1/sqrt(h), D_j Rademacher.
+ *  - llmdb.app page, section Mathematical Formulation: y_hat =
+ *    Q_w(W R^-1) Q_a(R x), no bias.
+ *
+ * Readings where the pages are silent (each one is listed with its reason
+ * in the design notes):
+ *  - RNG: SplitMix64 (Vigna's published reference generator).  Pi is a
+ *    Durstenfeld shuffle driven by it, j = floor(r * (i+1) / 2^64); the d
+ *    Rademacher signs are drawn next from the same stream, sign = top bit.
+ *  - Hadamard in Sylvester natural order, H[a][b] = (-1)^popcount(a & b).
+ *  - Gather convention y_i = s_i * u_{pi(i)}.
+ *  - Ties go to the upper level: code = #{k : z >= tau_k}; -0 counts as 0.
+ *  - Codes are stored in a tile-interleaved slot order inside every group of
+ *    128 coordinates, then packed as a little-endian bitstream.
+ *  - Parity pins for each function are in the oracle test files.  The
+ *    permutation itself has no value printed on any page: it is pinned only
+ *    through the SplitMix64 published outputs and the bijection property.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "oq_oracle.h"
+
+/* ------------------------------------------------------------------ RNG -- */
+
+/* SplitMix64: state advances by the golden-ratio gamma, output is the
+ * state passed through two xor-shift-multiply rounds and a final xor-shift
+ * (Vigna's public-domain splitmix64.c). */
+uint64_t oqo_splitmix64_next(uint64_t *state)
+{
+    uint64_t z;
+    *state += 0x9E3779B97F4A7C15ULL;
+    z = *state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+
+/* ----------------------------------------------------------- plan (Pi, D) -- */
+
+int oqo_block_size(int d)
+{
+    /* largest power of two that divides d */
+    int h = 1;
+    while (d % (2 * h) == 0) h *= 2;
+    return h;
+}
+
+/* Random permutation Pi (Durstenfeld shuffle) and Rademacher signs D, both
+ * drawn from one SplitMix64 stream seeded with `seed`. */
+void oqo_plan(int d, uint64_t seed, int32_t *perm, int8_t *sign)
+{
+    uint64_t state = seed;
+    for (int i = 0; i < d; i++) perm[i] = i;
+    for (int i = d - 1; i >= 1; i--) {
+        uint64_t r = oqo_splitmix64_next(&state);
+        /* j = floor(r * (i+1) / 2^64), the high word of a 128-bit product */
+        unsigned __int128 prod = (unsigned __int128)r * (unsigned __int128)(uint64_t)(i + 1);
+        int j = (int)(uint64_t)(prod >> 64);
+        int32_t t = perm[i];
+        perm[i] = perm[j];
+        perm[j] = t;
+    }
+    for (int i = 0; i < d; i++) {
+        uint64_t r = oqo_splitmix64_next(&state);
+        sign[i] = (r >> 63) ? -1 : +1;
+    }
+}
+
+/* ------------------------------------------------------------- codebook -- */
+
+static double std_pdf(double t)
+{
+    if (isinf(t)) return 0.0;
+    return exp(-0.5 * t * t) / sqrt(2.0 * M_PI);
+}
+
+/* P(a <= X < b) for X ~ N(0,1), written with erfc on the side where it does
+ * not cancel. */
+static double std_mass(double a, double b)
+{
+    if (a >= 0.0) /* both in the upper half: Q(a) - Q(b) */
+        return 0.5 * erfc(a / sqrt(2.0)) - 0.5 * erfc(b / sqrt(2.0));
+    if (b <= 0.0) /* both in the lower half: Phi(b) - Phi(a) */
+        return 0.5 * erfc(-b / sqrt(2.0)) - 0.5 * erfc(-a / sqrt(2.0));
+    return 1.0 - 0.5 * erfc(-a / sqrt(2.0)) - 0.5 * erfc(b / sqrt(2.0));
+}
+
+/* Lloyd-Max quantizer for N(0,1) with L = 2^bits levels (Lloyd 1982; Max
+ * 1960), by Lloyd's alternation: thresholds are the midpoints of adjacent
+ * levels, and each level is the conditional mean of its cell,
+ *     c_k = (pdf(t_k) - pdf(t_{k+1})) / P(t_k <= X < t_{k+1}).
+ * Stops when no level moves by more than 1e-15 (or after max_iter).
+ * Writes L unit-variance levels and L-1 thresholds; returns iterations. */
+int oqo_codebook_unit(int bits, double *levels, double *thresholds)
+{
+    const int L = 1 << bits;
+    double t[65 + 1];
+    int it;
+    for (int k = 0; k < L; k++) /* evenly spread start inside (-2, 2) */
+        levels[k] = -2.0 + 4.0 * (k + 0.5) / L;
+    for (it = 1; it <= 200000; it++) {
+        double move = 0.0;
+        t[0] = -INFINITY;
+        t[L] = INFINITY;
+        for (int k = 1; k < L; k++) t[k] = 0.5 * (levels[k - 1] + levels[k]);
+        for (int k = 0; k < L; k++) {
+            double c = (std_pdf(t[k]) - std_pdf(t[k + 1])) / std_mass(t[k], t[k + 1]);
+            double dm = fabs(c - levels[k]);
+            if (dm > move) move = dm;
+            levels[k] = c;
+        }
+        if (move < 1e-15) break;
+    }
+    for (int k = 1; k < L; k++) thresholds[k - 1] = 0.5 * (levels[k - 1] + levels[k]);
+    return it;
+}
+
+/* The codebook C_{d,b} for the dimension marginal N(0, 1/d): the unit
+ * codebook scaled by sigma = 1/sqrt(d). */
+int oqo_codebook(int d, int bits, double *levels, double *thresholds)
+{
+    const int L = 1 << bits;
+    const double sigma = 1.0 / sqrt((double)d);
+    int it = oqo_codebook_unit(bits, levels, thresholds);
+    for (int k = 0; k < L; k++) levels[k] *= sigma;
+    for (int k = 0; k < L - 1; k++) thresholds[k] *= sigma;
+    return it;
+}
+
+/* Mean squared error of the unit quantizer, E[(X - Q(X))^2], by the closed
+ * form  sum_k [ m_k (1 + c_k^2) - 2 c_k (pdf(a)-pdf(b)) + (a pdf(a) - b pdf(b)) ]
+ * where m_k is the cell mass. */
+double oqo_codebook_mse(int bits, const double *levels, const double *thresholds)
+{
+    const int L = 1 << bits;
+    double s = 0.0;
+    for (int k = 0; k < L; k++) {
+        double a = (k == 0) ? -INFINITY : thresholds[k - 1];
+        double b = (k == L - 1) ? INFINITY : thresholds[k];
+        double m = std_mass(a, b);
+        double pa = std_pdf(a), pb = std_pdf(b);
+        double apa = isinf(a) ? 0.0 : a * pa;
+        double bpb = isinf(b) ? 0.0 : b * pb;
+        /* E[X^2 1_cell] = m + a pdf(a) - b pdf(b);  E[X 1_cell] = pdf(a) - pdf(b) */
+        s += (m + apa - bpb) - 2.0 * levels[k] * (pa - pb) + levels[k] * levels[k] * m;
+    }
+    return s;
+}
+
+/* ------------------------------------------------------------- rotation -- */
+
+/* In-place unnormalised Walsh-Hadamard transform of length h (power of
+ * two), Sylvester natural order: out[a] = sum_b (-1)^popcount(a&b) in[b]. */
+void oqo_fwht(double *v, int h)
+{
+    for (int len = 1; len < h; len *= 2)
+        for (int i = 0; i < h; i += 2 * len)
+            for (int j = i; j < i + len; j++) {
+                double a = v[j], b = v[j + len];
+                v[j] = a + b;
+                v[j + len] = a - b;
+            }
+}
+
+/* One entry of the Sylvester Hadamard matrix (+-1, unnormalised). */
+int oqo_hadamard_entry(int a, int b)
+{
+    return (__builtin_popcount((unsigned)(a & b)) & 1) ? -1 : 1;
+}
+
+/* Rotate one token: s = ||x||, u = x / s (u = 0 when s = 0),
+ * y_i = D_i u_{pi(i)}, and z^(j) = H_h y^(j) / sqrt(h) for each of the
+ * k = d/h blocks.  Writes z (length d) and the norm. */
+void oqo_rotate_token(const double *x, int d, const int32_t *perm, const int8_t *sign,
+                      int use_signs, double *z, double *norm)
+{
+    const int h = oqo_block_size(d);
+    double ss = 0.0;
+    for (int i = 0; i < d; i++) ss += x[i] * x[i];
+    const double s = sqrt(ss);
+    *norm = s;
+    for (int i = 0; i < d; i++) {
+        double u = (s > 0.0) ? x[perm[i]] / s : 0.0;
+        z[i] = (use_signs && sign[i] < 0) ? -u : u;
+    }
+    for (int j = 0; j < d / h; j++) {
+        oqo_fwht(z + (size_t)j * h, h);
+        for (int i = 0; i < h; i++) z[(size_t)j * h + i] /= sqrt((double)h);
+    }
+}
+
+/* ------------------------------------------------------- quantize, pack -- */
+
+/* Nearest level of the codebook, ties to the upper level:
+ * code = #{k : z >= t_k} over the L-1 ascending thresholds. */
+int oqo_quantize_one(double z, const double *thresholds, int L)
+{
+    int code = 0;
+    for (int k = 0; k < L - 1; k++)
+        if (z >= thresholds[k]) code++;
+    return code;
+}
+
+/* Storage slot of coordinate i: inside each group of 128 coordinates,
+ * coordinate 128G + 32c + p (c < 4, p < 32) goes to slot
+ * 128G + 8 (p mod 16) + 4 floor(p / 16) + c. */
+int64_t oqo_slot_of(int64_t i)
+{
+    int64_t G = i / 128, r = i % 128;
+    int64_t c = r / 32, p = r % 32;
+    return 128 * G + 8 * (p % 16) + 4 * (p / 16) + c;
+}
+
+/* Pack one row: code of coordinate i goes to bits [b*slot(i), b*slot(i)+b)
+ * of the row's byte string, little-endian bit order. */
+void oqo_pack_row(const uint8_t *codes, int d, int bits, uint8_t *out)
+{
+    memset(out, 0, (size_t)d * bits / 8);
+    for (int i = 0; i < d; i++) {
+        int64_t bitpos = (int64_t)bits * oqo_slot_of(i);
+        for (int t = 0; t < bits; t++)
+            if ((codes[i] >> t) & 1)
+                out[(bitpos + t) / 8] |= (uint8_t)(1u << ((bitpos + t) % 8));
+    }
+}
+
+void oqo_unpack_row(const uint8_t *packed, int d, int bits, uint8_t *codes)
+{
+    for (int i = 0; i < d; i++) {
+        int64_t bitpos = (int64_t)bits * oqo_slot_of(i);
+        int c = 0;
+        for (int t = 0; t < bits; t++)
+            if ((packed[(bitpos + t) / 8] >> ((bitpos + t) % 8)) & 1) c |= 1 << t;
+        codes[i] = (uint8_t)c;
+    }
+}
+
+/* ------------------------------------------------------------- drivers -- */
+
+static double load_elem(const void *x, int dtype, size_t idx)
+{
+    if (dtype == OQO_F32) return (double)((const float *)x)[idx];
+    /* bf16: the 16 stored bits are the top half of an fp32 */
+    uint32_t u = (uint32_t)((const uint16_t *)x)[idx] << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Rotate and quantize `rows` rows of x (row-major, d columns).  codes may be
+ * NULL (then only z / norms); z may be NULL.  Rows run in parallel. */
+int oqo_rotate_quantize(const void *x, int dtype, int64_t rows, int d, uint64_t seed,
+                        int use_signs, int bits, uint8_t *codes, double *norms, double *z)
+{
+    if (d <= 0 || d % 128 != 0 || bits < 1 || bits > 4) return -1;
+    const int L = 1 << bits;
+    int32_t *perm = malloc(sizeof(int32_t) * d);
+    int8_t *sign = malloc(d);
+    double lv[16], th[16];
+    oqo_plan(d, seed, perm, sign);
+    oqo_codebook(d, bits, lv, th);
+#pragma omp parallel
+    {
+        double *xr = malloc(sizeof(double) * d);
+        double *zr = malloc(sizeof(double) * d);
+        uint8_t *cr = malloc(d);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < rows; r++) {
+            double nrm;
+            for (int i = 0; i < d; i++) xr[i] = load_elem(x, dtype, (size_t)r * d + i);
+            oqo_rotate_token(xr, d, perm, sign, use_signs, zr, &nrm);
+            if (norms) norms[r] = nrm;
+            if (z) memcpy(z + (size_t)r * d, zr, sizeof(double) * d);
+            if (codes) {
+                for (int i = 0; i < d; i++) cr[i] = (uint8_t)oqo_quantize_one(zr[i], th, L);
+                oqo_pack_row(cr, d, bits, codes + (size_t)r * d * bits / 8);
+            }
+        }
+        free(xr);
+        free(zr);
+        free(cr);
+    }
+    free(perm);
+    free(sign);
+    return 0;
+}
+
+/* The low-bit linear, in fp64:
+ *   y[m][n] = s_m r_n sum_k C_{K,bw}[p_nk] C_{K,ba}[q_mk]
+ * with sigma-scaled levels.  Only the rows listed in `rows` (indices into
+ * the activation rows) are computed; y is [nrows][N]. */
+int oqo_linear(const uint8_t *a_codes, const double *a_norms, int ba,
+               const uint8_t *w_codes, const double *w_norms, int bw,
+               int64_t N, int K, const int64_t *rows, int64_t nrows, double *y)
+{
+    if (K <= 0 || K % 128 != 0) return -1;
+    double la[16], ta[16], lw[16], tw[16];
+    oqo_codebook(K, ba, la, ta);
+    oqo_codebook(K, bw, lw, tw);
+    double *wd = malloc(sizeof(double) * (size_t)N * K);
+#pragma omp parallel
+    {
+        uint8_t *c = malloc(K);
+        double *ad = malloc(sizeof(double) * K);
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; n++) {
+            oqo_unpack_row(w_codes + (size_t)n * K * bw / 8, K, bw, c);
+            for (int k = 0; k < K; k++) wd[(size_t)n * K + k] = lw[c[k]];
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < nrows; i++) {
+            int64_t m = rows[i];
+            oqo_unpack_row(a_codes + (size_t)m * K * ba / 8, K, ba, c);
+            for (int k = 0; k < K; k++) ad[k] = la[c[k]];
+            for (int64_t n = 0; n < N; n++) {
+                double acc = 0.0;
+                const double *wr = wd + (size_t)n * K;
+                for (int k = 0; k < K; k++) acc += wr[k] * ad[k];
+                y[(size_t)i * N + n] = a_norms[m] * w_norms[n] * acc;
+            }
+        }
+        free(c);
+        free(ad);
+    }
+    free(wd);
+    return 0;
+}

@@ -1,0 +1,97 @@
+"""Pins for nearest-level quantization, the storage slot order and packing.
+
+Pages: llmdb.app Implementation Details (activations rotated, then quantized
+with the fixed Lloyd-Max codebook); paper.gecl.asia notes, Core Idea.  The
+tie rule, code encoding, slot order and bit packing are readings (the pages
+are silent) and are pinned by brute force and hand-built vectors.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_quantize_is_nearest_level_by_brute_force(bits):
+    d = 3072
+    lv, th = oracle.codebook(d, bits)
+    rng = np.random.default_rng(bits)
+    zs = list(rng.standard_normal(2000) / np.sqrt(d) * 1.5)
+    zs += [0.0, -0.0, 10.0, -10.0]
+    for z in zs:
+        got = oracle.quantize_one(z, th)
+        dist = [abs(z - c) for c in lv]
+        best = min(dist)
+        cand = [k for k in range(len(lv)) if dist[k] == best]
+        assert got == max(cand)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_ties_go_up_and_signed_zero(bits):
+    lv, th = oracle.codebook(256, bits)
+    L = 1 << bits
+    for k, t in enumerate(th):
+        assert oracle.quantize_one(t, th) == k + 1          # exactly on tau_{k+1}
+        assert oracle.quantize_one(np.nextafter(t, -1), th) == k
+    assert oracle.quantize_one(0.0, th) == L // 2
+    assert oracle.quantize_one(-0.0, th) == L // 2
+
+
+def test_slot_order_is_a_bijection_inside_each_group():
+    slots = [oracle.slot_of(i) for i in range(512)]
+    for g in range(4):
+        assert sorted(slots[128 * g:128 * g + 128]) == list(range(128 * g, 128 * g + 128))
+    # hand-worked entries: coordinate 32c + p -> 8 (p mod 16) + 4 (p div 16) + c
+    assert [oracle.slot_of(i) for i in (0, 1, 16, 31, 32, 33, 127, 128, 161)] == \
+        [0, 8, 4, 124, 1, 9, 127, 128, 137]
+
+
+def _load_pack_golden():
+    cases = []
+    with open(os.path.join(GOLD, "pack_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            bits, codes, hexbytes = [s.strip() for s in line.split("|")]
+            raw = bytearray()
+            for tok in hexbytes.split():
+                if "*" in tok:
+                    v, n = tok.split("*")
+                    raw += bytes.fromhex(v) * int(n)
+                else:
+                    raw += bytes.fromhex(tok)
+            cases.append((int(bits), codes, bytes(raw)))
+    return cases
+
+
+def _expand(codes_spec):
+    """'i:v i:v ... @ rest=v' -> 128 codes in coordinate order."""
+    head, _, rest = codes_spec.partition("@")
+    fill = int(rest.split("=")[1]) if rest else 0
+    codes = np.full(128, fill, np.uint8)
+    for tok in head.split():
+        i, v = tok.split(":")
+        codes[int(i)] = int(v)
+    return codes
+
+
+def test_pack_hand_built_vectors():
+    for bits, spec, expect in _load_pack_golden():
+        codes = _expand(spec)
+        got = oracle.pack_row(codes, bits)
+        assert got.tobytes() == expect, (bits, spec)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_pack_unpack_roundtrip(bits):
+    rng = np.random.default_rng(bits)
+    d = 384
+    codes = rng.integers(0, 1 << bits, d).astype(np.uint8)
+    packed = oracle.pack_row(codes, bits)
+    assert packed.shape[0] == d * bits // 8
+    assert np.array_equal(oracle.unpack_row(packed, d, bits), codes)
