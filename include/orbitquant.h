@@ -1,0 +1,143 @@
+/*
+ * orbitquant.h -- C ABI of liborbitquant.so, the MI355X (gfx950) library for
+ * OrbitQuant's online quantized-linear path.
+ *
+ * The method (sources: the paper's abstract as reprinted on hotpaper.ai and
+ * pith.science; paper.gecl.asia close-reading notes, section Method;
+ * llmdb.app summary, section Mathematical Formulation; pith.science
+ * Figure 2 caption and Supplementary A setup):
+ *   - every activation token x (length d) keeps its L2 norm s = ||x|| apart
+ *     and only its direction u = x / s is quantized;
+ *   - u is rotated by RPBH: a seeded random permutation Pi, Rademacher signs
+ *     D, then an orthonormal Walsh-Hadamard transform on each of the
+ *     k = d / h blocks, h = the largest power of two dividing d;
+ *   - each rotated coordinate is replaced by the nearest level of the
+ *     Lloyd-Max codebook C_{d,b} for N(0, 1/d) (b = 2..4 bits);
+ *   - weights are prepared offline as the rows of W Pi^T, i.e. each row w_i
+ *     goes through the same rotation and quantizer, with row norm r_i;
+ *   - the linear is y[m][n] = s_m r_n sum_k C_{K,bw}[p_nk] C_{K,ba}[q_mk]
+ *     (no bias; the rotation cancels inside the product).
+ *
+ * Conventions shared by every entry point
+ *   - Return value: OQ_OK (0) or a negative OQ_E* status; oq_strerror()
+ *     describes it.  Nothing throws across this boundary.
+ *   - Arguments are validated on the host before any HIP call is made; a
+ *     rejected call has no side effect.
+ *   - Device pointers are caller-owned device memory (e.g. from PyTorch).
+ *     The library never frees them.  Work is enqueued on `stream` (a
+ *     hipStream_t passed as void*; NULL = the null stream) and is
+ *     asynchronous: results are valid once the stream has reached them.
+ *   - The library owns only its rotation-plan tables (a few tens of KB per
+ *     (device, d, seed)); they live until oq_release_plans() or unload.
+ *   - The rotation seed and flags of a layer's weights and of its
+ *     activations must be the same; the library cannot check this.
+ *   - Code layout ("storage order"): inside each group of 128 consecutive
+ *     rotated coordinates, coordinate 32c + p (c < 4, p < 32) is stored at
+ *     slot 8 (p mod 16) + 4 (p div 16) + c; slot t of a row holds the code
+ *     in bits [b t, b t + b) of the row's bytes, little-endian bit order.
+ *     A row of d codes therefore takes d*b/8 bytes.  Codes are level
+ *     indices 0..2^b-1 in ascending level order.
+ *   - Limits: d (and K) a multiple of 128, 128 <= d <= 16384; bits in
+ *     {2, 3, 4} (1..4 for oq_codebook).  Zero rows are valid (a zero token
+ *     gets norm 0 and every code 2^(b-1)).  NaN/Inf inputs give unspecified
+ *     codes and no error.
+ */
+#ifndef ORBITQUANT_H
+#define ORBITQUANT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define OQ_OK 0
+#define OQ_EINVAL (-1)        /* bad argument (null/misaligned pointer, negative size, ...) */
+#define OQ_EUNSUPPORTED (-2)  /* valid but not supported (d, bits, bit pair) */
+#define OQ_ENOMEM (-3)        /* the library could not allocate its plan tables */
+#define OQ_EDEVICE (-4)       /* a HIP call or kernel launch failed */
+
+/* input element types */
+#define OQ_F32 0   /* IEEE fp32 */
+#define OQ_BF16 1  /* bfloat16, 16-bit patterns */
+
+/* flags */
+#define OQ_ROT_NO_SIGNS (1u << 0)     /* rotation without the Rademacher signs D (Pi then H only) */
+#define OQ_OUT_F32_ROTATED (1u << 1)  /* oq_rotate_quantize writes the rotated unit vector z
+                                         (fp32 [n_tok][d], coordinate order) instead of codes */
+
+/* Text for a status code.  Never NULL; the string is static. */
+const char *oq_strerror(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int oq_version(void);
+
+/* Lloyd-Max codebook C_{d,bits} for the dimension marginal N(0, 1/d)
+ * (paper.gecl.asia notes, Core Idea and Method item 3; pith.science
+ * Figure 2 caption).  Host only, synchronous.
+ *   levels:     caller buffer of 2^bits floats, ascending, sigma = 1/sqrt(d)
+ *   thresholds: caller buffer of 2^bits - 1 floats, the midpoints of
+ *               adjacent levels (decision boundaries)
+ * bits in 1..4, d >= 1.  Errors: OQ_EINVAL (null buffer, d < 1),
+ * OQ_EUNSUPPORTED (bits). */
+int oq_codebook(int d, int bits, float *levels, float *thresholds);
+
+/* Bytes of a packed code matrix: rows * d * bits / 8 (-1 on bad input). */
+int64_t oq_codes_bytes(int64_t rows, int d, int bits);
+
+/* Online activation path (paper.gecl.asia notes, Method items 1 and 4;
+ * pith.science Supplementary A setup; llmdb.app Implementation Details):
+ * for each of the n_tok rows of x, s = ||x||_2, z = RPBH(x / s), and each
+ * coordinate of z is quantized to the nearest level of C_{d,bits} (ties to
+ * the upper level).
+ *   x:      device, [n_tok][d] row-major, dtype OQ_F32 or OQ_BF16, 16-byte
+ *           aligned
+ *   seed:   rotation seed (selects Pi and D)
+ *   flags:  OQ_ROT_NO_SIGNS, OQ_OUT_F32_ROTATED
+ *   out:    device; packed codes uint8 [n_tok][d*bits/8] (storage order,
+ *           16-byte aligned), or with OQ_OUT_F32_ROTATED fp32 [n_tok][d]
+ *   norms:  device fp32 [n_tok], receives s (4-byte aligned)
+ * n_tok = 0 is a no-op that succeeds (the pointers may then be NULL).
+ * Errors: OQ_EINVAL, OQ_EUNSUPPORTED, OQ_ENOMEM, OQ_EDEVICE. */
+int oq_rotate_quantize(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
+                       uint32_t flags, int bits, void *out, float *norms, void *stream);
+
+/* Offline weight preparation (hotpaper.ai abstract: the same quantizer on
+ * the weight rows, rotation absorbed into the weights; paper.gecl.asia
+ * notes, Method item 2: W Pi^T): row i of W [n_out][d_in] becomes the
+ * packed codes of RPBH(w_i / r_i) under C_{d_in,bits} plus r_i = ||w_i||.
+ * Same layout, limits and errors as oq_rotate_quantize (w_codes
+ * [n_out][d_in*bits/8], row_norms [n_out]); OQ_OUT_F32_ROTATED is
+ * rejected here. */
+int oq_prepare_weights(const void *W, int dtype, int64_t n_out, int d_in, uint64_t seed,
+                       uint32_t flags, int bits, uint8_t *w_codes, float *row_norms,
+                       void *stream);
+
+/* Low-bit linear (llmdb.app Mathematical Formulation, y = Q_w(W R^-1)
+ * Q_a(R x), no bias):
+ *   y[m][n] = bf16( s_m r_n sum_k C_{K,w_bits}[p_nk] C_{K,a_bits}[q_mk] )
+ * with both code matrices in storage order (the sum runs over the same
+ * permuted coordinates on both sides).  Accumulation is fp32 over fp16
+ * copies of the unit-variance levels; the output is rounded once to bf16
+ * (round to nearest even).
+ *   a_codes [M][K*a_bits/8], a_norms [M], w_codes [N][K*w_bits/8],
+ *   w_norms [N]: device, as produced by oq_rotate_quantize /
+ *   oq_prepare_weights with the same seed, flags and K
+ *   y: device bf16 bit patterns, [M][N] row-major
+ * a_bits, w_bits in {2, 3, 4}.  M = 0 or N = 0 is a no-op that succeeds
+ * (the pointers may then be NULL).  Errors:
+ * OQ_EINVAL, OQ_EUNSUPPORTED, OQ_EDEVICE. */
+int oq_linear(const uint8_t *a_codes, const float *a_norms, int a_bits,
+              const uint8_t *w_codes, const float *w_norms, int w_bits,
+              int64_t M, int64_t N, int K, uint16_t *y, void *stream);
+
+/* Free every cached rotation plan on every device (the caller must ensure
+ * no enqueued work still uses them, e.g. by synchronising first). */
+int oq_release_plans(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ORBITQUANT_H */

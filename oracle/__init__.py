@@ -63,6 +63,8 @@ def _load():
     lib.oqo_linear.restype = ctypes.c_int
     lib.oqo_linear.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int,
                                ctypes.c_int64, ctypes.c_int, P, ctypes.c_int64, P]
+    lib.oqo_num_threads.restype = ctypes.c_int
+    lib.oqo_num_threads.argtypes = []
     _lib = lib
     return lib
 
@@ -205,3 +207,8 @@ def linear(a_codes, a_norms, ba, w_codes, w_norms, bw, K, rows=None):
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return y
+
+
+def num_threads():
+    """OpenMP threads the oracle's parallel loops use."""
+    return _load().oqo_num_threads()

@@ -38,6 +38,7 @@
  *    through the SplitMix64 published outputs and the bijection property.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -349,3 +350,6 @@ int oqo_linear(const uint8_t *a_codes, const double *a_norms, int ba,
     free(wd);
     return 0;
 }
+
+/* Threads an OpenMP region of this oracle uses (for reporting). */
+int oqo_num_threads(void) { return omp_get_max_threads(); }

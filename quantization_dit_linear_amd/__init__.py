@@ -1,0 +1,187 @@
+"""OrbitQuant online quantized-linear path for MI355X (gfx950).
+
+Thin Python binding over ``liborbitquant.so`` (C ABI in
+``include/orbitquant.h``).  This module only marshals arguments: every step
+of the path runs in the library's HIP kernels.  PyTorch supplies device
+memory and the current stream, nothing else.  There is no CPU fallback: if
+the library is missing or cannot run, the call raises.
+
+Functions mirror the C entry points:
+
+* :func:`codebook`        -> ``oq_codebook``
+* :func:`rotate_quantize` -> ``oq_rotate_quantize``
+* :func:`rotate`          -> ``oq_rotate_quantize`` with ``OQ_OUT_F32_ROTATED``
+* :func:`prepare_weights` -> ``oq_prepare_weights``
+* :func:`linear`          -> ``oq_linear``
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liborbitquant.so")
+
+OQ_OK, OQ_EINVAL, OQ_EUNSUPPORTED, OQ_ENOMEM, OQ_EDEVICE = 0, -1, -2, -3, -4
+OQ_F32, OQ_BF16 = 0, 1
+OQ_ROT_NO_SIGNS, OQ_OUT_F32_ROTATED = 1, 2
+
+# every symbol the header declares, with (restype, argtypes)
+_P = ctypes.c_void_p
+_SIGS = {
+    "oq_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "oq_version": (ctypes.c_int, []),
+    "oq_codebook": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _P, _P]),
+    "oq_codes_bytes": (ctypes.c_int64, [ctypes.c_int64, ctypes.c_int, ctypes.c_int]),
+    "oq_rotate_quantize": (ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                          ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int,
+                                          _P, _P, _P]),
+    "oq_prepare_weights": (ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                          ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int,
+                                          _P, _P, _P]),
+    "oq_linear": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_int64,
+                                 ctypes.c_int64, ctypes.c_int, _P, _P]),
+    "oq_release_plans": (ctypes.c_int, []),
+}
+
+_lib = None
+
+
+class OQError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+def lib():
+    """The loaded ctypes library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first (python -m "
+                "quantization_dit_linear_amd.build or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def strerror(status):
+    return lib().oq_strerror(status).decode()
+
+
+def _check(status, where):
+    if status != OQ_OK:
+        raise OQError(status, where)
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev_ptr(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ------------------------------------------------------------------- API --
+
+def codebook(d, bits):
+    """(levels float32[2^bits], thresholds float32[2^bits-1]) of C_{d,bits}."""
+    L = 1 << bits
+    lv = np.zeros(16, np.float32)
+    th = np.zeros(16, np.float32)
+    _check(lib().oq_codebook(d, bits, lv.ctypes.data, th.ctypes.data), "oq_codebook")
+    return lv[:L].copy(), th[:L - 1].copy()
+
+
+def codes_bytes(rows, d, bits):
+    return lib().oq_codes_bytes(rows, d, bits)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return OQ_BF16
+    if t.dtype == torch.float32:
+        return OQ_F32
+    raise TypeError(f"unsupported input dtype {t.dtype} (bfloat16 or float32)")
+
+
+def rotate_quantize(x, seed, bits, *, signs=True, out=None, norms=None, stream=None):
+    """Codes (uint8 [M, d*bits/8], storage order) and norms (float32 [M])."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, d]")
+    M, d = x.shape
+    if out is None:
+        out = torch.empty((M, d * bits // 8), dtype=torch.uint8, device=x.device)
+    if norms is None:
+        norms = torch.empty((M,), dtype=torch.float32, device=x.device)
+    flags = 0 if signs else OQ_ROT_NO_SIGNS
+    rc = lib().oq_rotate_quantize(_dev_ptr(x, "x"), _dtype_code(x), M, d, seed, flags, bits,
+                                  _dev_ptr(out, "out"), _dev_ptr(norms, "norms"),
+                                  _stream(stream))
+    _check(rc, "oq_rotate_quantize")
+    return out, norms
+
+
+def rotate(x, seed, *, signs=True, stream=None):
+    """Rotated unit vectors z (float32 [M, d], coordinate order) and norms."""
+    import torch
+    M, d = x.shape
+    z = torch.empty((M, d), dtype=torch.float32, device=x.device)
+    norms = torch.empty((M,), dtype=torch.float32, device=x.device)
+    flags = OQ_OUT_F32_ROTATED | (0 if signs else OQ_ROT_NO_SIGNS)
+    rc = lib().oq_rotate_quantize(_dev_ptr(x, "x"), _dtype_code(x), M, d, seed, flags, 4,
+                                  _dev_ptr(z, "z"), _dev_ptr(norms, "norms"), _stream(stream))
+    _check(rc, "oq_rotate_quantize")
+    return z, norms
+
+
+def prepare_weights(W, seed, bits, *, signs=True, out=None, norms=None, stream=None):
+    """Weight codes (uint8 [N, K*bits/8]) and row norms (float32 [N])."""
+    import torch
+    if W.dim() != 2:
+        raise ValueError("W must be [d_out, d_in]")
+    N, K = W.shape
+    if out is None:
+        out = torch.empty((N, K * bits // 8), dtype=torch.uint8, device=W.device)
+    if norms is None:
+        norms = torch.empty((N,), dtype=torch.float32, device=W.device)
+    flags = 0 if signs else OQ_ROT_NO_SIGNS
+    rc = lib().oq_prepare_weights(_dev_ptr(W, "W"), _dtype_code(W), N, K, seed, flags, bits,
+                                  _dev_ptr(out, "w_codes"), _dev_ptr(norms, "row_norms"),
+                                  _stream(stream))
+    _check(rc, "oq_prepare_weights")
+    return out, norms
+
+
+def linear(a_codes, a_norms, a_bits, w_codes, w_norms, w_bits, K, *, out=None, stream=None):
+    """bf16 y [M, N] = s_m r_n sum_k C_w[p_nk] C_a[q_mk]."""
+    import torch
+    M = a_codes.shape[0]
+    N = w_codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_codes.device)
+    rc = lib().oq_linear(_dev_ptr(a_codes, "a_codes"), _dev_ptr(a_norms, "a_norms"), a_bits,
+                         _dev_ptr(w_codes, "w_codes"), _dev_ptr(w_norms, "w_norms"), w_bits,
+                         M, N, K, _dev_ptr(out, "y"), _stream(stream))
+    _check(rc, "oq_linear")
+    return out
+
+
+def release_plans():
+    _check(lib().oq_release_plans(), "oq_release_plans")

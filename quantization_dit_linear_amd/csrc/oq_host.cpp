@@ -1,0 +1,326 @@
+// oq_host.cpp -- host side of liborbitquant: the C ABI declared in
+// include/orbitquant.h, argument validation, the Lloyd-Max codebook solver,
+// the rotation-plan builder and the per-device plan cache.
+//
+// The codebook is found with Max's method (J. Max, "Quantizing for minimum
+// distortion", 1960; cited by the pith.science page): shoot from the
+// zero threshold upwards, alternately solving the centroid condition for
+// the next threshold and the midpoint condition for the next level, and
+// bisect on the first positive level until the top cell's centroid
+// condition holds.  The plan uses SplitMix64 (Vigna's published generator)
+// driving a Durstenfeld shuffle, then one Rademacher sign per coordinate
+// from the same stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include "../../include/orbitquant.h"
+#include "oq_internal.h"
+
+namespace {
+
+// ------------------------------------------------------------- codebook --
+
+double npdf(double t) { return std::isinf(t) ? 0.0 : std::exp(-0.5 * t * t) * 0.3989422804014327; }
+
+// P(a <= X < b), X ~ N(0,1), for 0 <= a < b <= inf (upper half only).
+double upper_mass(double a, double b) {
+  return 0.5 * std::erfc(a * M_SQRT1_2) - (std::isinf(b) ? 0.0 : 0.5 * std::erfc(b * M_SQRT1_2));
+}
+
+double cell_mean(double a, double b) { return (npdf(a) - npdf(b)) / upper_mass(a, b); }
+
+// Given the lower edge a >= 0 of a cell and its level c (a < c < mean(a,inf)),
+// the upper edge b with mean(a, b) = c.  mean(a, b) rises from a to
+// mean(a, inf) as b grows, so bisection on b is safe.
+double edge_for_mean(double a, double c) {
+  double lo = a, hi = a + 1.0;
+  while (cell_mean(a, hi) <= c) {
+    lo = hi;
+    hi = a + 2.0 * (hi - a);
+    if (hi > 40.0) return INFINITY;
+  }
+  for (int i = 0; i < 200 && hi - lo > 1e-17 * hi; i++) {
+    double mid = 0.5 * (lo + hi);
+    if (cell_mean(a, mid) < c) lo = mid; else hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+// Shoot the positive half (P = L/2 levels) from the first positive level c0.
+// Returns > 0 if the shot overshoots (the top cell cannot have c0's
+// successor as its mean), < 0 if it undershoots.
+double shoot(double c0, int P, double *pos_levels, double *pos_edges) {
+  double a = 0.0, c = c0;
+  for (int k = 0; k < P - 1; k++) {
+    pos_levels[k] = c;
+    if (c >= cell_mean(a, INFINITY)) return 1.0;
+    double b = edge_for_mean(a, c);
+    if (std::isinf(b)) return 1.0;
+    pos_edges[k] = b;
+    c = 2.0 * b - c;  // the next level: b is the midpoint of c and c'
+    a = b;
+  }
+  pos_levels[P - 1] = c;
+  return c - cell_mean(a, INFINITY);
+}
+
+// Unit-variance Lloyd-Max codebook: L = 2^bits ascending levels, L-1
+// thresholds.  Cached: the result depends on bits only.
+void unit_codebook(int bits, double *levels, double *thresholds) {
+  static std::mutex mu;
+  static bool done[5] = {false, false, false, false, false};
+  static double lv[5][16], th[5][15];
+  std::lock_guard<std::mutex> g(mu);
+  const int L = 1 << bits, P = L / 2;
+  if (!done[bits]) {
+    double pl[8], pe[8];
+    if (P == 1) {
+      pl[0] = cell_mean(0.0, INFINITY);
+    } else {
+      double lo = 0.0, hi = cell_mean(0.0, INFINITY);
+      for (int i = 0; i < 400; i++) {
+        double mid = 0.5 * (lo + hi);
+        if (mid <= lo || mid >= hi) break;
+        if (shoot(mid, P, pl, pe) > 0) hi = mid; else lo = mid;
+      }
+      shoot(0.5 * (lo + hi), P, pl, pe);
+    }
+    for (int k = 0; k < P; k++) {
+      lv[bits][P + k] = pl[k];
+      lv[bits][P - 1 - k] = -pl[k];
+    }
+    for (int k = 0; k < L - 1; k++) th[bits][k] = 0.5 * (lv[bits][k] + lv[bits][k + 1]);
+    th[bits][P - 1] = 0.0;
+    done[bits] = true;
+  }
+  std::memcpy(levels, lv[bits], sizeof(double) * L);
+  std::memcpy(thresholds, th[bits], sizeof(double) * (L - 1));
+}
+
+uint16_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;  // round to nearest even
+  uint16_t u;
+  std::memcpy(&u, &h, 2);
+  return u;
+}
+
+// ----------------------------------------------------------------- plan --
+
+struct SplitMix64 {
+  uint64_t s;
+  uint64_t next() {
+    s += 0x9E3779B97F4A7C15ULL;
+    uint64_t z = s;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+  }
+};
+
+// perm[i] = pi(i) (the gather y_i = x_{pi(i)}), neg[i] = D_i < 0.
+void build_plan(int d, uint64_t seed, std::vector<int32_t> &perm, std::vector<uint8_t> &neg) {
+  SplitMix64 g{seed};
+  perm.resize(d);
+  neg.resize(d);
+  for (int i = 0; i < d; i++) perm[i] = i;
+  for (int i = d - 1; i >= 1; i--) {
+    unsigned __int128 p = (unsigned __int128)g.next() * (unsigned __int128)(uint64_t)(i + 1);
+    int j = (int)(uint64_t)(p >> 64);
+    std::swap(perm[i], perm[j]);
+  }
+  for (int i = 0; i < d; i++) neg[i] = (uint8_t)(g.next() >> 63);
+}
+
+struct PlanKey {
+  int dev, d;
+  uint64_t seed;
+  bool operator<(const PlanKey &o) const {
+    return std::tie(dev, d, seed) < std::tie(o.dev, o.d, o.seed);
+  }
+};
+
+std::mutex g_plan_mu;
+std::map<PlanKey, oq::DevicePlan> g_plans;
+
+int get_plan(int d, uint64_t seed, hipStream_t stream, const oq::DevicePlan **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return OQ_EDEVICE;
+  std::lock_guard<std::mutex> g(g_plan_mu);
+  PlanKey key{dev, d, seed};
+  auto it = g_plans.find(key);
+  if (it != g_plans.end()) {
+    *out = &it->second;
+    return OQ_OK;
+  }
+  std::vector<int32_t> perm;
+  std::vector<uint8_t> neg;
+  build_plan(d, seed, perm, neg);
+  std::vector<int32_t> sc(d), sc0(d);
+  for (int i = 0; i < d; i++) {
+    sc[perm[i]] = i | (neg[i] ? (int32_t)0x80000000 : 0);
+    sc0[perm[i]] = i;
+  }
+  oq::DevicePlan p;
+  p.d = d;
+  p.h = d & -d;
+  if (hipMalloc(&p.scatter, sizeof(int32_t) * d) != hipSuccess) return OQ_ENOMEM;
+  if (hipMalloc(&p.scatter_nosign, sizeof(int32_t) * d) != hipSuccess) {
+    (void)hipFree(p.scatter);
+    return OQ_ENOMEM;
+  }
+  // synchronous upload: the host vectors go out of scope afterwards
+  if (hipMemcpy(p.scatter, sc.data(), sizeof(int32_t) * d, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(p.scatter_nosign, sc0.data(), sizeof(int32_t) * d, hipMemcpyHostToDevice) !=
+          hipSuccess) {
+    (void)hipFree(p.scatter);
+    (void)hipFree(p.scatter_nosign);
+    return OQ_EDEVICE;
+  }
+  (void)stream;
+  auto res = g_plans.emplace(key, p);
+  *out = &res.first->second;
+  return OQ_OK;
+}
+
+// ----------------------------------------------------------- validation --
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_d_bits(int d, int bits) {
+  if (d <= 0) return OQ_EINVAL;
+  if (bits < 2 || bits > 4) return OQ_EUNSUPPORTED;
+  if (d % oq::kGroup != 0 || d > oq::kMaxD) return OQ_EUNSUPPORTED;
+  return OQ_OK;
+}
+
+int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed, uint32_t flags,
+                  int bits, void *out, float *norms, void *stream, bool allow_rotated) {
+  if (n_tok < 0) return OQ_EINVAL;
+  if (dtype != OQ_F32 && dtype != OQ_BF16) return OQ_EINVAL;
+  if (flags & ~(OQ_ROT_NO_SIGNS | OQ_OUT_F32_ROTATED)) return OQ_EINVAL;
+  if ((flags & OQ_OUT_F32_ROTATED) && !allow_rotated) return OQ_EINVAL;
+  int rc = check_d_bits(d, bits);
+  if (rc != OQ_OK) return rc;
+  if (n_tok == 0) return OQ_OK;  // empty input: nothing to do, pointers may be null
+  if (!x || !out || !norms) return OQ_EINVAL;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(norms, 4)) return OQ_EINVAL;
+  const oq::DevicePlan *plan = nullptr;
+  rc = get_plan(d, seed, (hipStream_t)stream, &plan);
+  if (rc != OQ_OK) return rc;
+  double lv[16], th[15];
+  unit_codebook(bits, lv, th);
+  oq::Thresholds t{};
+  t.count = (1 << bits) - 1;
+  for (int k = 0; k < t.count; k++) t.t[k] = (float)th[k];
+  oq::RotateArgs a{};
+  a.x = x;
+  a.dtype = dtype;
+  a.n_tok = n_tok;
+  a.d = d;
+  a.h = d & -d;
+  a.bits = bits;
+  a.signs = !(flags & OQ_ROT_NO_SIGNS);
+  a.rotated_out = (flags & OQ_OUT_F32_ROTATED) != 0;
+  a.out = out;
+  a.norms = norms;
+  a.stream = (hipStream_t)stream;
+  hipError_t e = oq::launch_rotate_quantize_generic(a, *plan, t);
+  return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ ABI --
+
+extern "C" {
+
+const char *oq_strerror(int status) {
+  switch (status) {
+    case OQ_OK: return "success";
+    case OQ_EINVAL: return "invalid argument (null or misaligned pointer, bad size, dtype or flag)";
+    case OQ_EUNSUPPORTED: return "unsupported configuration (d must be a multiple of 128 in [128, 16384]; bits in {2,3,4})";
+    case OQ_ENOMEM: return "out of device memory for the rotation plan";
+    case OQ_EDEVICE: return "HIP runtime or kernel launch failure";
+    default: return "unknown status";
+  }
+}
+
+int oq_version(void) { return 100; }
+
+int oq_codebook(int d, int bits, float *levels, float *thresholds) {
+  if (!levels || !thresholds || d < 1) return OQ_EINVAL;
+  if (bits < 1 || bits > 4) return OQ_EUNSUPPORTED;
+  double lv[16], th[15];
+  unit_codebook(bits, lv, th);
+  const double sigma = 1.0 / std::sqrt((double)d);
+  const int L = 1 << bits;
+  for (int k = 0; k < L; k++) levels[k] = (float)(lv[k] * sigma);
+  for (int k = 0; k < L - 1; k++) thresholds[k] = (float)(th[k] * sigma);
+  return OQ_OK;
+}
+
+int64_t oq_codes_bytes(int64_t rows, int d, int bits) {
+  if (rows < 0 || d < 0 || bits < 1 || bits > 8) return -1;
+  return rows * (int64_t)d * bits / 8;
+}
+
+int oq_rotate_quantize(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
+                       uint32_t flags, int bits, void *out, float *norms, void *stream) {
+  return rotate_common(x, dtype, n_tok, d, seed, flags, bits, out, norms, stream, true);
+}
+
+int oq_prepare_weights(const void *W, int dtype, int64_t n_out, int d_in, uint64_t seed,
+                       uint32_t flags, int bits, uint8_t *w_codes, float *row_norms,
+                       void *stream) {
+  return rotate_common(W, dtype, n_out, d_in, seed, flags, bits, w_codes, row_norms, stream,
+                       false);
+}
+
+int oq_linear(const uint8_t *a_codes, const float *a_norms, int a_bits, const uint8_t *w_codes,
+              const float *w_norms, int w_bits, int64_t M, int64_t N, int K, uint16_t *y,
+              void *stream) {
+  if (M < 0 || N < 0) return OQ_EINVAL;
+  int rc = check_d_bits(K, a_bits);
+  if (rc != OQ_OK) return rc;
+  rc = check_d_bits(K, w_bits);
+  if (rc != OQ_OK) return rc;
+  if (M == 0 || N == 0) return OQ_OK;  // empty output: pointers may be null
+  if (!a_codes || !a_norms || !w_codes || !w_norms || !y) return OQ_EINVAL;
+  if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_norms, 4) ||
+      !aligned(w_norms, 4) || !aligned(y, 2))
+    return OQ_EINVAL;
+  double lv[16], th[15];
+  oq::LevelsF16 la{}, lw{};
+  unit_codebook(a_bits, lv, th);
+  for (int k = 0; k < (1 << a_bits); k++) la.v[k] = f32_to_f16_bits((float)lv[k]);
+  unit_codebook(w_bits, lv, th);
+  for (int k = 0; k < (1 << w_bits); k++) lw.v[k] = f32_to_f16_bits((float)lv[k]);
+  oq::LinearArgs a{a_codes, a_norms, a_bits, w_codes, w_norms, w_bits, M, N, K, y,
+                   (hipStream_t)stream};
+  hipError_t e = oq::launch_linear(a, la, lw);
+  return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
+}
+
+int oq_release_plans(void) {
+  std::lock_guard<std::mutex> g(g_plan_mu);
+  int rc = OQ_OK;
+  for (auto &kv : g_plans) {
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    if (hipSetDevice(kv.first.dev) != hipSuccess) rc = OQ_EDEVICE;
+    if (kv.second.scatter) (void)hipFree(kv.second.scatter);
+    if (kv.second.scatter_nosign) (void)hipFree(kv.second.scatter_nosign);
+    (void)hipSetDevice(cur);
+  }
+  g_plans.clear();
+  return rc;
+}
+
+}  // extern "C"

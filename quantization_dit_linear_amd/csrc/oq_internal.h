@@ -1,0 +1,63 @@
+// oq_internal.h -- definitions shared by the host side of liborbitquant and
+// its HIP kernels (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oq {
+
+constexpr int kMaxD = 16384;
+constexpr int kGroup = 128;  // coordinates per storage-order group
+
+// Unit-variance decision thresholds of one codebook (fp32, ascending).
+struct Thresholds {
+  float t[15];
+  int count;  // 2^bits - 1
+};
+
+// Unit-variance levels of one codebook, as fp16 bit patterns.
+struct LevelsF16 {
+  uint16_t v[16];
+};
+
+// Device-side rotation plan for one (device, d, seed).
+struct DevicePlan {
+  int d = 0, h = 0;
+  // scatter table for the generic kernel: entry j = pi^-1(j), bit 31 set when
+  // the sign applied at that destination is negative.
+  int32_t *scatter = nullptr;         // with signs
+  int32_t *scatter_nosign = nullptr;  // signs dropped
+};
+
+struct RotateArgs {
+  const void *x;
+  int dtype;  // 0 fp32, 1 bf16
+  int64_t n_tok;
+  int d, h, bits;
+  bool signs;
+  bool rotated_out;
+  void *out;
+  float *norms;
+  hipStream_t stream;
+};
+
+// Kernel launchers (defined in the .hip files).  Return a hipError_t.
+hipError_t launch_rotate_quantize_generic(const RotateArgs &a, const DevicePlan &p,
+                                          const Thresholds &th);
+
+struct LinearArgs {
+  const uint8_t *a_codes;
+  const float *a_norms;
+  int a_bits;
+  const uint8_t *w_codes;
+  const float *w_norms;
+  int w_bits;
+  int64_t M, N;
+  int K;
+  uint16_t *y;
+  hipStream_t stream;
+};
+
+hipError_t launch_linear(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw);
+
+}  // namespace oq

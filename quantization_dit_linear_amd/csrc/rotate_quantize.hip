@@ -1,0 +1,154 @@
+// rotate_quantize.hip -- rotate + quantize kernels for gfx950.
+//
+// Per token x (length d): s = ||x||, y_i = D_i x_{pi(i)}, z = blockwise
+// H_h y / (s sqrt(h)), code = #{k : sqrt(d) z >= tau_k} over the unit
+// Lloyd-Max thresholds, packed in storage order.  (paper.gecl.asia notes,
+// Method items 1, 3, 4; pith.science Supplementary A setup.)
+//
+// This file holds the general kernel: any dtype, any h, one workgroup per
+// token, the token held in LDS as fp32.
+#include <hip/hip_runtime.h>
+
+#include "oq_internal.h"
+
+namespace oq {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float load_elem(const void *x, int dtype, int64_t idx) {
+  if (dtype == 1) {
+    uint32_t u = (uint32_t)((const uint16_t *)x)[idx] << 16;
+    return __uint_as_float(u);
+  }
+  return ((const float *)x)[idx];
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_codes(uint8_t *dst, uint32_t word) {
+  if constexpr (BITS == 4) {
+    *(uint32_t *)dst = word;
+  } else if constexpr (BITS == 2) {
+    *(uint16_t *)dst = (uint16_t)word;
+  } else {
+    dst[0] = (uint8_t)word;
+    dst[1] = (uint8_t)(word >> 8);
+    dst[2] = (uint8_t)(word >> 16);
+  }
+}
+
+// Workgroup sum of one double per thread; every thread gets the total.
+__device__ double block_sum(double v, double *scratch) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) scratch[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int w = 0; w < kThreads / 64; w++) t += scratch[w];
+  return t;
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void rq_generic_kernel(
+    const void *__restrict__ x, int dtype, int64_t n_tok, int d, int h,
+    const int32_t *__restrict__ scatter, Thresholds th, uint8_t *__restrict__ codes,
+    float *__restrict__ zout, float *__restrict__ norms) {
+  extern __shared__ float y[];  // d floats
+  __shared__ double red[kThreads / 64];
+  const int tid = threadIdx.x;
+  const int64_t row_bytes = (int64_t)d * BITS / 8;
+  for (int64_t t = blockIdx.x; t < n_tok; t += gridDim.x) {
+    // load, sum of squares, scatter with sign: y[pi^-1(j)] = D x_j
+    float ss = 0.f;
+    for (int j = tid; j < d; j += kThreads) {
+      float v = load_elem(x, dtype, t * d + j);
+      ss = fmaf(v, v, ss);
+      int32_t e = scatter[j];
+      y[e & 0x7fffffff] = (e < 0) ? -v : v;
+    }
+    double total = block_sum((double)ss, red);
+    __syncthreads();
+    // block Walsh-Hadamard (unnormalised, Sylvester order), radix 2
+    for (int len = 1; len < h; len <<= 1) {
+      for (int q = tid; q < d / 2; q += kThreads) {
+        int i = ((q & ~(len - 1)) << 1) | (q & (len - 1));
+        float a = y[i], b = y[i + len];
+        y[i] = a + b;
+        y[i + len] = a - b;
+      }
+      __syncthreads();
+    }
+    const double s = sqrt(total);
+    if (tid == 0) norms[t] = (float)s;
+    if (zout) {
+      const float zs = s > 0.0 ? (float)(1.0 / (s * sqrt((double)h))) : 0.f;
+      for (int i = tid; i < d; i += kThreads) zout[t * d + i] = y[i] * zs;
+    } else {
+      // unit-space value sqrt(d) z_i = y_i sqrt(d/h) / s
+      const float us = s > 0.0 ? (float)(sqrt((double)d / (double)h) / s) : 0.f;
+      for (int q = tid; q < d / 8; q += kThreads) {
+        const int G = q >> 4, n = q & 15;
+        uint32_t word = 0;
+#pragma unroll
+        for (int w = 0; w < 2; w++)
+#pragma unroll
+          for (int c = 0; c < 4; c++) {
+            const float u = y[G * 128 + 32 * c + 16 * w + n] * us;
+            uint32_t code = 0;
+            for (int k = 0; k < th.count; k++) code += (u >= th.t[k]) ? 1u : 0u;
+            word |= code << (BITS * (4 * w + c));
+          }
+        store_codes<BITS>(codes + t * row_bytes + 16 * BITS * G + BITS * n, word);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rotate_quantize_generic(const RotateArgs &a, const DevicePlan &p,
+                                          const Thresholds &th) {
+  const int32_t *sc = a.signs ? p.scatter : p.scatter_nosign;
+  int dev = 0, cus = 0;
+  (void)hipGetDevice(&dev);
+  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t want = (int64_t)(cus > 0 ? cus : 256) * 8;
+  const int grid = (int)(a.n_tok < want ? a.n_tok : want);
+  const size_t lds = sizeof(float) * a.d;
+  uint8_t *codes = a.rotated_out ? nullptr : (uint8_t *)a.out;
+  float *zout = a.rotated_out ? (float *)a.out : nullptr;
+  if (lds > 32768) {
+    // tokens above 8192 fp32 need more than the default dynamic-LDS cap
+    hipError_t e = hipSuccess;
+    if (a.bits == 2)
+      e = hipFuncSetAttribute((const void *)rq_generic_kernel<2>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    else if (a.bits == 3)
+      e = hipFuncSetAttribute((const void *)rq_generic_kernel<3>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    else
+      e = hipFuncSetAttribute((const void *)rq_generic_kernel<4>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  switch (a.bits) {
+    case 2:
+      hipLaunchKernelGGL(rq_generic_kernel<2>, dim3(grid), dim3(kThreads), lds, a.stream, a.x,
+                         a.dtype, a.n_tok, a.d, a.h, sc, th, codes, zout, a.norms);
+      break;
+    case 3:
+      hipLaunchKernelGGL(rq_generic_kernel<3>, dim3(grid), dim3(kThreads), lds, a.stream, a.x,
+                         a.dtype, a.n_tok, a.d, a.h, sc, th, codes, zout, a.norms);
+      break;
+    case 4:
+      hipLaunchKernelGGL(rq_generic_kernel<4>, dim3(grid), dim3(kThreads), lds, a.stream, a.x,
+                         a.dtype, a.n_tok, a.d, a.h, sc, th, codes, zout, a.norms);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace oq

@@ -1,0 +1,148 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, solves the codebook on the host, and rejects bad
+arguments before making any HIP call.  Also checks the numpy unpacker the
+parity tests use against the oracle's."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import parity
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def q():
+    import quantization_dit_linear_amd as q
+    return q
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "orbitquant.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(oq_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol(q):
+    names = _declared()
+    assert "oq_linear" in names and "oq_rotate_quantize" in names
+    lib = ctypes.CDLL(q.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(q._SIGS), "binding and header disagree"
+
+
+def test_version_and_strerror(q):
+    assert q.lib().oq_version() >= 100
+    for s in (0, -1, -2, -3, -4, -99):
+        assert isinstance(q.strerror(s), str) and q.strerror(s)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_host_codebook_properties(q, bits):
+    d = 3072
+    lv, th = q.codebook(d, bits)
+    L = 1 << bits
+    assert lv.dtype == np.float32 and lv.shape == (L,) and th.shape == (L - 1,)
+    assert np.all(np.diff(lv) > 0)
+    assert np.array_equal(lv, -lv[::-1])
+    assert th[L // 2 - 1] == 0.0
+    ol, ot = oracle.codebook(d, bits)
+    assert np.allclose(lv, ol, rtol=2e-7, atol=0)
+    assert np.allclose(th, ot, rtol=2e-7, atol=1e-12)
+
+
+def test_codebook_rejects(q):
+    L = q.lib()
+    buf = np.zeros(16, np.float32)
+    assert L.oq_codebook(256, 5, buf.ctypes.data, buf.ctypes.data) == q.OQ_EUNSUPPORTED
+    assert L.oq_codebook(256, 0, buf.ctypes.data, buf.ctypes.data) == q.OQ_EUNSUPPORTED
+    assert L.oq_codebook(0, 4, buf.ctypes.data, buf.ctypes.data) == q.OQ_EINVAL
+    assert L.oq_codebook(256, 4, None, buf.ctypes.data) == q.OQ_EINVAL
+
+
+def test_codes_bytes(q):
+    assert q.codes_bytes(10, 3072, 4) == 10 * 1536
+    assert q.codes_bytes(3, 256, 3) == 3 * 96
+    assert q.codes_bytes(-1, 256, 3) == -1
+
+
+# Fake but aligned, non-null "device" addresses: every call below must be
+# rejected by validation before the library touches the GPU.
+A16, B16, C16 = 0x100000, 0x200000, 0x300000
+
+
+@pytest.mark.parametrize("fn", ["oq_rotate_quantize", "oq_prepare_weights"])
+def test_rotate_validation_rejects_before_hip(q, fn):
+    f = getattr(q.lib(), fn)
+    ok_args = dict(x=A16, dt=1, n=8, d=3072, seed=1, flags=0, bits=4, out=B16, nrm=C16)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return f(a["x"], a["dt"], a["n"], a["d"], a["seed"], a["flags"], a["bits"], a["out"],
+                 a["nrm"], None)
+
+    assert call(x=None) == q.OQ_EINVAL
+    assert call(out=None) == q.OQ_EINVAL
+    assert call(nrm=None) == q.OQ_EINVAL
+    assert call(x=A16 + 2) == q.OQ_EINVAL
+    assert call(out=B16 + 4) == q.OQ_EINVAL
+    assert call(nrm=C16 + 1) == q.OQ_EINVAL
+    assert call(dt=7) == q.OQ_EINVAL
+    assert call(flags=1 << 5) == q.OQ_EINVAL
+    assert call(n=-1) == q.OQ_EINVAL
+    assert call(d=0) == q.OQ_EINVAL
+    assert call(d=3000) == q.OQ_EUNSUPPORTED
+    assert call(d=32768) == q.OQ_EUNSUPPORTED
+    assert call(bits=1) == q.OQ_EUNSUPPORTED
+    assert call(bits=5) == q.OQ_EUNSUPPORTED
+    # empty input is a no-op that succeeds without any device work
+    assert call(n=0) == q.OQ_OK
+    assert call(n=0, x=None, out=None, nrm=None) == q.OQ_OK
+    assert call(n=0, d=3000) == q.OQ_EUNSUPPORTED
+    if fn == "oq_prepare_weights":
+        assert call(flags=q.OQ_OUT_F32_ROTATED) == q.OQ_EINVAL
+
+
+def test_linear_validation_rejects_before_hip(q):
+    f = q.lib().oq_linear
+    base = dict(a=A16, sa=C16, ba=4, w=B16, sw=C16, bw=4, M=16, N=16, K=3072, y=A16)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["a"], a["sa"], a["ba"], a["w"], a["sw"], a["bw"], a["M"], a["N"], a["K"],
+                 a["y"], None)
+
+    assert call(a=None) == q.OQ_EINVAL
+    assert call(w=None) == q.OQ_EINVAL
+    assert call(y=None) == q.OQ_EINVAL
+    assert call(sa=None) == q.OQ_EINVAL
+    assert call(a=A16 + 8) == q.OQ_EINVAL
+    assert call(y=A16 + 1) == q.OQ_EINVAL
+    assert call(M=-1) == q.OQ_EINVAL
+    assert call(K=100) == q.OQ_EUNSUPPORTED
+    assert call(ba=5) == q.OQ_EUNSUPPORTED
+    assert call(bw=1) == q.OQ_EUNSUPPORTED
+    assert call(M=0) == q.OQ_OK
+    assert call(N=0) == q.OQ_OK
+    assert call(M=0, a=None, y=None) == q.OQ_OK
+
+
+def test_binding_fails_loudly_without_gpu_tensors(q):
+    import torch
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        q.rotate_quantize(x, 1, 4)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_numpy_unpacker_agrees_with_oracle(bits):
+    rng = np.random.default_rng(bits)
+    d = 384
+    codes = rng.integers(0, 1 << bits, (5, d)).astype(np.uint8)
+    packed = np.stack([oracle.pack_row(c, bits) for c in codes])
+    assert np.array_equal(parity.unpack_codes(packed, d, bits), codes)

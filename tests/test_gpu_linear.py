@@ -1,0 +1,130 @@
+"""GPU parity of oq_linear against the oracle's fp64 dequantised GEMM
+(relative Frobenius error <= 2e-3), for every bit pair, ragged shapes, the
+workload shapes at full size (sampled output rows), and the whole path
+end to end."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests import parity
+from tests.gpu_util import bf16_to_np, host, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    import torch
+    import quantization_dit_linear_amd as q
+    assert torch.cuda.is_available()
+    q.lib()
+    return q
+
+
+def _run(q, ac, an, ba, wc, wn, bw, K):
+    import torch
+    y = q.linear(to_device(ac), to_device(an), ba, to_device(wc), to_device(wn), bw, K)
+    torch.cuda.synchronize()
+    return bf16_to_np(y)
+
+
+@pytest.mark.parametrize("ba", [2, 3, 4])
+@pytest.mark.parametrize("bw", [2, 3, 4])
+def test_bit_pairs_ragged(q, ba, bw):
+    M, N, K = 200, 136, 384
+    ac, an = wl.random_codes(M, K, ba, 10 + ba)
+    wc, wn = wl.random_codes(N, K, bw, 20 + bw)
+    say("linear", M, N, K, "a", ba, "w", bw)
+    y = _run(q, ac, an, ba, wc, wn, bw, K)
+    ref = oracle.linear(ac, an, ba, wc, wn, bw, K)
+    assert parity.rel_fro(y, ref) <= parity.LINEAR_FRO
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (1, 300, 256), (129, 1, 128), (64, 256, 256),
+                                   (257, 129, 1152)])
+def test_small_and_ragged_shapes(q, M, N, K):
+    ac, an = wl.random_codes(M, K, 4, M)
+    wc, wn = wl.random_codes(N, K, 4, N + 1)
+    say("linear", M, N, K)
+    y = _run(q, ac, an, 4, wc, wn, 4, K)
+    ref = oracle.linear(ac, an, 4, wc, wn, 4, K)
+    assert parity.rel_fro(y, ref) <= parity.LINEAR_FRO
+    # each output element individually within bf16 rounding + fp16 levels
+    assert np.all(np.abs(y - ref) <= 1e-2 * np.abs(ref).max() + 1e-30)
+
+
+def test_oracle_codes_realistic_distribution(q):
+    """Codes produced by the oracle's own quantizer on workload inputs (the
+    Lloyd-Max cell frequencies, not uniform), fed to both sides."""
+    lin = wl.get_linear("image_qkv", "qkv")
+    K = lin.act.d
+    x = wl.activations("image_qkv", "qkv", np.arange(160))
+    W = wl.weights("image_qkv", "qkv")[:96]
+    ac, an, _ = oracle.rotate_quantize(x, wl.BF16, K, lin.seed, 4)
+    wc, wn, _ = oracle.rotate_quantize(W, wl.BF16, K, lin.seed, 4)
+    say("linear oracle-codes", ac.shape, wc.shape)
+    y = _run(q, ac, an.astype(np.float32), 4, wc, wn.astype(np.float32), 4, K)
+    ref = oracle.linear(ac, an, 4, wc, wn, 4, K)
+    assert parity.rel_fro(y, ref) <= parity.LINEAR_FRO
+
+
+FULL = [("image_qkv", "qkv", 4, 4), ("image_mlp", "up", 4, 4), ("image_mlp", "down", 2, 4),
+        ("video_block", "qkv", 4, 4), ("video_block", "up", 3, 4),
+        ("video_block", "down", 4, 4), ("stress", "proj", 2, 3)]
+
+
+@pytest.mark.parametrize("cfg,name,bw,ba", FULL)
+def test_full_size_sampled_rows(q, cfg, name, bw, ba):
+    lin = wl.get_linear(cfg, name)
+    M, N, K = lin.act.M, lin.weight.N, lin.act.d
+    ac, an = wl.random_codes(M, K, ba, 31)
+    wc, wn = wl.random_codes(N, K, bw, 32)
+    say("linear full", cfg, name, M, N, K)
+    y = _run(q, ac, an, ba, wc, wn, bw, K)
+    rows = wl.sample_rows(M, 24, 2)
+    ref = oracle.linear(ac, an, ba, wc, wn, bw, K, rows=rows)
+    assert parity.rel_fro(y[rows], ref) <= parity.LINEAR_FRO
+
+
+def test_end_to_end_tiny(q):
+    """x, W -> prepare, rotate-quantize, linear on the GPU vs the same three
+    steps in the oracle, and the quantised product's distance to W x."""
+    import torch
+    lin = wl.get_linear("tiny", "tiny")
+    x = wl.activations("tiny", "tiny")
+    W = wl.weights("tiny", "tiny")
+    K = 256
+    say("end-to-end tiny")
+    wc, wn = q.prepare_weights(to_device(W), lin.seed, 4)
+    ac, an = q.rotate_quantize(to_device(x), lin.seed, 4)
+    y = q.linear(ac, an, 4, wc, wn, 4, K)
+    torch.cuda.synchronize()
+    y = bf16_to_np(y)
+    oac, oan, _ = oracle.rotate_quantize(x, wl.F32, K, lin.seed, 4)
+    owc, own, _ = oracle.rotate_quantize(W, wl.F32, K, lin.seed, 4)
+    ref = oracle.linear(oac, oan, 4, owc, own, 4, K)
+    assert parity.rel_fro(y, ref) <= parity.LINEAR_FRO
+    exact = x.astype(np.float64) @ W.astype(np.float64).T
+    assert parity.rel_fro(y, exact) < 0.3
+
+
+@pytest.mark.parametrize("cfg,name", [("image_qkv", "qkv"), ("video_block", "down")])
+def test_end_to_end_sampled(q, cfg, name):
+    import torch
+    lin = wl.get_linear(cfg, name)
+    bw, ba = lin.bit_pairs[0]
+    K = lin.act.d
+    x = wl.activations(cfg, name)
+    W = wl.weights(cfg, name)
+    say("end-to-end", cfg, name)
+    wc, wn = q.prepare_weights(to_device(W), lin.seed, bw)
+    ac, an = q.rotate_quantize(to_device(x), lin.seed, ba)
+    y = q.linear(ac, an, ba, wc, wn, bw, K)
+    torch.cuda.synchronize()
+    rows = wl.sample_rows(lin.act.M, 16, 4)
+    y = bf16_to_np(y[torch.as_tensor(rows, device="cuda")])
+    oac, oan, _ = oracle.rotate_quantize(x[rows], lin.act.dtype, K, lin.seed, ba)
+    owc, own, _ = oracle.rotate_quantize(W, lin.weight.dtype, K, lin.seed, bw)
+    ref = oracle.linear(oac, oan, ba, owc, own, bw, K)
+    assert parity.rel_fro(y, ref) <= parity.LINEAR_FRO

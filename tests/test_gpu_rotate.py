@@ -1,0 +1,137 @@
+"""GPU parity of oq_rotate_quantize / oq_prepare_weights against the oracle.
+
+Codes bit-exact except within 1e-6 of a decision boundary (at most 1e-4 of
+coordinates), norms and rotated values within 1e-5 relative -- on the same
+seeded inputs, across the five workload shapes, all bit widths and both
+sign modes, plus edge cases (zero tokens, one token, ragged counts, empty
+input).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests import parity
+from tests.gpu_util import host, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    import torch
+    import quantization_dit_linear_amd as q
+    assert torch.cuda.is_available()
+    q.lib()
+    return q
+
+
+def _thr(bits):
+    return oracle.codebook_unit(bits)[1]
+
+
+def _check_rows(q, x, dtype, d, seed, bits, signs, what):
+    say(what, x.shape, "bits", bits, "signs", signs)
+    xd = to_device(x)
+    codes, norms = q.rotate_quantize(xd, seed, bits, signs=signs)
+    z_gpu, n2 = q.rotate(xd, seed, signs=signs)
+    import torch
+    torch.cuda.synchronize()
+    rc, rn, rz = oracle.rotate_quantize(x, dtype, d, seed, bits, use_signs=signs, want_z=True)
+    n_mis = parity.assert_codes_match(host(codes), rc, rz, d, bits, _thr(bits), what)
+    parity.assert_norms_match(host(norms), rn, what)
+    parity.assert_norms_match(host(n2), rn, what)
+    parity.assert_rotated_match(host(z_gpu), rz, what)
+    return n_mis
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("signs", [True, False])
+def test_tiny_config_full(q, bits, signs):
+    lin = wl.get_linear("tiny", "tiny")
+    x = wl.activations("tiny", "tiny")
+    _check_rows(q, x, wl.F32, 256, lin.seed, bits, signs, "tiny")
+
+
+CASES = [("image_qkv", "qkv", 4), ("image_mlp", "up", 4), ("image_mlp", "down", 4),
+         ("video_block", "qkv", 4), ("video_block", "down", 4),
+         ("stress", "proj", 3), ("stress", "proj", 4), ("video_block", "up", 2)]
+
+
+@pytest.mark.parametrize("cfg,name,bits", CASES)
+@pytest.mark.parametrize("signs", [True, False])
+def test_workload_rows(q, cfg, name, bits, signs):
+    """A few hundred rows of every workload activation: several workgroup
+    batches plus a ragged tail."""
+    lin = wl.get_linear(cfg, name)
+    rows = np.arange(0, 300, dtype=np.int64)
+    x = wl.activations(cfg, name, rows)
+    _check_rows(q, x, lin.act.dtype, lin.act.d, lin.seed, bits, signs, f"{cfg}/{name}")
+
+
+def test_zero_tokens_and_single_token(q):
+    import torch
+    d = 3072
+    x = wl.custom_activations(37, d, wl.BF16, 5, n_out=30, out_factor=50.0, sigma_s=1.0,
+                              zero_rows=(0, 5, 36))
+    _check_rows(q, x, wl.BF16, d, 99, 4, True, "zero-tokens")
+    say("zero token codes")
+    codes, norms = q.rotate_quantize(to_device(x), 99, 4)
+    torch.cuda.synchronize()
+    allc = parity.unpack_codes(host(codes), d, 4)
+    assert (allc[[0, 5, 36]] == 8).all() and (host(norms)[[0, 5, 36]] == 0).all()
+    _check_rows(q, x[3:4], wl.BF16, d, 99, 4, True, "single-token")
+
+
+def test_empty_input_is_noop(q):
+    import torch
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
+    say("empty")
+    codes, norms = q.rotate_quantize(x, 1, 4)
+    torch.cuda.synchronize()
+    assert codes.shape == (0, 128) and norms.shape == (0,)
+
+
+@pytest.mark.parametrize("d", [128, 384, 640, 1152, 2048, 4096, 8192, 16384])
+def test_other_dimensions(q, d):
+    """Block sizes 128..16384 and odd block counts."""
+    x = wl.custom_activations(70, d, wl.BF16, d, n_out=3, out_factor=30.0, sigma_s=1.0)
+    _check_rows(q, x, wl.BF16, d, 7, 4, True, f"d={d}")
+
+
+@pytest.mark.parametrize("cfg,name,bits", [("tiny", "tiny", 4), ("image_qkv", "qkv", 4),
+                                           ("image_mlp", "down", 2), ("video_block", "down", 3)])
+def test_weight_prep_rows(q, cfg, name, bits):
+    import torch
+    lin = wl.get_linear(cfg, name)
+    W = wl.weights(cfg, name)[:200]
+    K = lin.weight.K
+    say("prepare_weights", cfg, name, W.shape)
+    codes, rn = q.prepare_weights(to_device(W), lin.seed, bits)
+    torch.cuda.synchronize()
+    rc, rr, rz = oracle.rotate_quantize(W, lin.weight.dtype, K, lin.seed, bits, want_z=True)
+    parity.assert_codes_match(host(codes), rc, rz, K, bits, _thr(bits), f"W {cfg}/{name}")
+    parity.assert_norms_match(host(rn), rr, f"W {cfg}/{name}")
+
+
+FULL = [("image_qkv", "qkv"), ("image_mlp", "up"), ("image_mlp", "down"),
+        ("video_block", "qkv"), ("video_block", "up"), ("video_block", "down"),
+        ("stress", "proj")]
+
+
+@pytest.mark.parametrize("cfg,name", FULL)
+def test_full_size_sampled_rows(q, cfg, name):
+    """The whole activation matrix at its real size, in the launch the
+    benchmark times; the oracle checks a seeded sample of rows."""
+    import torch
+    lin = wl.get_linear(cfg, name)
+    d, bits = lin.act.d, lin.bit_pairs[0][1]
+    x = wl.activations(cfg, name)
+    say("full", cfg, name, x.shape)
+    xd = to_device(x)
+    codes, norms = q.rotate_quantize(xd, lin.seed, bits)
+    torch.cuda.synchronize()
+    rows = wl.sample_rows(lin.act.M, 96, 1)
+    rc, rn, rz = oracle.rotate_quantize(x[rows], lin.act.dtype, d, lin.seed, bits, want_z=True)
+    parity.assert_codes_match(host(codes)[rows], rc, rz, d, bits, _thr(bits), f"{cfg}/{name}")
+    parity.assert_norms_match(host(norms)[rows], rn, f"{cfg}/{name}")
