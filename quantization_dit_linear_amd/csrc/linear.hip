@@ -6,14 +6,25 @@
 // codebooks folded into the 1/K of the epilogue).  llmdb.app Mathematical
 // Formulation: y = Q_w(W R^-1) Q_a(R x), bias-free.  Both code matrices are
 // K-contiguous rows in the same storage order, so the contraction runs over
-// storage slots directly.
+// storage slots directly; any fixed reordering of the slots inside a K step
+// applied to both operands leaves the sum unchanged.
 //
-// Tiling: a 256-thread workgroup owns a 128 x 128 output tile; per 64-slot
-// K step every thread decodes 32 activation codes and 32 weight codes
-// through a 16-entry fp16 lookup table into LDS, then each of the four
-// waves multiplies its 64 x 64 quadrant with v_mfma_f32_16x16x32_f16
-// (fp32 accumulation).  The epilogue scales by s_m r_n / K and rounds once
-// to bf16 (nearest even).
+// Design (one 256-thread workgroup per 256 x 256 output tile):
+//   * per 64-slot K step each thread owns one activation row and one weight
+//     row of the tile: it loads their 64 codes (8*b bytes each) one step
+//     ahead into registers;
+//   * codes become fp16 levels in registers through v_perm_b32 byte tables
+//     (the fp16 low and high bytes of the 2^b levels), no memory lookups;
+//   * the fp16 tiles go to LDS (double buffered, 16-byte chunks XOR-swizzled
+//     by row), one barrier per K step;
+//   * each wave multiplies a 128 x 128 quadrant with
+//     v_mfma_f32_16x16x32_f16 (fp32 accumulation), the weight fragment as
+//     the first operand so every lane ends up with 4 consecutive output
+//     columns;
+//   * epilogue: scale by s_m r_n / K, round once to bf16 (nearest even),
+//     8-byte stores.
+//   * workgroup -> tile order: contiguous per XCD, grouped along M so tiles
+//     resident together share activation rows in L2.
 #include <hip/hip_runtime.h>
 
 #include "oq_internal.h"
@@ -23,123 +34,282 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
+constexpr int TM = 256, TN = 256, KS = 64;  // tile and K step (slots)
+constexpr int ROWB = KS * 2;                 // bytes per fp16 tile row
+constexpr int OPB = TM * ROWB;               // bytes per operand tile
+constexpr int STAGEB = 2 * OPB;              // A + B per stage
+constexpr int LDS_BYTES = 2 * STAGEB;        // double buffered: 128 KB
+constexpr int GROUP_M = 8;
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Decode 32 consecutive codes of BITS bits (little-endian bit string at p,
-// 4*BITS bytes, 4-byte aligned) through lut into dst[0..31].
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Byte tables of one codebook for v_perm: lo[j] / hi[j] hold the low / high
+// bytes of the fp16 levels 4j .. 4j+3.
+struct PermTab {
+  uint32_t lo[4], hi[4];
+};
+
+// Four codes (one per byte, in the low BITS bits; higher bits ignored) ->
+// two dwords of fp16 pairs [F(c0), F(c1)], [F(c2), F(c3)].
 template <int BITS>
-__device__ __forceinline__ void decode32(const uint8_t *__restrict__ p,
-                                         const _Float16 *__restrict__ lut, _Float16 *dst) {
-  uint32_t w[BITS];
+__device__ __forceinline__ void lut4(uint32_t v, const PermTab &t, uint32_t &o0, uint32_t &o1) {
+  uint32_t lo, hi;
+  if constexpr (BITS == 4) {
+    const uint32_t s = v & 0x07070707u;
+    const uint32_t l0 = perm(t.lo[1], t.lo[0], s), l1 = perm(t.lo[3], t.lo[2], s);
+    const uint32_t h0 = perm(t.hi[1], t.hi[0], s), h1 = perm(t.hi[3], t.hi[2], s);
+    const uint32_t m = ((v >> 1) & 0x04040404u) | 0x03020100u;  // byte i: i, or 4+i if bit 3
+    lo = perm(l1, l0, m);
+    hi = perm(h1, h0, m);
+  } else if constexpr (BITS == 3) {
+    const uint32_t s = v & 0x07070707u;
+    lo = perm(t.lo[1], t.lo[0], s);
+    hi = perm(t.hi[1], t.hi[0], s);
+  } else {
+    const uint32_t s = v & 0x03030303u;
+    lo = perm(t.lo[0], t.lo[0], s);
+    hi = perm(t.hi[0], t.hi[0], s);
+  }
+  o0 = perm(hi, lo, 0x05010400u);
+  o1 = perm(hi, lo, 0x07030602u);
+}
+
+// Decode the 64 codes of one K step (8*BITS bytes in w) into 8 chunks of 8
+// fp16 levels.  Chunk q holds slots 8q + {0,2,4,6,1,3,5,7}: the same order
+// for every bit width, so activation and weight chunks always line up.
+template <int BITS>
+__device__ __forceinline__ void decode_step(const uint32_t *w, const PermTab &t, u32x4 *out) {
+  if constexpr (BITS == 4) {
 #pragma unroll
-  for (int i = 0; i < BITS; i++) w[i] = ((const uint32_t *)p)[i];
+    for (int q = 0; q < 8; q++) {
+      uint32_t a0, a1, b0, b1;
+      lut4<4>(w[q], t, a0, a1);       // even nibbles: slots 0,2,4,6
+      lut4<4>(w[q] >> 4, t, b0, b1);  // odd nibbles: slots 1,3,5,7
+      out[q] = u32x4{a0, a1, b0, b1};
+    }
+  } else if constexpr (BITS == 2) {
 #pragma unroll
-  for (int j = 0; j < 32; j++) {
-    const int bit = BITS * j;
-    uint32_t v = w[bit >> 5] >> (bit & 31);
-    if ((bit & 31) + BITS > 32) v |= w[(bit >> 5) + 1] << (32 - (bit & 31));
-    dst[j] = lut[v & ((1u << BITS) - 1u)];
+    for (int p = 0; p < 4; p++) {
+      const uint32_t x = w[p];  // slots 16p .. 16p+15, byte i of x>>2r holds slot 4i+r
+      const uint32_t v0 = x, v1 = x >> 2, v2 = x >> 4, v3 = x >> 6;
+      uint32_t a0, a1, b0, b1;
+      lut4<2>(perm(v2, v0, 0x05010400u), t, a0, a1);  // slots 0,2,4,6
+      lut4<2>(perm(v3, v1, 0x05010400u), t, b0, b1);  // slots 1,3,5,7
+      out[2 * p] = u32x4{a0, a1, b0, b1};
+      lut4<2>(perm(v2, v0, 0x07030602u), t, a0, a1);  // slots 8,10,12,14
+      lut4<2>(perm(v3, v1, 0x07030602u), t, b0, b1);  // slots 9,11,13,15
+      out[2 * p + 1] = u32x4{a0, a1, b0, b1};
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      // slots 8q..8q+7 occupy bits [24q, 24q+24) of the 192-bit string
+      const int bit = 24 * q, wd = bit >> 5, sh = bit & 31;
+      uint32_t g = w[wd] >> sh;
+      if (sh > 8) g |= w[wd + 1] << (32 - sh);
+      const uint32_t ev = (g & 7u) | ((g >> 6) & 7u) << 8 | ((g >> 12) & 7u) << 16 |
+                          ((g >> 18) & 7u) << 24;
+      const uint32_t od = ((g >> 3) & 7u) | ((g >> 9) & 7u) << 8 | ((g >> 15) & 7u) << 16 |
+                          ((g >> 21) & 7u) << 24;
+      uint32_t a0, a1, b0, b1;
+      lut4<3>(ev, t, a0, a1);
+      lut4<3>(od, t, b0, b1);
+      out[q] = u32x4{a0, a1, b0, b1};
+    }
+  }
+}
+
+__device__ __forceinline__ int chunk_off(int row, int chunk) {
+  return row * ROWB + ((chunk ^ (row & 7)) << 4);
+}
+
+template <int BITS>
+__device__ __forceinline__ void load_codes(const uint8_t *p, uint32_t *w) {
+  if constexpr (BITS == 4) {
+    const u32x4 a = *(const u32x4 *)p, b = *(const u32x4 *)(p + 16);
+    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
+    w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
+  } else if constexpr (BITS == 2) {
+    const u32x4 a = *(const u32x4 *)p;
+    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
+  } else {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 a = *(const u32x2 *)p, b = *(const u32x2 *)(p + 8), c = *(const u32x2 *)(p + 16);
+    w[0] = a[0]; w[1] = a[1]; w[2] = b[0]; w[3] = b[1]; w[4] = c[0]; w[5] = c[1];
   }
 }
 
 template <int BA, int BW>
-__global__ __launch_bounds__(256) void linear_kernel(
+__global__ __launch_bounds__(256, 1) void linear_kernel(
     const uint8_t *__restrict__ A, const float *__restrict__ sa, const uint8_t *__restrict__ Wc,
-    const float *__restrict__ sw, int64_t M, int64_t N, int K, uint16_t *__restrict__ Y,
-    LevelsF16 la, LevelsF16 lw) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[BM][LDK];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[BN][LDK];
-  __shared__ _Float16 luta[16], lutw[16];
+    const float *__restrict__ sw, int M, int N, int K, uint16_t *__restrict__ Y, PermTab ta,
+    PermTab tw, int vec_store) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-  if (tid < 16) {
-    luta[tid] = __builtin_bit_cast(_Float16, la.v[tid]);
-    lutw[tid] = __builtin_bit_cast(_Float16, lw.v[tid]);
-  }
-  floatx4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // ---- workgroup -> tile (contiguous per XCD, grouped along M)
+  const int nbm = (M + TM - 1) / TM, nbn = (N + TN - 1) / TN, total = nbm * nbn;
+  int bid = blockIdx.x;
+  {
+    const int xcd = bid & 7, local = bid >> 3, per = total >> 3, rem = total & 7;
+    bid = xcd * per + (xcd < rem ? xcd : rem) + local;
+  }
+  const int gsz = GROUP_M * nbn, grp = bid / gsz, first_m = grp * GROUP_M;
+  const int gm = (nbm - first_m) < GROUP_M ? (nbm - first_m) : GROUP_M;
+  const int tm = first_m + (bid % gsz) % gm, tn = (bid % gsz) / gm;
+  const int m0 = tm * TM, n0 = tn * TN;
+
+  // ---- per-thread code rows
   const int64_t arow = (int64_t)K * BA / 8, wrow = (int64_t)K * BW / 8;
-  const int lr = tid >> 1, lh = tid & 1;
-  const int64_t am = (m0 + lr < M) ? m0 + lr : M - 1;
-  const int64_t wnr = (n0 + lr < N) ? n0 + lr : N - 1;
-  const uint8_t *pa = A + am * arow + lh * 4 * BA;
-  const uint8_t *pw = Wc + wnr * wrow + lh * 4 * BW;
+  const int am = (m0 + tid < M) ? m0 + tid : M - 1;
+  const int wr = (n0 + tid < N) ? n0 + tid : N - 1;
+  const uint8_t *pa = A + (int64_t)am * arow;
+  const uint8_t *pw = Wc + (int64_t)wr * wrow;
+  const int T = K / KS;
 
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    __syncthreads();
-    {
-      _Float16 tmp[32];
-      decode32<BA>(pa + (int64_t)k0 * BA / 8, luta, tmp);
+  uint32_t ca[2 * BA], cw[2 * BW];
+  floatx4 acc[8][8];
 #pragma unroll
-      for (int q = 0; q < 4; q++)
-        *(half8 *)&As[lr][32 * lh + 8 * q] =
-            half8{tmp[8 * q], tmp[8 * q + 1], tmp[8 * q + 2], tmp[8 * q + 3], tmp[8 * q + 4],
-                  tmp[8 * q + 5], tmp[8 * q + 6], tmp[8 * q + 7]};
-      decode32<BW>(pw + (int64_t)k0 * BW / 8, lutw, tmp);
+  for (int j = 0; j < 8; j++)
 #pragma unroll
-      for (int q = 0; q < 4; q++)
-        *(half8 *)&Bs[lr][32 * lh + 8 * q] =
-            half8{tmp[8 * q], tmp[8 * q + 1], tmp[8 * q + 2], tmp[8 * q + 3], tmp[8 * q + 4],
-                  tmp[8 * q + 5], tmp[8 * q + 6], tmp[8 * q + 7]};
+    for (int i = 0; i < 8; i++) acc[j][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto stage_codes = [&](int stage) {
+    u32x4 da[8], dw[8];
+    decode_step<BA>(ca, ta, da);
+    decode_step<BW>(cw, tw, dw);
+    uint8_t *sA = lds + stage * STAGEB;
+    uint8_t *sB = sA + OPB;
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      *(u32x4 *)(sA + chunk_off(tid, q)) = da[q];
+      *(u32x4 *)(sB + chunk_off(tid, q)) = dw[q];
     }
-    __syncthreads();
+  };
+
+  // One K step of MFMA work on LDS stage `cur`: two 32-slot halves.
+  auto mfma_step = [&](int cur) {
+    const uint8_t *sA = lds + cur * STAGEB;
+    const uint8_t *sB = sA + OPB;
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ks++) {
-      half8 af[4], bf[4];
+    for (int ks = 0; ks < 2; ks++) {
+      half8 af[8], bf[8];
+      const int ch = 4 * ks + (lane >> 4);
 #pragma unroll
-      for (int i = 0; i < 4; i++)
-        af[i] = *(const half8 *)&As[wm * 64 + 16 * i + (lane & 15)][32 * ks + 8 * (lane >> 4)];
+      for (int i = 0; i < 8; i++)
+        af[i] = *(const half8 *)(sA + chunk_off(wm * 128 + 16 * i + (lane & 15), ch));
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        bf[j] = *(const half8 *)&Bs[wn * 64 + 16 * j + (lane & 15)][32 * ks + 8 * (lane >> 4)];
+      for (int j = 0; j < 8; j++)
+        bf[j] = *(const half8 *)(sB + chunk_off(wn * 128 + 16 * j + (lane & 15), ch));
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int j = 0; j < 8; j++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < 8; i++)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[j], af[i], acc[j][i], 0, 0, 0);
     }
+  };
+
+  load_codes<BA>(pa, ca);
+  load_codes<BW>(pw, cw);
+  stage_codes(0);
+  if (T > 1) {
+    load_codes<BA>(pa + 8 * BA, ca);
+    load_codes<BW>(pw + 8 * BW, cw);
   }
 
-  const float invk = 1.0f / (float)K;
+  // Steady state: the barrier opens the body, and the rest is branch-free so
+  // the scheduler can interleave the MFMAs of step t with the decode of step
+  // t+1 (a single wave per SIMD has nothing else to overlap them with).
+  for (int t = 0; t + 1 < T; t++) {
+    __syncthreads();  // stage t&1 complete; stage (t+1)&1 no longer read
+    mfma_step(t & 1);
+    stage_codes((t + 1) & 1);
+    const int nxt = (t + 2 < T) ? t + 2 : T - 1;  // the last step re-reads harmlessly
+    load_codes<BA>(pa + (int64_t)nxt * 8 * BA, ca);
+    load_codes<BW>(pw + (int64_t)nxt * 8 * BW, cw);
+    // per half step: its fragment reads, then 64 x (1 MFMA + 3 VALU)
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+    for (int h = 0; h < 2; h++) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int64_t col = n0 + wn * 64 + 16 * j + (lane & 15);
-      if (col >= N) continue;
-      const float rn = sw[col] * invk;
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int64_t row = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + r;
-        if (row < M) Y[row * N + col] = f32_to_bf16_rne(acc[i][j][r] * sa[row] * rn);
+      for (int r = 0; r < 64; r++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
     }
+  }
+  __syncthreads();
+  mfma_step((T - 1) & 1);
+
+  // ---- epilogue: lane holds rows m = .. + (lane & 15), cols n = .. + 4 (lane >> 4) + r
+  const float invk = 1.0f / (float)K;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int m = m0 + wm * 128 + 16 * i + (lane & 15);
+    if (m >= M) continue;
+    const float s = sa[m] * invk;
+    uint16_t *yrow = Y + (int64_t)m * N;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int n = n0 + wn * 128 + 16 * j + 4 * (lane >> 4);
+      if (vec_store && n + 3 < N) {
+        const floatx4 r = *(const floatx4 *)(sw + n);
+        const uint32_t lo = f32_to_bf16_rne(acc[j][i][0] * s * r[0]) |
+                            (f32_to_bf16_rne(acc[j][i][1] * s * r[1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(acc[j][i][2] * s * r[2]) |
+                            (f32_to_bf16_rne(acc[j][i][3] * s * r[3]) << 16);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        *(u32x2 *)(yrow + n) = u32x2{lo, hi};
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+          if (n + r < N) yrow[n + r] = (uint16_t)f32_to_bf16_rne(acc[j][i][r] * s * sw[n + r]);
+      }
+    }
+  }
+}
+
+PermTab make_tab(const LevelsF16 &lv) {
+  PermTab t{};
+  for (int e = 0; e < 16; e++) {
+    t.lo[e >> 2] |= (uint32_t)(lv.v[e] & 0xFFu) << (8 * (e & 3));
+    t.hi[e >> 2] |= (uint32_t)(lv.v[e] >> 8) << (8 * (e & 3));
+  }
+  return t;
 }
 
 template <int BA, int BW>
 hipError_t launch_ab(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw) {
-  dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
-  hipLaunchKernelGGL((linear_kernel<BA, BW>), grid, dim3(256), 0, a.stream, a.a_codes, a.a_norms,
-                     a.w_codes, a.w_norms, a.M, a.N, a.K, a.y, la, lw);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)linear_kernel<BA, BW>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t tiles = ((a.M + TM - 1) / TM) * ((a.N + TN - 1) / TN);
+  const int vec = (a.N % 4 == 0) && (((uintptr_t)a.y & 7) == 0) && (((uintptr_t)a.w_norms & 15) == 0);
+  hipLaunchKernelGGL((linear_kernel<BA, BW>), dim3((unsigned)tiles), dim3(256), LDS_BYTES,
+                     a.stream, a.a_codes, a.a_norms, a.w_codes, a.w_norms, (int)a.M, (int)a.N,
+                     a.K, a.y, make_tab(la), make_tab(lw), vec);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_linear(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw) {
-  if ((a.M + BM - 1) / BM > 65535) return hipErrorInvalidValue;
+  if (a.M > (int64_t)1 << 30 || a.N > (int64_t)1 << 30) return hipErrorInvalidValue;
 #define OQ_CASE(x, y) \
   if (a.a_bits == x && a.w_bits == y) return launch_ab<x, y>(a, la, lw);
   OQ_CASE(2, 2) OQ_CASE(2, 3) OQ_CASE(2, 4)

@@ -163,29 +163,100 @@ int get_plan(int d, uint64_t seed, hipStream_t stream, const oq::DevicePlan **ou
   std::vector<uint8_t> neg;
   build_plan(d, seed, perm, neg);
   std::vector<int32_t> sc(d), sc0(d);
+  std::vector<uint32_t> fsc(d), fsg(d / 2), fz(d / 2, 0u);
   for (int i = 0; i < d; i++) {
     sc[perm[i]] = i | (neg[i] ? (int32_t)0x80000000 : 0);
     sc0[perm[i]] = i;
+    fsc[perm[i]] = 2u * (uint32_t)i;  // source j = pi(i) goes to byte 2i
+  }
+  for (int j = 0; j < d; j += 2) {
+    const int i0 = sc0[j], i1 = sc0[j + 1];
+    fsg[j / 2] = (neg[i0] ? 0x8000u : 0u) | (neg[i1] ? 0x80000000u : 0u);
   }
   oq::DevicePlan p;
   p.d = d;
   p.h = d & -d;
-  if (hipMalloc(&p.scatter, sizeof(int32_t) * d) != hipSuccess) return OQ_ENOMEM;
-  if (hipMalloc(&p.scatter_nosign, sizeof(int32_t) * d) != hipSuccess) {
-    (void)hipFree(p.scatter);
-    return OQ_ENOMEM;
+  struct Up {
+    void **dst;
+    const void *src;
+    size_t bytes;
+  } ups[] = {{(void **)&p.scatter, sc.data(), sizeof(int32_t) * d},
+             {(void **)&p.scatter_nosign, sc0.data(), sizeof(int32_t) * d},
+             {(void **)&p.fast_scatter, fsc.data(), sizeof(uint32_t) * d},
+             {(void **)&p.fast_signs, fsg.data(), sizeof(uint32_t) * (d / 2)},
+             {(void **)&p.fast_nosigns, fz.data(), sizeof(uint32_t) * (d / 2)}};
+  int rc = OQ_OK;
+  for (auto &u : ups) {
+    if (hipMalloc(u.dst, u.bytes) != hipSuccess) {
+      rc = OQ_ENOMEM;
+      break;
+    }
+    // synchronous upload: the host vectors go out of scope afterwards
+    if (hipMemcpy(*u.dst, u.src, u.bytes, hipMemcpyHostToDevice) != hipSuccess) {
+      rc = OQ_EDEVICE;
+      break;
+    }
   }
-  // synchronous upload: the host vectors go out of scope afterwards
-  if (hipMemcpy(p.scatter, sc.data(), sizeof(int32_t) * d, hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(p.scatter_nosign, sc0.data(), sizeof(int32_t) * d, hipMemcpyHostToDevice) !=
-          hipSuccess) {
-    (void)hipFree(p.scatter);
-    (void)hipFree(p.scatter_nosign);
-    return OQ_EDEVICE;
+  if (rc != OQ_OK) {
+    for (auto &u : ups)
+      if (*u.dst) (void)hipFree(*u.dst);
+    return rc;
   }
   (void)stream;
   auto res = g_plans.emplace(key, p);
   *out = &res.first->second;
+  return OQ_OK;
+}
+
+// Cell table of the fast path's quantizer for one bit width.  Cell c of the
+// grid (step delta = 1/8 in unit space) receives the values u with
+// round(2 u / delta + 2048) in {2c, 2c+1}, i.e. u in [delta (c - 1024.25),
+// delta (c - 1023.25)); widened by a margin it contains at most one
+// threshold.  Entry = byte offset of (slot copy s, base code) inside the
+// kernel's per-wave threshold table: 128 s + 8 base, base = the code at the
+// window's lower edge.
+int build_cells(int bits, std::vector<uint16_t> &out) {
+  double lv[16], th[15];
+  unit_codebook(bits, lv, th);
+  const int T = (1 << bits) - 1;
+  const double delta = 0.125, eps = 0.02 * delta;
+  out.assign(4 * oq::kFastCells, 0);
+  for (int c = 0; c < oq::kFastCells; c++) {
+    const double lo = delta * (c - 1024.25) - eps, hi = delta * (c - 1023.25) + eps;
+    int base = 0, inside = 0;
+    for (int k = 0; k < T; k++) {
+      if ((double)(float)th[k] <= lo) base++;
+      else if ((double)(float)th[k] <= hi) inside++;
+    }
+    if (inside > 1) return OQ_EUNSUPPORTED;  // grid too coarse for this codebook
+    for (int s = 0; s < 4; s++) out[s * oq::kFastCells + c] = (uint16_t)(128 * s + 8 * base);
+  }
+  return OQ_OK;
+}
+
+std::mutex g_cell_mu;
+std::map<std::pair<int, int>, uint16_t *> g_cells;  // (device, bits) -> table
+
+int get_cells(int bits, const uint16_t **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return OQ_EDEVICE;
+  std::lock_guard<std::mutex> g(g_cell_mu);
+  auto it = g_cells.find({dev, bits});
+  if (it != g_cells.end()) {
+    *out = it->second;
+    return OQ_OK;
+  }
+  std::vector<uint16_t> tab;
+  int rc = build_cells(bits, tab);
+  if (rc != OQ_OK) return rc;
+  uint16_t *dptr = nullptr;
+  if (hipMalloc(&dptr, tab.size() * 2) != hipSuccess) return OQ_ENOMEM;
+  if (hipMemcpy(dptr, tab.data(), tab.size() * 2, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(dptr);
+    return OQ_EDEVICE;
+  }
+  g_cells[{dev, bits}] = dptr;
+  *out = dptr;
   return OQ_OK;
 }
 
@@ -231,6 +302,15 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
   a.out = out;
   a.norms = norms;
   a.stream = (hipStream_t)stream;
+  if (a.dtype == OQ_BF16 && !a.rotated_out) {
+    const uint16_t *cells = nullptr;
+    rc = get_cells(bits, &cells);
+    if (rc != OQ_OK) return rc;
+    bool handled = false;
+    hipError_t e = oq::launch_rotate_quantize_fast(
+        a, plan->fast_scatter, a.signs ? plan->fast_signs : plan->fast_nosigns, cells, t, &handled);
+    if (handled) return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
+  }
   hipError_t e = oq::launch_rotate_quantize_generic(a, *plan, t);
   return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
 }
@@ -315,11 +395,22 @@ int oq_release_plans(void) {
     int cur = 0;
     (void)hipGetDevice(&cur);
     if (hipSetDevice(kv.first.dev) != hipSuccess) rc = OQ_EDEVICE;
-    if (kv.second.scatter) (void)hipFree(kv.second.scatter);
-    if (kv.second.scatter_nosign) (void)hipFree(kv.second.scatter_nosign);
+    for (void *ptr : {(void *)kv.second.scatter, (void *)kv.second.scatter_nosign,
+                      (void *)kv.second.fast_scatter, (void *)kv.second.fast_signs,
+                      (void *)kv.second.fast_nosigns})
+      if (ptr) (void)hipFree(ptr);
     (void)hipSetDevice(cur);
   }
   g_plans.clear();
+  std::lock_guard<std::mutex> gc(g_cell_mu);
+  for (auto &kv : g_cells) {
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    if (hipSetDevice(kv.first.first) != hipSuccess) rc = OQ_EDEVICE;
+    (void)hipFree(kv.second);
+    (void)hipSetDevice(cur);
+  }
+  g_cells.clear();
   return rc;
 }
 

@@ -27,6 +27,12 @@ struct DevicePlan {
   // the sign applied at that destination is negative.
   int32_t *scatter = nullptr;         // with signs
   int32_t *scatter_nosign = nullptr;  // signs dropped
+  // tables of the bf16 fast path: byte offset 2 pi^-1(j) of every source
+  // element j inside a token's LDS copy, and per source dword the XOR mask
+  // that applies the destination's sign to both bf16 halves.
+  uint32_t *fast_scatter = nullptr;
+  uint32_t *fast_signs = nullptr;
+  uint32_t *fast_nosigns = nullptr;
 };
 
 struct RotateArgs {
@@ -44,6 +50,12 @@ struct RotateArgs {
 // Kernel launchers (defined in the .hip files).  Return a hipError_t.
 hipError_t launch_rotate_quantize_generic(const RotateArgs &a, const DevicePlan &p,
                                           const Thresholds &th);
+// bf16 fast path; sets *handled = false (and does nothing) for shapes it does
+// not cover.  cells: the quantizer's cell table for a.bits (fast_cell_table).
+hipError_t launch_rotate_quantize_fast(const RotateArgs &a, const uint32_t *scat,
+                                       const uint32_t *smask, const uint16_t *cells,
+                                       const Thresholds &th, bool *handled);
+constexpr int kFastCells = 2048;  // cells per copy of the fast path's cell table
 
 struct LinearArgs {
   const uint8_t *a_codes;
