@@ -9,18 +9,19 @@
 // storage slots directly; any fixed reordering of the slots inside a K step
 // applied to both operands leaves the sum unchanged.
 //
-// Design (one 256-thread workgroup per 256 x 256 output tile):
-//   * per 64-slot K step each thread owns one activation row and one weight
-//     row of the tile: it loads their 64 codes (8*b bytes each) one step
-//     ahead into registers;
+// Design (one 512-thread workgroup per 256 x 256 output tile):
+//   * per 64-slot K step each thread owns one row of the tile (waves 0-3
+//     the 256 activation rows, waves 4-7 the 256 weight rows): it loads the
+//     row's 64 codes (8*b bytes) one step ahead into registers;
 //   * codes become fp16 levels in registers through v_perm_b32 byte tables
 //     (the fp16 low and high bytes of the 2^b levels), no memory lookups;
 //   * the fp16 tiles go to LDS (double buffered, 16-byte chunks XOR-swizzled
 //     by row), one barrier per K step;
-//   * each wave multiplies a 128 x 128 quadrant with
+//   * each of the 8 waves multiplies a 128 x 64 block with
 //     v_mfma_f32_16x16x32_f16 (fp32 accumulation), the weight fragment as
 //     the first operand so every lane ends up with 4 consecutive output
-//     columns;
+//     columns; two waves per SIMD let one wave's MFMAs overlap the other's
+//     decode;
 //   * epilogue: scale by s_m r_n / K, round once to bf16 (nearest even),
 //     8-byte stores.
 //   * workgroup -> tile order: contiguous per XCD, grouped along M so tiles
@@ -150,13 +151,13 @@ __device__ __forceinline__ void load_codes(const uint8_t *p, uint32_t *w) {
 }
 
 template <int BA, int BW>
-__global__ __launch_bounds__(256, 1) void linear_kernel(
+__global__ __launch_bounds__(512, 1) void linear_kernel(
     const uint8_t *__restrict__ A, const float *__restrict__ sa, const uint8_t *__restrict__ Wc,
     const float *__restrict__ sw, int M, int N, int K, uint16_t *__restrict__ Y, PermTab ta,
     PermTab tw, int vec_store) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
   // ---- workgroup -> tile (contiguous per XCD, grouped along M)
   const int nbm = (M + TM - 1) / TM, nbn = (N + TN - 1) / TN, total = nbm * nbn;
@@ -172,30 +173,27 @@ __global__ __launch_bounds__(256, 1) void linear_kernel(
 
   // ---- per-thread code rows
   const int64_t arow = (int64_t)K * BA / 8, wrow = (int64_t)K * BW / 8;
-  const int am = (m0 + tid < M) ? m0 + tid : M - 1;
-  const int wr = (n0 + tid < N) ? n0 + tid : N - 1;
+  const bool is_a = tid < 256;  // waves 0-3 decode activation rows, 4-7 weight rows
+  const int row = tid & 255;
+  const int am = (m0 + row < M) ? m0 + row : M - 1;
+  const int wr = (n0 + row < N) ? n0 + row : N - 1;
   const uint8_t *pa = A + (int64_t)am * arow;
   const uint8_t *pw = Wc + (int64_t)wr * wrow;
   const int T = K / KS;
 
   uint32_t ca[2 * BA], cw[2 * BW];
-  floatx4 acc[8][8];
+  floatx4 acc[4][8];
 #pragma unroll
-  for (int j = 0; j < 8; j++)
+  for (int j = 0; j < 4; j++)
 #pragma unroll
     for (int i = 0; i < 8; i++) acc[j][i] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   auto stage_codes = [&](int stage) {
-    u32x4 da[8], dw[8];
-    decode_step<BA>(ca, ta, da);
-    decode_step<BW>(cw, tw, dw);
-    uint8_t *sA = lds + stage * STAGEB;
-    uint8_t *sB = sA + OPB;
+    u32x4 d[8];
+    uint8_t *dst = lds + stage * STAGEB + (is_a ? 0 : OPB);
+    if (is_a) decode_step<BA>(ca, ta, d); else decode_step<BW>(cw, tw, d);
 #pragma unroll
-    for (int q = 0; q < 8; q++) {
-      *(u32x4 *)(sA + chunk_off(tid, q)) = da[q];
-      *(u32x4 *)(sB + chunk_off(tid, q)) = dw[q];
-    }
+    for (int q = 0; q < 8; q++) *(u32x4 *)(dst + chunk_off(row, q)) = d[q];
   };
 
   // One K step of MFMA work on LDS stage `cur`: two 32-slot halves.
@@ -204,50 +202,38 @@ __global__ __launch_bounds__(256, 1) void linear_kernel(
     const uint8_t *sB = sA + OPB;
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
-      half8 af[8], bf[8];
+      half8 af[8], bf[4];
       const int ch = 4 * ks + (lane >> 4);
 #pragma unroll
       for (int i = 0; i < 8; i++)
         af[i] = *(const half8 *)(sA + chunk_off(wm * 128 + 16 * i + (lane & 15), ch));
 #pragma unroll
-      for (int j = 0; j < 8; j++)
-        bf[j] = *(const half8 *)(sB + chunk_off(wn * 128 + 16 * j + (lane & 15), ch));
+      for (int j = 0; j < 4; j++)
+        bf[j] = *(const half8 *)(sB + chunk_off(wn * 64 + 16 * j + (lane & 15), ch));
 #pragma unroll
-      for (int j = 0; j < 8; j++)
+      for (int j = 0; j < 4; j++)
 #pragma unroll
         for (int i = 0; i < 8; i++)
           acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[j], af[i], acc[j][i], 0, 0, 0);
     }
   };
 
-  load_codes<BA>(pa, ca);
-  load_codes<BW>(pw, cw);
+  auto load_step = [&](int t) {
+    if (is_a) load_codes<BA>(pa + (int64_t)t * 8 * BA, ca);
+    else load_codes<BW>(pw + (int64_t)t * 8 * BW, cw);
+  };
+  load_step(0);
   stage_codes(0);
-  if (T > 1) {
-    load_codes<BA>(pa + 8 * BA, ca);
-    load_codes<BW>(pw + 8 * BW, cw);
-  }
+  if (T > 1) load_step(1);
 
-  // Steady state: the barrier opens the body, and the rest is branch-free so
-  // the scheduler can interleave the MFMAs of step t with the decode of step
-  // t+1 (a single wave per SIMD has nothing else to overlap them with).
+  // Steady state: the barrier opens the body; the decode of step t+1 and the
+  // MFMAs of step t run in the same branch-free block.
   for (int t = 0; t + 1 < T; t++) {
     __syncthreads();  // stage t&1 complete; stage (t+1)&1 no longer read
     mfma_step(t & 1);
     stage_codes((t + 1) & 1);
     const int nxt = (t + 2 < T) ? t + 2 : T - 1;  // the last step re-reads harmlessly
-    load_codes<BA>(pa + (int64_t)nxt * 8 * BA, ca);
-    load_codes<BW>(pw + (int64_t)nxt * 8 * BW, cw);
-    // per half step: its fragment reads, then 64 x (1 MFMA + 3 VALU)
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-#pragma unroll
-      for (int r = 0; r < 64; r++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-      }
-    }
+    load_step(nxt);
   }
   __syncthreads();
   mfma_step((T - 1) & 1);
@@ -261,8 +247,8 @@ __global__ __launch_bounds__(256, 1) void linear_kernel(
     const float s = sa[m] * invk;
     uint16_t *yrow = Y + (int64_t)m * N;
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const int n = n0 + wn * 128 + 16 * j + 4 * (lane >> 4);
+    for (int j = 0; j < 4; j++) {
+      const int n = n0 + wn * 64 + 16 * j + 4 * (lane >> 4);
       if (vec_store && n + 3 < N) {
         const floatx4 r = *(const floatx4 *)(sw + n);
         const uint32_t lo = f32_to_bf16_rne(acc[j][i][0] * s * r[0]) |
@@ -300,7 +286,7 @@ hipError_t launch_ab(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &
   }
   const int64_t tiles = ((a.M + TM - 1) / TM) * ((a.N + TN - 1) / TN);
   const int vec = (a.N % 4 == 0) && (((uintptr_t)a.y & 7) == 0) && (((uintptr_t)a.w_norms & 15) == 0);
-  hipLaunchKernelGGL((linear_kernel<BA, BW>), dim3((unsigned)tiles), dim3(256), LDS_BYTES,
+  hipLaunchKernelGGL((linear_kernel<BA, BW>), dim3((unsigned)tiles), dim3(512), LDS_BYTES,
                      a.stream, a.a_codes, a.a_norms, a.w_codes, a.w_norms, (int)a.M, (int)a.N,
                      a.K, a.y, make_tab(la), make_tab(lw), vec);
   return hipGetLastError();

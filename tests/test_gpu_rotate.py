@@ -92,7 +92,7 @@ def test_empty_input_is_noop(q):
     assert codes.shape == (0, 128) and norms.shape == (0,)
 
 
-@pytest.mark.parametrize("d", [128, 384, 640, 1152, 2048, 4096, 8192, 16384])
+@pytest.mark.parametrize("d", [128, 384, 640, 1024, 1152, 2048, 4096, 8192, 16384])
 def test_other_dimensions(q, d):
     """Block sizes 128..16384 and odd block counts."""
     x = wl.custom_activations(70, d, wl.BF16, d, n_out=3, out_factor=30.0, sigma_s=1.0)
