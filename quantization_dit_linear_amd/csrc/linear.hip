@@ -226,14 +226,24 @@ __global__ __launch_bounds__(512, 1) void linear_kernel(
   stage_codes(0);
   if (T > 1) load_step(1);
 
-  // Steady state: the barrier opens the body; the decode of step t+1 and the
-  // MFMAs of step t run in the same branch-free block.
+  // Steady state: the barrier opens the body, then the MFMAs of step t and
+  // the decode of step t+1.
+  // The two waves of each SIMD (w and w+4) run the step's two phases in
+  // opposite orders, so one wave's MFMAs overlap the other's decode on the
+  // same SIMD instead of both waiting on the same unit.
+  const bool mfma_first = wave < 4;
   for (int t = 0; t + 1 < T; t++) {
     __syncthreads();  // stage t&1 complete; stage (t+1)&1 no longer read
-    mfma_step(t & 1);
-    stage_codes((t + 1) & 1);
     const int nxt = (t + 2 < T) ? t + 2 : T - 1;  // the last step re-reads harmlessly
-    load_step(nxt);
+    if (mfma_first) {
+      mfma_step(t & 1);
+      stage_codes((t + 1) & 1);
+      load_step(nxt);
+    } else {
+      stage_codes((t + 1) & 1);
+      load_step(nxt);
+      mfma_step(t & 1);
+    }
   }
   __syncthreads();
   mfma_step((T - 1) & 1);
