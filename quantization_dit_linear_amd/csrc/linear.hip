@@ -10,22 +10,31 @@
 // applied to both operands leaves the sum unchanged.
 //
 // Design (one 512-thread workgroup per 256 x 256 output tile):
-//   * per 64-slot K step each thread owns one row of the tile (waves 0-3
-//     the 256 activation rows, waves 4-7 the 256 weight rows): it loads the
-//     row's 64 codes (8*b bytes) one step ahead into registers;
-//   * codes become fp16 levels in registers through v_perm_b32 byte tables
-//     (the fp16 low and high bytes of the 2^b levels), no memory lookups;
-//   * the fp16 tiles go to LDS (double buffered, 16-byte chunks XOR-swizzled
-//     by row), one barrier per K step;
+//   * every thread owns one row of the tile (waves 0-3 the 256 activation
+//     rows, waves 4-7 the 256 weight rows) and, per 64-slot K step, turns
+//     the row's 64 codes into fp16 levels with v_perm_b32 byte tables (the
+//     fp16 low and high bytes of the 2^b levels; no memory lookups);
+//   * decoded tiles live in LDS, double buffered, as 8 planes of 256 rows x
+//     16 bytes (one plane per 8-slot chunk): the decode stores and the MFMA
+//     fragment loads both touch consecutive 16-byte words, so neither has
+//     bank conflicts and every offset is an instruction immediate;
 //   * each of the 8 waves multiplies a 128 x 64 block with
-//     v_mfma_f32_16x16x32_f16 (fp32 accumulation), the weight fragment as
-//     the first operand so every lane ends up with 4 consecutive output
-//     columns; two waves per SIMD let one wave's MFMAs overlap the other's
-//     decode;
+//     v_mfma_f32_16x16x32_f16 (fp32 accumulation), weight fragment first so
+//     every lane ends up with 4 consecutive output columns;
+//   * one K step is one branch-free block of 8 chunks; chunk c issues 8
+//     MFMAs of step t, loads fragments for chunk c+1, decodes slot chunk c of
+//     step t+1 and stores it.  Scheduling fences between chunks keep the
+//     decode spread between the MFMAs, so both waves of a SIMD always have
+//     VALU work to issue while the matrix core runs; codes are loaded two
+//     steps ahead into alternating registers;
 //   * epilogue: scale by s_m r_n / K, round once to bf16 (nearest even),
-//     8-byte stores.
+//     8-byte stores;
 //   * workgroup -> tile order: contiguous per XCD, grouped along M so tiles
 //     resident together share activation rows in L2.
+//
+// Throughput is bound by the matrix core and the decode's VALU issue
+// together (about 3.1 VALU instructions per MFMA at 4 bits); the plain fp16
+// library GEMM of the same shape is the practical ceiling for comparison.
 #include <hip/hip_runtime.h>
 
 #include "oq_internal.h"
@@ -38,8 +47,8 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TM = 256, TN = 256, KS = 64;  // tile and K step (slots)
-constexpr int ROWB = KS * 2;                 // bytes per fp16 tile row
-constexpr int OPB = TM * ROWB;               // bytes per operand tile
+constexpr int PLANE = TM * 16;               // one 8-slot chunk of 256 rows
+constexpr int OPB = 8 * PLANE;               // bytes per operand tile (32 KB)
 constexpr int STAGEB = 2 * OPB;              // A + B per stage
 constexpr int LDS_BYTES = 2 * STAGEB;        // double buffered: 128 KB
 constexpr int GROUP_M = 8;
@@ -85,54 +94,40 @@ __device__ __forceinline__ void lut4(uint32_t v, const PermTab &t, uint32_t &o0,
   o1 = perm(hi, lo, 0x07030602u);
 }
 
-// Decode the 64 codes of one K step (8*BITS bytes in w) into 8 chunks of 8
-// fp16 levels.  Chunk q holds slots 8q + {0,2,4,6,1,3,5,7}: the same order
-// for every bit width, so activation and weight chunks always line up.
+// Decode slot chunk q (slots 8q .. 8q+7) of one K step, given the step's
+// 8*BITS code bytes in w.  The 8 fp16 levels come out in slot order
+// 8q + {0,2,4,6,1,3,5,7}, the same for every bit width, so activation and
+// weight chunks always line up.
 template <int BITS>
-__device__ __forceinline__ void decode_step(const uint32_t *w, const PermTab &t, u32x4 *out) {
+__device__ __forceinline__ u32x4 decode_q(const uint32_t *w, const PermTab &t, int q) {
+  uint32_t a0, a1, b0, b1;
   if constexpr (BITS == 4) {
-#pragma unroll
-    for (int q = 0; q < 8; q++) {
-      uint32_t a0, a1, b0, b1;
-      lut4<4>(w[q], t, a0, a1);       // even nibbles: slots 0,2,4,6
-      lut4<4>(w[q] >> 4, t, b0, b1);  // odd nibbles: slots 1,3,5,7
-      out[q] = u32x4{a0, a1, b0, b1};
-    }
+    lut4<4>(w[q], t, a0, a1);       // even nibbles: slots 0,2,4,6
+    lut4<4>(w[q] >> 4, t, b0, b1);  // odd nibbles: slots 1,3,5,7
   } else if constexpr (BITS == 2) {
-#pragma unroll
-    for (int p = 0; p < 4; p++) {
-      const uint32_t x = w[p];  // slots 16p .. 16p+15, byte i of x>>2r holds slot 4i+r
-      const uint32_t v0 = x, v1 = x >> 2, v2 = x >> 4, v3 = x >> 6;
-      uint32_t a0, a1, b0, b1;
-      lut4<2>(perm(v2, v0, 0x05010400u), t, a0, a1);  // slots 0,2,4,6
-      lut4<2>(perm(v3, v1, 0x05010400u), t, b0, b1);  // slots 1,3,5,7
-      out[2 * p] = u32x4{a0, a1, b0, b1};
-      lut4<2>(perm(v2, v0, 0x07030602u), t, a0, a1);  // slots 8,10,12,14
-      lut4<2>(perm(v3, v1, 0x07030602u), t, b0, b1);  // slots 9,11,13,15
-      out[2 * p + 1] = u32x4{a0, a1, b0, b1};
-    }
+    // slots 16p .. 16p+15 in w[p]; byte i of x >> 2r holds slot 4i + r
+    const uint32_t x = w[q >> 1];
+    const uint32_t v0 = x, v1 = x >> 2, v2 = x >> 4, v3 = x >> 6;
+    const uint32_t sel = (q & 1) ? 0x07030602u : 0x05010400u;
+    lut4<2>(perm(v2, v0, sel), t, a0, a1);
+    lut4<2>(perm(v3, v1, sel), t, b0, b1);
   } else {
-#pragma unroll
-    for (int q = 0; q < 8; q++) {
-      // slots 8q..8q+7 occupy bits [24q, 24q+24) of the 192-bit string
-      const int bit = 24 * q, wd = bit >> 5, sh = bit & 31;
-      uint32_t g = w[wd] >> sh;
-      if (sh > 8) g |= w[wd + 1] << (32 - sh);
-      const uint32_t ev = (g & 7u) | ((g >> 6) & 7u) << 8 | ((g >> 12) & 7u) << 16 |
-                          ((g >> 18) & 7u) << 24;
-      const uint32_t od = ((g >> 3) & 7u) | ((g >> 9) & 7u) << 8 | ((g >> 15) & 7u) << 16 |
-                          ((g >> 21) & 7u) << 24;
-      uint32_t a0, a1, b0, b1;
-      lut4<3>(ev, t, a0, a1);
-      lut4<3>(od, t, b0, b1);
-      out[q] = u32x4{a0, a1, b0, b1};
-    }
+    // slots 8q .. 8q+7 occupy bits [24q, 24q+24) of the 192-bit string
+    const int bit = 24 * q, wd = bit >> 5, sh = bit & 31;
+    uint32_t g = w[wd] >> sh;
+    if (sh > 8) g |= w[wd + 1] << (32 - sh);
+    const uint32_t ev = (g & 7u) | ((g >> 6) & 7u) << 8 | ((g >> 12) & 7u) << 16 |
+                        ((g >> 18) & 7u) << 24;
+    const uint32_t od = ((g >> 3) & 7u) | ((g >> 9) & 7u) << 8 | ((g >> 15) & 7u) << 16 |
+                        ((g >> 21) & 7u) << 24;
+    lut4<3>(ev, t, a0, a1);
+    lut4<3>(od, t, b0, b1);
   }
+  return u32x4{a0, a1, b0, b1};
 }
 
-__device__ __forceinline__ int chunk_off(int row, int chunk) {
-  return row * ROWB + ((chunk ^ (row & 7)) << 4);
-}
+// Byte offset of (row, chunk) inside one operand tile of the LDS layout.
+__device__ __forceinline__ int chunk_off(int row, int chunk) { return chunk * PLANE + row * 16; }
 
 template <int BITS>
 __device__ __forceinline__ void load_codes(const uint8_t *p, uint32_t *w) {
@@ -148,6 +143,94 @@ __device__ __forceinline__ void load_codes(const uint8_t *p, uint32_t *w) {
     const u32x2 a = *(const u32x2 *)p, b = *(const u32x2 *)(p + 8), c = *(const u32x2 *)(p + 16);
     w[0] = a[0]; w[1] = a[1]; w[2] = b[0]; w[3] = b[1]; w[4] = c[0]; w[5] = c[1];
   }
+}
+
+// The K loop of one tile for a thread whose row has BITS-bit codes at `prow`
+// (activation or weight row; the MFMA work is the same for both roles).
+template <int BITS>
+__device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[4][8], const uint8_t *prow,
+                                       const PermTab &tt, int opoff, int row, int lane, int wm,
+                                       int wn, int T) {
+  constexpr int RB = 8 * BITS;  // code bytes of one K step
+  uint32_t cb0[2 * BITS], cb1[2 * BITS];
+  uint8_t *wbase = lds + opoff;
+  load_codes<BITS>(prow, cb0);
+#pragma unroll
+  for (int q = 0; q < 8; q++) *(u32x4 *)(wbase + chunk_off(row, q)) = decode_q<BITS>(cb0, tt, q);
+  if (T > 1) load_codes<BITS>(prow + RB, cb1);
+
+  // fragment lanes: rows + (lane & 15), 8-slot chunk (lane >> 4) of each
+  // 32-slot half
+  const int fr = lane & 15, ch0 = lane >> 4, ch1 = 4 + (lane >> 4);
+
+  // One K step: the MFMAs of step t (stage t&1); when `decode`, also the
+  // decode of step t+1 (from `cur`) into stage (t+1)&1 and the load of
+  // step t+2's codes into `nb`.
+  auto step = [&](int t, const uint32_t *cur, uint32_t *nb, bool decode) {
+    __syncthreads();  // stage t&1 complete, stage (t+1)&1 no longer read
+    if (decode) {
+      const int n2 = (t + 2 < T) ? t + 2 : T - 1;  // past the end: a harmless re-read
+      load_codes<BITS>(prow + (int64_t)n2 * RB, nb);
+    }
+    const uint8_t *sA = lds + (t & 1) * STAGEB;
+    const uint8_t *sB = sA + OPB;
+    uint8_t *dst = wbase + ((t + 1) & 1) * STAGEB;
+    half8 af0[8], bf0[4], af1[8], bf1[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) bf0[j] = *(const half8 *)(sB + chunk_off(wn * 64 + 16 * j + fr, ch0));
+#pragma unroll
+    for (int i = 0; i < 2; i++) af0[i] = *(const half8 *)(sA + chunk_off(wm * 128 + 16 * i + fr, ch0));
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+      // fragments one chunk ahead: chunk c uses activation blocks 2(c&3),
+      // 2(c&3)+1 of half c>>2 against all 4 weight blocks of that half
+      if (c < 3) {
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+          const int i = 2 * (c + 1) + u;
+          af0[i] = *(const half8 *)(sA + chunk_off(wm * 128 + 16 * i + fr, ch0));
+        }
+      } else if (c == 3) {
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          bf1[j] = *(const half8 *)(sB + chunk_off(wn * 64 + 16 * j + fr, ch1));
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+          af1[i] = *(const half8 *)(sA + chunk_off(wm * 128 + 16 * i + fr, ch1));
+      } else if (c < 7) {
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+          const int i = 2 * (c - 3) + u;
+          af1[i] = *(const half8 *)(sA + chunk_off(wm * 128 + 16 * i + fr, ch1));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const int i = 2 * (c & 3) + u;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          if (c < 4)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf0[j], af0[i], acc[j][i], 0, 0, 0);
+          else
+            acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf1[j], af1[i], acc[j][i], 0, 0, 0);
+        }
+      }
+      if (decode) *(u32x4 *)(dst + chunk_off(row, c)) = decode_q<BITS>(cur, tt, c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // steps in pairs so the two code buffers alternate without copies
+  int t = 0;
+  for (; t + 2 < T; t += 2) {
+    step(t, cb1, cb0, true);
+    step(t + 1, cb0, cb1, true);
+  }
+  if (t + 1 < T) {
+    step(t, cb1, cb0, true);
+    t++;
+  }
+  step(t, cb1, cb0, false);
 }
 
 template <int BA, int BW>
@@ -171,82 +254,28 @@ __global__ __launch_bounds__(512, 1) void linear_kernel(
   const int tm = first_m + (bid % gsz) % gm, tn = (bid % gsz) / gm;
   const int m0 = tm * TM, n0 = tn * TN;
 
-  // ---- per-thread code rows
-  const int64_t arow = (int64_t)K * BA / 8, wrow = (int64_t)K * BW / 8;
-  const bool is_a = tid < 256;  // waves 0-3 decode activation rows, 4-7 weight rows
+  // ---- the row this thread decodes (rows past the edge repeat the last row)
+  const bool is_a = __builtin_amdgcn_readfirstlane(tid) < 256;  // wave-uniform
   const int row = tid & 255;
   const int am = (m0 + row < M) ? m0 + row : M - 1;
   const int wr = (n0 + row < N) ? n0 + row : N - 1;
-  const uint8_t *pa = A + (int64_t)am * arow;
-  const uint8_t *pw = Wc + (int64_t)wr * wrow;
+  const uint8_t *pa = A + (int64_t)am * ((int64_t)K * BA / 8);
+  const uint8_t *pw = Wc + (int64_t)wr * ((int64_t)K * BW / 8);
   const int T = K / KS;
 
-  uint32_t ca[2 * BA], cw[2 * BW];
   floatx4 acc[4][8];
 #pragma unroll
   for (int j = 0; j < 4; j++)
 #pragma unroll
     for (int i = 0; i < 8; i++) acc[j][i] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto stage_codes = [&](int stage) {
-    u32x4 d[8];
-    uint8_t *dst = lds + stage * STAGEB + (is_a ? 0 : OPB);
-    if (is_a) decode_step<BA>(ca, ta, d); else decode_step<BW>(cw, tw, d);
-#pragma unroll
-    for (int q = 0; q < 8; q++) *(u32x4 *)(dst + chunk_off(row, q)) = d[q];
-  };
-
-  // One K step of MFMA work on LDS stage `cur`: two 32-slot halves.
-  auto mfma_step = [&](int cur) {
-    const uint8_t *sA = lds + cur * STAGEB;
-    const uint8_t *sB = sA + OPB;
-#pragma unroll
-    for (int ks = 0; ks < 2; ks++) {
-      half8 af[8], bf[4];
-      const int ch = 4 * ks + (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < 8; i++)
-        af[i] = *(const half8 *)(sA + chunk_off(wm * 128 + 16 * i + (lane & 15), ch));
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-        bf[j] = *(const half8 *)(sB + chunk_off(wn * 64 + 16 * j + (lane & 15), ch));
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-#pragma unroll
-        for (int i = 0; i < 8; i++)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[j], af[i], acc[j][i], 0, 0, 0);
-    }
-  };
-
-  auto load_step = [&](int t) {
-    if (is_a) load_codes<BA>(pa + (int64_t)t * 8 * BA, ca);
-    else load_codes<BW>(pw + (int64_t)t * 8 * BW, cw);
-  };
-  load_step(0);
-  stage_codes(0);
-  if (T > 1) load_step(1);
-
-  // Steady state: the barrier opens the body, then the MFMAs of step t and
-  // the decode of step t+1.
-  // The two waves of each SIMD (w and w+4) run the step's two phases in
-  // opposite orders, so one wave's MFMAs overlap the other's decode on the
-  // same SIMD instead of both waiting on the same unit.
-  const bool mfma_first = wave < 4;
-  for (int t = 0; t + 1 < T; t++) {
-    __syncthreads();  // stage t&1 complete; stage (t+1)&1 no longer read
-    const int nxt = (t + 2 < T) ? t + 2 : T - 1;  // the last step re-reads harmlessly
-    if (mfma_first) {
-      mfma_step(t & 1);
-      stage_codes((t + 1) & 1);
-      load_step(nxt);
-    } else {
-      stage_codes((t + 1) & 1);
-      load_step(nxt);
-      mfma_step(t & 1);
-    }
+  if constexpr (BA == BW) {
+    k_loop<BA>(lds, acc, is_a ? pa : pw, is_a ? ta : tw, is_a ? 0 : OPB, row, lane, wm, wn, T);
+  } else {
+    // both branches run the same barriers; the branch is wave-uniform
+    if (is_a) k_loop<BA>(lds, acc, pa, ta, 0, row, lane, wm, wn, T);
+    else k_loop<BW>(lds, acc, pw, tw, OPB, row, lane, wm, wn, T);
   }
-  __syncthreads();
-  mfma_step((T - 1) & 1);
 
   // ---- epilogue: lane holds rows m = .. + (lane & 15), cols n = .. + 4 (lane >> 4) + r
   const float invk = 1.0f / (float)K;
