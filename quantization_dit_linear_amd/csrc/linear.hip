@@ -46,12 +46,26 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TM = 256, TN = 256, KS = 64;  // tile and K step (slots)
-constexpr int PLANE = TM * 16;               // one 8-slot chunk of 256 rows
-constexpr int OPB = 8 * PLANE;               // bytes per operand tile (32 KB)
-constexpr int STAGEB = 2 * OPB;              // A + B per stage
-constexpr int LDS_BYTES = 2 * STAGEB;        // double buffered: 128 KB
-constexpr int GROUP_M = 8;
+constexpr int KS = 64;      // K step (slots)
+constexpr int GROUP_M = 8;  // tile rows per group of the tile order
+constexpr int BIG = 256;    // main tile edge
+
+// Tile shape: TT x TT output tile, WM x WN waves, one decoded row per thread.
+template <int TT, int WM, int WN>
+struct Tile {
+  static constexpr int T = TT;
+  static constexpr int THREADS = 2 * TT;          // TT activation + TT weight rows
+  static constexpr int IB = TT / WM / 16;         // 16-row activation blocks per wave
+  static constexpr int JB = TT / WN / 16;         // 16-row weight blocks per wave
+  static constexpr int PLANE = TT * 16;           // one 8-slot chunk of TT rows
+  static constexpr int OPB = 8 * PLANE;           // bytes per operand tile
+  static constexpr int STAGEB = 2 * OPB;          // A + B per stage
+  static constexpr int LDS = 2 * STAGEB;          // double buffered
+  static_assert(WM * WN * 64 == THREADS, "one wave per 64 rows");
+  static_assert(IB % 4 == 0 && JB >= 1, "4 chunks per K half");
+};
+using BigTile = Tile<256, 2, 4>;    // 128 x 64 per wave, 128 KB LDS
+using SmallTile = Tile<128, 2, 2>;  // 64 x 64 per wave, 64 KB LDS
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
@@ -127,7 +141,8 @@ __device__ __forceinline__ u32x4 decode_q(const uint32_t *w, const PermTab &t, i
 }
 
 // Byte offset of (row, chunk) inside one operand tile of the LDS layout.
-__device__ __forceinline__ int chunk_off(int row, int chunk) { return chunk * PLANE + row * 16; }
+template <class TL>
+__device__ __forceinline__ int chunk_off(int row, int chunk) { return chunk * TL::PLANE + row * 16; }
 
 template <int BITS>
 __device__ __forceinline__ void load_codes(const uint8_t *p, uint32_t *w) {
@@ -147,21 +162,25 @@ __device__ __forceinline__ void load_codes(const uint8_t *p, uint32_t *w) {
 
 // The K loop of one tile for a thread whose row has BITS-bit codes at `prow`
 // (activation or weight row; the MFMA work is the same for both roles).
-template <int BITS>
-__device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[4][8], const uint8_t *prow,
-                                       const PermTab &tt, int opoff, int row, int lane, int wm,
-                                       int wn, int T) {
-  constexpr int RB = 8 * BITS;  // code bytes of one K step
+template <class TL, int BITS>
+__device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[TL::JB][TL::IB],
+                                       const uint8_t *prow, const PermTab &tt, int opoff, int row,
+                                       int lane, int wm, int wn, int T) {
+  constexpr int RB = 8 * BITS;           // code bytes of one K step
+  constexpr int IB = TL::IB, JB = TL::JB;
+  constexpr int IPC = IB / 4;            // activation blocks per chunk
   uint32_t cb0[2 * BITS], cb1[2 * BITS];
   uint8_t *wbase = lds + opoff;
   load_codes<BITS>(prow, cb0);
 #pragma unroll
-  for (int q = 0; q < 8; q++) *(u32x4 *)(wbase + chunk_off(row, q)) = decode_q<BITS>(cb0, tt, q);
+  for (int q = 0; q < 8; q++)
+    *(u32x4 *)(wbase + chunk_off<TL>(row, q)) = decode_q<BITS>(cb0, tt, q);
   if (T > 1) load_codes<BITS>(prow + RB, cb1);
 
   // fragment lanes: rows + (lane & 15), 8-slot chunk (lane >> 4) of each
   // 32-slot half
   const int fr = lane & 15, ch0 = lane >> 4, ch1 = 4 + (lane >> 4);
+  const int arow0 = wm * (16 * IB) + fr, brow0 = wn * (16 * JB) + fr;
 
   // One K step: the MFMAs of step t (stage t&1); when `decode`, also the
   // decode of step t+1 (from `cur`) into stage (t+1)&1 and the load of
@@ -172,50 +191,50 @@ __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[4][8], const
       const int n2 = (t + 2 < T) ? t + 2 : T - 1;  // past the end: a harmless re-read
       load_codes<BITS>(prow + (int64_t)n2 * RB, nb);
     }
-    const uint8_t *sA = lds + (t & 1) * STAGEB;
-    const uint8_t *sB = sA + OPB;
-    uint8_t *dst = wbase + ((t + 1) & 1) * STAGEB;
-    half8 af0[8], bf0[4], af1[8], bf1[4];
+    const uint8_t *sA = lds + (t & 1) * TL::STAGEB;
+    const uint8_t *sB = sA + TL::OPB;
+    uint8_t *dst = wbase + ((t + 1) & 1) * TL::STAGEB;
+    half8 af0[IB], bf0[JB], af1[IB], bf1[JB];
 #pragma unroll
-    for (int j = 0; j < 4; j++) bf0[j] = *(const half8 *)(sB + chunk_off(wn * 64 + 16 * j + fr, ch0));
+    for (int j = 0; j < JB; j++) bf0[j] = *(const half8 *)(sB + chunk_off<TL>(brow0 + 16 * j, ch0));
 #pragma unroll
-    for (int i = 0; i < 2; i++) af0[i] = *(const half8 *)(sA + chunk_off(wm * 128 + 16 * i + fr, ch0));
+    for (int u = 0; u < IPC; u++) af0[u] = *(const half8 *)(sA + chunk_off<TL>(arow0 + 16 * u, ch0));
 #pragma unroll
     for (int c = 0; c < 8; c++) {
-      // fragments one chunk ahead: chunk c uses activation blocks 2(c&3),
-      // 2(c&3)+1 of half c>>2 against all 4 weight blocks of that half
+      // chunk c: activation blocks IPC*(c&3) .. of K half c>>2 against all
+      // weight blocks of that half; fragments are loaded one chunk ahead
       if (c < 3) {
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-          const int i = 2 * (c + 1) + u;
-          af0[i] = *(const half8 *)(sA + chunk_off(wm * 128 + 16 * i + fr, ch0));
+        for (int u = 0; u < IPC; u++) {
+          const int i = IPC * (c + 1) + u;
+          af0[i] = *(const half8 *)(sA + chunk_off<TL>(arow0 + 16 * i, ch0));
         }
       } else if (c == 3) {
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-          bf1[j] = *(const half8 *)(sB + chunk_off(wn * 64 + 16 * j + fr, ch1));
+        for (int j = 0; j < JB; j++)
+          bf1[j] = *(const half8 *)(sB + chunk_off<TL>(brow0 + 16 * j, ch1));
 #pragma unroll
-        for (int i = 0; i < 2; i++)
-          af1[i] = *(const half8 *)(sA + chunk_off(wm * 128 + 16 * i + fr, ch1));
+        for (int u = 0; u < IPC; u++)
+          af1[u] = *(const half8 *)(sA + chunk_off<TL>(arow0 + 16 * u, ch1));
       } else if (c < 7) {
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-          const int i = 2 * (c - 3) + u;
-          af1[i] = *(const half8 *)(sA + chunk_off(wm * 128 + 16 * i + fr, ch1));
+        for (int u = 0; u < IPC; u++) {
+          const int i = IPC * (c - 3) + u;
+          af1[i] = *(const half8 *)(sA + chunk_off<TL>(arow0 + 16 * i, ch1));
         }
       }
 #pragma unroll
-      for (int u = 0; u < 2; u++) {
-        const int i = 2 * (c & 3) + u;
+      for (int u = 0; u < IPC; u++) {
+        const int i = IPC * (c & 3) + u;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
+        for (int j = 0; j < JB; j++) {
           if (c < 4)
             acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf0[j], af0[i], acc[j][i], 0, 0, 0);
           else
             acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf1[j], af1[i], acc[j][i], 0, 0, 0);
         }
       }
-      if (decode) *(u32x4 *)(dst + chunk_off(row, c)) = decode_q<BITS>(cur, tt, c);
+      if (decode) *(u32x4 *)(dst + chunk_off<TL>(row, c)) = decode_q<BITS>(cur, tt, c);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -233,61 +252,84 @@ __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[4][8], const
   step(t, cb1, cb0, false);
 }
 
-template <int BA, int BW>
-__global__ __launch_bounds__(512, 1) void linear_kernel(
+// Group-major tile order: index g -> 256 x 256 tile (tm, tn), GROUP_M tile
+// rows per group, column-major inside a group.
+__device__ __forceinline__ void big_tile_of(int g, int nbm, int nbn, int &tm, int &tn) {
+  const int gsz = GROUP_M * nbn, grp = g / gsz, first_m = grp * GROUP_M;
+  const int gm = (nbm - first_m) < GROUP_M ? (nbm - first_m) : GROUP_M;
+  tm = first_m + (g % gsz) % gm;
+  tn = (g % gsz) / gm;
+}
+
+// One workgroup per output tile.  TL = BigTile: `count` tiles of the
+// group-major order from index `first` (block ids spread so each XCD takes a
+// contiguous run).  TL = SmallTile: each 256 x 256 tile from index `first`
+// on is split into four 128 x 128 tiles, one workgroup each.
+template <class TL, int BA, int BW>
+__global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
     const uint8_t *__restrict__ A, const float *__restrict__ sa, const uint8_t *__restrict__ Wc,
     const float *__restrict__ sw, int M, int N, int K, uint16_t *__restrict__ Y, PermTab ta,
-    PermTab tw, int vec_store) {
+    PermTab tw, int vec_store, int first, int count) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int TT = TL::T, IB = TL::IB, JB = TL::JB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wn_count = TT / (16 * JB);
+  const int wm = wave / wn_count, wn = wave % wn_count;
 
-  // ---- workgroup -> tile (contiguous per XCD, grouped along M)
-  const int nbm = (M + TM - 1) / TM, nbn = (N + TN - 1) / TN, total = nbm * nbn;
-  int bid = blockIdx.x;
-  {
-    const int xcd = bid & 7, local = bid >> 3, per = total >> 3, rem = total & 7;
+  // ---- workgroup -> tile
+  const int nbm = (M + BIG - 1) / BIG, nbn = (N + BIG - 1) / BIG;
+  int m0, n0;
+  if constexpr (TT == BIG) {
+    int bid = blockIdx.x;
+    const int xcd = bid & 7, local = bid >> 3, per = count >> 3, rem = count & 7;
     bid = xcd * per + (xcd < rem ? xcd : rem) + local;
+    int tm, tn;
+    big_tile_of(first + bid, nbm, nbn, tm, tn);
+    m0 = tm * BIG;
+    n0 = tn * BIG;
+  } else {
+    int tm, tn;
+    big_tile_of(first + (int)(blockIdx.x >> 2), nbm, nbn, tm, tn);
+    const int sub = blockIdx.x & 3;
+    m0 = tm * BIG + (sub >> 1) * TT;
+    n0 = tn * BIG + (sub & 1) * TT;
   }
-  const int gsz = GROUP_M * nbn, grp = bid / gsz, first_m = grp * GROUP_M;
-  const int gm = (nbm - first_m) < GROUP_M ? (nbm - first_m) : GROUP_M;
-  const int tm = first_m + (bid % gsz) % gm, tn = (bid % gsz) / gm;
-  const int m0 = tm * TM, n0 = tn * TN;
 
   // ---- the row this thread decodes (rows past the edge repeat the last row)
-  const bool is_a = __builtin_amdgcn_readfirstlane(tid) < 256;  // wave-uniform
-  const int row = tid & 255;
+  const bool is_a = __builtin_amdgcn_readfirstlane(tid) < TT;  // wave-uniform
+  const int row = tid % TT;
   const int am = (m0 + row < M) ? m0 + row : M - 1;
   const int wr = (n0 + row < N) ? n0 + row : N - 1;
   const uint8_t *pa = A + (int64_t)am * ((int64_t)K * BA / 8);
   const uint8_t *pw = Wc + (int64_t)wr * ((int64_t)K * BW / 8);
   const int T = K / KS;
 
-  floatx4 acc[4][8];
+  floatx4 acc[JB][IB];
 #pragma unroll
-  for (int j = 0; j < 4; j++)
+  for (int j = 0; j < JB; j++)
 #pragma unroll
-    for (int i = 0; i < 8; i++) acc[j][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < IB; i++) acc[j][i] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   if constexpr (BA == BW) {
-    k_loop<BA>(lds, acc, is_a ? pa : pw, is_a ? ta : tw, is_a ? 0 : OPB, row, lane, wm, wn, T);
+    k_loop<TL, BA>(lds, acc, is_a ? pa : pw, is_a ? ta : tw, is_a ? 0 : TL::OPB, row, lane, wm,
+                   wn, T);
   } else {
     // both branches run the same barriers; the branch is wave-uniform
-    if (is_a) k_loop<BA>(lds, acc, pa, ta, 0, row, lane, wm, wn, T);
-    else k_loop<BW>(lds, acc, pw, tw, OPB, row, lane, wm, wn, T);
+    if (is_a) k_loop<TL, BA>(lds, acc, pa, ta, 0, row, lane, wm, wn, T);
+    else k_loop<TL, BW>(lds, acc, pw, tw, TL::OPB, row, lane, wm, wn, T);
   }
 
   // ---- epilogue: lane holds rows m = .. + (lane & 15), cols n = .. + 4 (lane >> 4) + r
   const float invk = 1.0f / (float)K;
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int m = m0 + wm * 128 + 16 * i + (lane & 15);
+  for (int i = 0; i < IB; i++) {
+    const int m = m0 + wm * (16 * IB) + 16 * i + (lane & 15);
     if (m >= M) continue;
     const float s = sa[m] * invk;
     uint16_t *yrow = Y + (int64_t)m * N;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int n = n0 + wn * 64 + 16 * j + 4 * (lane >> 4);
+    for (int j = 0; j < JB; j++) {
+      const int n = n0 + wn * (16 * JB) + 16 * j + 4 * (lane >> 4);
       if (vec_store && n + 3 < N) {
         const floatx4 r = *(const floatx4 *)(sw + n);
         const uint32_t lo = f32_to_bf16_rne(acc[j][i][0] * s * r[0]) |
@@ -314,21 +356,49 @@ PermTab make_tab(const LevelsF16 &lv) {
   return t;
 }
 
-template <int BA, int BW>
-hipError_t launch_ab(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw) {
-  static bool attr_set = false;
+template <class TL, int BA, int BW>
+hipError_t launch_tiles(const LinearArgs &a, const PermTab &ta, const PermTab &tw, int vec,
+                        int first, int count, unsigned grid) {
+  static bool attr_set = false;  // per instantiation; the attribute is per function
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)linear_kernel<BA, BW>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    hipError_t e = hipFuncSetAttribute((const void *)linear_kernel<TL, BA, BW>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, TL::LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t tiles = ((a.M + TM - 1) / TM) * ((a.N + TN - 1) / TN);
-  const int vec = (a.N % 4 == 0) && (((uintptr_t)a.y & 7) == 0) && (((uintptr_t)a.w_norms & 15) == 0);
-  hipLaunchKernelGGL((linear_kernel<BA, BW>), dim3((unsigned)tiles), dim3(512), LDS_BYTES,
+  hipLaunchKernelGGL((linear_kernel<TL, BA, BW>), dim3(grid), dim3(TL::THREADS), TL::LDS,
                      a.stream, a.a_codes, a.a_norms, a.w_codes, a.w_norms, (int)a.M, (int)a.N,
-                     a.K, a.y, make_tab(la), make_tab(lw), vec);
+                     a.K, a.y, ta, tw, vec, first, count);
   return hipGetLastError();
+}
+
+// Tiles of 256 x 256, one workgroup per CU at a time.  A problem too small
+// to fill a quarter of the CUs runs as 128 x 128 tiles instead (four times
+// the workgroups).  A sparse last round of a large problem stays as it is:
+// workgroups finish staggered, so it costs far less than a full round, and
+// 128 x 128 tiles (one wave per SIMD) take about half a round's time anyway.
+template <int BA, int BW>
+hipError_t launch_ab(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw) {
+  const PermTab ta = make_tab(la), tw = make_tab(lw);
+  const int vec = (a.N % 4 == 0) && (((uintptr_t)a.y & 7) == 0) && (((uintptr_t)a.w_norms & 15) == 0);
+  const int64_t tiles = ((a.M + BIG - 1) / BIG) * ((a.N + BIG - 1) / BIG);
+  if (tiles > (int64_t)(INT32_MAX / 4)) return hipErrorInvalidValue;
+  int cus = 256;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess)
+      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (cus <= 0) cus = 256;
+  }
+  const int64_t full = (4 * tiles <= cus) ? 0 : tiles;
+  if (full > 0) {
+    hipError_t e = launch_tiles<BigTile, BA, BW>(a, ta, tw, vec, 0, (int)full, (unsigned)full);
+    if (e != hipSuccess) return e;
+  }
+  if (full < tiles)
+    return launch_tiles<SmallTile, BA, BW>(a, ta, tw, vec, (int)full, (int)(tiles - full),
+                                           (unsigned)(4 * (tiles - full)));
+  return hipSuccess;
 }
 
 }  // namespace

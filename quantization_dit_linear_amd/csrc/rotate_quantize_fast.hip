@@ -24,6 +24,13 @@
 //    h <= 1024 here), so each lane ends up holding 4 chunks x 2 positions
 //    of one slot per 128-coordinate group.
 //  * Remaining stages (chunk bits) are register butterflies.
+//  * Blocks of 2048 or 4096: the transform runs on 1024-element slots as
+//    above, and the four slots of a wave tile (one per 16-lane row of the
+//    MFMA output) are the 1024-element quarters of one block (or halves of
+//    two blocks).  The last one or two butterfly stages pair the rows:
+//    v_permlane16_swap / v_permlane32_swap hand each lane its partner's
+//    value, and the butterfly leaves the slot bit in the register index and
+//    a group bit in the lane, which the store addressing follows.
 //  * Quantize.  A magic-number fma turns v into a cell index of a uniform
 //    grid (step 1/8 sigma, narrower than any threshold gap); an LDS cell
 //    table gives the code at the cell's lower edge and points into the
@@ -48,9 +55,9 @@ constexpr float kMagic = 12582912.0f;        // 1.5 * 2^23
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
-constexpr int pick_waves(int wt, int ch) {
+constexpr int pick_waves(int wt, int ch, int maxw) {
   int best = 1;
-  for (int w = 1; w <= 16; w++)
+  for (int w = 1; w <= maxw; w++)
     if (wt % w == 0 && ch % w == 0) best = w;
   return best;
 }
@@ -59,12 +66,15 @@ constexpr int pick_waves(int wt, int ch) {
 template <int D>
 struct Shape {
   static constexpr int H = D & -D;                    // Hadamard block
-  static constexpr int S = H;                         // slot = one block (h <= 1024 here)
+  static constexpr int S = H < 1024 ? H : 1024;       // slot: a block, or 1024 of one
+  static constexpr int XB = ilog2(H / S);             // butterfly stages across slots
   static constexpr int P = D / S;                     // slots per token
   static constexpr int TB = 4;                        // tokens per batch (one cell-table copy each)
   static constexpr int WT = TB * P / 4;               // wave tiles per batch
   static constexpr int CH = D / 512;                  // 8-element chunks per token per 64 threads
-  static constexpr int W = pick_waves(WT, CH);
+  // waves per workgroup: divide both the wave tiles and the staging chunks;
+  // with stages across slots at most 2 waves per SIMD (register budget)
+  static constexpr int W = pick_waves(WT, CH, XB > 0 ? 8 : 16);
   static constexpr int CPT = CH / W;                  // chunks per thread per token
   static constexpr int G = S / 128;                   // 128-coordinate groups per slot
   static constexpr int CBITS = ilog2(S) - 5;          // chunk bits transformed in registers
@@ -74,8 +84,10 @@ struct Shape {
   static constexpr int NP_OFF = CT_OFF + kCellBytes;  // [TB][W] partial sums of squares
   static constexpr int YB_OFF = NP_OFF + ((TB * W * 4 + 15) / 16) * 16;
   static constexpr int LDS = YB_OFF + TB * D * 2;
-  static constexpr bool PREFETCH = (TB * CPT * 4) <= 32;  // register budget of the prefetch
+  // register budget of the one-batch-ahead prefetch
+  static constexpr bool PREFETCH = (TB * CPT * 4) <= (W <= 8 ? 48 : 32);
   static_assert(S <= 1024 && S >= 128, "slot size");
+  static_assert(XB <= 2 && (1 << XB) <= G, "at most 4 slots per block");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
@@ -184,8 +196,13 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
 
     // ---- compute: wave tiles q = wave, wave + W, ...
     for (int q = wave; q < WT; q += W) {
-      // output side: slot so = lane >> 4 of the tile -> token tko, block jo
-      const int sig_o = 4 * q + (lane >> 4);
+      // output side: row rl = lane >> 4 of the tile.  Before the stages
+      // across slots it holds slot 4q + rl; after them the low XB bits of
+      // the slot are register-index bits (group bits, see below) and the low
+      // XB bits of rl are group bits.  All slots a lane ends up with belong
+      // to one token.
+      const int rl = lane >> 4;
+      const int sig_o = 4 * q + (rl & ~((1 << SH::XB) - 1));
       const int tko = sig_o / P, jo = sig_o - tko * P;
       float ss = 0.f;
 #pragma unroll
@@ -230,9 +247,33 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
               }
             }
       }
-      // quantize + pack + store
+      // stages across the tile's slots: slot bit x pairs lane rows r, r ^ (1 << x)
+#pragma unroll
+      for (int x = 0; x < SH::XB; x++) {
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+          if (g & (1 << x)) continue;
+          const int g2 = g | (1 << x);
+#pragma unroll
+          for (int w = 0; w < 2; w++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const uint32_t a = __float_as_uint(v[g][w][i]), c = __float_as_uint(v[g2][w][i]);
+              // row pairs: this lane receives its partner's copy of the same
+              // register; rows with bit x clear keep register g, the others g2
+              const auto sw = (x == 0) ? __builtin_amdgcn_permlane16_swap(a, c, false, false)
+                                       : __builtin_amdgcn_permlane32_swap(a, c, false, false);
+              const float lo = __uint_as_float(sw[0]), hi = __uint_as_float(sw[1]);
+              v[g][w][i] = lo + hi;   // slot bit x = 0
+              v[g2][w][i] = lo - hi;  // slot bit x = 1
+            }
+        }
+      }
+      // quantize + pack + store.  Register group g holds slot jo + (g & m)
+      // and group (g & ~m) | (rl & m) of that slot, m = 2^XB - 1.
+      constexpr int XM = (1 << SH::XB) - 1;
       const int64_t tok = b * TB + tko;
-      uint8_t *dst0 = codes + tok * row_bytes + 16 * BITS * (jo * G) + BITS * (lane & 15);
+      uint8_t *dst0 = codes + tok * row_bytes + 16 * BITS * (jo * G + (rl & XM)) + BITS * (lane & 15);
 #pragma unroll
       for (int g = 0; g < G; g++) {
         uint32_t word = 0;
@@ -251,7 +292,7 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
             word |= code << (BITS * (4 * w + i));
           }
         if (tok < n_tok) {
-          uint8_t *dst = dst0 + 16 * BITS * g;
+          uint8_t *dst = dst0 + 16 * BITS * ((g & XM) * G + (g & ~XM));
           if constexpr (BITS == 4) {
             *(uint32_t *)dst = word;
           } else if constexpr (BITS == 2) {
@@ -305,8 +346,11 @@ hipError_t launch_rotate_quantize_fast(const RotateArgs &a, const uint32_t *scat
   *handled = true;
   switch (a.d) {
     case 1024: return launch_d<1024>(a, scat, smask, cells, th);
+    case 2048: return launch_d<2048>(a, scat, smask, cells, th);
     case 3072: return launch_d<3072>(a, scat, smask, cells, th);
+    case 4096: return launch_d<4096>(a, scat, smask, cells, th);
     case 5120: return launch_d<5120>(a, scat, smask, cells, th);
+    case 12288: return launch_d<12288>(a, scat, smask, cells, th);
     case 13824: return launch_d<13824>(a, scat, smask, cells, th);
     default: break;
   }

@@ -54,6 +54,33 @@ def test_small_and_ragged_shapes(q, M, N, K):
     assert np.all(np.abs(y - ref) <= 1e-2 * np.abs(ref).max() + 1e-30)
 
 
+@pytest.mark.parametrize("M,N,K,ba,bw", [
+    (1000, 700, 256, 4, 4),    # 12 tiles: run as 128 x 128 tiles
+    (1000, 700, 256, 3, 2),    # the same with mixed widths
+    (2600, 2344, 384, 4, 4),   # 110 tiles of 256 x 256, ragged edges
+    (7387, 2204, 512, 4, 4),   # 261 tiles: a 5-tile last round
+    (7387, 2204, 512, 2, 4),   # the same with mixed widths
+])
+def test_tile_paths(q, M, N, K, ba, bw):
+    """Shapes that run each tile size; the checked rows include the ragged
+    bottom edge and the row band of the last round's tiles (tile rows 24-28,
+    last tile column, for 261 tiles)."""
+    ac, an = wl.random_codes(M, K, ba, M + 3)
+    wc, wn = wl.random_codes(N, K, bw, N + 5)
+    say("linear tile paths", M, N, K, ba, bw)
+    y = _run(q, ac, an, ba, wc, wn, bw, K)
+    if M <= 1000:
+        rows = np.arange(M)
+    else:
+        rows = np.unique(np.concatenate([wl.sample_rows(M, 16, 7),
+                                         np.linspace(min(6144, M - 1), M - 1, 24).astype(np.int64),
+                                         [0, M - 1]]))
+    ref = oracle.linear(ac, an, ba, wc, wn, bw, K, rows=rows)
+    assert parity.rel_fro(y[rows], ref) <= parity.LINEAR_FRO
+    # every checked element individually, so a wrong tile cannot hide
+    assert np.all(np.abs(y[rows] - ref) <= 1e-2 * np.abs(ref).max() + 1e-30)
+
+
 def test_oracle_codes_realistic_distribution(q):
     """Codes produced by the oracle's own quantizer on workload inputs (the
     Lloyd-Max cell frequencies, not uniform), fed to both sides."""
