@@ -50,6 +50,16 @@ def parse():
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="before the steps, copy a buffer of this many MiB once (untimed), "
                         "as the known-size reference for HBM byte counters")
+    p.add_argument("--no-ref-gemm", action="store_true",
+                   help="skip timing the library fp16 GEMM of the linear's shape")
+    p.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
+                   help="no benchmark: turn rocprofv3 output of this workload (kernel trace, "
+                        "FETCH_SIZE and WRITE_SIZE runs) into the summaries under profiles/")
+    p.add_argument("--profile-command", default="",
+                   help="with --summarize-profiles: the rocprofv3 commands, recorded verbatim")
+    p.add_argument("--profile-bench-log", default=None,
+                   help="with --summarize-profiles: output of the traced bench.py run, whose "
+                        "own per-kernel event timings are compared with the trace")
     return p.parse_args()
 
 
@@ -115,8 +125,162 @@ def cpu_baseline(cfg, lin, bw, ba, rows_n):
     }
 
 
+def library_fp16_gemm(M, N, K, iters=10):
+    """Context, not part of the path: the vendor library's dense fp16 GEMM
+    (torch.matmul) on the linear's shape, fp16 in and out, random operands.
+    It does no decoding, so it is a practical ceiling for the linear."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    x = torch.randn((M, K), generator=g, device="cuda").to(torch.float16)
+    w = torch.randn((N, K), generator=g, device="cuda").to(torch.float16)
+    for _ in range(2):
+        y = x @ w.t()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        y = x @ w.t()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del x, w, y
+    return {"what": "torch.matmul fp16 x fp16 -> fp16, same M, N, K (vendor library GEMM)",
+            "ms": round(ms, 4), "TFLOP/s": round(2.0 * M * N * K / ms / 1e9, 1)}
+
+
+def _short_kernel_name(name):
+    n = name.replace("(anonymous namespace)::", "").replace("oq::", "")
+    if "(" in n:
+        n = n[:n.index("(")]
+    return n.replace("void ", "").strip()
+
+
+def summarize_profiles(a):
+    """Write profiles/<workload>_kernel_stats.txt, _traffic.txt and the
+    traffic table bench.py reads, from rocprofv3 csv output."""
+    import csv
+    import glob
+    import workloads as wl
+    cfg = a.workload
+    lin = wl.CONFIGS[cfg]["linears"][0] if a.linear is None else wl.get_linear(cfg, a.linear)
+    bw, ba = lin.bit_pairs[0] if a.bits is None else tuple(int(v) for v in a.bits.split(","))
+    M, N, K = lin.act.M, lin.weight.N, lin.act.d
+    in_b = 2 if lin.act.dtype == wl.BF16 else 4
+    tag = f"{cfg}_w{bw}a{ba}"
+    kt_dir, f_dir, w_dir = a.summarize_profiles
+
+    def one(pattern, d):
+        files = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+        if not files:
+            raise SystemExit(f"no {pattern} under {d}")
+        return files[0]
+
+    rows = list(csv.DictReader(open(one("*kernel_stats.csv", kt_dir))))
+    lines = []
+    for r in rows:
+        lines.append((_short_kernel_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                      float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    lin_name = next(n for n, *_ in lines if n.startswith("linear_kernel"))
+    rot_name = next(n for n, *_ in lines if n.startswith("rq_"))
+    with open(os.path.join(ROOT, "profiles", f"{tag}_kernel_stats.txt"), "w") as f:
+        f.write(f"Kernel timing on one MI355X (gfx950), workload {cfg}/{lin.name}: {M} tokens, "
+                f"d_in {K} -> d_out {N}, W{bw}A{ba}.\nCommands (repository root on the GPU "
+                f"host):\n{a.profile_command}\n\n")
+        f.write(f"{'kernel':70s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} "
+                f"{'pct':>6s}\n")
+        for n, c, av, mn, mx, pc in lines:
+            f.write(f"{n[:70]:70s} {c:6d} {av:9.1f} {mn:9.1f} {mx:9.1f} {pc:6.2f}\n")
+        f.write(f"\n{lin_name}: 2*{M}*{N}*{K} = {2.0 * M * N * K:.4g} flop per launch\n")
+        f.write(f"{rot_name}: rows*(d*{in_b} + d*b/8 + 4) algorithmic bytes per launch "
+                f"({M} activation rows at {ba} bits, {N} weight rows at {bw} bits)\n")
+        if a.profile_bench_log:
+            line = [l for l in open(a.profile_bench_log) if l.startswith("{")][-1]
+            kb = json.loads(line)["kernels"]
+            lin_us = next(av for n, c, av, *_ in lines if n == lin_name)
+            f.write(f"\nAgreement: in the traced run bench.py's own HIP events (on the stream "
+                    f"the kernels run on) averaged {kb['linear']['ms'] * 1e3:.1f} us per linear "
+                    f"launch vs {lin_us:.1f} us in the trace; rotate+quantize "
+                    f"{kb['rotate_quantize']['ms'] * 1e3:.1f} us (events include the gaps "
+                    f"between launches).\n")
+
+    def counters(d, cname):
+        per = {}
+        for r in csv.DictReader(open(one("*counter_collection.csv", d))):
+            if r["Counter_Name"] != cname:
+                continue
+            per.setdefault(r["Kernel_Name"], []).append(
+                (int(r["Grid_Size"]), float(r["Counter_Value"])))
+        return per
+
+    fetch, write = counters(f_dir, "FETCH_SIZE"), counters(w_dir, "WRITE_SIZE")
+
+    def calib(per):
+        copies = [v for k, vals in per.items() if "copyBuffer" in k for v in vals]
+        if not copies:
+            raise SystemExit("no copy kernel in the counter run (use --calib-copy-mib)")
+        return max(copies)[1]  # the largest copy: the calibration buffer
+
+    f_ref, w_ref = calib(fetch), calib(write)
+    copy_kib = 1024 * 1024  # 1 GiB read and written by the calibration copy
+    f_scale, w_scale = copy_kib / f_ref, copy_kib / w_ref
+
+    def kib(per, prefix, grid=None):
+        vals = [v for k, vs in per.items() if _short_kernel_name(k).startswith(prefix)
+                for (gsz, v) in vs]
+        return float(np.mean(vals))
+
+    lin_fetch = kib(fetch, "linear_kernel") * 1024 * f_scale
+    lin_write = kib(write, "linear_kernel") * 1024 * w_scale
+    # activation launches only (the weight-preparation launches have N rows)
+    rot_f = [v for k, vs in fetch.items() if _short_kernel_name(k).startswith("rq_")
+             for (g, v) in vs]
+    rot_w = [v for k, vs in write.items() if _short_kernel_name(k).startswith("rq_")
+             for (g, v) in vs]
+    rot_fetch = float(np.mean(rot_f)) * 1024 * f_scale
+    rot_write = float(np.mean(rot_w)) * 1024 * w_scale
+    lin_alg_r = M * K * ba / 8 + N * K * bw / 8 + 4 * (M + N)
+    lin_alg_w = 2 * M * N
+    rot_rows = (M + N) / 2.0  # mean over the activation and weight launches
+    rot_alg_r = rot_rows * K * in_b
+    rot_alg_w = (M * (K * ba / 8 + 4) + N * (K * bw / 8 + 4)) / 2.0
+    lin_digest = src_digest("linear.hip")
+    rot_digest = src_digest("rotate_quantize.hip", "rotate_quantize_fast.hip")
+    table = {
+        "linear": {"kernel": lin_name, "source_digest": lin_digest,
+                   "bytes_per_launch": int(lin_fetch + lin_write), "fetch_bytes": int(lin_fetch),
+                   "write_bytes": int(lin_write), "algorithmic_read_bytes": int(lin_alg_r),
+                   "algorithmic_write_bytes": int(lin_alg_w)},
+        "rotate_quantize": {"kernel": rot_name, "source_digest": rot_digest,
+                            "bytes_per_launch": int(rot_fetch + rot_write),
+                            "fetch_bytes": int(rot_fetch), "write_bytes": int(rot_write),
+                            "algorithmic_read_bytes": int(rot_alg_r),
+                            "algorithmic_write_bytes": int(rot_alg_w),
+                            "note": "mean over the activation and weight-preparation launches"},
+        "workload": tag, "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(table, f, indent=1)
+    with open(os.path.join(ROOT, "profiles", f"{tag}_traffic.txt"), "w") as f:
+        f.write(f"HBM-side traffic per launch from rocprofv3 counters, workload {cfg}/{lin.name} "
+                f"({M} x {K} -> {N}, W{bw}A{ba}).\nCommands (repository root on the GPU host):\n"
+                f"{a.profile_command}\n\n")
+        f.write(f"reference: the calibration copy of 1 GiB: FETCH_SIZE {f_ref:.0f} KiB -> scale "
+                f"{f_scale:.4f}; WRITE_SIZE {w_ref:.0f} KiB -> scale {w_scale:.4f}\n\n")
+        for key in ("linear", "rotate_quantize"):
+            e = table[key]
+            f.write(f"{e['kernel']}: fetch {e['fetch_bytes'] / 1e6:.1f} MB (algorithmic reads "
+                    f"{e['algorithmic_read_bytes'] / 1e6:.1f} MB); write "
+                    f"{e['write_bytes'] / 1e6:.1f} MB (algorithmic writes "
+                    f"{e['algorithmic_write_bytes'] / 1e6:.1f} MB)\n")
+    print(json.dumps(table))
+    return 0
+
+
 def main():
     a = parse()
+    if a.summarize_profiles:
+        return summarize_profiles(a)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): this build has no "
               "multi-GPU path; see the sharding notes in DESIGN.md", flush=True)
@@ -188,6 +352,9 @@ def main():
     t_prep = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     t_rot = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     t_lin = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    per_step = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    lin_steps = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    ref_gemm = None if a.no_ref_gemm else library_fp16_gemm(M, N, K)
 
     flops = 2.0 * M * N * K
     in_b = 2 if lin.act.dtype == wl.BF16 else 4
@@ -221,8 +388,12 @@ def main():
                                f"W{bw}A{ba}, activations "
                                f"{'bf16' if lin.act.dtype == wl.BF16 else 'fp32'}",
                    "M": M, "N": N, "K": K, "w_bits": bw, "a_bits": ba},
+        "step_ms_median": round(float(np.median(per_step)), 4),
+        "step_ms_iqr": [round(float(np.percentile(per_step, 25)), 4),
+                        round(float(np.percentile(per_step, 75)), 4)],
         "kernels": {
             "linear": {"ms": round(t_lin, 4), "TFLOP/s": round(lin_tflops, 2),
+                       "ms_median": round(float(np.median(lin_steps)), 4),
                        "frac_of_mfma_fp16_peak": round(lin_tflops / MFMA_FP16_PEAK_TFLOPS, 4)},
             "rotate_quantize": {"ms": round(t_rot, 4), "GB/s": round(rot_gbs, 1),
                                 "frac_of_hbm_peak": round(rot_gbs / HBM_PEAK_GBS, 4)},
@@ -238,6 +409,9 @@ def main():
                                      "frac": round(rot_gbs / HBM_PEAK_GBS, 4),
                                      "traffic": stored_traffic("rotate_quantize", rot_digest)},
     }
+    if ref_gemm is not None:
+        out["reference_fp16_gemm"] = dict(ref_gemm, linear_over_reference=round(
+            ref_gemm["ms"] / t_lin, 3))
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, lin, bw, ba, a.cpu_rows)
     print(json.dumps(out), flush=True)
