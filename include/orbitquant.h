@@ -67,6 +67,9 @@ extern "C" {
 #define OQ_ROT_NO_SIGNS (1u << 0)     /* rotation without the Rademacher signs D (Pi then H only) */
 #define OQ_OUT_F32_ROTATED (1u << 1)  /* oq_rotate_quantize writes the rotated unit vector z
                                          (fp32 [n_tok][d], coordinate order) instead of codes */
+#define OQ_OUT_BF16_DEQUANT (1u << 2) /* oq_rotate_quantize writes the dequantized rotated token
+                                         s * c_{code_i} (bf16 [n_tok][d], coordinate order, round
+                                         to nearest even) instead of codes: fake quantization */
 
 /* Text for a status code.  Never NULL; the string is static. */
 const char *oq_strerror(int status);
@@ -95,9 +98,16 @@ int64_t oq_codes_bytes(int64_t rows, int d, int bits);
  *   x:      device, [n_tok][d] row-major, dtype OQ_F32 or OQ_BF16, 16-byte
  *           aligned
  *   seed:   rotation seed (selects Pi and D)
- *   flags:  OQ_ROT_NO_SIGNS, OQ_OUT_F32_ROTATED
+ *   flags:  OQ_ROT_NO_SIGNS, and at most one of OQ_OUT_F32_ROTATED,
+ *           OQ_OUT_BF16_DEQUANT
  *   out:    device; packed codes uint8 [n_tok][d*bits/8] (storage order,
- *           16-byte aligned), or with OQ_OUT_F32_ROTATED fp32 [n_tok][d]
+ *           16-byte aligned), or with OQ_OUT_F32_ROTATED fp32 [n_tok][d], or
+ *           with OQ_OUT_BF16_DEQUANT bf16 [n_tok][d]: coordinate i holds
+ *           s * C_{d,bits}[code_i], the token's reconstruction in the rotated
+ *           basis.  A bf16 GEMM of two such matrices (activations and weight
+ *           rows, same seed) is the fake-quantized product the pages evaluate
+ *           (paper.gecl.asia notes, Dataset/Evaluation; llmdb.app
+ *           Implementation Details), equal to oq_linear up to operand rounding
  *   norms:  device fp32 [n_tok], receives s (4-byte aligned)
  * n_tok = 0 is a no-op that succeeds (the pointers may then be NULL).
  * Errors: OQ_EINVAL, OQ_EUNSUPPORTED, OQ_ENOMEM, OQ_EDEVICE. */
@@ -109,8 +119,9 @@ int oq_rotate_quantize(const void *x, int dtype, int64_t n_tok, int d, uint64_t 
  * notes, Method item 2: W Pi^T): row i of W [n_out][d_in] becomes the
  * packed codes of RPBH(w_i / r_i) under C_{d_in,bits} plus r_i = ||w_i||.
  * Same layout, limits and errors as oq_rotate_quantize (w_codes
- * [n_out][d_in*bits/8], row_norms [n_out]); OQ_OUT_F32_ROTATED is
- * rejected here. */
+ * [n_out][d_in*bits/8], row_norms [n_out]); OQ_OUT_F32_ROTATED and
+ * OQ_OUT_BF16_DEQUANT are rejected here (oq_rotate_quantize on the weight
+ * rows gives the same outputs). */
 int oq_prepare_weights(const void *W, int dtype, int64_t n_out, int d_in, uint64_t seed,
                        uint32_t flags, int bits, uint8_t *w_codes, float *row_norms,
                        void *stream);

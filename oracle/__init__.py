@@ -63,6 +63,9 @@ def _load():
     lib.oqo_linear.restype = ctypes.c_int
     lib.oqo_linear.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int,
                                ctypes.c_int64, ctypes.c_int, P, ctypes.c_int64, P]
+    lib.oqo_fake_quantize.restype = ctypes.c_int
+    lib.oqo_fake_quantize.argtypes = [P, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_uint64, ctypes.c_int, ctypes.c_int, P, P]
     lib.oqo_num_threads.restype = ctypes.c_int
     lib.oqo_num_threads.argtypes = []
     _lib = lib
@@ -207,6 +210,22 @@ def linear(a_codes, a_norms, ba, w_codes, w_norms, bw, K, rows=None):
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return y
+
+
+def fake_quantize(x, dtype, d, seed, bits, use_signs=True):
+    """Fake quantization: fp64 s * C_{d,bits}[code(z_i)] for every rotated
+    coordinate i (coordinate order), and the norms s.  paper.gecl.asia notes,
+    Dataset/Evaluation (the pages evaluate with dequantized operands)."""
+    x = np.ascontiguousarray(x)
+    rows = x.shape[0]
+    assert x.shape[1] == d
+    out = np.empty((rows, d), np.float64)
+    norms = np.empty(rows, np.float64)
+    rc = _load().oqo_fake_quantize(_ptr(x), dtype, rows, d, seed, int(use_signs), bits,
+                                   _ptr(out), _ptr(norms))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out, norms
 
 
 def num_threads():

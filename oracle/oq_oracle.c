@@ -351,5 +351,41 @@ int oqo_linear(const uint8_t *a_codes, const double *a_norms, int ba,
     return 0;
 }
 
+/* Fake quantization, the evaluation path of the pages (paper.gecl.asia
+ * notes, Dataset/Evaluation; llmdb.app Implementation Details): every
+ * coordinate of the rotated unit token is replaced by its codebook level
+ * and scaled back by the norm, out[r][i] = s_r * C_{d,bits}[code(z_ri)], in
+ * coordinate order (no packing).  fp64. */
+int oqo_fake_quantize(const void *x, int dtype, int64_t rows, int d, uint64_t seed,
+                      int use_signs, int bits, double *out, double *norms)
+{
+    if (d <= 0 || d % 128 != 0 || bits < 1 || bits > 4) return -1;
+    const int L = 1 << bits;
+    int32_t *perm = malloc(sizeof(int32_t) * d);
+    int8_t *sign = malloc(d);
+    double lv[16], th[16];
+    oqo_plan(d, seed, perm, sign);
+    oqo_codebook(d, bits, lv, th);
+#pragma omp parallel
+    {
+        double *xr = malloc(sizeof(double) * d);
+        double *zr = malloc(sizeof(double) * d);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < rows; r++) {
+            double nrm;
+            for (int i = 0; i < d; i++) xr[i] = load_elem(x, dtype, (size_t)r * d + i);
+            oqo_rotate_token(xr, d, perm, sign, use_signs, zr, &nrm);
+            if (norms) norms[r] = nrm;
+            for (int i = 0; i < d; i++)
+                out[(size_t)r * d + i] = nrm * lv[oqo_quantize_one(zr[i], th, L)];
+        }
+        free(xr);
+        free(zr);
+    }
+    free(perm);
+    free(sign);
+    return 0;
+}
+
 /* Threads an OpenMP region of this oracle uses (for reporting). */
 int oqo_num_threads(void) { return omp_get_max_threads(); }

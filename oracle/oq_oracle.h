@@ -31,5 +31,7 @@ int oqo_rotate_quantize(const void *x, int dtype, int64_t rows, int d, uint64_t 
 int oqo_linear(const uint8_t *a_codes, const double *a_norms, int ba,
                const uint8_t *w_codes, const double *w_norms, int bw,
                int64_t N, int K, const int64_t *rows, int64_t nrows, double *y);
+int oqo_fake_quantize(const void *x, int dtype, int64_t rows, int d, uint64_t seed,
+                      int use_signs, int bits, double *out, double *norms);
 int oqo_num_threads(void);
 #endif

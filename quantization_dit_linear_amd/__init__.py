@@ -11,6 +11,7 @@ Functions mirror the C entry points:
 * :func:`codebook`        -> ``oq_codebook``
 * :func:`rotate_quantize` -> ``oq_rotate_quantize``
 * :func:`rotate`          -> ``oq_rotate_quantize`` with ``OQ_OUT_F32_ROTATED``
+* :func:`fake_quantize`   -> ``oq_rotate_quantize`` with ``OQ_OUT_BF16_DEQUANT``
 * :func:`prepare_weights` -> ``oq_prepare_weights``
 * :func:`linear`          -> ``oq_linear``
 """
@@ -24,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "liborbitquant.so")
 
 OQ_OK, OQ_EINVAL, OQ_EUNSUPPORTED, OQ_ENOMEM, OQ_EDEVICE = 0, -1, -2, -3, -4
 OQ_F32, OQ_BF16 = 0, 1
-OQ_ROT_NO_SIGNS, OQ_OUT_F32_ROTATED = 1, 2
+OQ_ROT_NO_SIGNS, OQ_OUT_F32_ROTATED, OQ_OUT_BF16_DEQUANT = 1, 2, 4
 
 # every symbol the header declares, with (restype, argtypes)
 _P = ctypes.c_void_p
@@ -149,6 +150,27 @@ def rotate(x, seed, *, signs=True, stream=None):
                                   _dev_ptr(z, "z"), _dev_ptr(norms, "norms"), _stream(stream))
     _check(rc, "oq_rotate_quantize")
     return z, norms
+
+
+def fake_quantize(x, seed, bits, *, signs=True, out=None, norms=None, stream=None):
+    """Dequantized rotated rows (bfloat16 [M, d], coordinate order): row m,
+    coordinate i holds s_m * C_{d,bits}[code_mi]; and the norms.  Works for
+    activation tokens and weight rows alike (the same quantizer); a bf16 GEMM
+    of two such matrices with the same seed is the fake-quantized product."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, d]")
+    M, d = x.shape
+    if out is None:
+        out = torch.empty((M, d), dtype=torch.bfloat16, device=x.device)
+    if norms is None:
+        norms = torch.empty((M,), dtype=torch.float32, device=x.device)
+    flags = OQ_OUT_BF16_DEQUANT | (0 if signs else OQ_ROT_NO_SIGNS)
+    rc = lib().oq_rotate_quantize(_dev_ptr(x, "x"), _dtype_code(x), M, d, seed, flags, bits,
+                                  _dev_ptr(out, "out"), _dev_ptr(norms, "norms"),
+                                  _stream(stream))
+    _check(rc, "oq_rotate_quantize")
+    return out, norms
 
 
 def prepare_weights(W, seed, bits, *, signs=True, out=None, norms=None, stream=None):

@@ -275,8 +275,10 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
                   int bits, void *out, float *norms, void *stream, bool allow_rotated) {
   if (n_tok < 0) return OQ_EINVAL;
   if (dtype != OQ_F32 && dtype != OQ_BF16) return OQ_EINVAL;
-  if (flags & ~(OQ_ROT_NO_SIGNS | OQ_OUT_F32_ROTATED)) return OQ_EINVAL;
-  if ((flags & OQ_OUT_F32_ROTATED) && !allow_rotated) return OQ_EINVAL;
+  const uint32_t outs = OQ_OUT_F32_ROTATED | OQ_OUT_BF16_DEQUANT;
+  if (flags & ~(OQ_ROT_NO_SIGNS | outs)) return OQ_EINVAL;
+  if ((flags & outs) && !allow_rotated) return OQ_EINVAL;
+  if ((flags & outs) == outs) return OQ_EINVAL;
   int rc = check_d_bits(d, bits);
   if (rc != OQ_OK) return rc;
   if (n_tok == 0) return OQ_OK;  // empty input: nothing to do, pointers may be null
@@ -299,6 +301,8 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
   a.bits = bits;
   a.signs = !(flags & OQ_ROT_NO_SIGNS);
   a.rotated_out = (flags & OQ_OUT_F32_ROTATED) != 0;
+  a.dequant_out = (flags & OQ_OUT_BF16_DEQUANT) != 0;
+  for (int k = 0; k < (1 << bits); k++) a.levels.v[k] = (float)lv[k];
   a.out = out;
   a.norms = norms;
   a.stream = (hipStream_t)stream;

@@ -20,6 +20,11 @@ struct LevelsF16 {
   uint16_t v[16];
 };
 
+// Unit-variance levels of one codebook, fp32 (dequantized outputs).
+struct LevelsF32 {
+  float v[16];
+};
+
 // Device-side rotation plan for one (device, d, seed).
 struct DevicePlan {
   int d = 0, h = 0;
@@ -41,7 +46,9 @@ struct RotateArgs {
   int64_t n_tok;
   int d, h, bits;
   bool signs;
-  bool rotated_out;
+  bool rotated_out;  // fp32 rotated unit vector instead of codes
+  bool dequant_out;  // bf16 s * level[code] instead of codes
+  LevelsF32 levels;  // unit levels (dequant_out)
   void *out;
   float *norms;
   hipStream_t stream;

@@ -6,7 +6,9 @@
 // Method items 1, 3, 4; pith.science Supplementary A setup.)
 //
 // This file holds the general kernel: any dtype, any h, one workgroup per
-// token, the token held in LDS as fp32.
+// token, the token held in LDS as fp32.  Besides packed codes it can write
+// the rotated unit vector (fp32) or the dequantized rotated token
+// s * c_{code_i} (bf16, fake quantization).
 #include <hip/hip_runtime.h>
 
 #include "oq_internal.h"
@@ -48,11 +50,17 @@ __device__ double block_sum(double v, double *scratch) {
   return t;
 }
 
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void rq_generic_kernel(
     const void *__restrict__ x, int dtype, int64_t n_tok, int d, int h,
-    const int32_t *__restrict__ scatter, Thresholds th, uint8_t *__restrict__ codes,
-    float *__restrict__ zout, float *__restrict__ norms) {
+    const int32_t *__restrict__ scatter, Thresholds th, LevelsF32 lv, uint8_t *__restrict__ codes,
+    float *__restrict__ zout, uint16_t *__restrict__ dq, float *__restrict__ norms) {
   extern __shared__ float y[];  // d floats
   __shared__ double red[kThreads / 64];
   const int tid = threadIdx.x;
@@ -86,6 +94,7 @@ __global__ __launch_bounds__(kThreads) void rq_generic_kernel(
     } else {
       // unit-space value sqrt(d) z_i = y_i sqrt(d/h) / s
       const float us = s > 0.0 ? (float)(sqrt((double)d / (double)h) / s) : 0.f;
+      const float fs = (float)(s / sqrt((double)d));  // dequantized value = s * level / sqrt(d)
       for (int q = tid; q < d / 8; q += kThreads) {
         const int G = q >> 4, n = q & 15;
         uint32_t word = 0;
@@ -93,12 +102,14 @@ __global__ __launch_bounds__(kThreads) void rq_generic_kernel(
         for (int w = 0; w < 2; w++)
 #pragma unroll
           for (int c = 0; c < 4; c++) {
-            const float u = y[G * 128 + 32 * c + 16 * w + n] * us;
+            const int i = G * 128 + 32 * c + 16 * w + n;
+            const float u = y[i] * us;
             uint32_t code = 0;
             for (int k = 0; k < th.count; k++) code += (u >= th.t[k]) ? 1u : 0u;
+            if (dq) dq[t * d + i] = f32_to_bf16_rne(fs * lv.v[code]);
             word |= code << (BITS * (4 * w + c));
           }
-        store_codes<BITS>(codes + t * row_bytes + 16 * BITS * G + BITS * n, word);
+        if (!dq) store_codes<BITS>(codes + t * row_bytes + 16 * BITS * G + BITS * n, word);
       }
     }
     __syncthreads();
@@ -116,8 +127,9 @@ hipError_t launch_rotate_quantize_generic(const RotateArgs &a, const DevicePlan 
   const int64_t want = (int64_t)(cus > 0 ? cus : 256) * 8;
   const int grid = (int)(a.n_tok < want ? a.n_tok : want);
   const size_t lds = sizeof(float) * a.d;
-  uint8_t *codes = a.rotated_out ? nullptr : (uint8_t *)a.out;
+  uint8_t *codes = (a.rotated_out || a.dequant_out) ? nullptr : (uint8_t *)a.out;
   float *zout = a.rotated_out ? (float *)a.out : nullptr;
+  uint16_t *dq = a.dequant_out ? (uint16_t *)a.out : nullptr;
   if (lds > 32768) {
     // tokens above 8192 fp32 need more than the default dynamic-LDS cap
     hipError_t e = hipSuccess;
@@ -135,15 +147,15 @@ hipError_t launch_rotate_quantize_generic(const RotateArgs &a, const DevicePlan 
   switch (a.bits) {
     case 2:
       hipLaunchKernelGGL(rq_generic_kernel<2>, dim3(grid), dim3(kThreads), lds, a.stream, a.x,
-                         a.dtype, a.n_tok, a.d, a.h, sc, th, codes, zout, a.norms);
+                         a.dtype, a.n_tok, a.d, a.h, sc, th, a.levels, codes, zout, dq, a.norms);
       break;
     case 3:
       hipLaunchKernelGGL(rq_generic_kernel<3>, dim3(grid), dim3(kThreads), lds, a.stream, a.x,
-                         a.dtype, a.n_tok, a.d, a.h, sc, th, codes, zout, a.norms);
+                         a.dtype, a.n_tok, a.d, a.h, sc, th, a.levels, codes, zout, dq, a.norms);
       break;
     case 4:
       hipLaunchKernelGGL(rq_generic_kernel<4>, dim3(grid), dim3(kThreads), lds, a.stream, a.x,
-                         a.dtype, a.n_tok, a.d, a.h, sc, th, codes, zout, a.norms);
+                         a.dtype, a.n_tok, a.d, a.h, sc, th, a.levels, codes, zout, dq, a.norms);
       break;
     default:
       return hipErrorInvalidValue;

@@ -37,7 +37,8 @@
 //    batch's threshold table at the only threshold that can fall inside the
 //    cell; one exact fp32 compare settles the code.
 //  * Pack.  A lane's 8 codes per group are exactly 8 consecutive storage
-//    slots, so they pack into one b-byte word per lane.
+//    slots, so they pack into one b-byte word per lane.  (Fake-quantization
+//    mode instead stores bf16 s * level[code] at every coordinate.)
 #include <hip/hip_runtime.h>
 
 #include "oq_internal.h"
@@ -82,7 +83,8 @@ struct Shape {
   static constexpr int TT_OFF = 0;                    // [TB][16] x {float T, uint base}
   static constexpr int CT_OFF = TT_OFF + TB * 16 * 8;
   static constexpr int NP_OFF = CT_OFF + kCellBytes;  // [TB][W] partial sums of squares
-  static constexpr int YB_OFF = NP_OFF + ((TB * W * 4 + 15) / 16) * 16;
+  static constexpr int LV_OFF = NP_OFF + ((TB * W * 4 + 15) / 16) * 16;  // 16 unit levels
+  static constexpr int YB_OFF = LV_OFF + 64;
   static constexpr int LDS = YB_OFF + TB * D * 2;
   // register budget of the one-batch-ahead prefetch
   static constexpr bool PREFETCH = (TB * CPT * 4) <= (W <= 8 ? 48 : 32);
@@ -91,11 +93,19 @@ struct Shape {
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <int D, int BITS>
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// DQ: write bf16 s * level[code] at every coordinate (dq) instead of codes.
+template <int D, int BITS, bool DQ>
 __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
     const uint16_t *__restrict__ x, int64_t n_tok, const uint32_t *__restrict__ scat,
     const uint32_t *__restrict__ smask, const uint16_t *__restrict__ cells, Thresholds th,
-    uint8_t *__restrict__ codes, float *__restrict__ norms) {
+    LevelsF32 lv, uint8_t *__restrict__ codes, uint16_t *__restrict__ dq,
+    float *__restrict__ norms) {
   using SH = Shape<D>;
   constexpr int S = SH::S, P = SH::P, TB = SH::TB, WT = SH::WT, W = SH::W, CPT = SH::CPT;
   constexpr int G = SH::G;
@@ -108,6 +118,9 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
   // cell tables (all 4 copies) into LDS
   for (int i = tid; i < kCellBytes / 16; i += W * 64)
     ((u32x4 *)(lds + SH::CT_OFF))[i] = ((const u32x4 *)cells)[i];
+  if constexpr (DQ) {
+    if (tid < 16) ((float *)(lds + SH::LV_OFF))[tid] = lv.v[tid];
+  }
 
   // per-thread staging: chunk c of every token covers x[8*pos, 8*pos+8)
   uint32_t saddr[CPT][8], smk[CPT][4];
@@ -274,6 +287,10 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
       constexpr int XM = (1 << SH::XB) - 1;
       const int64_t tok = b * TB + tko;
       uint8_t *dst0 = codes + tok * row_bytes + 16 * BITS * (jo * G + (rl & XM)) + BITS * (lane & 15);
+      // fake quantization: coordinate of register (g, w, i) is
+      // (jo + (g & XM)) S + ((g & ~XM) | (rl & XM)) 128 + 32 i + 16 w + (lane & 15)
+      uint16_t *dq0 = dq + tok * D + jo * S + (rl & XM) * 128 + (lane & 15);
+      const float fs = s * (1.0f / __builtin_sqrtf((float)D));  // s / sqrt(d)
 #pragma unroll
       for (int g = 0; g < G; g++) {
         uint32_t word = 0;
@@ -289,9 +306,14 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
             const u32x2 ent = *(const u32x2 *)(lds + SH::TT_OFF + e);  // {T, base}, 8-aligned
             const float tv = __uint_as_float(ent[0]);
             const uint32_t code = ent[1] + (val >= tv ? 1u : 0u);
+            if constexpr (DQ) {
+              const float lvv = *(const float *)(lds + SH::LV_OFF + 4 * code);
+              if (tok < n_tok)
+                dq0[(g & XM) * S + (g & ~XM) * 128 + 32 * i + 16 * w] = f32_to_bf16_rne(fs * lvv);
+            }
             word |= code << (BITS * (4 * w + i));
           }
-        if (tok < n_tok) {
+        if (!DQ && tok < n_tok) {
           uint8_t *dst = dst0 + 16 * BITS * ((g & XM) * G + (g & ~XM));
           if constexpr (BITS == 4) {
             *(uint32_t *)dst = word;
@@ -313,7 +335,7 @@ template <int D, int BITS>
 hipError_t launch_one(const RotateArgs &a, const uint32_t *scat, const uint32_t *smask,
                       const uint16_t *cells, const Thresholds &th) {
   using SH = Shape<D>;
-  auto k = rq_fast_kernel<D, BITS>;
+  auto k = a.dequant_out ? rq_fast_kernel<D, BITS, true> : rq_fast_kernel<D, BITS, false>;
   int dev = 0, cus = 0;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -321,8 +343,10 @@ hipError_t launch_one(const RotateArgs &a, const uint32_t *scat, const uint32_t 
   const int64_t nb = (a.n_tok + SH::TB - 1) / SH::TB;
   const int64_t want = (int64_t)(cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
   const int grid = (int)(nb < want ? nb : want);
+  uint8_t *codes = a.dequant_out ? nullptr : (uint8_t *)a.out;
+  uint16_t *dq = a.dequant_out ? (uint16_t *)a.out : nullptr;
   hipLaunchKernelGGL(k, dim3(grid), dim3(64 * SH::W), 0, a.stream, (const uint16_t *)a.x,
-                     a.n_tok, scat, smask, cells, th, (uint8_t *)a.out, a.norms);
+                     a.n_tok, scat, smask, cells, th, a.levels, codes, dq, a.norms);
   return hipGetLastError();
 }
 

@@ -7,7 +7,10 @@ The acceptance rules (applied element by element):
   * norms and rotated values: within 1e-5 relative (rotated values: per
     token ||dz|| <= 1e-5 since ||z|| = 1, and max |dz_i| <= 1e-5 max |z|);
   * linear outputs: relative Frobenius error <= 2e-3 against the oracle's
-    fp64 dequantised GEMM.
+    fp64 dequantised GEMM;
+  * fake-quantized (dequantized) values: within 2^-8 relative (one bf16
+    rounding of s * level, plus the norm tolerance), except coordinates
+    whose code may differ under the code rule above.
 """
 import numpy as np
 
@@ -16,6 +19,7 @@ CODE_MAX_FRAC = 1e-4
 NORM_RTOL = 1e-5
 ROT_TOL = 1e-5
 LINEAR_FRO = 2e-3
+DEQUANT_RTOL = 2.0 ** -8
 
 
 def slot_index(d):
@@ -83,3 +87,20 @@ def assert_rotated_match(z_gpu, z_ref, what=""):
 def rel_fro(y, ref):
     y = np.asarray(y, np.float64)
     return float(np.linalg.norm(y - ref) / np.linalg.norm(ref))
+
+
+def assert_dequant_match(gpu, ref, z_ref, d, thr_unit, what=""):
+    """gpu: dequantized values (any float dtype) [R, d]; ref: oracle fp64."""
+    g = np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    bad = np.abs(g - r) > DEQUANT_RTOL * np.abs(r)
+    n_bad = int(bad.sum())
+    if n_bad:
+        u = np.sqrt(d) * z_ref[bad]
+        tau = np.asarray(thr_unit, np.float64)
+        dist = np.abs(u[:, None] - tau[None, :])
+        win = CODE_WINDOW * np.maximum(np.abs(tau), 1.0)[None, :]
+        outside = int((~(dist <= win).any(axis=1)).sum())
+        assert outside == 0, f"{what}: {outside} dequantized values off outside the window"
+    assert n_bad <= CODE_MAX_FRAC * g.size, f"{what}: {n_bad}/{g.size} values differ"
+    return n_bad

@@ -104,8 +104,11 @@ def test_rotate_validation_rejects_before_hip(q, fn):
     assert call(n=0) == q.OQ_OK
     assert call(n=0, x=None, out=None, nrm=None) == q.OQ_OK
     assert call(n=0, d=3000) == q.OQ_EUNSUPPORTED
+    # the two alternative outputs exclude each other
+    assert call(flags=q.OQ_OUT_F32_ROTATED | q.OQ_OUT_BF16_DEQUANT) == q.OQ_EINVAL
     if fn == "oq_prepare_weights":
         assert call(flags=q.OQ_OUT_F32_ROTATED) == q.OQ_EINVAL
+        assert call(flags=q.OQ_OUT_BF16_DEQUANT) == q.OQ_EINVAL
 
 
 def test_linear_validation_rejects_before_hip(q):
@@ -146,3 +149,12 @@ def test_numpy_unpacker_agrees_with_oracle(bits):
     codes = rng.integers(0, 1 << bits, (5, d)).astype(np.uint8)
     packed = np.stack([oracle.pack_row(c, bits) for c in codes])
     assert np.array_equal(parity.unpack_codes(packed, d, bits), codes)
+
+
+def test_flag_and_status_constants_match_header(q):
+    """The binding's constants are the header's #defines / enum values."""
+    src = open(os.path.join(ROOT, "include", "orbitquant.h")).read()
+    for name, val in re.findall(r"#define\s+(OQ_[A-Z0-9_]+)\s+\(1u\s*<<\s*(\d+)\)", src):
+        assert getattr(q, name) == 1 << int(val), name
+    for name in ("OQ_ROT_NO_SIGNS", "OQ_OUT_F32_ROTATED", "OQ_OUT_BF16_DEQUANT"):
+        assert re.search(r"#define\s+" + name + r"\b", src), name
