@@ -51,7 +51,8 @@ def parse():
                    help="before the steps, copy a buffer of this many MiB once (untimed), "
                         "as the known-size reference for HBM byte counters")
     p.add_argument("--no-ref-gemm", action="store_true",
-                   help="skip timing the library fp16 GEMM of the linear's shape")
+                   help="skip timing the library fp16 GEMM of the linear's shape and the "
+                        "fake-quantization path")
     p.add_argument("--summarize-profiles", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="no benchmark: turn rocprofv3 output of this workload (kernel trace, "
                         "FETCH_SIZE and WRITE_SIZE runs) into the summaries under profiles/")
@@ -148,6 +149,40 @@ def library_fp16_gemm(M, N, K, iters=10):
     del x, w, y
     return {"what": "torch.matmul fp16 x fp16 -> fp16, same M, N, K (vendor library GEMM)",
             "ms": round(ms, 4), "TFLOP/s": round(2.0 * M * N * K / ms / 1e9, 1)}
+
+
+def fake_quant_path(q, x, W, seed, ba, bw, iters=10):
+    """Context: the pages' own evaluation path on the same inputs -- both
+    operands fake-quantized to bf16 by the library (oq_rotate_quantize with
+    OQ_OUT_BF16_DEQUANT), then the vendor bf16 GEMM -- timed per step."""
+    import torch
+    M, K = x.shape
+    N = W.shape[0]
+    xh = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
+    wh = torch.empty((N, K), dtype=torch.bfloat16, device=x.device)
+    xn = torch.empty((M,), dtype=torch.float32, device=x.device)
+    wn = torch.empty((N,), dtype=torch.float32, device=x.device)
+    wt = torch.empty((K, N), dtype=torch.bfloat16, device=x.device)
+
+    def run():
+        q.fake_quantize(W, seed, bw, out=wh, norms=wn)
+        wt.copy_(wh.t())
+        q.fake_quantize(x, seed, ba, out=xh, norms=xn)
+        return torch.mm(xh, wt)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    return {"what": "fake-quantize W and x to bf16 (library), transpose W, vendor bf16 GEMM",
+            "ms": round(ms, 4)}
 
 
 def _short_kernel_name(name):
@@ -355,6 +390,7 @@ def main():
     per_step = np.array([e[0].elapsed_time(e[3]) for e in evs])
     lin_steps = np.array([e[2].elapsed_time(e[3]) for e in evs])
     ref_gemm = None if a.no_ref_gemm else library_fp16_gemm(M, N, K)
+    fq_path = None if a.no_ref_gemm else fake_quant_path(q, xs[0], Ws[0], lin.seed, ba, bw)
 
     flops = 2.0 * M * N * K
     in_b = 2 if lin.act.dtype == wl.BF16 else 4
@@ -412,6 +448,9 @@ def main():
     if ref_gemm is not None:
         out["reference_fp16_gemm"] = dict(ref_gemm, linear_over_reference=round(
             ref_gemm["ms"] / t_lin, 3))
+    if fq_path is not None:
+        out["fake_quant_path"] = dict(fq_path, native_step_speedup=round(
+            fq_path["ms"] / ms_step, 3))
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, lin, bw, ba, a.cpu_rows)
     print(json.dumps(out), flush=True)

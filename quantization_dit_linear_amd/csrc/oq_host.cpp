@@ -16,6 +16,7 @@
 #include <cstdint>
 #include <cstring>
 #include <map>
+#include <limits>
 #include <mutex>
 #include <tuple>
 #include <vector>
@@ -215,29 +216,40 @@ int get_plan(int d, uint64_t seed, hipStream_t stream, const oq::DevicePlan **ou
 // threshold.  Entry = byte offset of (slot copy s, base code) inside the
 // kernel's per-wave threshold table: 128 s + 8 base, base = the code at the
 // window's lower edge.
-int build_cells(int bits, std::vector<uint16_t> &out) {
+// Cell table of the bf16 fast path.  The kernel maps a unit-space value u
+// (= sqrt(d) z) to cell c = floor(8 u + 1024 + 1/16) of a 1/8-sigma grid
+// (2048 cells cover |u| < 128; |u| <= sqrt(d) < 128 for the fast path's d);
+// entry c = {tau, base}: base = number of thresholds at or below the cell,
+// tau = the only threshold that can fall inside it (or +inf), so the code is
+// base + (u >= tau).  A cell holding two thresholds would need a finer grid:
+// rejected (never the case for 2-4 bit Lloyd-Max codebooks).
+int build_cells(int bits, std::vector<uint32_t> &out) {
   double lv[16], th[15];
   unit_codebook(bits, lv, th);
   const int T = (1 << bits) - 1;
   const double delta = 0.125, eps = 0.02 * delta;
-  out.assign(4 * oq::kFastCells, 0);
+  out.assign(2 * oq::kFastCells, 0);
   for (int c = 0; c < oq::kFastCells; c++) {
-    const double lo = delta * (c - 1024.25) - eps, hi = delta * (c - 1023.25) + eps;
+    const double lo = delta * (c - 1024.0625) - eps, hi = delta * (c - 1023.0625) + eps;
     int base = 0, inside = 0;
     for (int k = 0; k < T; k++) {
       if ((double)(float)th[k] <= lo) base++;
       else if ((double)(float)th[k] <= hi) inside++;
     }
-    if (inside > 1) return OQ_EUNSUPPORTED;  // grid too coarse for this codebook
-    for (int s = 0; s < 4; s++) out[s * oq::kFastCells + c] = (uint16_t)(128 * s + 8 * base);
+    if (inside > 1) return OQ_EUNSUPPORTED;
+    const float tau = base < T ? (float)th[base] : std::numeric_limits<float>::infinity();
+    uint32_t tb;
+    std::memcpy(&tb, &tau, 4);
+    out[2 * c] = tb;
+    out[2 * c + 1] = (uint32_t)base;
   }
   return OQ_OK;
 }
 
 std::mutex g_cell_mu;
-std::map<std::pair<int, int>, uint16_t *> g_cells;  // (device, bits) -> table
+std::map<std::pair<int, int>, uint32_t *> g_cells;  // (device, bits) -> table
 
-int get_cells(int bits, const uint16_t **out) {
+int get_cells(int bits, const uint32_t **out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return OQ_EDEVICE;
   std::lock_guard<std::mutex> g(g_cell_mu);
@@ -246,12 +258,12 @@ int get_cells(int bits, const uint16_t **out) {
     *out = it->second;
     return OQ_OK;
   }
-  std::vector<uint16_t> tab;
+  std::vector<uint32_t> tab;
   int rc = build_cells(bits, tab);
   if (rc != OQ_OK) return rc;
-  uint16_t *dptr = nullptr;
-  if (hipMalloc(&dptr, tab.size() * 2) != hipSuccess) return OQ_ENOMEM;
-  if (hipMemcpy(dptr, tab.data(), tab.size() * 2, hipMemcpyHostToDevice) != hipSuccess) {
+  uint32_t *dptr = nullptr;
+  if (hipMalloc(&dptr, tab.size() * 4) != hipSuccess) return OQ_ENOMEM;
+  if (hipMemcpy(dptr, tab.data(), tab.size() * 4, hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(dptr);
     return OQ_EDEVICE;
   }
@@ -307,7 +319,7 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
   a.norms = norms;
   a.stream = (hipStream_t)stream;
   if (a.dtype == OQ_BF16 && !a.rotated_out) {
-    const uint16_t *cells = nullptr;
+    const uint32_t *cells = nullptr;
     rc = get_cells(bits, &cells);
     if (rc != OQ_OK) return rc;
     bool handled = false;

@@ -60,9 +60,9 @@ hipError_t launch_rotate_quantize_generic(const RotateArgs &a, const DevicePlan 
 // bf16 fast path; sets *handled = false (and does nothing) for shapes it does
 // not cover.  cells: the quantizer's cell table for a.bits (fast_cell_table).
 hipError_t launch_rotate_quantize_fast(const RotateArgs &a, const uint32_t *scat,
-                                       const uint32_t *smask, const uint16_t *cells,
+                                       const uint32_t *smask, const uint32_t *cells,
                                        const Thresholds &th, bool *handled);
-constexpr int kFastCells = 2048;  // cells per copy of the fast path's cell table
+constexpr int kFastCells = 2048;  // cells of the fast path's cell table ({tau, base} each)
 
 struct LinearArgs {
   const uint8_t *a_codes;

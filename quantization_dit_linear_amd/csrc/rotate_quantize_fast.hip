@@ -31,11 +31,12 @@
 //    v_permlane16_swap / v_permlane32_swap hand each lane its partner's
 //    value, and the butterfly leaves the slot bit in the register index and
 //    a group bit in the lane, which the store addressing follows.
-//  * Quantize.  A magic-number fma turns v into a cell index of a uniform
-//    grid (step 1/8 sigma, narrower than any threshold gap); an LDS cell
-//    table gives the code at the cell's lower edge and points into the
-//    batch's threshold table at the only threshold that can fall inside the
-//    cell; one exact fp32 compare settles the code.
+//  * Quantize.  A magic-number fma turns v into the byte offset of its cell
+//    in a uniform grid over sqrt(d) z (step 1/8, narrower than any threshold
+//    gap); one 8-byte LDS read gives the code at the cell's lower edge and
+//    the only threshold that can fall inside the cell; one exact fp32
+//    compare of sqrt(d) z with it settles the code.  The table does not
+//    depend on the token, so it is loaded once per workgroup.
 //  * Pack.  A lane's 8 codes per group are exactly 8 consecutive storage
 //    slots, so they pack into one b-byte word per lane.  (Fake-quantization
 //    mode instead stores bf16 s * level[code] at every coordinate.)
@@ -51,7 +52,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCells = kFastCells;           // grid cells per table copy
-constexpr int kCellBytes = 4 * kCells * 2;   // 4 copies (one per token of a batch), u16
+constexpr int kCellBytes = kCells * 8;       // {float tau, uint base} per cell
 constexpr float kMagic = 12582912.0f;        // 1.5 * 2^23
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
@@ -80,8 +81,7 @@ struct Shape {
   static constexpr int G = S / 128;                   // 128-coordinate groups per slot
   static constexpr int CBITS = ilog2(S) - 5;          // chunk bits transformed in registers
   // LDS layout: tables first so their offsets fit instruction immediates
-  static constexpr int TT_OFF = 0;                    // [TB][16] x {float T, uint base}
-  static constexpr int CT_OFF = TT_OFF + TB * 16 * 8;
+  static constexpr int CT_OFF = 0;                    // cell table, offsets are immediates
   static constexpr int NP_OFF = CT_OFF + kCellBytes;  // [TB][W] partial sums of squares
   static constexpr int LV_OFF = NP_OFF + ((TB * W * 4 + 15) / 16) * 16;  // 16 unit levels
   static constexpr int YB_OFF = LV_OFF + 64;
@@ -103,7 +103,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 template <int D, int BITS, bool DQ>
 __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
     const uint16_t *__restrict__ x, int64_t n_tok, const uint32_t *__restrict__ scat,
-    const uint32_t *__restrict__ smask, const uint16_t *__restrict__ cells, Thresholds th,
+    const uint32_t *__restrict__ smask, const uint32_t *__restrict__ cells, Thresholds th,
     LevelsF32 lv, uint8_t *__restrict__ codes, uint16_t *__restrict__ dq,
     float *__restrict__ norms) {
   using SH = Shape<D>;
@@ -191,22 +191,6 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
     }
     __syncthreads();
 
-    // ---- threshold table of the batch (v-space): entry (token tk, base k)
-    if (wave == 0) {
-      const int tk = lane >> 4, k = lane & 15;
-      float ss = 0.f;
-#pragma unroll
-      for (int w = 0; w < W; w++) ss += npart[tk * W + w];
-      const float s = sqrtf(ss);
-      const float tv = (k < th.count) ? th.t[k] * s * scale_hd : __builtin_inff();
-      uint32_t *ent = (uint32_t *)(lds + SH::TT_OFF + 8 * lane);
-      ent[0] = __float_as_uint(tv);
-      ent[1] = (uint32_t)k;
-      const int64_t tok = b * TB + tk;
-      if (k == 0 && tok < n_tok) norms[tok] = s;
-    }
-    __syncthreads();
-
     // ---- compute: wave tiles q = wave, wave + W, ...
     for (int q = wave; q < WT; q += W) {
       // output side: row rl = lane >> 4 of the tile.  Before the stages
@@ -221,9 +205,9 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
 #pragma unroll
       for (int w = 0; w < W; w++) ss += npart[tko * W + w];
       const float s = sqrtf(ss);
-      const float us = (s > 0.f) ? 1.0f / (s * scale_hd) : 0.f;  // sqrt(d/h)/s
-      const float a2 = us * 16.0f;                               // 2 / delta, delta = 1/8
-      const float m2 = kMagic + (float)kCells + (float)(2 * kCells * tko);
+      const float us = (s > 0.f) ? 1.0f / (s * scale_hd) : 0.f;  // v -> sqrt(d) z
+      const float a8 = us * 64.0f;                               // 8 bytes / (1/8 cell)
+      constexpr float m8 = kMagic + (float)(kCellBytes / 2);      // cell 1024 at u = 0
       // input side: MFMA row r = lane & 15 -> slot r>>2, chunk (r&3) of each group
       const int sig_i = 4 * q + ((lane & 15) >> 2);
       const int tki = sig_i / P, ji = sig_i - tki * P;
@@ -286,6 +270,7 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
       // and group (g & ~m) | (rl & m) of that slot, m = 2^XB - 1.
       constexpr int XM = (1 << SH::XB) - 1;
       const int64_t tok = b * TB + tko;
+      if ((lane & 15) == 0 && (rl & XM) == 0 && jo == 0 && tok < n_tok) norms[tok] = s;
       uint8_t *dst0 = codes + tok * row_bytes + 16 * BITS * (jo * G + (rl & XM)) + BITS * (lane & 15);
       // fake quantization: coordinate of register (g, w, i) is
       // (jo + (g & XM)) S + ((g & ~XM) | (rl & XM)) 128 + 32 i + 16 w + (lane & 15)
@@ -299,13 +284,12 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
 #pragma unroll
           for (int i = 0; i < 4; i++) {
             const float val = v[g][w][i];
-            const float tq = __builtin_fmaf(val, a2, m2);
-            const uint32_t cell = __float_as_uint(tq) & 0x3FFEu;
-            const uint32_t e = *(const uint16_t *)(lds + SH::CT_OFF + cell);
+            // byte offset 8 floor(8u + 1024 + 1/16) of the cell (|u| < 128)
+            const float tq = __builtin_fmaf(val, a8, m8);
+            const uint32_t off = __float_as_uint(tq) & (uint32_t)(kCellBytes - 8);
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-            const u32x2 ent = *(const u32x2 *)(lds + SH::TT_OFF + e);  // {T, base}, 8-aligned
-            const float tv = __uint_as_float(ent[0]);
-            const uint32_t code = ent[1] + (val >= tv ? 1u : 0u);
+            const u32x2 ent = *(const u32x2 *)(lds + SH::CT_OFF + off);  // {tau, base}
+            const uint32_t code = ent[1] + (val * us >= __uint_as_float(ent[0]) ? 1u : 0u);
             if constexpr (DQ) {
               const float lvv = *(const float *)(lds + SH::LV_OFF + 4 * code);
               if (tok < n_tok)
@@ -333,15 +317,21 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
 
 template <int D, int BITS>
 hipError_t launch_one(const RotateArgs &a, const uint32_t *scat, const uint32_t *smask,
-                      const uint16_t *cells, const Thresholds &th) {
+                      const uint32_t *cells, const Thresholds &th) {
   using SH = Shape<D>;
   auto k = a.dequant_out ? rq_fast_kernel<D, BITS, true> : rq_fast_kernel<D, BITS, false>;
   int dev = 0, cus = 0;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  const int per_cu = (160 * 1024) / SH::LDS;
+  // persistent workgroups: exactly as many as can be resident at once
+  // (registers and LDS decide), each looping over batches, so no second
+  // partial round of workgroups and each pays its table set-up once
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 64 * SH::W, 0) != hipSuccess ||
+      per_cu <= 0)
+    per_cu = 1;
   const int64_t nb = (a.n_tok + SH::TB - 1) / SH::TB;
-  const int64_t want = (int64_t)(cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+  const int64_t want = (int64_t)(cus > 0 ? cus : 256) * per_cu;
   const int grid = (int)(nb < want ? nb : want);
   uint8_t *codes = a.dequant_out ? nullptr : (uint8_t *)a.out;
   uint16_t *dq = a.dequant_out ? (uint16_t *)a.out : nullptr;
@@ -352,7 +342,7 @@ hipError_t launch_one(const RotateArgs &a, const uint32_t *scat, const uint32_t 
 
 template <int D>
 hipError_t launch_d(const RotateArgs &a, const uint32_t *scat, const uint32_t *smask,
-                    const uint16_t *cells, const Thresholds &th) {
+                    const uint32_t *cells, const Thresholds &th) {
   switch (a.bits) {
     case 2: return launch_one<D, 2>(a, scat, smask, cells, th);
     case 3: return launch_one<D, 3>(a, scat, smask, cells, th);
@@ -363,7 +353,7 @@ hipError_t launch_d(const RotateArgs &a, const uint32_t *scat, const uint32_t *s
 }  // namespace
 
 hipError_t launch_rotate_quantize_fast(const RotateArgs &a, const uint32_t *scat,
-                                       const uint32_t *smask, const uint16_t *cells,
+                                       const uint32_t *smask, const uint32_t *cells,
                                        const Thresholds &th, bool *handled) {
   *handled = false;
   if (a.dtype != 1 || a.rotated_out) return hipSuccess;
