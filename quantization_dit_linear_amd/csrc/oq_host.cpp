@@ -217,11 +217,12 @@ int get_plan(int d, uint64_t seed, hipStream_t stream, const oq::DevicePlan **ou
 // kernel's per-wave threshold table: 128 s + 8 base, base = the code at the
 // window's lower edge.
 // Cell table of the bf16 fast path.  The kernel maps a unit-space value u
-// (= sqrt(d) z) to cell c = floor(8 u + 1024 + 1/16) of a 1/8-sigma grid
-// (2048 cells cover |u| < 128; |u| <= sqrt(d) < 128 for the fast path's d);
-// entry c = {tau, base}: base = number of thresholds at or below the cell,
-// tau = the only threshold that can fall inside it (or +inf), so the code is
-// base + (u >= tau).  A cell holding two thresholds would need a finer grid:
+// (= sqrt(d) z), clamped to [-8, 8), to cell c = floor(8 u + 64 + 1/16) of
+// a 1/8-sigma grid (128 cells; the first and last cells also take every
+// value beyond, where no threshold lies); entry c = {tau, base}: base =
+// number of thresholds at or below the cell, tau = the only threshold that
+// can fall inside it (or +inf), so the code is base + (u >= tau) with the
+// unclamped u.  A cell holding two thresholds would need a finer grid:
 // rejected (never the case for 2-4 bit Lloyd-Max codebooks).
 int build_cells(int bits, std::vector<uint32_t> &out) {
   double lv[16], th[15];
@@ -230,7 +231,9 @@ int build_cells(int bits, std::vector<uint32_t> &out) {
   const double delta = 0.125, eps = 0.02 * delta;
   out.assign(2 * oq::kFastCells, 0);
   for (int c = 0; c < oq::kFastCells; c++) {
-    const double lo = delta * (c - 1024.0625) - eps, hi = delta * (c - 1023.0625) + eps;
+    const double inf = std::numeric_limits<double>::infinity();
+    const double lo = c == 0 ? -inf : delta * (c - 64.0625) - eps;
+    const double hi = c == oq::kFastCells - 1 ? inf : delta * (c - 63.0625) + eps;
     int base = 0, inside = 0;
     for (int k = 0; k < T; k++) {
       if ((double)(float)th[k] <= lo) base++;

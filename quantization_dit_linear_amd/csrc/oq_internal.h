@@ -62,7 +62,7 @@ hipError_t launch_rotate_quantize_generic(const RotateArgs &a, const DevicePlan 
 hipError_t launch_rotate_quantize_fast(const RotateArgs &a, const uint32_t *scat,
                                        const uint32_t *smask, const uint32_t *cells,
                                        const Thresholds &th, bool *handled);
-constexpr int kFastCells = 2048;  // cells of the fast path's cell table ({tau, base} each)
+constexpr int kFastCells = 128;  // cells of the fast path's cell table ({tau, base} each)
 
 struct LinearArgs {
   const uint8_t *a_codes;

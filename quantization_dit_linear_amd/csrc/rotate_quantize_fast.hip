@@ -33,10 +33,11 @@
 //    a group bit in the lane, which the store addressing follows.
 //  * Quantize.  A magic-number fma turns v into the byte offset of its cell
 //    in a uniform grid over sqrt(d) z (step 1/8, narrower than any threshold
-//    gap); one 8-byte LDS read gives the code at the cell's lower edge and
-//    the only threshold that can fall inside the cell; one exact fp32
-//    compare of sqrt(d) z with it settles the code.  The table does not
-//    depend on the token, so it is loaded once per workgroup.
+//    gap; clamped to |sqrt(d) z| < 8, beyond every threshold); one 8-byte
+//    LDS read gives the code at the cell's lower edge and the only threshold
+//    that can fall inside the cell; one exact fp32 compare of sqrt(d) z with
+//    it settles the code.  The 1 KB table does not depend on the token, so
+//    it is loaded once per workgroup.
 //  * Pack.  A lane's 8 codes per group are exactly 8 consecutive storage
 //    slots, so they pack into one b-byte word per lane.  (Fake-quantization
 //    mode instead stores bf16 s * level[code] at every coordinate.)
@@ -51,7 +52,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kCells = kFastCells;           // grid cells per table copy
+constexpr int kCells = kFastCells;           // grid cells: |sqrt(d) z| < 8 in steps of 1/8
 constexpr int kCellBytes = kCells * 8;       // {float tau, uint base} per cell
 constexpr float kMagic = 12582912.0f;        // 1.5 * 2^23
 
@@ -71,7 +72,8 @@ struct Shape {
   static constexpr int S = H < 1024 ? H : 1024;       // slot: a block, or 1024 of one
   static constexpr int XB = ilog2(H / S);             // butterfly stages across slots
   static constexpr int P = D / S;                     // slots per token
-  static constexpr int TB = 4;                        // tokens per batch (one cell-table copy each)
+  // tokens per batch: 4, or 2 for long tokens when the slots still tile
+  static constexpr int TB = (D * 2 * 4 > 64 * 1024 && (2 * P) % 4 == 0) ? 2 : 4;
   static constexpr int WT = TB * P / 4;               // wave tiles per batch
   static constexpr int CH = D / 512;                  // 8-element chunks per token per 64 threads
   // waves per workgroup: divide both the wave tiles and the staging chunks;
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
       const float s = sqrtf(ss);
       const float us = (s > 0.f) ? 1.0f / (s * scale_hd) : 0.f;  // v -> sqrt(d) z
       const float a8 = us * 64.0f;                               // 8 bytes / (1/8 cell)
-      constexpr float m8 = kMagic + (float)(kCellBytes / 2);      // cell 1024 at u = 0
+      constexpr float m8 = kMagic + (float)(kCellBytes / 2);      // cell 64 at u = 0
       // input side: MFMA row r = lane & 15 -> slot r>>2, chunk (r&3) of each group
       const int sig_i = 4 * q + ((lane & 15) >> 2);
       const int tki = sig_i / P, ji = sig_i - tki * P;
@@ -284,8 +286,9 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
 #pragma unroll
           for (int i = 0; i < 4; i++) {
             const float val = v[g][w][i];
-            // byte offset 8 floor(8u + 1024 + 1/16) of the cell (|u| < 128)
-            const float tq = __builtin_fmaf(val, a8, m8);
+            // byte offset 8 floor(8u + 64 + 1/16) of the cell, u clamped to [-8, 8)
+            const float tq = __builtin_amdgcn_fmed3f(__builtin_fmaf(val, a8, m8), kMagic,
+                                                     kMagic + (float)(kCellBytes - 1));
             const uint32_t off = __float_as_uint(tq) & (uint32_t)(kCellBytes - 8);
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
             const u32x2 ent = *(const u32x2 *)(lds + SH::CT_OFF + off);  // {tau, base}
