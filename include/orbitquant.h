@@ -70,6 +70,10 @@ extern "C" {
 #define OQ_OUT_BF16_DEQUANT (1u << 2) /* oq_rotate_quantize writes the dequantized rotated token
                                          s * c_{code_i} (bf16 [n_tok][d], coordinate order, round
                                          to nearest even) instead of codes: fake quantization */
+#define OQ_ROT_INPUT_PERMUTED (1u << 3) /* the input rows are already in rotation order,
+                                           x'_i = x_{pi(i)} (see oq_permute_rows); only D and
+                                           H are applied.  Same outputs as the unpermuted rows
+                                           without this flag */
 
 /* Text for a status code.  Never NULL; the string is static. */
 const char *oq_strerror(int status);
@@ -98,8 +102,8 @@ int64_t oq_codes_bytes(int64_t rows, int d, int bits);
  *   x:      device, [n_tok][d] row-major, dtype OQ_F32 or OQ_BF16, 16-byte
  *           aligned
  *   seed:   rotation seed (selects Pi and D)
- *   flags:  OQ_ROT_NO_SIGNS, and at most one of OQ_OUT_F32_ROTATED,
- *           OQ_OUT_BF16_DEQUANT
+ *   flags:  OQ_ROT_NO_SIGNS, OQ_ROT_INPUT_PERMUTED, and at most one of
+ *           OQ_OUT_F32_ROTATED, OQ_OUT_BF16_DEQUANT
  *   out:    device; packed codes uint8 [n_tok][d*bits/8] (storage order,
  *           16-byte aligned), or with OQ_OUT_F32_ROTATED fp32 [n_tok][d], or
  *           with OQ_OUT_BF16_DEQUANT bf16 [n_tok][d]: coordinate i holds
@@ -145,8 +149,41 @@ int oq_linear(const uint8_t *a_codes, const float *a_norms, int a_bits,
               int64_t M, int64_t N, int K, uint16_t *y, void *stream);
 
 /* Free every cached rotation plan on every device (the caller must ensure
- * no enqueued work still uses them, e.g. by synchronising first). */
+ * no enqueued work still uses them, e.g. by synchronising first).  Handles
+ * from oq_plan_create stay valid to destroy but name no tables any more. */
 int oq_release_plans(void);
+
+/* Permute rows by the rotation permutation pi of (d = rows, seed):
+ * dst row i = src row pi(i), rows of row_bytes bytes each (any dtype).
+ * Folds pi into a producer: permuting the output rows of the layer that
+ * feeds the activations (and its bias), with an elementwise function such
+ * as GELU between, makes the activations arrive in rotation order, and
+ * oq_rotate_quantize with OQ_ROT_INPUT_PERMUTED then skips the permutation
+ * (paper.gecl.asia notes, Limitations: rotation and norm cost at run time).
+ * The signs D cannot be folded through a nonlinearity and stay in the call.
+ *   src, dst: device, caller-owned, distinct (no in-place), [rows][row_bytes]
+ *   rows:     the permutation length d: 128 <= d <= 16384, d % 128 == 0
+ *   row_bytes >= 1
+ * rows = 0 is rejected (there is no plan of length 0).
+ * Errors: OQ_EINVAL (null or equal pointers, row_bytes < 1), OQ_EUNSUPPORTED
+ * (rows), OQ_ENOMEM, OQ_EDEVICE. */
+int oq_permute_rows(const void *src, void *dst, int64_t rows, int64_t row_bytes, uint64_t seed,
+                    void *stream);
+
+/* Optional explicit plan ownership.  The compute calls build the rotation
+ * plan of (current device, d, seed) -- the permutation Pi and the signs D
+ * (pith.science Supplementary A setup) as device tables -- on first use and
+ * cache it.  oq_plan_create builds it now (no first-call latency) and pins
+ * it; oq_plan_destroy drops the pin and frees the tables when no other
+ * handle pins them (the caller must ensure no enqueued work still uses
+ * them).  A later compute call with the same (d, seed) rebuilds the plan.
+ *   d:     128 <= d <= 16384, d % 128 == 0   (else OQ_EUNSUPPORTED)
+ *   flags: 0 or OQ_ROT_NO_SIGNS (one plan serves both sign modes)
+ *   plan:  receives an opaque handle (NULL on error)
+ * Errors: OQ_EINVAL (null out pointer, bad flags, d <= 0, or a handle not
+ * made by oq_plan_create), OQ_EUNSUPPORTED, OQ_ENOMEM, OQ_EDEVICE. */
+int oq_plan_create(int d, uint64_t seed, uint32_t flags, void **plan);
+int oq_plan_destroy(void *plan);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "liborbitquant.so")
 
 OQ_OK, OQ_EINVAL, OQ_EUNSUPPORTED, OQ_ENOMEM, OQ_EDEVICE = 0, -1, -2, -3, -4
 OQ_F32, OQ_BF16 = 0, 1
-OQ_ROT_NO_SIGNS, OQ_OUT_F32_ROTATED, OQ_OUT_BF16_DEQUANT = 1, 2, 4
+OQ_ROT_NO_SIGNS, OQ_OUT_F32_ROTATED, OQ_OUT_BF16_DEQUANT, OQ_ROT_INPUT_PERMUTED = 1, 2, 4, 8
 
 # every symbol the header declares, with (restype, argtypes)
 _P = ctypes.c_void_p
@@ -43,6 +43,11 @@ _SIGS = {
     "oq_linear": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_int64,
                                  ctypes.c_int64, ctypes.c_int, _P, _P]),
     "oq_release_plans": (ctypes.c_int, []),
+    "oq_plan_create": (ctypes.c_int, [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32,
+                                      ctypes.POINTER(ctypes.c_void_p)]),
+    "oq_plan_destroy": (ctypes.c_int, [ctypes.c_void_p]),
+    "oq_permute_rows": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint64,
+                                       _P]),
 }
 
 _lib = None
@@ -121,8 +126,10 @@ def _dtype_code(t):
     raise TypeError(f"unsupported input dtype {t.dtype} (bfloat16 or float32)")
 
 
-def rotate_quantize(x, seed, bits, *, signs=True, out=None, norms=None, stream=None):
-    """Codes (uint8 [M, d*bits/8], storage order) and norms (float32 [M])."""
+def rotate_quantize(x, seed, bits, *, signs=True, permuted=False, out=None, norms=None,
+                    stream=None):
+    """Codes (uint8 [M, d*bits/8], storage order) and norms (float32 [M]).
+    permuted=True: x's columns are already in rotation order (OQ_ROT_INPUT_PERMUTED)."""
     import torch
     if x.dim() != 2:
         raise ValueError("x must be [tokens, d]")
@@ -131,7 +138,7 @@ def rotate_quantize(x, seed, bits, *, signs=True, out=None, norms=None, stream=N
         out = torch.empty((M, d * bits // 8), dtype=torch.uint8, device=x.device)
     if norms is None:
         norms = torch.empty((M,), dtype=torch.float32, device=x.device)
-    flags = 0 if signs else OQ_ROT_NO_SIGNS
+    flags = (0 if signs else OQ_ROT_NO_SIGNS) | (OQ_ROT_INPUT_PERMUTED if permuted else 0)
     rc = lib().oq_rotate_quantize(_dev_ptr(x, "x"), _dtype_code(x), M, d, seed, flags, bits,
                                   _dev_ptr(out, "out"), _dev_ptr(norms, "norms"),
                                   _stream(stream))
@@ -205,5 +212,42 @@ def linear(a_codes, a_norms, a_bits, w_codes, w_norms, w_bits, K, *, out=None, s
     return out
 
 
+def permute_rows(src, seed, *, out=None, stream=None):
+    """dst row i = src row pi(i) for the rotation permutation of (d =
+    src.shape[0], seed): folds pi into a producer's output rows (any dtype)."""
+    import torch
+    if out is None:
+        out = torch.empty_like(src)
+    rows = src.shape[0]
+    row_bytes = src[0].numel() * src.element_size() if rows else 0
+    rc = lib().oq_permute_rows(_dev_ptr(src, "src"), _dev_ptr(out, "dst"), rows, row_bytes,
+                               seed, _stream(stream))
+    _check(rc, "oq_permute_rows")
+    return out
+
+
 def release_plans():
     _check(lib().oq_release_plans(), "oq_release_plans")
+
+
+class Plan:
+    """Explicitly owned rotation plan of (current device, d, seed): built at
+    construction, its device tables freed by close() (or on leaving a
+    ``with`` block) once no other handle pins them."""
+
+    def __init__(self, d, seed, *, signs=True):
+        h = ctypes.c_void_p()
+        flags = 0 if signs else OQ_ROT_NO_SIGNS
+        _check(lib().oq_plan_create(d, seed, flags, ctypes.byref(h)), "oq_plan_create")
+        self._h = h
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            h, self._h = self._h, None
+            _check(lib().oq_plan_destroy(h), "oq_plan_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

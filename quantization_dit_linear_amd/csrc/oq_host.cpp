@@ -150,6 +150,13 @@ struct PlanKey {
 std::mutex g_plan_mu;
 std::map<PlanKey, oq::DevicePlan> g_plans;
 
+void free_plan_tables(const oq::DevicePlan &p) {
+  for (void *ptr : {(void *)p.scatter, (void *)p.scatter_nosign, (void *)p.fast_scatter,
+                    (void *)p.fast_signs, (void *)p.fast_nosigns, (void *)p.scatter_id,
+                    (void *)p.fast_signs_id, (void *)p.perm_inv})
+    if (ptr) (void)hipFree(ptr);
+}
+
 int get_plan(int d, uint64_t seed, hipStream_t stream, const oq::DevicePlan **out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return OQ_EDEVICE;
@@ -163,16 +170,18 @@ int get_plan(int d, uint64_t seed, hipStream_t stream, const oq::DevicePlan **ou
   std::vector<int32_t> perm;
   std::vector<uint8_t> neg;
   build_plan(d, seed, perm, neg);
-  std::vector<int32_t> sc(d), sc0(d);
-  std::vector<uint32_t> fsc(d), fsg(d / 2), fz(d / 2, 0u);
+  std::vector<int32_t> sc(d), sc0(d), sid(d);
+  std::vector<uint32_t> fsc(d), fsg(d / 2), fz(d / 2, 0u), fsid(d / 2);
   for (int i = 0; i < d; i++) {
     sc[perm[i]] = i | (neg[i] ? (int32_t)0x80000000 : 0);
     sc0[perm[i]] = i;
     fsc[perm[i]] = 2u * (uint32_t)i;  // source j = pi(i) goes to byte 2i
+    sid[i] = i | (neg[i] ? (int32_t)0x80000000 : 0);
   }
   for (int j = 0; j < d; j += 2) {
     const int i0 = sc0[j], i1 = sc0[j + 1];
     fsg[j / 2] = (neg[i0] ? 0x8000u : 0u) | (neg[i1] ? 0x80000000u : 0u);
+    fsid[j / 2] = (neg[j] ? 0x8000u : 0u) | (neg[j + 1] ? 0x80000000u : 0u);
   }
   oq::DevicePlan p;
   p.d = d;
@@ -185,7 +194,10 @@ int get_plan(int d, uint64_t seed, hipStream_t stream, const oq::DevicePlan **ou
              {(void **)&p.scatter_nosign, sc0.data(), sizeof(int32_t) * d},
              {(void **)&p.fast_scatter, fsc.data(), sizeof(uint32_t) * d},
              {(void **)&p.fast_signs, fsg.data(), sizeof(uint32_t) * (d / 2)},
-             {(void **)&p.fast_nosigns, fz.data(), sizeof(uint32_t) * (d / 2)}};
+             {(void **)&p.fast_nosigns, fz.data(), sizeof(uint32_t) * (d / 2)},
+             {(void **)&p.scatter_id, sid.data(), sizeof(int32_t) * d},
+             {(void **)&p.fast_signs_id, fsid.data(), sizeof(uint32_t) * (d / 2)},
+             {(void **)&p.perm_inv, sc0.data(), sizeof(int32_t) * d}};
   int rc = OQ_OK;
   for (auto &u : ups) {
     if (hipMalloc(u.dst, u.bytes) != hipSuccess) {
@@ -209,13 +221,6 @@ int get_plan(int d, uint64_t seed, hipStream_t stream, const oq::DevicePlan **ou
   return OQ_OK;
 }
 
-// Cell table of the fast path's quantizer for one bit width.  Cell c of the
-// grid (step delta = 1/8 in unit space) receives the values u with
-// round(2 u / delta + 2048) in {2c, 2c+1}, i.e. u in [delta (c - 1024.25),
-// delta (c - 1023.25)); widened by a margin it contains at most one
-// threshold.  Entry = byte offset of (slot copy s, base code) inside the
-// kernel's per-wave threshold table: 128 s + 8 base, base = the code at the
-// window's lower edge.
 // Cell table of the bf16 fast path.  The kernel maps a unit-space value u
 // (= sqrt(d) z), clamped to [-8, 8), to cell c = floor(8 u + 64 + 1/16) of
 // a 1/8-sigma grid (128 cells; the first and last cells also take every
@@ -291,7 +296,7 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
   if (n_tok < 0) return OQ_EINVAL;
   if (dtype != OQ_F32 && dtype != OQ_BF16) return OQ_EINVAL;
   const uint32_t outs = OQ_OUT_F32_ROTATED | OQ_OUT_BF16_DEQUANT;
-  if (flags & ~(OQ_ROT_NO_SIGNS | outs)) return OQ_EINVAL;
+  if (flags & ~(OQ_ROT_NO_SIGNS | OQ_ROT_INPUT_PERMUTED | outs)) return OQ_EINVAL;
   if ((flags & outs) && !allow_rotated) return OQ_EINVAL;
   if ((flags & outs) == outs) return OQ_EINVAL;
   int rc = check_d_bits(d, bits);
@@ -317,6 +322,7 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
   a.signs = !(flags & OQ_ROT_NO_SIGNS);
   a.rotated_out = (flags & OQ_OUT_F32_ROTATED) != 0;
   a.dequant_out = (flags & OQ_OUT_BF16_DEQUANT) != 0;
+  a.input_permuted = (flags & OQ_ROT_INPUT_PERMUTED) != 0;
   for (int k = 0; k < (1 << bits); k++) a.levels.v[k] = (float)lv[k];
   a.out = out;
   a.norms = norms;
@@ -326,8 +332,10 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
     rc = get_cells(bits, &cells);
     if (rc != OQ_OK) return rc;
     bool handled = false;
-    hipError_t e = oq::launch_rotate_quantize_fast(
-        a, plan->fast_scatter, a.signs ? plan->fast_signs : plan->fast_nosigns, cells, t, &handled);
+    const uint32_t *smask = a.input_permuted ? (a.signs ? plan->fast_signs_id : plan->fast_nosigns)
+                                             : (a.signs ? plan->fast_signs : plan->fast_nosigns);
+    hipError_t e =
+        oq::launch_rotate_quantize_fast(a, plan->fast_scatter, smask, cells, t, &handled);
     if (handled) return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
   }
   hipError_t e = oq::launch_rotate_quantize_generic(a, *plan, t);
@@ -407,6 +415,71 @@ int oq_linear(const uint8_t *a_codes, const float *a_norms, int a_bits, const ui
   return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
 }
 
+int oq_permute_rows(const void *src, void *dst, int64_t rows, int64_t row_bytes, uint64_t seed,
+                    void *stream) {
+  if (!src || !dst || src == dst || row_bytes < 1 || rows <= 0) return OQ_EINVAL;
+  if (rows % oq::kGroup != 0 || rows > oq::kMaxD) return OQ_EUNSUPPORTED;
+  const oq::DevicePlan *plan = nullptr;
+  int rc = get_plan((int)rows, seed, (hipStream_t)stream, &plan);
+  if (rc != OQ_OK) return rc;
+  hipError_t e =
+      oq::launch_permute_rows(src, dst, rows, row_bytes, plan->perm_inv, (hipStream_t)stream);
+  return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
+}
+
+// Explicit plan handles: a handle names a cache entry and pins it; the
+// entry's tables are freed when its last handle is destroyed (entries made
+// implicitly by the compute calls stay until oq_release_plans).
+struct PlanHandle {
+  uint32_t magic;
+  int dev, d;
+  uint64_t seed;
+};
+constexpr uint32_t kPlanMagic = 0x4f51504cu;  // "OQPL"
+
+int oq_plan_create(int d, uint64_t seed, uint32_t flags, void **plan) {
+  if (!plan) return OQ_EINVAL;
+  *plan = nullptr;
+  if (flags & ~OQ_ROT_NO_SIGNS) return OQ_EINVAL;
+  if (d <= 0) return OQ_EINVAL;
+  if (d % oq::kGroup != 0 || d > oq::kMaxD) return OQ_EUNSUPPORTED;
+  const oq::DevicePlan *p = nullptr;
+  int rc = get_plan(d, seed, nullptr, &p);
+  if (rc != OQ_OK) return rc;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return OQ_EDEVICE;
+  {
+    std::lock_guard<std::mutex> g(g_plan_mu);
+    auto it = g_plans.find(PlanKey{dev, d, seed});
+    if (it == g_plans.end()) return OQ_EDEVICE;  // released concurrently
+    it->second.pins++;
+  }
+  *plan = new PlanHandle{kPlanMagic, dev, d, seed};
+  return OQ_OK;
+}
+
+int oq_plan_destroy(void *plan) {
+  if (!plan) return OQ_EINVAL;
+  PlanHandle *h = (PlanHandle *)plan;
+  if (h->magic != kPlanMagic) return OQ_EINVAL;
+  int rc = OQ_OK;
+  {
+    std::lock_guard<std::mutex> g(g_plan_mu);
+    auto it = g_plans.find(PlanKey{h->dev, h->d, h->seed});
+    if (it != g_plans.end() && --it->second.pins <= 0) {
+      int cur = 0;
+      (void)hipGetDevice(&cur);
+      if (hipSetDevice(h->dev) != hipSuccess) rc = OQ_EDEVICE;
+      free_plan_tables(it->second);
+      (void)hipSetDevice(cur);
+      g_plans.erase(it);
+    }
+  }
+  h->magic = 0;
+  delete h;
+  return rc;
+}
+
 int oq_release_plans(void) {
   std::lock_guard<std::mutex> g(g_plan_mu);
   int rc = OQ_OK;
@@ -414,10 +487,7 @@ int oq_release_plans(void) {
     int cur = 0;
     (void)hipGetDevice(&cur);
     if (hipSetDevice(kv.first.dev) != hipSuccess) rc = OQ_EDEVICE;
-    for (void *ptr : {(void *)kv.second.scatter, (void *)kv.second.scatter_nosign,
-                      (void *)kv.second.fast_scatter, (void *)kv.second.fast_signs,
-                      (void *)kv.second.fast_nosigns})
-      if (ptr) (void)hipFree(ptr);
+    free_plan_tables(kv.second);
     (void)hipSetDevice(cur);
   }
   g_plans.clear();

@@ -38,6 +38,11 @@ struct DevicePlan {
   uint32_t *fast_scatter = nullptr;
   uint32_t *fast_signs = nullptr;
   uint32_t *fast_nosigns = nullptr;
+  // input already in rotation order (x'_i = x_{pi(i)}): identity placement
+  int32_t *scatter_id = nullptr;   // generic kernel: j | sign bit of D_j
+  uint32_t *fast_signs_id = nullptr;  // fast path: per dword pair, signs of D_j, D_j+1
+  int32_t *perm_inv = nullptr;     // pi^-1 (row permutation of oq_permute_rows)
+  int pins = 0;  // explicit handles (oq_plan_create) holding this plan
 };
 
 struct RotateArgs {
@@ -48,6 +53,7 @@ struct RotateArgs {
   bool signs;
   bool rotated_out;  // fp32 rotated unit vector instead of codes
   bool dequant_out;  // bf16 s * level[code] instead of codes
+  bool input_permuted;  // x already in rotation order: D and H only
   LevelsF32 levels;  // unit levels (dequant_out)
   void *out;
   float *norms;
@@ -78,5 +84,9 @@ struct LinearArgs {
 };
 
 hipError_t launch_linear(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw);
+
+// dst row pi^-1(j) = src row j, i.e. dst[i] = src[pi(i)], rows of row_bytes
+hipError_t launch_permute_rows(const void *src, void *dst, int64_t rows, int64_t row_bytes,
+                               const int32_t *perm_inv, hipStream_t stream);
 
 }  // namespace oq

@@ -59,8 +59,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void rq_generic_kernel(
     const void *__restrict__ x, int dtype, int64_t n_tok, int d, int h,
-    const int32_t *__restrict__ scatter, Thresholds th, LevelsF32 lv, uint8_t *__restrict__ codes,
-    float *__restrict__ zout, uint16_t *__restrict__ dq, float *__restrict__ norms) {
+    const int32_t *__restrict__ scatter, int sign_on, Thresholds th, LevelsF32 lv,
+    uint8_t *__restrict__ codes, float *__restrict__ zout, uint16_t *__restrict__ dq,
+    float *__restrict__ norms) {
   extern __shared__ float y[];  // d floats
   __shared__ double red[kThreads / 64];
   const int tid = threadIdx.x;
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void rq_generic_kernel(
       float v = load_elem(x, dtype, t * d + j);
       ss = fmaf(v, v, ss);
       int32_t e = scatter[j];
-      y[e & 0x7fffffff] = (e < 0) ? -v : v;
+      y[e & 0x7fffffff] = (e < 0 && sign_on) ? -v : v;
     }
     double total = block_sum((double)ss, red);
     __syncthreads();
@@ -116,11 +117,48 @@ __global__ __launch_bounds__(kThreads) void rq_generic_kernel(
   }
 }
 
+// Row permutation: source row j goes to destination row perm_inv[j], in
+// units of V bytes (16 when sizes and pointers allow).
+template <typename V>
+__global__ __launch_bounds__(256) void permute_rows_kernel(const V *__restrict__ src,
+                                                           V *__restrict__ dst, int64_t rows,
+                                                           int64_t row_units,
+                                                           const int32_t *__restrict__ perm_inv) {
+  for (int64_t j = blockIdx.x; j < rows; j += gridDim.x) {
+    const V *s = src + j * row_units;
+    V *d = dst + (int64_t)perm_inv[j] * row_units;
+    for (int64_t u = threadIdx.x; u < row_units; u += blockDim.x) d[u] = s[u];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_permute_rows(const void *src, void *dst, int64_t rows, int64_t row_bytes,
+                               const int32_t *perm_inv, hipStream_t stream) {
+  const uintptr_t al = (uintptr_t)src | (uintptr_t)dst | (uintptr_t)row_bytes;
+  const int grid = (int)(rows < 4096 ? rows : 4096);
+  if (al % 16 == 0) {
+    hipLaunchKernelGGL(permute_rows_kernel<uint4>, dim3(grid), dim3(256), 0, stream,
+                       (const uint4 *)src, (uint4 *)dst, rows, row_bytes / 16, perm_inv);
+  } else if (al % 4 == 0) {
+    hipLaunchKernelGGL(permute_rows_kernel<uint32_t>, dim3(grid), dim3(256), 0, stream,
+                       (const uint32_t *)src, (uint32_t *)dst, rows, row_bytes / 4, perm_inv);
+  } else if (al % 2 == 0) {
+    hipLaunchKernelGGL(permute_rows_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
+                       (const uint16_t *)src, (uint16_t *)dst, rows, row_bytes / 2, perm_inv);
+  } else {
+    hipLaunchKernelGGL(permute_rows_kernel<uint8_t>, dim3(grid), dim3(256), 0, stream,
+                       (const uint8_t *)src, (uint8_t *)dst, rows, row_bytes, perm_inv);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_rotate_quantize_generic(const RotateArgs &a, const DevicePlan &p,
                                           const Thresholds &th) {
-  const int32_t *sc = a.signs ? p.scatter : p.scatter_nosign;
+  // placement table: pi^-1 with sign bits, or the identity with sign bits
+  // when the input is already in rotation order
+  const int32_t *sc = a.input_permuted ? p.scatter_id : (a.signs ? p.scatter : p.scatter_nosign);
+  const int sign_on = a.signs ? 1 : 0;
   int dev = 0, cus = 0;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -147,15 +185,15 @@ hipError_t launch_rotate_quantize_generic(const RotateArgs &a, const DevicePlan 
   switch (a.bits) {
     case 2:
       hipLaunchKernelGGL(rq_generic_kernel<2>, dim3(grid), dim3(kThreads), lds, a.stream, a.x,
-                         a.dtype, a.n_tok, a.d, a.h, sc, th, a.levels, codes, zout, dq, a.norms);
+                         a.dtype, a.n_tok, a.d, a.h, sc, sign_on, th, a.levels, codes, zout, dq, a.norms);
       break;
     case 3:
       hipLaunchKernelGGL(rq_generic_kernel<3>, dim3(grid), dim3(kThreads), lds, a.stream, a.x,
-                         a.dtype, a.n_tok, a.d, a.h, sc, th, a.levels, codes, zout, dq, a.norms);
+                         a.dtype, a.n_tok, a.d, a.h, sc, sign_on, th, a.levels, codes, zout, dq, a.norms);
       break;
     case 4:
       hipLaunchKernelGGL(rq_generic_kernel<4>, dim3(grid), dim3(kThreads), lds, a.stream, a.x,
-                         a.dtype, a.n_tok, a.d, a.h, sc, th, a.levels, codes, zout, dq, a.norms);
+                         a.dtype, a.n_tok, a.d, a.h, sc, sign_on, th, a.levels, codes, zout, dq, a.norms);
       break;
     default:
       return hipErrorInvalidValue;

@@ -15,6 +15,9 @@
 //    ds_write_b16 to its permuted position pi^-1(j) in LDS.  Scatter
 //    addresses and sign masks stay in registers for the whole kernel; d is a
 //    template parameter so every LDS base folds into instruction offsets.
+//    When the input arrives already in rotation order (the producer's output
+//    rows were permuted by pi, see oq_permute_rows) the chunk is stored as
+//    one 16-byte LDS write after the sign XOR: no scatter at all.
 //  * Norm.  The 8 bf16 of a staged chunk are an MFMA operand as they are:
 //    mfma(X, X) accumulates X X^T, whose trace is the sum of squares.
 //  * Walsh-Hadamard, stages 0-4.  bf16 values are exact MFMA operands and
@@ -102,7 +105,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 // DQ: write bf16 s * level[code] at every coordinate (dq) instead of codes.
-template <int D, int BITS, bool DQ>
+// IDENT: the input is already in rotation order (x'_i = x_{pi(i)}); scat is
+// unused and smask holds the sign masks of the coordinates in place.
+template <int D, int BITS, bool DQ, bool IDENT>
 __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
     const uint16_t *__restrict__ x, int64_t n_tok, const uint32_t *__restrict__ scat,
     const uint32_t *__restrict__ smask, const uint32_t *__restrict__ cells, Thresholds th,
@@ -125,15 +130,18 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
   }
 
   // per-thread staging: chunk c of every token covers x[8*pos, 8*pos+8)
-  uint32_t saddr[CPT][8], smk[CPT][4];
+  uint32_t saddr[IDENT ? 1 : CPT][8], smk[CPT][4];
 #pragma unroll
   for (int c = 0; c < CPT; c++) {
     const int pos = tid + c * W * 64;
+    if constexpr (!IDENT) {
 #pragma unroll
-    for (int e = 0; e < 8; e++) saddr[c][e] = scat[pos * 8 + e];
+      for (int e = 0; e < 8; e++) saddr[c][e] = scat[pos * 8 + e];
+    }
 #pragma unroll
     for (int e = 0; e < 4; e++) smk[c][e] = smask[pos * 4 + e];
   }
+  (void)saddr;
 
   // H_32 operands: lane holds H[k][n] for k = 8(lane>>4)+e, n = lane&15 (+16)
   bf16x8 hb0, hb1;
@@ -174,11 +182,17 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
       for (int c = 0; c < CPT; c++) {
         const bf16x8 xv = __builtin_bit_cast(bf16x8, stg[tk][c]);
         gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, xv, gram, 0, 0, 0);
+        if constexpr (IDENT) {
+          *(u32x4 *)(yb + 16 * (tid + c * W * 64)) =
+              u32x4{stg[tk][c][0] ^ smk[c][0], stg[tk][c][1] ^ smk[c][1],
+                    stg[tk][c][2] ^ smk[c][2], stg[tk][c][3] ^ smk[c][3]};
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const uint32_t v = stg[tk][c][e] ^ smk[c][e];
-          *(uint16_t *)(yb + saddr[c][2 * e]) = (uint16_t)v;
-          *(uint16_t *)(yb + saddr[c][2 * e + 1]) = (uint16_t)(v >> 16);
+          for (int e = 0; e < 4; e++) {
+            const uint32_t v = stg[tk][c][e] ^ smk[c][e];
+            *(uint16_t *)(yb + saddr[c][2 * e]) = (uint16_t)v;
+            *(uint16_t *)(yb + saddr[c][2 * e + 1]) = (uint16_t)(v >> 16);
+          }
         }
       }
       // trace of the Gram matrix: diagonal entry r sits in lane 16(r/4)+r, register r%4
@@ -322,7 +336,10 @@ template <int D, int BITS>
 hipError_t launch_one(const RotateArgs &a, const uint32_t *scat, const uint32_t *smask,
                       const uint32_t *cells, const Thresholds &th) {
   using SH = Shape<D>;
-  auto k = a.dequant_out ? rq_fast_kernel<D, BITS, true> : rq_fast_kernel<D, BITS, false>;
+  auto k = a.dequant_out ? (a.input_permuted ? rq_fast_kernel<D, BITS, true, true>
+                                             : rq_fast_kernel<D, BITS, true, false>)
+                         : (a.input_permuted ? rq_fast_kernel<D, BITS, false, true>
+                                             : rq_fast_kernel<D, BITS, false, false>);
   int dev = 0, cus = 0;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

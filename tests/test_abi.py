@@ -158,3 +158,30 @@ def test_flag_and_status_constants_match_header(q):
         assert getattr(q, name) == 1 << int(val), name
     for name in ("OQ_ROT_NO_SIGNS", "OQ_OUT_F32_ROTATED", "OQ_OUT_BF16_DEQUANT"):
         assert re.search(r"#define\s+" + name + r"\b", src), name
+
+
+def test_plan_handles_validate_before_hip(q):
+    import ctypes
+    L = q.lib()
+    h = ctypes.c_void_p(123)
+    assert L.oq_plan_create(3072, 1, 0, None) == q.OQ_EINVAL
+    assert L.oq_plan_create(3072, 1, 1 << 4, ctypes.byref(h)) == q.OQ_EINVAL
+    assert h.value is None  # cleared on error
+    assert L.oq_plan_create(0, 1, 0, ctypes.byref(h)) == q.OQ_EINVAL
+    assert L.oq_plan_create(3000, 1, 0, ctypes.byref(h)) == q.OQ_EUNSUPPORTED
+    assert L.oq_plan_create(32768, 1, 0, ctypes.byref(h)) == q.OQ_EUNSUPPORTED
+    assert L.oq_plan_destroy(None) == q.OQ_EINVAL
+    junk = (ctypes.c_uint32 * 8)()  # not a handle: wrong tag
+    assert L.oq_plan_destroy(ctypes.cast(junk, ctypes.c_void_p)) == q.OQ_EINVAL
+
+
+def test_permute_rows_validates_before_hip(q):
+    L = q.lib()
+    f = L.oq_permute_rows
+    assert f(None, B16, 3072, 16, 1, None) == q.OQ_EINVAL
+    assert f(A16, None, 3072, 16, 1, None) == q.OQ_EINVAL
+    assert f(A16, A16, 3072, 16, 1, None) == q.OQ_EINVAL  # in place is not supported
+    assert f(A16, B16, 3072, 0, 1, None) == q.OQ_EINVAL
+    assert f(A16, B16, 0, 16, 1, None) == q.OQ_EINVAL
+    assert f(A16, B16, 3000, 16, 1, None) == q.OQ_EUNSUPPORTED
+    assert f(A16, B16, 32768, 16, 1, None) == q.OQ_EUNSUPPORTED

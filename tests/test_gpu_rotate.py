@@ -135,3 +135,26 @@ def test_full_size_sampled_rows(q, cfg, name):
     rc, rn, rz = oracle.rotate_quantize(x[rows], lin.act.dtype, d, lin.seed, bits, want_z=True)
     parity.assert_codes_match(host(codes)[rows], rc, rz, d, bits, _thr(bits), f"{cfg}/{name}")
     parity.assert_norms_match(host(norms)[rows], rn, f"{cfg}/{name}")
+
+
+def test_explicit_plan_handles(q):
+    """oq_plan_create / oq_plan_destroy: results are the same with a pinned
+    plan, after it is freed (rebuilt lazily), and with two handles."""
+    import torch
+    d = 3072
+    x = wl.custom_activations(20, d, wl.BF16, 77, n_out=2, out_factor=20.0, sigma_s=1.0)
+    xd = to_device(x)
+    say("plan handles")
+    with q.Plan(d, 1234):
+        c1, n1 = q.rotate_quantize(xd, 1234, 4)
+        torch.cuda.synchronize()
+    c2, n2 = q.rotate_quantize(xd, 1234, 4)
+    torch.cuda.synchronize()
+    p1, p2 = q.Plan(d, 1234), q.Plan(d, 1234)
+    p1.close()
+    c3, _ = q.rotate_quantize(xd, 1234, 4)
+    torch.cuda.synchronize()
+    p2.close()
+    assert torch.equal(c1, c2) and torch.equal(c1, c3) and torch.equal(n1, n2)
+    rc, rn, rz = oracle.rotate_quantize(x, wl.BF16, d, 1234, 4, want_z=True)
+    parity.assert_codes_match(host(c1), rc, rz, d, 4, _thr(4), "plan handles")
