@@ -185,6 +185,48 @@ def fake_quant_path(q, x, W, seed, ba, bw, iters=10):
             "ms": round(ms, 4)}
 
 
+def adaln_rtn4(q, name, iters=50):
+    """The AdaLN modulation projection of the same model size with INT4
+    weight-only RTN weights (oq_rtn4_linear), HBM-bound: weight nibbles +
+    scales + activations + outputs per launch."""
+    import torch
+    import workloads as wl
+    x_np, W_np = wl.adaln_inputs(name)
+    x, W = to_dev(x_np), to_dev(W_np)
+    q4, sc = q.rtn4_prepare_weights(W)
+    M, K = x.shape
+    N = W.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    for _ in range(3):
+        q.rtn4_linear(x, q4, sc, out=y)
+    torch.cuda.synchronize()
+    # a launch takes a few microseconds on the GPU and more on the host side
+    # (Python, ctypes): replay the launches from a captured HIP graph so the
+    # timing is the GPU's
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for _ in range(iters):
+            q.rtn4_linear(x, q4, sc, out=y)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 4
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (iters * reps)
+    byts = N * K / 2 + 4 * N + 2 * M * K + 2 * M * N
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"shape": f"{M} x {K} -> {N} ({name} DiT block)", "ms": round(ms, 5),
+            "timing": "HIP graph of back-to-back launches",
+            "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def _short_kernel_name(name):
     n = name.replace("(anonymous namespace)::", "").replace("oq::", "")
     if "(" in n:
@@ -391,6 +433,7 @@ def main():
     lin_steps = np.array([e[2].elapsed_time(e[3]) for e in evs])
     ref_gemm = None if a.no_ref_gemm else library_fp16_gemm(M, N, K)
     fq_path = None if a.no_ref_gemm else fake_quant_path(q, xs[0], Ws[0], lin.seed, ba, bw)
+    adaln = None if a.no_ref_gemm else adaln_rtn4(q, "image" if K == 3072 else "video")
 
     flops = 2.0 * M * N * K
     in_b = 2 if lin.act.dtype == wl.BF16 else 4
@@ -448,6 +491,8 @@ def main():
     if ref_gemm is not None:
         out["reference_fp16_gemm"] = dict(ref_gemm, linear_over_reference=round(
             ref_gemm["ms"] / t_lin, 3))
+    if adaln is not None:
+        out["adaln_rtn4"] = adaln
     if fq_path is not None:
         out["fake_quant_path"] = dict(fq_path, native_step_speedup=round(
             fq_path["ms"] / ms_step, 3))

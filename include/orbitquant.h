@@ -153,6 +153,32 @@ int oq_linear(const uint8_t *a_codes, const float *a_norms, int a_bits,
  * from oq_plan_create stay valid to destroy but name no tables any more. */
 int oq_release_plans(void);
 
+/* INT4 weight-only round-to-nearest for the AdaLN modulation projections
+ * (paper.gecl.asia notes, Method item 5: a rotation cannot be folded into a
+ * dynamic modulation, so those weights get INT4 RTN and the activations
+ * stay unquantized; researchpod.app transcript).  Per output row n:
+ * amax = max_k |W_nk|, scale_n = amax / 7, q_nk = rint(W_nk * (7 / amax)) in
+ * [-7, 7], the decisions taken in fp32 (IEEE division and product, ties to
+ * even); a zero row gives q = 0, scale 0.
+ *   W:      device, fp32 or bf16 [n_out][d_in] (4-byte aligned)
+ *   q4:     device uint8 [n_out][d_in/2] (16-byte aligned): nibble q + 8,
+ *           coordinate 2i in the low nibble of byte i
+ *   scales: device fp32 [n_out]
+ *   d_in % 32 == 0, d_in <= 16384 (else OQ_EUNSUPPORTED); n_out = 0 no-op.
+ * Errors: OQ_EINVAL, OQ_EUNSUPPORTED, OQ_EDEVICE. */
+int oq_rtn4_prepare_weights(const void *W, int dtype, int64_t n_out, int d_in, uint8_t *q4,
+                            float *scales, void *stream);
+
+/* The AdaLN projection with those weights:
+ *   y[m][n] = bf16( scale_n sum_k x_mk q_nk )
+ * fp32 accumulation (exact products), one bf16 rounding (nearest even), no
+ * bias.  x: device fp32 or bf16 [M][K] (16-byte aligned); y: bf16 [M][N].
+ * Sized for modulation inputs (one row per sample): weights are read once
+ * per block of 8 rows.  K % 32 == 0, K <= 16384; M = 0 or N = 0 no-op.
+ * Errors: OQ_EINVAL, OQ_EUNSUPPORTED, OQ_EDEVICE. */
+int oq_rtn4_linear(const void *x, int dtype, int64_t M, const uint8_t *q4, const float *scales,
+                   int64_t N, int K, uint16_t *y, void *stream);
+
 /* Permute rows by the rotation permutation pi of (d = rows, seed):
  * dst row i = src row pi(i), rows of row_bytes bytes each (any dtype).
  * Folds pi into a producer: permuting the output rows of the layer that

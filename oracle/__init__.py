@@ -66,6 +66,11 @@ def _load():
     lib.oqo_fake_quantize.restype = ctypes.c_int
     lib.oqo_fake_quantize.argtypes = [P, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                       ctypes.c_uint64, ctypes.c_int, ctypes.c_int, P, P]
+    lib.oqo_rtn4_quantize.restype = ctypes.c_int
+    lib.oqo_rtn4_quantize.argtypes = [P, ctypes.c_int, ctypes.c_int64, ctypes.c_int, P, P]
+    lib.oqo_rtn4_linear.restype = ctypes.c_int
+    lib.oqo_rtn4_linear.argtypes = [P, ctypes.c_int, ctypes.c_int64, P, P, ctypes.c_int64,
+                                    ctypes.c_int, P]
     lib.oqo_num_threads.restype = ctypes.c_int
     lib.oqo_num_threads.argtypes = []
     _lib = lib
@@ -226,6 +231,32 @@ def fake_quantize(x, dtype, d, seed, bits, use_signs=True):
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out, norms
+
+
+def rtn4_quantize(W, dtype, d):
+    """INT4 weight-only RTN per row (AdaLN projections): (q int8 [rows, d] in
+    [-7, 7], scales float32 [rows]).  paper.gecl.asia notes, Method item 5."""
+    W = np.ascontiguousarray(W)
+    rows = W.shape[0]
+    assert W.shape[1] == d
+    q = np.empty((rows, d), np.int8)
+    scales = np.empty(rows, np.float32)
+    if _load().oqo_rtn4_quantize(_ptr(W), dtype, rows, d, _ptr(q), _ptr(scales)) != 0:
+        raise ValueError("oracle rejected the arguments")
+    return q, scales
+
+
+def rtn4_linear(x, dtype, q, scales):
+    """fp64 y[m][n] = scale_n sum_k x_mk q_nk."""
+    x = np.ascontiguousarray(x)
+    q = np.ascontiguousarray(q, np.int8)
+    scales = np.ascontiguousarray(scales, np.float32)
+    M, K = x.shape
+    N = q.shape[0]
+    y = np.empty((M, N), np.float64)
+    if _load().oqo_rtn4_linear(_ptr(x), dtype, M, _ptr(q), _ptr(scales), N, K, _ptr(y)) != 0:
+        raise ValueError("oracle rejected the arguments")
+    return y
 
 
 def num_threads():

@@ -387,5 +387,53 @@ int oqo_fake_quantize(const void *x, int dtype, int64_t rows, int d, uint64_t se
     return 0;
 }
 
+/* INT4 weight-only round-to-nearest of the AdaLN modulation projections
+ * (paper.gecl.asia notes, Method item 5: no rotation can be folded into a
+ * dynamic modulation, so those weights get INT4 RTN only; researchpod.app
+ * transcript).  Per output row: amax = max |w|, scale = amax / 7,
+ * q = rint(w * (7 / amax)) in [-7, 7].  These are integer decisions made in
+ * floating point, so they are taken in fp32 (IEEE division and product,
+ * ties to even) exactly as the library takes them; amax = 0 gives q = 0 and
+ * scale 0. */
+int oqo_rtn4_quantize(const void *W, int dtype, int64_t rows, int d, int8_t *q, float *scales)
+{
+    if (d <= 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        float amax = 0.0f;
+        for (int k = 0; k < d; k++) {
+            const float w = (float)load_elem(W, dtype, (size_t)r * d + k);
+            const float a = fabsf(w);
+            if (a > amax) amax = a;
+        }
+        const float inv = amax > 0.0f ? 7.0f / amax : 0.0f;
+        scales[r] = amax / 7.0f;
+        for (int k = 0; k < d; k++) {
+            const float w = (float)load_elem(W, dtype, (size_t)r * d + k);
+            const float t = w * inv;
+            q[(size_t)r * d + k] = (int8_t)rintf(t);
+        }
+    }
+    return 0;
+}
+
+/* y[m][n] = scale_n sum_k x_mk q_nk in fp64 (the AdaLN projection with
+ * INT4 RTN weights; activations unquantized). */
+int oqo_rtn4_linear(const void *x, int dtype, int64_t M, const int8_t *q, const float *scales,
+                    int64_t N, int K, double *y)
+{
+    if (K <= 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t n = 0; n < N; n++) {
+            double acc = 0.0;
+            for (int k = 0; k < K; k++)
+                acc += load_elem(x, dtype, (size_t)m * K + k) * (double)q[(size_t)n * K + k];
+            y[(size_t)m * N + n] = acc * (double)scales[n];
+        }
+    }
+    return 0;
+}
+
 /* Threads an OpenMP region of this oracle uses (for reporting). */
 int oqo_num_threads(void) { return omp_get_max_threads(); }

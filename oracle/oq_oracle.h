@@ -33,5 +33,8 @@ int oqo_linear(const uint8_t *a_codes, const double *a_norms, int ba,
                int64_t N, int K, const int64_t *rows, int64_t nrows, double *y);
 int oqo_fake_quantize(const void *x, int dtype, int64_t rows, int d, uint64_t seed,
                       int use_signs, int bits, double *out, double *norms);
+int oqo_rtn4_quantize(const void *W, int dtype, int64_t rows, int d, int8_t *q, float *scales);
+int oqo_rtn4_linear(const void *x, int dtype, int64_t M, const int8_t *q, const float *scales,
+                    int64_t N, int K, double *y);
 int oqo_num_threads(void);
 #endif

@@ -48,6 +48,10 @@ _SIGS = {
     "oq_plan_destroy": (ctypes.c_int, [ctypes.c_void_p]),
     "oq_permute_rows": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint64,
                                        _P]),
+    "oq_rtn4_prepare_weights": (ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                               _P, _P, _P]),
+    "oq_rtn4_linear": (ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int64, _P, _P, ctypes.c_int64,
+                                      ctypes.c_int, _P, _P]),
 }
 
 _lib = None
@@ -209,6 +213,36 @@ def linear(a_codes, a_norms, a_bits, w_codes, w_norms, w_bits, K, *, out=None, s
                          _dev_ptr(w_codes, "w_codes"), _dev_ptr(w_norms, "w_norms"), w_bits,
                          M, N, K, _dev_ptr(out, "y"), _stream(stream))
     _check(rc, "oq_linear")
+    return out
+
+
+def rtn4_prepare_weights(W, *, out=None, scales=None, stream=None):
+    """INT4 weight-only RTN of the AdaLN projection weights W [N, K]:
+    (uint8 [N, K/2] offset-binary nibbles, float32 scales [N])."""
+    import torch
+    N, K = W.shape
+    if out is None:
+        out = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    if scales is None:
+        scales = torch.empty((N,), dtype=torch.float32, device=W.device)
+    rc = lib().oq_rtn4_prepare_weights(_dev_ptr(W, "W"), _dtype_code(W), N, K,
+                                       _dev_ptr(out, "q4"), _dev_ptr(scales, "scales"),
+                                       _stream(stream))
+    _check(rc, "oq_rtn4_prepare_weights")
+    return out, scales
+
+
+def rtn4_linear(x, q4, scales, *, out=None, stream=None):
+    """bf16 y [M, N] = scale_n sum_k x_mk q_nk (AdaLN projection)."""
+    import torch
+    M, K = x.shape
+    N = q4.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    rc = lib().oq_rtn4_linear(_dev_ptr(x, "x"), _dtype_code(x), M, _dev_ptr(q4, "q4"),
+                              _dev_ptr(scales, "scales"), N, K, _dev_ptr(out, "y"),
+                              _stream(stream))
+    _check(rc, "oq_rtn4_linear")
     return out
 
 

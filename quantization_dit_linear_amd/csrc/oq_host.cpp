@@ -415,6 +415,33 @@ int oq_linear(const uint8_t *a_codes, const float *a_norms, int a_bits, const ui
   return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
 }
 
+int oq_rtn4_prepare_weights(const void *W, int dtype, int64_t n_out, int d_in, uint8_t *q4,
+                            float *scales, void *stream) {
+  if (n_out < 0 || d_in <= 0) return OQ_EINVAL;
+  if (dtype != OQ_F32 && dtype != OQ_BF16) return OQ_EINVAL;
+  if (d_in % 32 != 0 || d_in > 16384) return OQ_EUNSUPPORTED;
+  if (n_out == 0) return OQ_OK;
+  if (!W || !q4 || !scales) return OQ_EINVAL;
+  if (!aligned(W, 4) || !aligned(q4, 16) || !aligned(scales, 4)) return OQ_EINVAL;
+  hipError_t e = oq::launch_rtn4_prepare(W, dtype, n_out, d_in, q4, scales, (hipStream_t)stream);
+  return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
+}
+
+int oq_rtn4_linear(const void *x, int dtype, int64_t M, const uint8_t *q4, const float *scales,
+                   int64_t N, int K, uint16_t *y, void *stream) {
+  if (M < 0 || N < 0 || K <= 0) return OQ_EINVAL;
+  if (dtype != OQ_F32 && dtype != OQ_BF16) return OQ_EINVAL;
+  if (K % 32 != 0 || K > 16384) return OQ_EUNSUPPORTED;
+  if (M == 0 || N == 0) return OQ_OK;
+  if (N > ((int64_t)1 << 34) / 16) return OQ_EUNSUPPORTED;
+  if (!x || !q4 || !scales || !y) return OQ_EINVAL;
+  if (!aligned(x, 16) || !aligned(q4, 16) || !aligned(scales, 4) || !aligned(y, 2))
+    return OQ_EINVAL;
+  hipError_t e =
+      oq::launch_rtn4_linear(x, dtype, M, q4, scales, N, K, y, (hipStream_t)stream);
+  return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
+}
+
 int oq_permute_rows(const void *src, void *dst, int64_t rows, int64_t row_bytes, uint64_t seed,
                     void *stream) {
   if (!src || !dst || src == dst || row_bytes < 1 || rows <= 0) return OQ_EINVAL;

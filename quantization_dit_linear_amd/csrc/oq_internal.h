@@ -85,6 +85,13 @@ struct LinearArgs {
 
 hipError_t launch_linear(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw);
 
+// INT4 weight-only round-to-nearest (AdaLN projections)
+hipError_t launch_rtn4_prepare(const void *W, int dtype, int64_t rows, int d, uint8_t *q4,
+                               float *scales, hipStream_t stream);
+hipError_t launch_rtn4_linear(const void *x, int dtype, int64_t M, const uint8_t *q4,
+                              const float *scales, int64_t N, int K, uint16_t *y,
+                              hipStream_t stream);
+
 // dst row pi^-1(j) = src row j, i.e. dst[i] = src[pi(i)], rows of row_bytes
 hipError_t launch_permute_rows(const void *src, void *dst, int64_t rows, int64_t row_bytes,
                                const int32_t *perm_inv, hipStream_t stream);

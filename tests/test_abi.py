@@ -185,3 +185,22 @@ def test_permute_rows_validates_before_hip(q):
     assert f(A16, B16, 0, 16, 1, None) == q.OQ_EINVAL
     assert f(A16, B16, 3000, 16, 1, None) == q.OQ_EUNSUPPORTED
     assert f(A16, B16, 32768, 16, 1, None) == q.OQ_EUNSUPPORTED
+
+
+def test_rtn4_validates_before_hip(q):
+    L = q.lib()
+    p = L.oq_rtn4_prepare_weights
+    assert p(None, 1, 8, 256, B16, C16, None) == q.OQ_EINVAL
+    assert p(A16, 1, 8, 256, None, C16, None) == q.OQ_EINVAL
+    assert p(A16, 1, 8, 256, B16 + 4, C16, None) == q.OQ_EINVAL
+    assert p(A16, 5, 8, 256, B16, C16, None) == q.OQ_EINVAL
+    assert p(A16, 1, 8, 100, B16, C16, None) == q.OQ_EUNSUPPORTED
+    assert p(A16, 1, -1, 256, B16, C16, None) == q.OQ_EINVAL
+    assert p(None, 1, 0, 256, None, None, None) == q.OQ_OK
+    f = L.oq_rtn4_linear
+    assert f(None, 1, 2, B16, C16, 8, 256, A16, None) == q.OQ_EINVAL
+    assert f(A16, 1, 2, B16 + 8, C16, 8, 256, A16, None) == q.OQ_EINVAL
+    assert f(A16 + 4, 1, 2, B16, C16, 8, 256, A16, None) == q.OQ_EINVAL
+    assert f(A16, 1, 2, B16, C16, 8, 100, A16, None) == q.OQ_EUNSUPPORTED
+    assert f(A16, 1, 2, B16, C16, 8, 32768, A16, None) == q.OQ_EUNSUPPORTED
+    assert f(None, 1, 0, None, None, 8, 256, None, None) == q.OQ_OK

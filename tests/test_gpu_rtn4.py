@@ -1,0 +1,82 @@
+"""GPU parity of the AdaLN INT4 weight-only RTN path (oq_rtn4_prepare_weights,
+oq_rtn4_linear) against the oracle: codes and scales bit-exact (the same
+fp32 decisions), outputs within one bf16 rounding of the fp64 projection
+plus the fp32 summation bound K u sum |x q| scale.
+paper.gecl.asia notes, Method item 5."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests.gpu_util import bf16_to_np, host, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    import torch
+    import quantization_dit_linear_amd as q
+    assert torch.cuda.is_available()
+    q.lib()
+    return q
+
+
+def _pack(qv):
+    """Oracle int8 codes [N, K] -> offset-binary nibbles, even k low."""
+    u = (qv.astype(np.int16) + 8).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _check_out(y, x, code, rq, rs):
+    """One bf16 rounding of the result plus the fp32 summation bound
+    K u sum_k |x_mk q_nk| scale_n (u = 2^-24)."""
+    ref = oracle.rtn4_linear(x, code, rq, rs)
+    xf = wl.bf16_bits_to_f32(x) if code == wl.BF16 else x
+    mag = np.abs(xf.astype(np.float64)) @ np.abs(rq.astype(np.float64)).T * rs[None, :]
+    K = x.shape[1]
+    tol = 2.0 ** -8 * np.abs(ref) + 2.0 * K * 2.0 ** -24 * mag + 1e-30
+    assert np.all(np.abs(y - ref) <= tol), float(np.max(np.abs(y - ref) / tol))
+
+
+def _prep_check(q, W, code, K, what):
+    import torch
+    say("rtn4 prepare", what, W.shape)
+    q4, sc = q.rtn4_prepare_weights(to_device(W))
+    torch.cuda.synchronize()
+    rq, rs = oracle.rtn4_quantize(W, code, K)
+    np.testing.assert_array_equal(host(q4), _pack(rq))
+    np.testing.assert_array_equal(host(sc), rs)
+    return q4, sc, rq, rs
+
+
+@pytest.mark.parametrize("name", ["image", "video"])
+def test_adaln_shapes(q, name):
+    import torch
+    x, W = wl.adaln_inputs(name)
+    M, K = x.shape
+    q4, sc, rq, rs = _prep_check(q, W, wl.BF16, K, name)
+    say("rtn4 linear", name)
+    y = bf16_to_np(q.rtn4_linear(to_device(x), q4, sc))
+    torch.cuda.synchronize()
+    _check_out(y, x, wl.BF16, rq, rs)
+
+
+def test_edge_rows_and_fp32(q):
+    """Zero rows, an outlier row, exact ties, fp32 weights and activations,
+    more activation rows than one block (8)."""
+    import torch
+    rng = np.random.default_rng(3)
+    K = 256
+    W = (rng.standard_normal((40, K)) * 0.02).astype(np.float32)
+    W[1] = 0.0
+    W[2, 5] = 3.0
+    W[3, :8] = [7.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 6.5]
+    W[3, 8:] = 0.0
+    q4, sc, rq, rs = _prep_check(q, W, wl.F32, K, "edge fp32")
+    x = rng.standard_normal((19, K)).astype(np.float32)
+    say("rtn4 linear fp32", x.shape)
+    y = bf16_to_np(q.rtn4_linear(to_device(x), q4, sc))
+    torch.cuda.synchronize()
+    _check_out(y, x, wl.F32, rq, rs)
+    assert np.all(y[:, 1] == 0)

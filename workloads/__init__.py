@@ -202,6 +202,24 @@ def custom_activations(M, d, dtype, seed, base="normal", n_out=0, out_factor=1.0
     return out if dtype == F32 else f32_to_bf16_bits(out)
 
 
+# AdaLN modulation projections (INT4 weight-only, not rotated): one input
+# row per sample (2 = the two guidance branches), hidden size K, 6 K outputs
+# (shift, scale, gate for attention and MLP).  Input SiLU(N(0, 1)) as the
+# conditioning vector after its activation; weights N(0, 0.02^2).  Shapes of
+# an image DiT (3072) and a video DiT (5120) block.
+ADALN = {"image": (2, 3072, 6 * 3072, 61), "video": (2, 5120, 6 * 5120, 62)}
+
+
+def adaln_inputs(name):
+    """(x bf16 bits [M, K], W bf16 bits [N, K]) of an AdaLN projection."""
+    M, K, N, seed = ADALN[name]
+    rng = np.random.default_rng([seed, 1])
+    c = rng.standard_normal((M, K)).astype(np.float32)
+    x = c / (1.0 + np.exp(-c))
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    return f32_to_bf16_bits(x.astype(np.float32)), f32_to_bf16_bits(W)
+
+
 def random_codes(rows, K, bits, seed):
     """Uniformly random packed code bytes [rows, K*bits/8] and positive norms."""
     rng = np.random.default_rng([seed, 7])
