@@ -42,6 +42,10 @@ def _load():
     lib.oqo_codebook.argtypes = [ctypes.c_int, ctypes.c_int, P, P]
     lib.oqo_codebook_mse.restype = ctypes.c_double
     lib.oqo_codebook_mse.argtypes = [ctypes.c_int, P, P]
+    lib.oqo_codebook_sphere.restype = ctypes.c_int
+    lib.oqo_codebook_sphere.argtypes = [ctypes.c_int, ctypes.c_int, P, P]
+    lib.oqo_sphere_mass.restype = ctypes.c_double
+    lib.oqo_sphere_mass.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int]
     lib.oqo_fwht.restype = None
     lib.oqo_fwht.argtypes = [P, ctypes.c_int]
     lib.oqo_hadamard_entry.restype = ctypes.c_int
@@ -60,6 +64,13 @@ def _load():
     lib.oqo_rotate_quantize.argtypes = [P, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                         ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
                                         P, P, P]
+    lib.oqo_rotate_quantize_ex.restype = ctypes.c_int
+    lib.oqo_rotate_quantize_ex.argtypes = [P, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                           ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, P, P, P]
+    lib.oqo_linear_ex.restype = ctypes.c_int
+    lib.oqo_linear_ex.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int64, ctypes.c_int, P, ctypes.c_int64, P]
     lib.oqo_linear.restype = ctypes.c_int
     lib.oqo_linear.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int,
                                ctypes.c_int64, ctypes.c_int, P, ctypes.c_int64, P]
@@ -123,6 +134,23 @@ def codebook(d, bits):
     return lv[:L].copy(), th[:L - 1].copy()
 
 
+def codebook_sphere(d, bits):
+    """Lloyd-Max (levels, thresholds) for the exact marginal of a coordinate
+    of a uniform point on S^{d-1}, in units of z (fp64), and iterations."""
+    L = 1 << bits
+    lv = np.zeros(L, np.float64)
+    th = np.zeros(max(L - 1, 1), np.float64)
+    it = _load().oqo_codebook_sphere(d, bits, _ptr(lv), _ptr(th))
+    if it < 0:
+        raise ValueError("oracle rejected the arguments")
+    return lv, th[:L - 1], it
+
+
+def sphere_mass(a, b, d):
+    """P(a <= T < b) for one coordinate T of a uniform point on S^{d-1}."""
+    return _load().oqo_sphere_mass(a, b, d)
+
+
 def codebook_mse(bits, levels, thresholds):
     lv = np.zeros(16, np.float64)
     th = np.zeros(16, np.float64)
@@ -179,10 +207,12 @@ def unpack_row(packed, d, bits):
     return codes
 
 
-def rotate_quantize(x, dtype, d, seed, bits, use_signs=True, want_codes=True, want_z=False):
+def rotate_quantize(x, dtype, d, seed, bits, use_signs=True, want_codes=True, want_z=False,
+                    sphere=False):
     """Rotate + quantize every row of x.
 
     x: np.float32 [rows, d] (dtype=F32) or np.uint16 bf16 bits (dtype=BF16).
+    sphere: the exact-sphere-marginal codebook instead of the Gaussian one.
     Returns (codes uint8 [rows, d*bits/8] or None, norms fp64 [rows],
     z fp64 [rows, d] or None)."""
     x = np.ascontiguousarray(x)
@@ -191,15 +221,16 @@ def rotate_quantize(x, dtype, d, seed, bits, use_signs=True, want_codes=True, wa
     codes = np.empty((rows, d * bits // 8), np.uint8) if want_codes else None
     norms = np.empty(rows, np.float64)
     z = np.empty((rows, d), np.float64) if want_z else None
-    rc = _load().oqo_rotate_quantize(_ptr(x), dtype, rows, d, seed, int(use_signs), bits,
-                                     _ptr(codes), _ptr(norms), _ptr(z))
+    rc = _load().oqo_rotate_quantize_ex(_ptr(x), dtype, rows, d, seed, int(use_signs), bits,
+                                        int(sphere), _ptr(codes), _ptr(norms), _ptr(z))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return codes, norms, z
 
 
-def linear(a_codes, a_norms, ba, w_codes, w_norms, bw, K, rows=None):
-    """fp64 y[rows][N] = s_m r_n sum_k C_w[p_nk] C_a[q_mk] (sigma-scaled levels)."""
+def linear(a_codes, a_norms, ba, w_codes, w_norms, bw, K, rows=None, sphere=False):
+    """fp64 y[rows][N] = s_m r_n sum_k C_w[p_nk] C_a[q_mk] (sigma-scaled levels;
+    sphere: the exact-sphere-marginal codebooks)."""
     a_codes = np.ascontiguousarray(a_codes, np.uint8)
     w_codes = np.ascontiguousarray(w_codes, np.uint8)
     a_norms = np.ascontiguousarray(a_norms, np.float64)
@@ -210,8 +241,8 @@ def linear(a_codes, a_norms, ba, w_codes, w_norms, bw, K, rows=None):
         rows = np.arange(M, dtype=np.int64)
     rows = np.ascontiguousarray(rows, np.int64)
     y = np.empty((rows.shape[0], N), np.float64)
-    rc = _load().oqo_linear(_ptr(a_codes), _ptr(a_norms), ba, _ptr(w_codes), _ptr(w_norms),
-                            bw, N, K, _ptr(rows), rows.shape[0], _ptr(y))
+    rc = _load().oqo_linear_ex(_ptr(a_codes), _ptr(a_norms), ba, _ptr(w_codes), _ptr(w_norms),
+                               bw, int(sphere), N, K, _ptr(rows), rows.shape[0], _ptr(y))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return y

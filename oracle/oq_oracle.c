@@ -172,6 +172,117 @@ double oqo_codebook_mse(int bits, const double *levels, const double *thresholds
     return s;
 }
 
+/* ------------------------------------------- exact sphere marginal -- */
+
+/* Regularized incomplete beta I_x(a, b) by its continued fraction
+ * (DLMF 8.17.22), evaluated with the modified Lentz method, on the side of
+ * the symmetry I_x(a,b) = 1 - I_{1-x}(b,a) where it converges quickly.
+ * `upper` asks for 1 - I_x(a,b) without cancellation. */
+static double betacf(double a, double b, double x)
+{
+    const double tiny = 1e-300;
+    double c = 1.0, dd = 1.0 - (a + b) * x / (a + 1.0);
+    if (fabs(dd) < tiny) dd = tiny;
+    dd = 1.0 / dd;
+    double h = dd;
+    for (int m = 1; m <= 100000; m++) {
+        double num = m * (b - m) * x / ((a + 2.0 * m - 1.0) * (a + 2.0 * m));
+        dd = 1.0 + num * dd; if (fabs(dd) < tiny) dd = tiny;
+        c = 1.0 + num / c;   if (fabs(c) < tiny) c = tiny;
+        dd = 1.0 / dd; h *= dd * c;
+        num = -(a + m) * (a + b + m) * x / ((a + 2.0 * m) * (a + 2.0 * m + 1.0));
+        dd = 1.0 + num * dd; if (fabs(dd) < tiny) dd = tiny;
+        c = 1.0 + num / c;   if (fabs(c) < tiny) c = tiny;
+        dd = 1.0 / dd;
+        const double del = dd * c;
+        h *= del;
+        if (fabs(del - 1.0) < 1e-16) break;
+    }
+    return h;
+}
+
+static double ibeta(double a, double b, double x, int upper)
+{
+    if (x <= 0.0) return upper ? 1.0 : 0.0;
+    if (x >= 1.0) return upper ? 0.0 : 1.0;
+    const double lfront = lgamma(a + b) - lgamma(a) - lgamma(b) + a * log(x) + b * log1p(-x);
+    if (x < (a + 1.0) / (a + b + 2.0)) {
+        const double v = exp(lfront) * betacf(a, b, x) / a;
+        return upper ? 1.0 - v : v;
+    }
+    const double w = exp(lfront) * betacf(b, a, 1.0 - x) / b; /* = 1 - I_x(a,b) */
+    return upper ? w : 1.0 - w;
+}
+
+/* Mass of [a, b] under the marginal of one coordinate T of a uniform point
+ * on the unit sphere S^{d-1}: T^2 ~ Beta(1/2, (d-1)/2), symmetric about 0.
+ * Tail masses use the upper incomplete beta (no cancellation). */
+static double sphere_tail(double t, int d) /* P(T >= t) for t >= 0 */
+{
+    return 0.5 * ibeta(0.5, 0.5 * (d - 1), t * t, 1);
+}
+
+static double sphere_mass(double a, double b, int d)
+{
+    if (a >= 0.0) return sphere_tail(a, d) - sphere_tail(b, d);
+    if (b <= 0.0) return sphere_tail(-b, d) - sphere_tail(-a, d);
+    return 1.0 - sphere_tail(-a, d) - sphere_tail(b, d);
+}
+
+/* E[T 1{a <= T < b}] in closed form: the density is
+ * c_d (1 - t^2)^((d-3)/2), c_d = Gamma(d/2) / (sqrt(pi) Gamma((d-1)/2)), and
+ * t (1 - t^2)^((d-3)/2) integrates to -(1 - t^2)^((d-1)/2) / (d - 1). */
+static double sphere_moment(double a, double b, int d)
+{
+    const double lc = lgamma(0.5 * d) - 0.5 * log(M_PI) - lgamma(0.5 * (d - 1));
+    const double pa = (a <= -1.0 || a >= 1.0) ? 0.0 : exp(0.5 * (d - 1) * log1p(-a * a));
+    const double pb = (b <= -1.0 || b >= 1.0) ? 0.0 : exp(0.5 * (d - 1) * log1p(-b * b));
+    return exp(lc) * (pa - pb) / (d - 1);
+}
+
+/* Lloyd-Max quantizer for the exact marginal of one coordinate of a uniform
+ * point on S^{d-1} (pith.science: the referee's minor comment 1 asks for
+ * this closed-form marginal; the Figure 2 caption uses its Gaussian limit
+ * N(0, 1/d)): Lloyd's alternation as for the Gaussian, with the cell masses
+ * and first moments of f_d.  Writes levels and thresholds in units of z
+ * (the sigma = 1/sqrt(d) scale is built in).  d >= 3. */
+int oqo_codebook_sphere(int d, int bits, double *levels, double *thresholds)
+{
+    if (d < 3 || bits < 1 || bits > 8) return -1;
+    const int L = 1 << bits;
+    double t[257];
+    double ul[256], ut[255];
+    oqo_codebook_unit(bits <= 4 ? bits : 4, ul, ut); /* a start near the fixed point */
+    if (bits <= 4) {
+        for (int k = 0; k < L; k++) levels[k] = ul[k] / sqrt((double)d);
+    } else {
+        for (int k = 0; k < L; k++) levels[k] = (-1.0 + (2.0 * k + 1.0) / L) * 2.5 / sqrt((double)d);
+    }
+    for (int k = 0; k < L; k++) { /* keep the start inside (-1, 1) */
+        if (levels[k] <= -1.0) levels[k] = -1.0 + (k + 0.5) / L;
+        if (levels[k] >= 1.0) levels[k] = 1.0 - (L - k - 0.5) / L;
+    }
+    int it;
+    for (it = 1; it <= 400000; it++) {
+        double move = 0.0;
+        t[0] = -1.0;
+        t[L] = 1.0;
+        for (int k = 1; k < L; k++) t[k] = 0.5 * (levels[k - 1] + levels[k]);
+        for (int k = 0; k < L; k++) {
+            const double c = sphere_moment(t[k], t[k + 1], d) / sphere_mass(t[k], t[k + 1], d);
+            const double dm = fabs(c - levels[k]) * sqrt((double)d);
+            if (dm > move) move = dm;
+            levels[k] = c;
+        }
+        if (move < 1e-13) break; /* the incomplete beta is good to about 1e-15 */
+    }
+    for (int k = 1; k < L; k++) thresholds[k - 1] = 0.5 * (levels[k - 1] + levels[k]);
+    return it;
+}
+
+/* P(a <= T < b) for the sphere marginal (exported for the pins). */
+double oqo_sphere_mass(double a, double b, int d) { return sphere_mass(a, b, d); }
+
 /* ------------------------------------------------------------- rotation -- */
 
 /* In-place unnormalised Walsh-Hadamard transform of length h (power of
@@ -274,8 +385,16 @@ static double load_elem(const void *x, int dtype, size_t idx)
 
 /* Rotate and quantize `rows` rows of x (row-major, d columns).  codes may be
  * NULL (then only z / norms); z may be NULL.  Rows run in parallel. */
-int oqo_rotate_quantize(const void *x, int dtype, int64_t rows, int d, uint64_t seed,
-                        int use_signs, int bits, uint8_t *codes, double *norms, double *z)
+/* The codebook of a family: 0 = Lloyd-Max for N(0, 1/d), 1 = Lloyd-Max for
+ * the exact sphere marginal of dimension d. */
+static int family_codebook(int family, int d, int bits, double *lv, double *th)
+{
+    return family ? oqo_codebook_sphere(d, bits, lv, th) : oqo_codebook(d, bits, lv, th);
+}
+
+int oqo_rotate_quantize_ex(const void *x, int dtype, int64_t rows, int d, uint64_t seed,
+                           int use_signs, int bits, int family, uint8_t *codes, double *norms,
+                           double *z)
 {
     if (d <= 0 || d % 128 != 0 || bits < 1 || bits > 4) return -1;
     const int L = 1 << bits;
@@ -283,7 +402,7 @@ int oqo_rotate_quantize(const void *x, int dtype, int64_t rows, int d, uint64_t 
     int8_t *sign = malloc(d);
     double lv[16], th[16];
     oqo_plan(d, seed, perm, sign);
-    oqo_codebook(d, bits, lv, th);
+    family_codebook(family, d, bits, lv, th);
 #pragma omp parallel
     {
         double *xr = malloc(sizeof(double) * d);
@@ -310,18 +429,24 @@ int oqo_rotate_quantize(const void *x, int dtype, int64_t rows, int d, uint64_t 
     return 0;
 }
 
+int oqo_rotate_quantize(const void *x, int dtype, int64_t rows, int d, uint64_t seed,
+                        int use_signs, int bits, uint8_t *codes, double *norms, double *z)
+{
+    return oqo_rotate_quantize_ex(x, dtype, rows, d, seed, use_signs, bits, 0, codes, norms, z);
+}
+
 /* The low-bit linear, in fp64:
  *   y[m][n] = s_m r_n sum_k C_{K,bw}[p_nk] C_{K,ba}[q_mk]
  * with sigma-scaled levels.  Only the rows listed in `rows` (indices into
  * the activation rows) are computed; y is [nrows][N]. */
-int oqo_linear(const uint8_t *a_codes, const double *a_norms, int ba,
-               const uint8_t *w_codes, const double *w_norms, int bw,
-               int64_t N, int K, const int64_t *rows, int64_t nrows, double *y)
+int oqo_linear_ex(const uint8_t *a_codes, const double *a_norms, int ba,
+                  const uint8_t *w_codes, const double *w_norms, int bw, int family,
+                  int64_t N, int K, const int64_t *rows, int64_t nrows, double *y)
 {
     if (K <= 0 || K % 128 != 0) return -1;
     double la[16], ta[16], lw[16], tw[16];
-    oqo_codebook(K, ba, la, ta);
-    oqo_codebook(K, bw, lw, tw);
+    family_codebook(family, K, ba, la, ta);
+    family_codebook(family, K, bw, lw, tw);
     double *wd = malloc(sizeof(double) * (size_t)N * K);
 #pragma omp parallel
     {
@@ -433,6 +558,13 @@ int oqo_rtn4_linear(const void *x, int dtype, int64_t M, const int8_t *q, const 
         }
     }
     return 0;
+}
+
+int oqo_linear(const uint8_t *a_codes, const double *a_norms, int ba,
+               const uint8_t *w_codes, const double *w_norms, int bw,
+               int64_t N, int K, const int64_t *rows, int64_t nrows, double *y)
+{
+    return oqo_linear_ex(a_codes, a_norms, ba, w_codes, w_norms, bw, 0, N, K, rows, nrows, y);
 }
 
 /* Threads an OpenMP region of this oracle uses (for reporting). */

@@ -15,6 +15,8 @@ void oqo_plan(int d, uint64_t seed, int32_t *perm, int8_t *sign);
 int oqo_codebook_unit(int bits, double *levels, double *thresholds);
 int oqo_codebook(int d, int bits, double *levels, double *thresholds);
 double oqo_codebook_mse(int bits, const double *levels, const double *thresholds);
+int oqo_codebook_sphere(int d, int bits, double *levels, double *thresholds);
+double oqo_sphere_mass(double a, double b, int d);
 
 void oqo_fwht(double *v, int h);
 int oqo_hadamard_entry(int a, int b);
@@ -28,6 +30,12 @@ void oqo_unpack_row(const uint8_t *packed, int d, int bits, uint8_t *codes);
 
 int oqo_rotate_quantize(const void *x, int dtype, int64_t rows, int d, uint64_t seed,
                         int use_signs, int bits, uint8_t *codes, double *norms, double *z);
+int oqo_rotate_quantize_ex(const void *x, int dtype, int64_t rows, int d, uint64_t seed,
+                           int use_signs, int bits, int family, uint8_t *codes, double *norms,
+                           double *z);
+int oqo_linear_ex(const uint8_t *a_codes, const double *a_norms, int ba,
+                  const uint8_t *w_codes, const double *w_norms, int bw, int family,
+                  int64_t N, int K, const int64_t *rows, int64_t nrows, double *y);
 int oqo_linear(const uint8_t *a_codes, const double *a_norms, int ba,
                const uint8_t *w_codes, const double *w_norms, int bw,
                int64_t N, int K, const int64_t *rows, int64_t nrows, double *y);

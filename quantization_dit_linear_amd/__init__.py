@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(_HERE, "liborbitquant.so")
 OQ_OK, OQ_EINVAL, OQ_EUNSUPPORTED, OQ_ENOMEM, OQ_EDEVICE = 0, -1, -2, -3, -4
 OQ_F32, OQ_BF16 = 0, 1
 OQ_ROT_NO_SIGNS, OQ_OUT_F32_ROTATED, OQ_OUT_BF16_DEQUANT, OQ_ROT_INPUT_PERMUTED = 1, 2, 4, 8
+OQ_CODEBOOK_SPHERE = 16
 
 # every symbol the header declares, with (restype, argtypes)
 _P = ctypes.c_void_p
@@ -34,6 +35,9 @@ _SIGS = {
     "oq_version": (ctypes.c_int, []),
     "oq_codebook": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _P, _P]),
     "oq_codes_bytes": (ctypes.c_int64, [ctypes.c_int64, ctypes.c_int, ctypes.c_int]),
+    "oq_codebook_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_uint32, _P, _P]),
+    "oq_linear_ex": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_int, ctypes.c_uint32, _P, _P]),
     "oq_rotate_quantize": (ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                           ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int,
                                           _P, _P, _P]),
@@ -108,12 +112,14 @@ def _dev_ptr(t, name):
 
 # ------------------------------------------------------------------- API --
 
-def codebook(d, bits):
-    """(levels float32[2^bits], thresholds float32[2^bits-1]) of C_{d,bits}."""
+def codebook(d, bits, *, sphere=False):
+    """(levels float32[2^bits], thresholds float32[2^bits-1]) of C_{d,bits}
+    (sphere: the exact-sphere-marginal family)."""
     L = 1 << bits
     lv = np.zeros(16, np.float32)
     th = np.zeros(16, np.float32)
-    _check(lib().oq_codebook(d, bits, lv.ctypes.data, th.ctypes.data), "oq_codebook")
+    flags = OQ_CODEBOOK_SPHERE if sphere else 0
+    _check(lib().oq_codebook_ex(d, bits, flags, lv.ctypes.data, th.ctypes.data), "oq_codebook_ex")
     return lv[:L].copy(), th[:L - 1].copy()
 
 
@@ -130,10 +136,11 @@ def _dtype_code(t):
     raise TypeError(f"unsupported input dtype {t.dtype} (bfloat16 or float32)")
 
 
-def rotate_quantize(x, seed, bits, *, signs=True, permuted=False, out=None, norms=None,
-                    stream=None):
+def rotate_quantize(x, seed, bits, *, signs=True, permuted=False, sphere=False, out=None,
+                    norms=None, stream=None):
     """Codes (uint8 [M, d*bits/8], storage order) and norms (float32 [M]).
-    permuted=True: x's columns are already in rotation order (OQ_ROT_INPUT_PERMUTED)."""
+    permuted=True: x's columns are already in rotation order (OQ_ROT_INPUT_PERMUTED);
+    sphere=True: the exact-sphere-marginal codebook (OQ_CODEBOOK_SPHERE)."""
     import torch
     if x.dim() != 2:
         raise ValueError("x must be [tokens, d]")
@@ -142,7 +149,8 @@ def rotate_quantize(x, seed, bits, *, signs=True, permuted=False, out=None, norm
         out = torch.empty((M, d * bits // 8), dtype=torch.uint8, device=x.device)
     if norms is None:
         norms = torch.empty((M,), dtype=torch.float32, device=x.device)
-    flags = (0 if signs else OQ_ROT_NO_SIGNS) | (OQ_ROT_INPUT_PERMUTED if permuted else 0)
+    flags = ((0 if signs else OQ_ROT_NO_SIGNS) | (OQ_ROT_INPUT_PERMUTED if permuted else 0)
+             | (OQ_CODEBOOK_SPHERE if sphere else 0))
     rc = lib().oq_rotate_quantize(_dev_ptr(x, "x"), _dtype_code(x), M, d, seed, flags, bits,
                                   _dev_ptr(out, "out"), _dev_ptr(norms, "norms"),
                                   _stream(stream))
@@ -163,7 +171,8 @@ def rotate(x, seed, *, signs=True, stream=None):
     return z, norms
 
 
-def fake_quantize(x, seed, bits, *, signs=True, out=None, norms=None, stream=None):
+def fake_quantize(x, seed, bits, *, signs=True, sphere=False, out=None, norms=None,
+                  stream=None):
     """Dequantized rotated rows (bfloat16 [M, d], coordinate order): row m,
     coordinate i holds s_m * C_{d,bits}[code_mi]; and the norms.  Works for
     activation tokens and weight rows alike (the same quantizer); a bf16 GEMM
@@ -176,7 +185,8 @@ def fake_quantize(x, seed, bits, *, signs=True, out=None, norms=None, stream=Non
         out = torch.empty((M, d), dtype=torch.bfloat16, device=x.device)
     if norms is None:
         norms = torch.empty((M,), dtype=torch.float32, device=x.device)
-    flags = OQ_OUT_BF16_DEQUANT | (0 if signs else OQ_ROT_NO_SIGNS)
+    flags = (OQ_OUT_BF16_DEQUANT | (0 if signs else OQ_ROT_NO_SIGNS)
+             | (OQ_CODEBOOK_SPHERE if sphere else 0))
     rc = lib().oq_rotate_quantize(_dev_ptr(x, "x"), _dtype_code(x), M, d, seed, flags, bits,
                                   _dev_ptr(out, "out"), _dev_ptr(norms, "norms"),
                                   _stream(stream))
@@ -184,7 +194,8 @@ def fake_quantize(x, seed, bits, *, signs=True, out=None, norms=None, stream=Non
     return out, norms
 
 
-def prepare_weights(W, seed, bits, *, signs=True, out=None, norms=None, stream=None):
+def prepare_weights(W, seed, bits, *, signs=True, sphere=False, out=None, norms=None,
+                    stream=None):
     """Weight codes (uint8 [N, K*bits/8]) and row norms (float32 [N])."""
     import torch
     if W.dim() != 2:
@@ -194,7 +205,7 @@ def prepare_weights(W, seed, bits, *, signs=True, out=None, norms=None, stream=N
         out = torch.empty((N, K * bits // 8), dtype=torch.uint8, device=W.device)
     if norms is None:
         norms = torch.empty((N,), dtype=torch.float32, device=W.device)
-    flags = 0 if signs else OQ_ROT_NO_SIGNS
+    flags = (0 if signs else OQ_ROT_NO_SIGNS) | (OQ_CODEBOOK_SPHERE if sphere else 0)
     rc = lib().oq_prepare_weights(_dev_ptr(W, "W"), _dtype_code(W), N, K, seed, flags, bits,
                                   _dev_ptr(out, "w_codes"), _dev_ptr(norms, "row_norms"),
                                   _stream(stream))
@@ -202,16 +213,24 @@ def prepare_weights(W, seed, bits, *, signs=True, out=None, norms=None, stream=N
     return out, norms
 
 
-def linear(a_codes, a_norms, a_bits, w_codes, w_norms, w_bits, K, *, out=None, stream=None):
-    """bf16 y [M, N] = s_m r_n sum_k C_w[p_nk] C_a[q_mk]."""
+def linear(a_codes, a_norms, a_bits, w_codes, w_norms, w_bits, K, *, sphere=False, out=None,
+           stream=None):
+    """bf16 y [M, N] = s_m r_n sum_k C_w[p_nk] C_a[q_mk] (sphere: the
+    exact-sphere-marginal codebooks, oq_linear_ex)."""
     import torch
     M = a_codes.shape[0]
     N = w_codes.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a_codes.device)
-    rc = lib().oq_linear(_dev_ptr(a_codes, "a_codes"), _dev_ptr(a_norms, "a_norms"), a_bits,
-                         _dev_ptr(w_codes, "w_codes"), _dev_ptr(w_norms, "w_norms"), w_bits,
-                         M, N, K, _dev_ptr(out, "y"), _stream(stream))
+    if sphere:
+        rc = lib().oq_linear_ex(_dev_ptr(a_codes, "a_codes"), _dev_ptr(a_norms, "a_norms"),
+                                a_bits, _dev_ptr(w_codes, "w_codes"), _dev_ptr(w_norms, "w_norms"),
+                                w_bits, M, N, K, OQ_CODEBOOK_SPHERE, _dev_ptr(out, "y"),
+                                _stream(stream))
+    else:
+        rc = lib().oq_linear(_dev_ptr(a_codes, "a_codes"), _dev_ptr(a_norms, "a_norms"), a_bits,
+                             _dev_ptr(w_codes, "w_codes"), _dev_ptr(w_norms, "w_norms"), w_bits,
+                             M, N, K, _dev_ptr(out, "y"), _stream(stream))
     _check(rc, "oq_linear")
     return out
 

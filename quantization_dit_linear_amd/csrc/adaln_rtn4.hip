@@ -215,9 +215,12 @@ hipError_t launch_rtn4_linear(const void *x, int dtype, int64_t M, const uint8_t
   int dev = 0, cus = 0;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  // as many workgroups as fit two per CU, each with the same number of row
+  // groups (no partial last round of groups)
   const int64_t groups = (N + kRows - 1) / kRows;
   const int64_t want = (int64_t)(cus > 0 ? cus : 256) * 2;
-  const int64_t grid = groups < want ? groups : want;
+  const int64_t per = (groups + want - 1) / want;
+  const int64_t grid = (groups + per - 1) / per;
   hipLaunchKernelGGL(rtn4_linear_kernel, dim3((unsigned)grid), dim3(256),
                      (size_t)mb * (K / 32) * kPad * 4,
                      stream, x, dtype, M, (const u32x4 *)q4, scales, N, K, mb, y);

@@ -105,6 +105,142 @@ void unit_codebook(int bits, double *levels, double *thresholds) {
   std::memcpy(thresholds, th[bits], sizeof(double) * (L - 1));
 }
 
+// ---- exact sphere marginal.  One coordinate of a uniform point on
+// S^{d-1} has density c_d (1 - t^2)^((d-3)/2); in unit-variance units
+// u = sqrt(d) t the upper-half masses come from Gauss-Legendre quadrature
+// and the first moments from the closed form
+//   int u g(u) du = -sqrt(d) c_d (1 - u^2/d)^((d-1)/2) / (d - 1).
+
+struct GaussLegendre {
+  static constexpr int n = 32;
+  double x[n], w[n];
+  GaussLegendre() {  // nodes on [-1, 1] by Newton's method on P_n
+    for (int i = 0; i < n; i++) {
+      double z = std::cos(M_PI * (i + 0.75) / (n + 0.5)), pp = 1.0;
+      for (int it = 0; it < 100; it++) {
+        double p1 = 1.0, p2 = 0.0;
+        for (int j = 1; j <= n; j++) {
+          const double p3 = p2;
+          p2 = p1;
+          p1 = ((2.0 * j - 1.0) * z * p2 - (j - 1.0) * p3) / j;
+        }
+        pp = n * (z * p1 - p2) / (z * z - 1.0);
+        const double dz = p1 / pp;
+        z -= dz;
+        if (std::fabs(dz) < 1e-16) break;
+      }
+      x[i] = z;
+      w[i] = 2.0 / ((1.0 - z * z) * pp * pp);
+    }
+  }
+};
+
+struct SphereDist {
+  int d;
+  double lc;  // log c_d
+  explicit SphereDist(int d_) : d(d_) {
+    lc = std::lgamma(0.5 * d) - 0.5 * std::log(M_PI) - std::lgamma(0.5 * (d - 1));
+  }
+  double top() const { return std::sqrt((double)d); }
+  double g(double u) const {  // density of u
+    const double r = 1.0 - u * u / d;
+    return r <= 0.0 ? 0.0 : std::exp(lc + 0.5 * (d - 3) * std::log(r)) / std::sqrt((double)d);
+  }
+  double mass(double a, double b) const {  // 0 <= a < b
+    static const GaussLegendre gl;
+    b = std::min(b, std::min(top(), a + 48.0));  // beyond: below 1e-300
+    double s = 0.0;
+    for (double lo = a; lo < b; lo += 0.25) {
+      const double hi = std::min(lo + 0.25, b), h = 0.5 * (hi - lo), m = 0.5 * (hi + lo);
+      for (int i = 0; i < GaussLegendre::n; i++) s += gl.w[i] * g(m + h * gl.x[i]) * h;
+    }
+    return s;
+  }
+  double moment(double a, double b) const {
+    auto pw = [&](double u) {
+      const double r = 1.0 - u * u / d;
+      return r <= 0.0 ? 0.0 : std::exp(0.5 * (d - 1) * std::log(r));
+    };
+    return std::sqrt((double)d) * std::exp(lc) * (pw(a) - pw(b)) / (d - 1);
+  }
+  double mean(double a, double b) const { return moment(a, b) / mass(a, b); }
+};
+
+// Max's shooting method on the upper half of a symmetric density: the first
+// positive level c0 is bisected until the last cell's mean matches.
+template <class Mean>
+void shoot_codebook(int bits, double top, const Mean &mean, double *lv, double *th) {
+  const int L = 1 << bits, P = L / 2;
+  double pl[128], pe[128];
+  auto edge_for = [&](double a, double c) {  // b with mean(a, b) = c
+    double lo = a, hi = std::min(a + 1.0, top);
+    while (mean(a, hi) <= c) {
+      if (hi >= top) return top;
+      lo = hi;
+      hi = std::min(a + 2.0 * (hi - a), top);
+    }
+    for (int i = 0; i < 200 && hi - lo > 1e-17 * hi; i++) {
+      const double mid = 0.5 * (lo + hi);
+      if (mean(a, mid) < c) lo = mid; else hi = mid;
+    }
+    return 0.5 * (lo + hi);
+  };
+  auto shot = [&](double c0) {
+    double a = 0.0, c = c0;
+    for (int k = 0; k < P - 1; k++) {
+      pl[k] = c;
+      if (c >= mean(a, top)) return 1.0;
+      const double b = edge_for(a, c);
+      if (b >= top) return 1.0;
+      pe[k] = b;
+      c = 2.0 * b - c;
+      a = b;
+    }
+    pl[P - 1] = c;
+    return c - mean(a, top);
+  };
+  if (P == 1) {
+    pl[0] = mean(0.0, top);
+  } else {
+    double lo = 0.0, hi = mean(0.0, top);
+    for (int i = 0; i < 400; i++) {
+      const double mid = 0.5 * (lo + hi);
+      if (mid <= lo || mid >= hi) break;
+      if (shot(mid) > 0) hi = mid; else lo = mid;
+    }
+    shot(0.5 * (lo + hi));
+  }
+  for (int k = 0; k < P; k++) {
+    lv[P + k] = pl[k];
+    lv[P - 1 - k] = -pl[k];
+  }
+  for (int k = 0; k < L - 1; k++) th[k] = 0.5 * (lv[k] + lv[k + 1]);
+  th[P - 1] = 0.0;
+}
+
+// Unit-variance codebook of a family: Gaussian (d-independent) or the exact
+// sphere marginal of dimension d (cached per (d, bits)).
+void family_codebook(int d, int bits, bool sphere, double *levels, double *thresholds) {
+  if (!sphere) {
+    unit_codebook(bits, levels, thresholds);
+    return;
+  }
+  static std::mutex mu;
+  static std::map<std::pair<int, int>, std::vector<double>> cache;
+  const int L = 1 << bits;
+  std::lock_guard<std::mutex> g(mu);
+  auto it = cache.find({d, bits});
+  if (it == cache.end()) {
+    SphereDist dist(d);
+    std::vector<double> v(2 * L);
+    shoot_codebook(bits, dist.top(), [&](double a, double b) { return dist.mean(a, b); },
+                   v.data(), v.data() + L);
+    it = cache.emplace(std::make_pair(d, bits), v).first;
+  }
+  std::memcpy(levels, it->second.data(), sizeof(double) * L);
+  std::memcpy(thresholds, it->second.data() + L, sizeof(double) * (L - 1));
+}
+
 uint16_t f32_to_f16_bits(float f) {
   _Float16 h = (_Float16)f;  // round to nearest even
   uint16_t u;
@@ -229,9 +365,9 @@ int get_plan(int d, uint64_t seed, hipStream_t stream, const oq::DevicePlan **ou
 // can fall inside it (or +inf), so the code is base + (u >= tau) with the
 // unclamped u.  A cell holding two thresholds would need a finer grid:
 // rejected (never the case for 2-4 bit Lloyd-Max codebooks).
-int build_cells(int bits, std::vector<uint32_t> &out) {
+int build_cells(int d, int bits, bool sphere, std::vector<uint32_t> &out) {
   double lv[16], th[15];
-  unit_codebook(bits, lv, th);
+  family_codebook(d, bits, sphere, lv, th);
   const int T = (1 << bits) - 1;
   const double delta = 0.125, eps = 0.02 * delta;
   out.assign(2 * oq::kFastCells, 0);
@@ -255,19 +391,21 @@ int build_cells(int bits, std::vector<uint32_t> &out) {
 }
 
 std::mutex g_cell_mu;
-std::map<std::pair<int, int>, uint32_t *> g_cells;  // (device, bits) -> table
+// (device, bits, d for the sphere family or 0) -> table
+std::map<std::tuple<int, int, int>, uint32_t *> g_cells;
 
-int get_cells(int bits, const uint32_t **out) {
+int get_cells(int d, int bits, bool sphere, const uint32_t **out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return OQ_EDEVICE;
   std::lock_guard<std::mutex> g(g_cell_mu);
-  auto it = g_cells.find({dev, bits});
+  const auto key = std::make_tuple(dev, bits, sphere ? d : 0);
+  auto it = g_cells.find(key);
   if (it != g_cells.end()) {
     *out = it->second;
     return OQ_OK;
   }
   std::vector<uint32_t> tab;
-  int rc = build_cells(bits, tab);
+  int rc = build_cells(d, bits, sphere, tab);
   if (rc != OQ_OK) return rc;
   uint32_t *dptr = nullptr;
   if (hipMalloc(&dptr, tab.size() * 4) != hipSuccess) return OQ_ENOMEM;
@@ -275,7 +413,7 @@ int get_cells(int bits, const uint32_t **out) {
     (void)hipFree(dptr);
     return OQ_EDEVICE;
   }
-  g_cells[{dev, bits}] = dptr;
+  g_cells[key] = dptr;
   *out = dptr;
   return OQ_OK;
 }
@@ -296,7 +434,9 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
   if (n_tok < 0) return OQ_EINVAL;
   if (dtype != OQ_F32 && dtype != OQ_BF16) return OQ_EINVAL;
   const uint32_t outs = OQ_OUT_F32_ROTATED | OQ_OUT_BF16_DEQUANT;
-  if (flags & ~(OQ_ROT_NO_SIGNS | OQ_ROT_INPUT_PERMUTED | outs)) return OQ_EINVAL;
+  if (flags & ~(OQ_ROT_NO_SIGNS | OQ_ROT_INPUT_PERMUTED | OQ_CODEBOOK_SPHERE | outs))
+    return OQ_EINVAL;
+  const bool sphere = (flags & OQ_CODEBOOK_SPHERE) != 0;
   if ((flags & outs) && !allow_rotated) return OQ_EINVAL;
   if ((flags & outs) == outs) return OQ_EINVAL;
   int rc = check_d_bits(d, bits);
@@ -308,7 +448,7 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
   rc = get_plan(d, seed, (hipStream_t)stream, &plan);
   if (rc != OQ_OK) return rc;
   double lv[16], th[15];
-  unit_codebook(bits, lv, th);
+  family_codebook(d, bits, sphere, lv, th);
   oq::Thresholds t{};
   t.count = (1 << bits) - 1;
   for (int k = 0; k < t.count; k++) t.t[k] = (float)th[k];
@@ -329,7 +469,7 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
   a.stream = (hipStream_t)stream;
   if (a.dtype == OQ_BF16 && !a.rotated_out) {
     const uint32_t *cells = nullptr;
-    rc = get_cells(bits, &cells);
+    rc = get_cells(d, bits, sphere, &cells);
     if (rc != OQ_OK) return rc;
     bool handled = false;
     const uint32_t *smask = a.input_permuted ? (a.signs ? plan->fast_signs_id : plan->fast_nosigns)
@@ -361,16 +501,23 @@ const char *oq_strerror(int status) {
 
 int oq_version(void) { return 100; }
 
-int oq_codebook(int d, int bits, float *levels, float *thresholds) {
+int oq_codebook_ex(int d, int bits, uint32_t flags, float *levels, float *thresholds) {
   if (!levels || !thresholds || d < 1) return OQ_EINVAL;
+  if (flags & ~OQ_CODEBOOK_SPHERE) return OQ_EINVAL;
   if (bits < 1 || bits > 4) return OQ_EUNSUPPORTED;
+  const bool sphere = (flags & OQ_CODEBOOK_SPHERE) != 0;
+  if (sphere && (d % oq::kGroup != 0 || d > oq::kMaxD)) return OQ_EUNSUPPORTED;
   double lv[16], th[15];
-  unit_codebook(bits, lv, th);
+  family_codebook(d, bits, sphere, lv, th);
   const double sigma = 1.0 / std::sqrt((double)d);
   const int L = 1 << bits;
   for (int k = 0; k < L; k++) levels[k] = (float)(lv[k] * sigma);
   for (int k = 0; k < L - 1; k++) thresholds[k] = (float)(th[k] * sigma);
   return OQ_OK;
+}
+
+int oq_codebook(int d, int bits, float *levels, float *thresholds) {
+  return oq_codebook_ex(d, bits, 0, levels, thresholds);
 }
 
 int64_t oq_codes_bytes(int64_t rows, int d, int bits) {
@@ -390,10 +537,12 @@ int oq_prepare_weights(const void *W, int dtype, int64_t n_out, int d_in, uint64
                        false);
 }
 
-int oq_linear(const uint8_t *a_codes, const float *a_norms, int a_bits, const uint8_t *w_codes,
-              const float *w_norms, int w_bits, int64_t M, int64_t N, int K, uint16_t *y,
-              void *stream) {
+int oq_linear_ex(const uint8_t *a_codes, const float *a_norms, int a_bits, const uint8_t *w_codes,
+                 const float *w_norms, int w_bits, int64_t M, int64_t N, int K, uint32_t flags,
+                 uint16_t *y, void *stream) {
   if (M < 0 || N < 0) return OQ_EINVAL;
+  if (flags & ~OQ_CODEBOOK_SPHERE) return OQ_EINVAL;
+  const bool sphere = (flags & OQ_CODEBOOK_SPHERE) != 0;
   int rc = check_d_bits(K, a_bits);
   if (rc != OQ_OK) return rc;
   rc = check_d_bits(K, w_bits);
@@ -405,14 +554,20 @@ int oq_linear(const uint8_t *a_codes, const float *a_norms, int a_bits, const ui
     return OQ_EINVAL;
   double lv[16], th[15];
   oq::LevelsF16 la{}, lw{};
-  unit_codebook(a_bits, lv, th);
+  family_codebook(K, a_bits, sphere, lv, th);
   for (int k = 0; k < (1 << a_bits); k++) la.v[k] = f32_to_f16_bits((float)lv[k]);
-  unit_codebook(w_bits, lv, th);
+  family_codebook(K, w_bits, sphere, lv, th);
   for (int k = 0; k < (1 << w_bits); k++) lw.v[k] = f32_to_f16_bits((float)lv[k]);
   oq::LinearArgs a{a_codes, a_norms, a_bits, w_codes, w_norms, w_bits, M, N, K, y,
                    (hipStream_t)stream};
   hipError_t e = oq::launch_linear(a, la, lw);
   return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
+}
+
+int oq_linear(const uint8_t *a_codes, const float *a_norms, int a_bits, const uint8_t *w_codes,
+              const float *w_norms, int w_bits, int64_t M, int64_t N, int K, uint16_t *y,
+              void *stream) {
+  return oq_linear_ex(a_codes, a_norms, a_bits, w_codes, w_norms, w_bits, M, N, K, 0, y, stream);
 }
 
 int oq_rtn4_prepare_weights(const void *W, int dtype, int64_t n_out, int d_in, uint8_t *q4,
@@ -522,7 +677,7 @@ int oq_release_plans(void) {
   for (auto &kv : g_cells) {
     int cur = 0;
     (void)hipGetDevice(&cur);
-    if (hipSetDevice(kv.first.first) != hipSuccess) rc = OQ_EDEVICE;
+    if (hipSetDevice(std::get<0>(kv.first)) != hipSuccess) rc = OQ_EDEVICE;
     (void)hipFree(kv.second);
     (void)hipSetDevice(cur);
   }

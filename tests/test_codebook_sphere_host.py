@@ -1,0 +1,36 @@
+"""The library's exact-sphere codebook (oq_codebook_ex with
+OQ_CODEBOOK_SPHERE: Gauss-Legendre masses and Max's shooting method on the
+host) against the oracle's (incomplete beta and Lloyd's iteration); both
+are fp64 and independent, the library rounds to fp32.  CPU only."""
+import numpy as np
+import pytest
+
+import oracle
+
+
+@pytest.fixture(scope="module")
+def q():
+    import quantization_dit_linear_amd as q
+    q.lib()
+    return q
+
+
+@pytest.mark.parametrize("d", [128, 256, 3072, 5120, 12288, 13824, 16384])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_library_sphere_codebook_matches_oracle(q, d, bits):
+    lv, th = q.codebook(d, bits, sphere=True)
+    rl, rt, _ = oracle.codebook_sphere(d, bits)
+    np.testing.assert_allclose(lv, rl, rtol=2e-7, atol=1e-9 / np.sqrt(d))
+    np.testing.assert_allclose(th, rt, rtol=2e-7, atol=1e-9 / np.sqrt(d))
+
+
+def test_family_flag_validation(q):
+    import ctypes
+    lv = np.zeros(16, np.float32)
+    th = np.zeros(16, np.float32)
+    L = q.lib()
+    assert L.oq_codebook_ex(3072, 4, 1 << 7, lv.ctypes.data, th.ctypes.data) == q.OQ_EINVAL
+    assert L.oq_codebook_ex(3000, 4, q.OQ_CODEBOOK_SPHERE, lv.ctypes.data,
+                            th.ctypes.data) == q.OQ_EUNSUPPORTED
+    # the Gaussian family stays defined for any d
+    assert L.oq_codebook_ex(3000, 4, 0, lv.ctypes.data, th.ctypes.data) == q.OQ_OK
