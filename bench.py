@@ -58,6 +58,9 @@ def parse():
                         "FETCH_SIZE and WRITE_SIZE runs) into the summaries under profiles/")
     p.add_argument("--profile-command", default="",
                    help="with --summarize-profiles: the rocprofv3 commands, recorded verbatim")
+    p.add_argument("--profile-counters", nargs="*", default=[],
+                   help="with --summarize-profiles: rocprofv3 --pmc output folders whose "
+                        "per-kernel counter averages go into profiles/<workload>_counters.txt")
     p.add_argument("--profile-bench-log", default=None,
                    help="with --summarize-profiles: output of the traced bench.py run, whose "
                         "own per-kernel event timings are compared with the trace")
@@ -350,8 +353,63 @@ def summarize_profiles(a):
                     f"{e['algorithmic_read_bytes'] / 1e6:.1f} MB); write "
                     f"{e['write_bytes'] / 1e6:.1f} MB (algorithmic writes "
                     f"{e['algorithmic_write_bytes'] / 1e6:.1f} MB)\n")
+    if a.profile_counters:
+        write_counter_summary(a, tag, lin_name, rot_name, M, N, K, ba, bw, in_b)
     print(json.dumps(table))
     return 0
+
+
+def write_counter_summary(a, tag, lin_name, rot_name, M, N, K, ba, bw, in_b):
+    """Per-kernel averages of SQ/GRBM counters from rocprofv3 --pmc runs,
+    with the derived rates the kernels are tuned by."""
+    import csv
+    import glob
+    per = {}
+    for d in a.profile_counters:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                k = _short_kernel_name(r["Kernel_Name"])
+                if k not in (lin_name, rot_name):
+                    continue
+                per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    lines = [f"SQ/GRBM counters per launch (rocprofv3 --pmc), workload {tag} "
+             f"({M} x {K} -> {N}).", "Commands (repository root on the GPU host):",
+             a.profile_command, ""]
+    n_mfma = 2.0 * M * N * K / 16384  # 16x16x32 f16 MFMAs of the linear
+    for k in (lin_name, rot_name):
+        c = {n: float(np.mean(v)) for n, v in per.get(k, {}).items()}
+        if not c:
+            continue
+        lines.append(k)
+        for n in sorted(c):
+            lines.append(f"  {n:30s} {c[n]:.6g}")
+        gui = c.get("GRBM_GUI_ACTIVE")
+        if k == lin_name:
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c and gui:
+                lines.append(f"  MFMA busy per SIMD (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / "
+                             f"(GRBM_GUI_ACTIVE / 8 XCDs)): "
+                             f"{c['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / (gui / 8):.3f}")
+            if "SQ_INSTS_MFMA" in c:
+                lines.append(f"  MFMA instructions: {c['SQ_INSTS_MFMA']:.4g} "
+                             f"(2MNK/16384 = {n_mfma:.4g})")
+            if "SQ_INSTS_VALU" in c and "SQ_INSTS_MFMA" in c:
+                lines.append(f"  non-MFMA VALU instructions per MFMA: "
+                             f"{(c['SQ_INSTS_VALU'] - c['SQ_INSTS_MFMA']) / c['SQ_INSTS_MFMA']:.2f}")
+        else:
+            elems = (M + N) / 2.0 * K  # mean over activation and weight launches
+            for n in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
+                      "SQ_LDS_IDX_ACTIVE"):
+                if n in c:
+                    lines.append(f"  {n} per coordinate: {c[n] / elems * 64:.3f}"
+                                 + (" (wave instructions x 64 lanes)" if "INSTS" in n
+                                    else " (cycles per 64 coordinates)"))
+            if "SQ_ACTIVE_INST_VALU" in c and gui:
+                lines.append(f"  VALU busy per SIMD: "
+                             f"{c['SQ_ACTIVE_INST_VALU'] * 4 / 1024 / (gui / 8):.3f}")
+        lines.append("")
+    with open(os.path.join(ROOT, "profiles", f"{tag}_counters.txt"), "w") as f:
+        f.write("\n".join(lines))
 
 
 def main():
