@@ -118,8 +118,8 @@ def codebook_unit(bits):
     """(levels[L], thresholds[L-1], iterations) for N(0,1), fp64."""
     lib = _load()
     L = 1 << bits
-    lv = np.zeros(16, np.float64)
-    th = np.zeros(16, np.float64)
+    lv = np.zeros(256, np.float64)
+    th = np.zeros(256, np.float64)
     it = lib.oqo_codebook_unit(bits, _ptr(lv), _ptr(th))
     return lv[:L].copy(), th[:L - 1].copy(), it
 
@@ -128,8 +128,8 @@ def codebook(d, bits):
     """(levels, thresholds) of C_{d,b}: the unit codebook times 1/sqrt(d)."""
     lib = _load()
     L = 1 << bits
-    lv = np.zeros(16, np.float64)
-    th = np.zeros(16, np.float64)
+    lv = np.zeros(256, np.float64)
+    th = np.zeros(256, np.float64)
     lib.oqo_codebook(d, bits, _ptr(lv), _ptr(th))
     return lv[:L].copy(), th[:L - 1].copy()
 
@@ -152,8 +152,8 @@ def sphere_mass(a, b, d):
 
 
 def codebook_mse(bits, levels, thresholds):
-    lv = np.zeros(16, np.float64)
-    th = np.zeros(16, np.float64)
+    lv = np.zeros(256, np.float64)
+    th = np.zeros(256, np.float64)
     lv[:len(levels)] = levels
     th[:len(thresholds)] = thresholds
     return _load().oqo_codebook_mse(bits, _ptr(lv), _ptr(th))
@@ -183,7 +183,7 @@ def rotate_token(x, perm, sign, use_signs=True):
 
 
 def quantize_one(z, thresholds):
-    th = np.zeros(16, np.float64)
+    th = np.zeros(256, np.float64)
     th[:len(thresholds)] = thresholds
     return _load().oqo_quantize_one(float(z), _ptr(th), len(thresholds) + 1)
 

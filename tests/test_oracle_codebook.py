@@ -102,3 +102,61 @@ def test_dimension_scaling(d):
         ld, td = oracle.codebook(d, bits)
         assert np.allclose(ld, lu / np.sqrt(d), rtol=1e-15, atol=0)
         assert np.allclose(td, tu / np.sqrt(d), rtol=1e-15, atol=0)
+
+
+# ---- 5 to 8 bits (W8A8 is the top of the pages' bit range: llmdb.app
+# summary).  No page prints these codebooks; they are pinned by the two
+# Lloyd-Max conditions evaluated by quadrature (a log-concave density has
+# exactly one quantizer meeting both, Fleischer 1964), by symmetry, and by
+# the Panter-Dite high-resolution distortion (sqrt(3) pi / 2) 4^-b.
+
+
+@pytest.mark.parametrize("bits", [5, 8])
+def test_high_rate_levels_are_cell_centroids_by_quadrature(bits):
+    lv, th, _ = oracle.codebook_unit(bits)
+    L = 1 << bits
+    assert np.all(np.diff(lv) > 0)
+    assert np.max(np.abs(lv + lv[::-1])) < 1e-12
+    assert np.allclose(th, 0.5 * (lv[:-1] + lv[1:]), atol=0, rtol=1e-15)
+    edges = np.concatenate([[-np.inf], th, [np.inf]])
+    worst = 0.0
+    for k in range(L):
+        a, b = edges[k], edges[k + 1]
+        m, _ = integrate.quad(stats.norm.pdf, a, b, epsabs=1e-16, epsrel=1e-13)
+        mu, _ = integrate.quad(lambda t: t * stats.norm.pdf(t), a, b, epsabs=1e-16,
+                               epsrel=1e-13)
+        worst = max(worst, abs(mu / m - lv[k]))
+    assert worst < 1e-8
+
+
+def test_eight_bit_distortion_against_panter_dite():
+    pd = np.sqrt(3.0) * np.pi / 2.0
+    ratios = []
+    for bits in (5, 6, 7, 8):
+        lv, th, _ = oracle.codebook_unit(bits)
+        ratios.append(oracle.codebook_mse(bits, lv, th) * 4.0 ** bits / pd)
+    # below the asymptote and approaching it monotonically from below
+    assert all(0.9 < r < 1.0 for r in ratios)
+    assert all(a < b for a, b in zip(ratios, ratios[1:]))
+    assert ratios[-1] > 0.985
+
+
+def test_eight_bit_codebook_is_a_local_minimum():
+    """Moving any one of a few levels (inner, middle, outer) raises the
+    distortion, by quadrature over the affected cells only."""
+    lv, th, _ = oracle.codebook_unit(8)
+
+    def local_mse(levels, lo, hi):
+        t = 0.5 * (levels[:-1] + levels[1:])
+        edges = np.concatenate([[-np.inf], t, [np.inf]])
+        return sum(integrate.quad(lambda x: (x - levels[k]) ** 2 * stats.norm.pdf(x),
+                                  edges[k], edges[k + 1], epsabs=1e-18, epsrel=1e-12)[0]
+                   for k in range(lo, hi))
+
+    for k in (0, 64, 127, 128, 200, 255):
+        lo, hi = max(k - 1, 0), min(k + 2, 256)
+        base = local_mse(lv, lo, hi)
+        for eps in (1e-3, -1e-3):
+            p = lv.copy()
+            p[k] += eps
+            assert local_mse(p, lo, hi) > base

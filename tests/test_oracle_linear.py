@@ -15,7 +15,7 @@ import oracle
 import workloads as wl
 
 
-@pytest.mark.parametrize("ba,bw", [(4, 4), (4, 2), (3, 2), (4, 3), (2, 2)])
+@pytest.mark.parametrize("ba,bw", [(4, 4), (4, 2), (3, 2), (4, 3), (2, 2), (8, 8)])
 def test_linear_brute_force_tiny(ba, bw):
     M, N, K = 3, 5, 128
     ac, an = wl.random_codes(M, K, ba, 1)
@@ -65,12 +65,14 @@ def test_pipeline_approaches_exact_product_as_bits_grow():
     W = (rng.standard_normal((N, d)) * 0.02).astype(np.float32)
     ref = x.astype(np.float64) @ W.astype(np.float64).T
     errs = {}
-    for b in (2, 3, 4):
+    for b in (2, 3, 4, 8):
         ac, an, _ = oracle.rotate_quantize(x, oracle.F32, d, seed, b)
         wc, wn, _ = oracle.rotate_quantize(W, oracle.F32, d, seed, b)
         y = oracle.linear(ac, an, b, wc, wn, b, d)
         errs[b] = np.linalg.norm(y - ref) / np.linalg.norm(ref)
-    assert errs[2] > errs[3] > errs[4]
+    assert errs[2] > errs[3] > errs[4] > errs[8]
+    # 8 bits: distortion 4.1e-5 (near Panter-Dite), same sqrt(2 D) law
+    assert 0.5 * np.sqrt(2 * 4.12e-5) < errs[8] < 2.0 * np.sqrt(2 * 4.12e-5)
     # unit-variance Lloyd-Max distortions: 0.1175 (2b), 0.0345 (3b), 0.0095 (4b);
     # cosine error of each factor ~ distortion, so the product error ~ sqrt(2 D)
     assert 0.5 * np.sqrt(2 * 0.0095) < errs[4] < 2.0 * np.sqrt(2 * 0.0095)

@@ -15,7 +15,7 @@ import oracle
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
 
-@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
 def test_quantize_is_nearest_level_by_brute_force(bits):
     d = 3072
     lv, th = oracle.codebook(d, bits)
@@ -30,7 +30,7 @@ def test_quantize_is_nearest_level_by_brute_force(bits):
         assert got == max(cand)
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_ties_go_up_and_signed_zero(bits):
     lv, th = oracle.codebook(256, bits)
     L = 1 << bits
@@ -87,7 +87,7 @@ def test_pack_hand_built_vectors():
         assert got.tobytes() == expect, (bits, spec)
 
 
-@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
 def test_pack_unpack_roundtrip(bits):
     rng = np.random.default_rng(bits)
     d = 384
@@ -95,3 +95,26 @@ def test_pack_unpack_roundtrip(bits):
     packed = oracle.pack_row(codes, bits)
     assert packed.shape[0] == d * bits // 8
     assert np.array_equal(oracle.unpack_row(packed, d, bits), codes)
+
+
+def test_eight_bit_codes_are_whole_bytes_in_slot_order():
+    """At 8 bits the little-endian bitstream is plain byte addressing: byte
+    slot(i) of the row is the code of coordinate i."""
+    rng = np.random.default_rng(8)
+    d = 256
+    codes = rng.integers(0, 256, d).astype(np.uint8)
+    packed = oracle.pack_row(codes, 8)
+    assert packed.shape[0] == d
+    for i in range(d):
+        assert packed[oracle.slot_of(i)] == codes[i]
+
+
+def test_eight_bit_quantize_matches_sorted_search():
+    """#{k : z >= tau_k} is the insertion index of z after equal keys."""
+    lv, th = oracle.codebook(3072, 8)
+    rng = np.random.default_rng(5)
+    zs = np.concatenate([rng.standard_normal(3000) / np.sqrt(3072) * 1.3, th, -th[:5],
+                         [0.0, 1.0, -1.0]])
+    want = np.searchsorted(th, zs, side="right")
+    got = np.array([oracle.quantize_one(z, th) for z in zs])
+    assert np.array_equal(got, want)
