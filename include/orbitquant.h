@@ -12,7 +12,8 @@
  *     D, then an orthonormal Walsh-Hadamard transform on each of the
  *     k = d / h blocks, h = the largest power of two dividing d;
  *   - each rotated coordinate is replaced by the nearest level of the
- *     Lloyd-Max codebook C_{d,b} for N(0, 1/d) (b = 2..4 bits);
+ *     Lloyd-Max codebook C_{d,b} for N(0, 1/d) (b = 2..4 bits, or 8: the
+ *     pages' bit range runs from W2A4 up to W8A8, llmdb.app summary);
  *   - weights are prepared offline as the rows of W Pi^T, i.e. each row w_i
  *     goes through the same rotation and quantizer, with row norm r_i;
  *   - the linear is y[m][n] = s_m r_n sum_k C_{K,bw}[p_nk] C_{K,ba}[q_mk]
@@ -37,10 +38,11 @@
  *     in bits [b t, b t + b) of the row's bytes, little-endian bit order.
  *     A row of d codes therefore takes d*b/8 bytes.  Codes are level
  *     indices 0..2^b-1 in ascending level order.
+ *     At 8 bits this is plain byte addressing: byte slot(i) holds code i.
  *   - Limits: d (and K) a multiple of 128, 128 <= d <= 16384; bits in
- *     {2, 3, 4} (1..4 for oq_codebook).  Zero rows are valid (a zero token
- *     gets norm 0 and every code 2^(b-1)).  NaN/Inf inputs give unspecified
- *     codes and no error.
+ *     {2, 3, 4, 8} (1..8 for oq_codebook; the exact-sphere family up to 4).
+ *     Zero rows are valid (a zero token gets norm 0 and every code
+ *     2^(b-1)).  NaN/Inf inputs give unspecified codes and no error.
  */
 #ifndef ORBITQUANT_H
 #define ORBITQUANT_H
@@ -91,8 +93,9 @@ int oq_version(void);
  *   levels:     caller buffer of 2^bits floats, ascending, sigma = 1/sqrt(d)
  *   thresholds: caller buffer of 2^bits - 1 floats, the midpoints of
  *               adjacent levels (decision boundaries)
- * bits in 1..4, d >= 1.  Errors: OQ_EINVAL (null buffer, d < 1),
- * OQ_EUNSUPPORTED (bits). */
+ * bits in 1..8, d >= 1.  Errors: OQ_EINVAL (null buffer, d < 1),
+ * OQ_EUNSUPPORTED (bits).  The solver is Max's shooting method; at 8 bits
+ * its levels lie within about 1e-9 (unit scale) of the fixed point. */
 int oq_codebook(int d, int bits, float *levels, float *thresholds);
 
 /* oq_codebook with a codebook family (flags 0 or OQ_CODEBOOK_SPHERE).  The
@@ -100,7 +103,7 @@ int oq_codebook(int d, int bits, float *levels, float *thresholds);
  * c_d (1 - t^2)^((d-3)/2) of one coordinate of a uniform point on S^{d-1}
  * (pith.science: the referee's minor comment 1 asks for this closed-form
  * marginal), defined for the dimensions the kernels take (d % 128 == 0,
- * d <= 16384; else OQ_EUNSUPPORTED).  It differs from the Gaussian one by
+ * d <= 16384) and bits 1..4 (else OQ_EUNSUPPORTED).  It differs from the Gaussian one by
  * 0.8% of a level at d = 256 and 0.015% at d = 13824 (4 bits). */
 int oq_codebook_ex(int d, int bits, uint32_t flags, float *levels, float *thresholds);
 
@@ -154,7 +157,9 @@ int oq_prepare_weights(const void *W, int dtype, int64_t n_out, int d_in, uint64
  *   w_norms [N]: device, as produced by oq_rotate_quantize /
  *   oq_prepare_weights with the same seed, flags and K
  *   y: device bf16 bit patterns, [M][N] row-major
- * a_bits, w_bits in {2, 3, 4}.  M = 0 or N = 0 is a no-op that succeeds
+ * a_bits, w_bits in {2, 3, 4}, any pair, or both 8 (W8A8: the codes are
+ * decoded through an fp16 table of the 256 levels; a pair with only one
+ * side at 8 bits is OQ_EUNSUPPORTED).  M = 0 or N = 0 is a no-op that succeeds
  * (the pointers may then be NULL).  Errors:
  * OQ_EINVAL, OQ_EUNSUPPORTED, OQ_EDEVICE. */
 int oq_linear(const uint8_t *a_codes, const float *a_norms, int a_bits,
@@ -164,7 +169,7 @@ int oq_linear(const uint8_t *a_codes, const float *a_norms, int a_bits,
 /* oq_linear with a codebook family for both operands (flags 0 or
  * OQ_CODEBOOK_SPHERE; the codes must come from rotate/prepare calls with
  * the same family).  Same layout, limits and errors; flags outside the
- * family bit give OQ_EINVAL. */
+ * family bit give OQ_EINVAL; the sphere family at 8 bits, OQ_EUNSUPPORTED. */
 int oq_linear_ex(const uint8_t *a_codes, const float *a_norms, int a_bits,
                  const uint8_t *w_codes, const float *w_norms, int w_bits,
                  int64_t M, int64_t N, int K, uint32_t flags, uint16_t *y, void *stream);

@@ -116,8 +116,8 @@ def codebook(d, bits, *, sphere=False):
     """(levels float32[2^bits], thresholds float32[2^bits-1]) of C_{d,bits}
     (sphere: the exact-sphere-marginal family)."""
     L = 1 << bits
-    lv = np.zeros(16, np.float32)
-    th = np.zeros(16, np.float32)
+    lv = np.zeros(256, np.float32)
+    th = np.zeros(256, np.float32)
     flags = OQ_CODEBOOK_SPHERE if sphere else 0
     _check(lib().oq_codebook_ex(d, bits, flags, lv.ctypes.data, th.ctypes.data), "oq_codebook_ex")
     return lv[:L].copy(), th[:L - 1].copy()

@@ -35,6 +35,13 @@
 // Throughput is bound by the matrix core and the decode's VALU issue
 // together (about 3.1 VALU instructions per MFMA at 4 bits); the plain fp16
 // library GEMM of the same shape is the practical ceiling for comparison.
+//
+// 8-bit codes (W8A8) take the same path except for the decode: 256 levels do
+// not fit byte-permute tables, so each workgroup first converts the fp32
+// unit levels to an fp16 table at the start of LDS (512 bytes; activation
+// and weight codes of one linear share K, bit width and codebook family, so
+// they share the table) and a code becomes one 16-bit LDS read at address
+// 2 * code.  The decoded tiles follow the table.
 #include <hip/hip_runtime.h>
 
 #include "oq_internal.h"
@@ -61,6 +68,8 @@ struct Tile {
   static constexpr int OPB = 8 * PLANE;           // bytes per operand tile
   static constexpr int STAGEB = 2 * OPB;          // A + B per stage
   static constexpr int LDS = 2 * STAGEB;          // double buffered
+  static constexpr int LUT8 = 512;                 // 8 bits: level table before the tiles
+
   static_assert(WM * WN * 64 == THREADS, "one wave per 64 rows");
   static_assert(IB % 4 == 0 && JB >= 1, "4 chunks per K half");
 };
@@ -140,13 +149,50 @@ __device__ __forceinline__ u32x4 decode_q(const uint32_t *w, const PermTab &t, i
   return u32x4{a0, a1, b0, b1};
 }
 
+// 8 bits: slots 8q .. 8q+7 are bytes 0-3 of w[2q] and w[2q+1]; each code
+// is a 16-bit read from the fp16 level table lut (in LDS), and the levels
+// come out in the same slot order as above.
+__device__ __forceinline__ uint32_t lut_pair(const uint16_t *lut, uint32_t v, int sh0, int sh1) {
+  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+  const _Float16 *l = (const _Float16 *)lut;
+  half2v r;
+  r[0] = l[(v >> sh0) & 0xFFu];  // 16-bit reads straight into the two halves
+  r[1] = l[(v >> sh1) & 0xFFu];
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ u32x4 decode_q8(const uint32_t *w, const uint16_t *lut, int q) {
+  const uint32_t w0 = w[2 * q], w1 = w[2 * q + 1];
+  return u32x4{lut_pair(lut, w0, 0, 16), lut_pair(lut, w1, 0, 16), lut_pair(lut, w0, 8, 24),
+               lut_pair(lut, w1, 8, 24)};
+}
+
+// The decode of one role: byte-permute tables (2-4 bits) or an LDS level
+// table (8 bits).
+struct Decoder {
+  PermTab t;
+  const uint16_t *lut;
+};
+
+template <int BITS>
+__device__ __forceinline__ u32x4 decode_chunk(const uint32_t *w, const Decoder &dc, int q) {
+  if constexpr (BITS == 8) return decode_q8(w, dc.lut, q);
+  else return decode_q<BITS>(w, dc.t, q);
+}
+
 // Byte offset of (row, chunk) inside one operand tile of the LDS layout.
 template <class TL>
 __device__ __forceinline__ int chunk_off(int row, int chunk) { return chunk * TL::PLANE + row * 16; }
 
 template <int BITS>
 __device__ __forceinline__ void load_codes(const uint8_t *p, uint32_t *w) {
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 8) {
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const u32x4 a = *(const u32x4 *)(p + 16 * v);
+      w[4 * v] = a[0]; w[4 * v + 1] = a[1]; w[4 * v + 2] = a[2]; w[4 * v + 3] = a[3];
+    }
+  } else if constexpr (BITS == 4) {
     const u32x4 a = *(const u32x4 *)p, b = *(const u32x4 *)(p + 16);
     w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
     w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
@@ -164,41 +210,51 @@ __device__ __forceinline__ void load_codes(const uint8_t *p, uint32_t *w) {
 // (activation or weight row; the MFMA work is the same for both roles).
 template <class TL, int BITS>
 __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[TL::JB][TL::IB],
-                                       const uint8_t *prow, const PermTab &tt, int opoff, int row,
+                                       const uint8_t *prow, const Decoder &tt, int opoff, int row,
                                        int lane, int wm, int wn, int T) {
   constexpr int RB = 8 * BITS;           // code bytes of one K step
   constexpr int IB = TL::IB, JB = TL::JB;
   constexpr int IPC = IB / 4;            // activation blocks per chunk
-  uint32_t cb0[2 * BITS], cb1[2 * BITS];
+  // 8 bits: one 64-byte code buffer, refilled 16 bytes at a time as soon as
+  // a pair of chunks has been decoded from it (registers are too tight for
+  // two), still about three quarters of a step ahead of use
+  constexpr bool REFILL = BITS == 8;
+  uint32_t cb0[2 * BITS], cb1[REFILL ? 1 : 2 * BITS];
   uint8_t *wbase = lds + opoff;
   load_codes<BITS>(prow, cb0);
 #pragma unroll
   for (int q = 0; q < 8; q++)
-    *(u32x4 *)(wbase + chunk_off<TL>(row, q)) = decode_q<BITS>(cb0, tt, q);
-  if (T > 1) load_codes<BITS>(prow + RB, cb1);
+    *(u32x4 *)(wbase + chunk_off<TL>(row, q)) = decode_chunk<BITS>(cb0, tt, q);
+  if (T > 1) load_codes<BITS>(prow + RB, REFILL ? cb0 : cb1);
 
   // fragment lanes: rows + (lane & 15), 8-slot chunk (lane >> 4) of each
-  // 32-slot half
-  const int fr = lane & 15, ch0 = lane >> 4, ch1 = 4 + (lane >> 4);
-  const int arow0 = wm * (16 * IB) + fr, brow0 = wn * (16 * JB) + fr;
+  // 32-slot half.  The per-lane byte offsets are made opaque to the
+  // compiler (an empty asm), so it cannot rewrite base + constant as a
+  // bitwise or and every fragment and chunk offset below stays an
+  // instruction immediate: a few address registers instead of one per
+  // fragment.
+  const int fr = lane & 15, ch0 = lane >> 4;
+  uint32_t aoff = chunk_off<TL>(wm * (16 * IB) + fr, ch0);
+  uint32_t boff = TL::OPB + chunk_off<TL>(wn * (16 * JB) + fr, ch0);
+  uint32_t woff = opoff + row * 16;
+  asm volatile("" : "+v"(aoff), "+v"(boff), "+v"(woff));
+  constexpr int H1 = 4 * TL::PLANE;  // chunk ch0 + 4: the second 32-slot half
 
   // One K step: the MFMAs of step t (stage t&1); when `decode`, also the
   // decode of step t+1 (from `cur`) into stage (t+1)&1 and the load of
   // step t+2's codes into `nb`.
-  auto step = [&](int t, const uint32_t *cur, uint32_t *nb, bool decode) {
+  auto step = [&](int t, uint32_t *cur, uint32_t *nb, bool decode) {
     __syncthreads();  // stage t&1 complete, stage (t+1)&1 no longer read
-    if (decode) {
-      const int n2 = (t + 2 < T) ? t + 2 : T - 1;  // past the end: a harmless re-read
-      load_codes<BITS>(prow + (int64_t)n2 * RB, nb);
-    }
-    const uint8_t *sA = lds + (t & 1) * TL::STAGEB;
-    const uint8_t *sB = sA + TL::OPB;
-    uint8_t *dst = wbase + ((t + 1) & 1) * TL::STAGEB;
+    const int n2 = (t + 2 < T) ? t + 2 : T - 1;  // past the end: a harmless re-read
+    if (decode && !REFILL) load_codes<BITS>(prow + (int64_t)n2 * RB, nb);
+    const uint8_t *stg = lds + (t & 1) * TL::STAGEB;
+    const uint8_t *sA = stg + aoff, *sB = stg + boff;
+    uint8_t *dst = lds + ((t + 1) & 1) * TL::STAGEB + woff;
     half8 af0[IB], bf0[JB], af1[IB], bf1[JB];
 #pragma unroll
-    for (int j = 0; j < JB; j++) bf0[j] = *(const half8 *)(sB + chunk_off<TL>(brow0 + 16 * j, ch0));
+    for (int j = 0; j < JB; j++) bf0[j] = *(const half8 *)(sB + 256 * j);
 #pragma unroll
-    for (int u = 0; u < IPC; u++) af0[u] = *(const half8 *)(sA + chunk_off<TL>(arow0 + 16 * u, ch0));
+    for (int u = 0; u < IPC; u++) af0[u] = *(const half8 *)(sA + 256 * u);
 #pragma unroll
     for (int c = 0; c < 8; c++) {
       // chunk c: activation blocks IPC*(c&3) .. of K half c>>2 against all
@@ -207,20 +263,18 @@ __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[TL::JB][TL::
 #pragma unroll
         for (int u = 0; u < IPC; u++) {
           const int i = IPC * (c + 1) + u;
-          af0[i] = *(const half8 *)(sA + chunk_off<TL>(arow0 + 16 * i, ch0));
+          af0[i] = *(const half8 *)(sA + 256 * i);
         }
       } else if (c == 3) {
 #pragma unroll
-        for (int j = 0; j < JB; j++)
-          bf1[j] = *(const half8 *)(sB + chunk_off<TL>(brow0 + 16 * j, ch1));
+        for (int j = 0; j < JB; j++) bf1[j] = *(const half8 *)(sB + H1 + 256 * j);
 #pragma unroll
-        for (int u = 0; u < IPC; u++)
-          af1[u] = *(const half8 *)(sA + chunk_off<TL>(arow0 + 16 * u, ch1));
+        for (int u = 0; u < IPC; u++) af1[u] = *(const half8 *)(sA + H1 + 256 * u);
       } else if (c < 7) {
 #pragma unroll
         for (int u = 0; u < IPC; u++) {
           const int i = IPC * (c - 3) + u;
-          af1[i] = *(const half8 *)(sA + chunk_off<TL>(arow0 + 16 * i, ch1));
+          af1[i] = *(const half8 *)(sA + H1 + 256 * i);
         }
       }
 #pragma unroll
@@ -234,22 +288,29 @@ __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[TL::JB][TL::
             acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf1[j], af1[i], acc[j][i], 0, 0, 0);
         }
       }
-      if (decode) *(u32x4 *)(dst + chunk_off<TL>(row, c)) = decode_q<BITS>(cur, tt, c);
+      if (decode) *(u32x4 *)(dst + c * TL::PLANE) = decode_chunk<BITS>(cur, tt, c);
+      if constexpr (REFILL) {
+        if (decode && (c & 1)) {  // words 2c-2 .. 2c+1 are free: step t+2's bytes 8c-8 ..
+          const u32x4 v = *(const u32x4 *)(prow + (int64_t)n2 * RB + 8 * (c - 1));
+          cur[2 * c - 2] = v[0]; cur[2 * c - 1] = v[1]; cur[2 * c] = v[2]; cur[2 * c + 1] = v[3];
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // steps in pairs so the two code buffers alternate without copies
+  uint32_t *b0 = REFILL ? cb0 : cb1, *b1 = cb0;
   int t = 0;
   for (; t + 2 < T; t += 2) {
-    step(t, cb1, cb0, true);
-    step(t + 1, cb0, cb1, true);
+    step(t, b0, b1, true);
+    step(t + 1, b1, b0, true);
   }
   if (t + 1 < T) {
-    step(t, cb1, cb0, true);
+    step(t, b0, b1, true);
     t++;
   }
-  step(t, cb1, cb0, false);
+  step(t, b0, b1, false);
 }
 
 // Group-major tile order: index g -> 256 x 256 tile (tm, tn), GROUP_M tile
@@ -265,12 +326,15 @@ __device__ __forceinline__ void big_tile_of(int g, int nbm, int nbn, int &tm, in
 // group-major order from index `first` (block ids spread so each XCD takes a
 // contiguous run).  TL = SmallTile: each 256 x 256 tile from index `first`
 // on is split into four 128 x 128 tiles, one workgroup each.
+// lv8 (8 bits only): fp32 unit levels of the shared codebook.
 template <class TL, int BA, int BW>
 __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
     const uint8_t *__restrict__ A, const float *__restrict__ sa, const uint8_t *__restrict__ Wc,
     const float *__restrict__ sw, int M, int N, int K, uint16_t *__restrict__ Y, PermTab ta,
-    PermTab tw, int vec_store, int first, int count) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    PermTab tw, const float *__restrict__ lv8, int vec_store, int first, int count) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_base[];
+  static_assert(BA != 8 || BW == 8, "8-bit codes on both sides");
+  uint8_t *lds = lds_base + (BA == 8 ? TL::LUT8 : 0);  // decoded tiles
   constexpr int TT = TL::T, IB = TL::IB, JB = TL::JB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn_count = TT / (16 * JB);
@@ -310,13 +374,24 @@ __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
 #pragma unroll
     for (int i = 0; i < IB; i++) acc[j][i] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  Decoder da{ta, nullptr}, dw{tw, nullptr};
+  if constexpr (BA == 8) {
+    // fp16 level table (round to nearest even, as on the host) into LDS
+    uint16_t *lut = (uint16_t *)lds_base;
+    for (int i = tid; i < 256; i += TL::THREADS)
+      lut[i] = __builtin_bit_cast(uint16_t, (_Float16)lv8[i]);
+    __syncthreads();
+    da.lut = lut;
+    dw.lut = lut;
+  }
+
   if constexpr (BA == BW) {
-    k_loop<TL, BA>(lds, acc, is_a ? pa : pw, is_a ? ta : tw, is_a ? 0 : TL::OPB, row, lane, wm,
+    k_loop<TL, BA>(lds, acc, is_a ? pa : pw, is_a ? da : dw, is_a ? 0 : TL::OPB, row, lane, wm,
                    wn, T);
   } else {
     // both branches run the same barriers; the branch is wave-uniform
-    if (is_a) k_loop<TL, BA>(lds, acc, pa, ta, 0, row, lane, wm, wn, T);
-    else k_loop<TL, BW>(lds, acc, pw, tw, TL::OPB, row, lane, wm, wn, T);
+    if (is_a) k_loop<TL, BA>(lds, acc, pa, da, 0, row, lane, wm, wn, T);
+    else k_loop<TL, BW>(lds, acc, pw, dw, TL::OPB, row, lane, wm, wn, T);
   }
 
   // ---- epilogue: lane holds rows m = .. + (lane & 15), cols n = .. + 4 (lane >> 4) + r
@@ -357,18 +432,19 @@ PermTab make_tab(const LevelsF16 &lv) {
 }
 
 template <class TL, int BA, int BW>
-hipError_t launch_tiles(const LinearArgs &a, const PermTab &ta, const PermTab &tw, int vec,
-                        int first, int count, unsigned grid) {
+hipError_t launch_tiles(const LinearArgs &a, const PermTab &ta, const PermTab &tw,
+                        const float *lv8, int vec, int first, int count, unsigned grid) {
+  constexpr int lds = TL::LDS + (BA == 8 ? TL::LUT8 : 0);
   static bool attr_set = false;  // per instantiation; the attribute is per function
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void *)linear_kernel<TL, BA, BW>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, TL::LDS);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((linear_kernel<TL, BA, BW>), dim3(grid), dim3(TL::THREADS), TL::LDS,
-                     a.stream, a.a_codes, a.a_norms, a.w_codes, a.w_norms, (int)a.M, (int)a.N,
-                     a.K, a.y, ta, tw, vec, first, count);
+  hipLaunchKernelGGL((linear_kernel<TL, BA, BW>), dim3(grid), dim3(TL::THREADS), lds, a.stream,
+                     a.a_codes, a.a_norms, a.w_codes, a.w_norms, (int)a.M, (int)a.N, a.K, a.y, ta,
+                     tw, lv8, vec, first, count);
   return hipGetLastError();
 }
 
@@ -378,7 +454,8 @@ hipError_t launch_tiles(const LinearArgs &a, const PermTab &ta, const PermTab &t
 // workgroups finish staggered, so it costs far less than a full round, and
 // 128 x 128 tiles (one wave per SIMD) take about half a round's time anyway.
 template <int BA, int BW>
-hipError_t launch_ab(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw) {
+hipError_t launch_ab(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw,
+                     const float *lv8) {
   const PermTab ta = make_tab(la), tw = make_tab(lw);
   const int vec = (a.N % 4 == 0) && (((uintptr_t)a.y & 7) == 0) && (((uintptr_t)a.w_norms & 15) == 0);
   const int64_t tiles = ((a.M + BIG - 1) / BIG) * ((a.N + BIG - 1) / BIG);
@@ -392,21 +469,28 @@ hipError_t launch_ab(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &
   }
   const int64_t full = (4 * tiles <= cus) ? 0 : tiles;
   if (full > 0) {
-    hipError_t e = launch_tiles<BigTile, BA, BW>(a, ta, tw, vec, 0, (int)full, (unsigned)full);
+    hipError_t e =
+        launch_tiles<BigTile, BA, BW>(a, ta, tw, lv8, vec, 0, (int)full, (unsigned)full);
     if (e != hipSuccess) return e;
   }
   if (full < tiles)
-    return launch_tiles<SmallTile, BA, BW>(a, ta, tw, vec, (int)full, (int)(tiles - full),
-                                           (unsigned)(4 * (tiles - full)));
+    return launch_tiles<SmallTile, BA, BW>(a, ta, tw, lv8, vec, (int)full,
+                                           (int)(tiles - full), (unsigned)(4 * (tiles - full)));
   return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_linear(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw) {
+hipError_t launch_linear(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw,
+                         const uint32_t *ta, const uint32_t *tw) {
   if (a.M > (int64_t)1 << 30 || a.N > (int64_t)1 << 30) return hipErrorInvalidValue;
+  if (a.a_bits == 8 && a.w_bits == 8) {
+    // one codebook for both operands: same K, bit width and family
+    if (!ta || ta != tw) return hipErrorInvalidValue;
+    return launch_ab<8, 8>(a, la, lw, (const float *)(ta + table_levels_word(8)));
+  }
 #define OQ_CASE(x, y) \
-  if (a.a_bits == x && a.w_bits == y) return launch_ab<x, y>(a, la, lw);
+  if (a.a_bits == x && a.w_bits == y) return launch_ab<x, y>(a, la, lw, nullptr);
   OQ_CASE(2, 2) OQ_CASE(2, 3) OQ_CASE(2, 4)
   OQ_CASE(3, 2) OQ_CASE(3, 3) OQ_CASE(3, 4)
   OQ_CASE(4, 2) OQ_CASE(4, 3) OQ_CASE(4, 4)

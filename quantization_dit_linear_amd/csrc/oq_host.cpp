@@ -73,15 +73,18 @@ double shoot(double c0, int P, double *pos_levels, double *pos_edges) {
 }
 
 // Unit-variance Lloyd-Max codebook: L = 2^bits ascending levels, L-1
-// thresholds.  Cached: the result depends on bits only.
+// thresholds, bits 1..8.  Cached: the result depends on bits only.  At 8
+// bits the shot carries the first level's rounding through 127 cells; the
+// levels still come out within about 1e-9 of the fixed point, far below the
+// fp32 precision the kernels use them in.
 void unit_codebook(int bits, double *levels, double *thresholds) {
   static std::mutex mu;
-  static bool done[5] = {false, false, false, false, false};
-  static double lv[5][16], th[5][15];
+  static bool done[9] = {};
+  static double lv[9][256], th[9][255];
   std::lock_guard<std::mutex> g(mu);
   const int L = 1 << bits, P = L / 2;
   if (!done[bits]) {
-    double pl[8], pe[8];
+    double pl[128], pe[128];
     if (P == 1) {
       pl[0] = cell_mean(0.0, INFINITY);
     } else {
@@ -357,24 +360,27 @@ int get_plan(int d, uint64_t seed, hipStream_t stream, const oq::DevicePlan **ou
   return OQ_OK;
 }
 
-// Cell table of the bf16 fast path.  The kernel maps a unit-space value u
-// (= sqrt(d) z), clamped to [-8, 8), to cell c = floor(8 u + 64 + 1/16) of
-// a 1/8-sigma grid (128 cells; the first and last cells also take every
-// value beyond, where no threshold lies); entry c = {tau, base}: base =
-// number of thresholds at or below the cell, tau = the only threshold that
-// can fall inside it (or +inf), so the code is base + (u >= tau) with the
-// unclamped u.  A cell holding two thresholds would need a finer grid:
-// rejected (never the case for 2-4 bit Lloyd-Max codebooks).
+// Device codebook table (layout in oq_internal.h).  Cell grid of the bf16
+// fast path: the kernel maps a unit-space value u (= sqrt(d) z), clamped to
+// the grid's range, to cell c = floor(u / delta + C/2 + 1/16) (C cells of
+// width delta; the first and last cells also take every value beyond, where
+// no threshold lies).  Entry c = {tau, base}: base = number of thresholds at
+// or below the cell, tau = the only threshold that can fall inside it (or
+// +inf), so the code is base + (u >= tau) with the unclamped u.  The cell's
+// extent allows for the kernel's rounding (1/16 cell each side, plus 2%); a
+// cell holding two thresholds would need a finer grid: rejected (never the
+// case for the 2-4 bit grid of 1/8 or the 8-bit grid of 1/128, whose
+// closest Gaussian thresholds are 0.0169 apart).
 int build_cells(int d, int bits, bool sphere, std::vector<uint32_t> &out) {
-  double lv[16], th[15];
+  double lv[256], th[255];
   family_codebook(d, bits, sphere, lv, th);
-  const int T = (1 << bits) - 1;
-  const double delta = 0.125, eps = 0.02 * delta;
-  out.assign(2 * oq::kFastCells, 0);
-  for (int c = 0; c < oq::kFastCells; c++) {
+  const int T = (1 << bits) - 1, C = oq::cells_for_bits(bits);
+  const double delta = bits == 8 ? 1.0 / 128.0 : 0.125, eps = 0.02 * delta;
+  out.assign(oq::table_thresholds_word(bits) + T, 0);
+  for (int c = 0; c < C; c++) {
     const double inf = std::numeric_limits<double>::infinity();
-    const double lo = c == 0 ? -inf : delta * (c - 64.0625) - eps;
-    const double hi = c == oq::kFastCells - 1 ? inf : delta * (c - 63.0625) + eps;
+    const double lo = c == 0 ? -inf : delta * (c - 0.5 * C - 0.0625) - eps;
+    const double hi = c == C - 1 ? inf : delta * (c - 0.5 * C + 0.9375) + eps;
     int base = 0, inside = 0;
     for (int k = 0; k < T; k++) {
       if ((double)(float)th[k] <= lo) base++;
@@ -387,11 +393,19 @@ int build_cells(int d, int bits, bool sphere, std::vector<uint32_t> &out) {
     out[2 * c] = tb;
     out[2 * c + 1] = (uint32_t)base;
   }
+  for (int k = 0; k <= T; k++) {
+    const float f = (float)lv[k];
+    std::memcpy(&out[oq::table_levels_word(bits) + k], &f, 4);
+  }
+  for (int k = 0; k < T; k++) {
+    const float f = (float)th[k];
+    std::memcpy(&out[oq::table_thresholds_word(bits) + k], &f, 4);
+  }
   return OQ_OK;
 }
 
 std::mutex g_cell_mu;
-// (device, bits, d for the sphere family or 0) -> table
+// (device, bits, d for the sphere family or 0) -> device codebook table
 std::map<std::tuple<int, int, int>, uint32_t *> g_cells;
 
 int get_cells(int d, int bits, bool sphere, const uint32_t **out) {
@@ -424,7 +438,7 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int check_d_bits(int d, int bits) {
   if (d <= 0) return OQ_EINVAL;
-  if (bits < 2 || bits > 4) return OQ_EUNSUPPORTED;
+  if ((bits < 2 || bits > 4) && bits != 8) return OQ_EUNSUPPORTED;
   if (d % oq::kGroup != 0 || d > oq::kMaxD) return OQ_EUNSUPPORTED;
   return OQ_OK;
 }
@@ -441,17 +455,18 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
   if ((flags & outs) == outs) return OQ_EINVAL;
   int rc = check_d_bits(d, bits);
   if (rc != OQ_OK) return rc;
+  if (sphere && bits > 4) return OQ_EUNSUPPORTED;
   if (n_tok == 0) return OQ_OK;  // empty input: nothing to do, pointers may be null
   if (!x || !out || !norms) return OQ_EINVAL;
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(norms, 4)) return OQ_EINVAL;
   const oq::DevicePlan *plan = nullptr;
   rc = get_plan(d, seed, (hipStream_t)stream, &plan);
   if (rc != OQ_OK) return rc;
-  double lv[16], th[15];
+  double lv[256], th[255];
   family_codebook(d, bits, sphere, lv, th);
   oq::Thresholds t{};
   t.count = (1 << bits) - 1;
-  for (int k = 0; k < t.count; k++) t.t[k] = (float)th[k];
+  for (int k = 0; k < t.count && k < 15; k++) t.t[k] = (float)th[k];
   oq::RotateArgs a{};
   a.x = x;
   a.dtype = dtype;
@@ -463,22 +478,22 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
   a.rotated_out = (flags & OQ_OUT_F32_ROTATED) != 0;
   a.dequant_out = (flags & OQ_OUT_BF16_DEQUANT) != 0;
   a.input_permuted = (flags & OQ_ROT_INPUT_PERMUTED) != 0;
-  for (int k = 0; k < (1 << bits); k++) a.levels.v[k] = (float)lv[k];
+  for (int k = 0; k < (1 << bits) && k < 16; k++) a.levels.v[k] = (float)lv[k];
   a.out = out;
   a.norms = norms;
   a.stream = (hipStream_t)stream;
+  const uint32_t *table = nullptr;
+  rc = get_cells(d, bits, sphere, &table);
+  if (rc != OQ_OK) return rc;
   if (a.dtype == OQ_BF16 && !a.rotated_out) {
-    const uint32_t *cells = nullptr;
-    rc = get_cells(d, bits, sphere, &cells);
-    if (rc != OQ_OK) return rc;
     bool handled = false;
     const uint32_t *smask = a.input_permuted ? (a.signs ? plan->fast_signs_id : plan->fast_nosigns)
                                              : (a.signs ? plan->fast_signs : plan->fast_nosigns);
     hipError_t e =
-        oq::launch_rotate_quantize_fast(a, plan->fast_scatter, smask, cells, t, &handled);
+        oq::launch_rotate_quantize_fast(a, plan->fast_scatter, smask, table, &handled);
     if (handled) return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
   }
-  hipError_t e = oq::launch_rotate_quantize_generic(a, *plan, t);
+  hipError_t e = oq::launch_rotate_quantize_generic(a, *plan, t, table);
   return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
 }
 
@@ -492,7 +507,7 @@ const char *oq_strerror(int status) {
   switch (status) {
     case OQ_OK: return "success";
     case OQ_EINVAL: return "invalid argument (null or misaligned pointer, bad size, dtype or flag)";
-    case OQ_EUNSUPPORTED: return "unsupported configuration (d must be a multiple of 128 in [128, 16384]; bits in {2,3,4})";
+    case OQ_EUNSUPPORTED: return "unsupported configuration (d must be a multiple of 128 in [128, 16384]; bits in {2,3,4,8}; 8 bits on both sides of a linear; the sphere codebook up to 4 bits)";
     case OQ_ENOMEM: return "out of device memory for the rotation plan";
     case OQ_EDEVICE: return "HIP runtime or kernel launch failure";
     default: return "unknown status";
@@ -504,10 +519,10 @@ int oq_version(void) { return 100; }
 int oq_codebook_ex(int d, int bits, uint32_t flags, float *levels, float *thresholds) {
   if (!levels || !thresholds || d < 1) return OQ_EINVAL;
   if (flags & ~OQ_CODEBOOK_SPHERE) return OQ_EINVAL;
-  if (bits < 1 || bits > 4) return OQ_EUNSUPPORTED;
+  if (bits < 1 || bits > 8) return OQ_EUNSUPPORTED;
   const bool sphere = (flags & OQ_CODEBOOK_SPHERE) != 0;
-  if (sphere && (d % oq::kGroup != 0 || d > oq::kMaxD)) return OQ_EUNSUPPORTED;
-  double lv[16], th[15];
+  if (sphere && (d % oq::kGroup != 0 || d > oq::kMaxD || bits > 4)) return OQ_EUNSUPPORTED;
+  double lv[256], th[255];
   family_codebook(d, bits, sphere, lv, th);
   const double sigma = 1.0 / std::sqrt((double)d);
   const int L = 1 << bits;
@@ -547,20 +562,30 @@ int oq_linear_ex(const uint8_t *a_codes, const float *a_norms, int a_bits, const
   if (rc != OQ_OK) return rc;
   rc = check_d_bits(K, w_bits);
   if (rc != OQ_OK) return rc;
+  if ((a_bits == 8) != (w_bits == 8)) return OQ_EUNSUPPORTED;  // W8A8 only, no mixed pair
+  if (sphere && a_bits == 8) return OQ_EUNSUPPORTED;
   if (M == 0 || N == 0) return OQ_OK;  // empty output: pointers may be null
   if (!a_codes || !a_norms || !w_codes || !w_norms || !y) return OQ_EINVAL;
   if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_norms, 4) ||
       !aligned(w_norms, 4) || !aligned(y, 2))
     return OQ_EINVAL;
-  double lv[16], th[15];
   oq::LevelsF16 la{}, lw{};
-  family_codebook(K, a_bits, sphere, lv, th);
-  for (int k = 0; k < (1 << a_bits); k++) la.v[k] = f32_to_f16_bits((float)lv[k]);
-  family_codebook(K, w_bits, sphere, lv, th);
-  for (int k = 0; k < (1 << w_bits); k++) lw.v[k] = f32_to_f16_bits((float)lv[k]);
+  const uint32_t *ta = nullptr, *tw = nullptr;
+  if (a_bits == 8) {  // 256 levels: the kernel reads them from the device tables
+    rc = get_cells(K, a_bits, sphere, &ta);
+    if (rc != OQ_OK) return rc;
+    rc = get_cells(K, w_bits, sphere, &tw);
+    if (rc != OQ_OK) return rc;
+  } else {
+    double lv[16], th[15];
+    family_codebook(K, a_bits, sphere, lv, th);
+    for (int k = 0; k < (1 << a_bits); k++) la.v[k] = f32_to_f16_bits((float)lv[k]);
+    family_codebook(K, w_bits, sphere, lv, th);
+    for (int k = 0; k < (1 << w_bits); k++) lw.v[k] = f32_to_f16_bits((float)lv[k]);
+  }
   oq::LinearArgs a{a_codes, a_norms, a_bits, w_codes, w_norms, w_bits, M, N, K, y,
                    (hipStream_t)stream};
-  hipError_t e = oq::launch_linear(a, la, lw);
+  hipError_t e = oq::launch_linear(a, la, lw, ta, tw);
   return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
 }
 

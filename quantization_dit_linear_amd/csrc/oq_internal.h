@@ -61,14 +61,28 @@ struct RotateArgs {
 };
 
 // Kernel launchers (defined in the .hip files).  Return a hipError_t.
+// General kernel.  Up to 4 bits the codebook comes in th and a.levels; at 8
+// bits from the device table (layout above).
 hipError_t launch_rotate_quantize_generic(const RotateArgs &a, const DevicePlan &p,
-                                          const Thresholds &th);
+                                          const Thresholds &th, const uint32_t *table);
 // bf16 fast path; sets *handled = false (and does nothing) for shapes it does
-// not cover.  cells: the quantizer's cell table for a.bits (fast_cell_table).
+// not cover.  table: the device codebook table of a.bits (layout above).
 hipError_t launch_rotate_quantize_fast(const RotateArgs &a, const uint32_t *scat,
-                                       const uint32_t *smask, const uint32_t *cells,
-                                       const Thresholds &th, bool *handled);
-constexpr int kFastCells = 128;  // cells of the fast path's cell table ({tau, base} each)
+                                       const uint32_t *smask, const uint32_t *table,
+                                       bool *handled);
+// Device codebook table of one (bits, family, d): the fast path's cell grid
+// ({tau, base} per cell), then the 2^bits unit levels (fp32), then the
+// 2^bits - 1 unit thresholds (fp32), all as 32-bit words.  The grid is 1/8
+// of a unit over [-8, 8) up to 4 bits and 1/128 over [-5, 5) at 8 bits.
+constexpr int kFastCells = 128;
+constexpr int kFastCells8 = 1280;
+constexpr __host__ __device__ int cells_for_bits(int bits) {
+  return bits == 8 ? kFastCells8 : kFastCells;
+}
+constexpr __host__ __device__ int table_levels_word(int bits) { return 2 * cells_for_bits(bits); }
+constexpr __host__ __device__ int table_thresholds_word(int bits) {
+  return 2 * cells_for_bits(bits) + (1 << bits);
+}
 
 struct LinearArgs {
   const uint8_t *a_codes;
@@ -83,7 +97,10 @@ struct LinearArgs {
   hipStream_t stream;
 };
 
-hipError_t launch_linear(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw);
+// Up to 4 bits the levels come as fp16 bit patterns in la / lw; at 8 bits
+// as the fp32 unit levels of the device tables ta / tw (layout above).
+hipError_t launch_linear(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw,
+                         const uint32_t *ta, const uint32_t *tw);
 
 // INT4 weight-only round-to-nearest (AdaLN projections)
 hipError_t launch_rtn4_prepare(const void *W, int dtype, int64_t rows, int d, uint8_t *q4,

@@ -8,7 +8,9 @@
 // This file holds the general kernel: any dtype, any h, one workgroup per
 // token, the token held in LDS as fp32.  Besides packed codes it can write
 // the rotated unit vector (fp32) or the dequantized rotated token
-// s * c_{code_i} (bf16, fake quantization).
+// s * c_{code_i} (bf16, fake quantization).  Up to 4 bits the code counts
+// the thresholds at or below the value one by one; at 8 bits it is found by
+// an 8-step binary search over the 255 thresholds held in LDS.
 #include <hip/hip_runtime.h>
 
 #include "oq_internal.h"
@@ -27,8 +29,10 @@ __device__ __forceinline__ float load_elem(const void *x, int dtype, int64_t idx
 }
 
 template <int BITS>
-__device__ __forceinline__ void store_codes(uint8_t *dst, uint32_t word) {
-  if constexpr (BITS == 4) {
+__device__ __forceinline__ void store_codes(uint8_t *dst, uint64_t word) {
+  if constexpr (BITS == 8) {
+    *(uint64_t *)dst = word;
+  } else if constexpr (BITS == 4) {
     *(uint32_t *)dst = word;
   } else if constexpr (BITS == 2) {
     *(uint16_t *)dst = (uint16_t)word;
@@ -56,16 +60,46 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Number of unit thresholds at or below u.
+template <int BITS>
+__device__ __forceinline__ uint32_t code_of(float u, const Thresholds &th, const float *t8) {
+  if constexpr (BITS == 8) {
+    uint32_t pos = 0;
+#pragma unroll
+    for (int step = 128; step >= 1; step >>= 1)
+      if (u >= t8[pos + step - 1]) pos += step;
+    return pos;
+  } else {
+    uint32_t code = 0;
+    for (int k = 0; k < th.count; k++) code += (u >= th.t[k]) ? 1u : 0u;
+    return code;
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ float level_of(uint32_t code, const LevelsF32 &lv, const float *l8) {
+  if constexpr (BITS == 8) return l8[code];
+  else return lv.v[code];
+}
+
+// table (8 bits only): the device codebook table; its levels and thresholds
+// are copied into LDS after the token.
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void rq_generic_kernel(
     const void *__restrict__ x, int dtype, int64_t n_tok, int d, int h,
     const int32_t *__restrict__ scatter, int sign_on, Thresholds th, LevelsF32 lv,
-    uint8_t *__restrict__ codes, float *__restrict__ zout, uint16_t *__restrict__ dq,
-    float *__restrict__ norms) {
-  extern __shared__ float y[];  // d floats
+    const uint32_t *__restrict__ table, uint8_t *__restrict__ codes, float *__restrict__ zout,
+    uint16_t *__restrict__ dq, float *__restrict__ norms) {
+  extern __shared__ float y[];  // d floats, then (8 bits) 256 levels, 256 thresholds
   __shared__ double red[kThreads / 64];
   const int tid = threadIdx.x;
   const int64_t row_bytes = (int64_t)d * BITS / 8;
+  float *l8 = y + d, *t8 = y + d + 256;
+  if constexpr (BITS == 8) {
+    l8[tid] = __uint_as_float(table[table_levels_word(8) + tid]);
+    if (tid < 255) t8[tid] = __uint_as_float(table[table_thresholds_word(8) + tid]);
+    __syncthreads();
+  }
   for (int64_t t = blockIdx.x; t < n_tok; t += gridDim.x) {
     // load, sum of squares, scatter with sign: y[pi^-1(j)] = D x_j
     float ss = 0.f;
@@ -98,17 +132,16 @@ __global__ __launch_bounds__(kThreads) void rq_generic_kernel(
       const float fs = (float)(s / sqrt((double)d));  // dequantized value = s * level / sqrt(d)
       for (int q = tid; q < d / 8; q += kThreads) {
         const int G = q >> 4, n = q & 15;
-        uint32_t word = 0;
+        uint64_t word = 0;
 #pragma unroll
         for (int w = 0; w < 2; w++)
 #pragma unroll
           for (int c = 0; c < 4; c++) {
             const int i = G * 128 + 32 * c + 16 * w + n;
             const float u = y[i] * us;
-            uint32_t code = 0;
-            for (int k = 0; k < th.count; k++) code += (u >= th.t[k]) ? 1u : 0u;
-            if (dq) dq[t * d + i] = f32_to_bf16_rne(fs * lv.v[code]);
-            word |= code << (BITS * (4 * w + c));
+            const uint32_t code = code_of<BITS>(u, th, t8);
+            if (dq) dq[t * d + i] = f32_to_bf16_rne(fs * level_of<BITS>(code, lv, l8));
+            word |= (uint64_t)code << (BITS * (4 * w + c));
           }
         if (!dq) store_codes<BITS>(codes + t * row_bytes + 16 * BITS * G + BITS * n, word);
       }
@@ -153,8 +186,25 @@ hipError_t launch_permute_rows(const void *src, void *dst, int64_t rows, int64_t
   return hipGetLastError();
 }
 
+template <int BITS>
+hipError_t launch_generic_bits(const RotateArgs &a, const int32_t *sc, int sign_on,
+                               const Thresholds &th, const uint32_t *table, int grid,
+                               uint8_t *codes, float *zout, uint16_t *dq) {
+  const size_t lds = sizeof(float) * (a.d + (BITS == 8 ? 512 : 0));
+  if (lds > 32768) {
+    // tokens above 8192 fp32 need more than the default dynamic-LDS cap
+    hipError_t e = hipFuncSetAttribute((const void *)rq_generic_kernel<BITS>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(rq_generic_kernel<BITS>, dim3(grid), dim3(kThreads), lds, a.stream, a.x,
+                     a.dtype, a.n_tok, a.d, a.h, sc, sign_on, th, a.levels, table, codes, zout,
+                     dq, a.norms);
+  return hipGetLastError();
+}
+
 hipError_t launch_rotate_quantize_generic(const RotateArgs &a, const DevicePlan &p,
-                                          const Thresholds &th) {
+                                          const Thresholds &th, const uint32_t *table) {
   // placement table: pi^-1 with sign bits, or the identity with sign bits
   // when the input is already in rotation order
   const int32_t *sc = a.input_permuted ? p.scatter_id : (a.signs ? p.scatter : p.scatter_nosign);
@@ -164,41 +214,18 @@ hipError_t launch_rotate_quantize_generic(const RotateArgs &a, const DevicePlan 
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int64_t want = (int64_t)(cus > 0 ? cus : 256) * 8;
   const int grid = (int)(a.n_tok < want ? a.n_tok : want);
-  const size_t lds = sizeof(float) * a.d;
   uint8_t *codes = (a.rotated_out || a.dequant_out) ? nullptr : (uint8_t *)a.out;
   float *zout = a.rotated_out ? (float *)a.out : nullptr;
   uint16_t *dq = a.dequant_out ? (uint16_t *)a.out : nullptr;
-  if (lds > 32768) {
-    // tokens above 8192 fp32 need more than the default dynamic-LDS cap
-    hipError_t e = hipSuccess;
-    if (a.bits == 2)
-      e = hipFuncSetAttribute((const void *)rq_generic_kernel<2>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    else if (a.bits == 3)
-      e = hipFuncSetAttribute((const void *)rq_generic_kernel<3>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    else
-      e = hipFuncSetAttribute((const void *)rq_generic_kernel<4>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
   switch (a.bits) {
-    case 2:
-      hipLaunchKernelGGL(rq_generic_kernel<2>, dim3(grid), dim3(kThreads), lds, a.stream, a.x,
-                         a.dtype, a.n_tok, a.d, a.h, sc, sign_on, th, a.levels, codes, zout, dq, a.norms);
-      break;
-    case 3:
-      hipLaunchKernelGGL(rq_generic_kernel<3>, dim3(grid), dim3(kThreads), lds, a.stream, a.x,
-                         a.dtype, a.n_tok, a.d, a.h, sc, sign_on, th, a.levels, codes, zout, dq, a.norms);
-      break;
-    case 4:
-      hipLaunchKernelGGL(rq_generic_kernel<4>, dim3(grid), dim3(kThreads), lds, a.stream, a.x,
-                         a.dtype, a.n_tok, a.d, a.h, sc, sign_on, th, a.levels, codes, zout, dq, a.norms);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 2: return launch_generic_bits<2>(a, sc, sign_on, th, table, grid, codes, zout, dq);
+    case 3: return launch_generic_bits<3>(a, sc, sign_on, th, table, grid, codes, zout, dq);
+    case 4: return launch_generic_bits<4>(a, sc, sign_on, th, table, grid, codes, zout, dq);
+    case 8:
+      if (!table) return hipErrorInvalidValue;
+      return launch_generic_bits<8>(a, sc, sign_on, th, table, grid, codes, zout, dq);
+    default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace oq

@@ -35,14 +35,15 @@
 //    value, and the butterfly leaves the slot bit in the register index and
 //    a group bit in the lane, which the store addressing follows.
 //  * Quantize.  A magic-number fma turns v into the byte offset of its cell
-//    in a uniform grid over sqrt(d) z (step 1/8, narrower than any threshold
-//    gap; clamped to |sqrt(d) z| < 8, beyond every threshold); one 8-byte
+//    in a uniform grid over sqrt(d) z (narrower than any threshold gap:
+//    step 1/8 over [-8, 8) up to 4 bits, 1/128 over [-5, 5) at 8 bits;
+//    clamped to the grid, whose ends lie beyond every threshold); one 8-byte
 //    LDS read gives the code at the cell's lower edge and the only threshold
 //    that can fall inside the cell; one exact fp32 compare of sqrt(d) z with
-//    it settles the code.  The 1 KB table does not depend on the token, so
-//    it is loaded once per workgroup.
+//    it settles the code.  The table (1 KB, or 10 KB at 8 bits) does not
+//    depend on the token, so it is loaded once per workgroup.
 //  * Pack.  A lane's 8 codes per group are exactly 8 consecutive storage
-//    slots, so they pack into one b-byte word per lane.  (Fake-quantization
+//    slots, so they pack into one b-byte word per lane (8 bytes at 8 bits).  (Fake-quantization
 //    mode instead stores bf16 s * level[code] at every coordinate.)
 #include <hip/hip_runtime.h>
 
@@ -55,9 +56,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kCells = kFastCells;           // grid cells: |sqrt(d) z| < 8 in steps of 1/8
-constexpr int kCellBytes = kCells * 8;       // {float tau, uint base} per cell
 constexpr float kMagic = 12582912.0f;        // 1.5 * 2^23
+
+// Cell grid of a bit width: bytes of the {float tau, uint base} table, and
+// the fma scale from a unit-space value to bytes (8 bytes per cell).
+template <int BITS>
+struct Grid {
+  static constexpr int CELLB = 8 * cells_for_bits(BITS);
+  static constexpr float PER_UNIT = BITS == 8 ? 1024.0f : 64.0f;  // 8 / step
+  // offset mask: keeps every offset inside the workgroup's LDS even for a NaN
+  static constexpr uint32_t MASK = BITS == 8 ? 0x3FF8u : 0x3F8u;
+  static_assert(CELLB <= (int)MASK + 8, "mask covers the table");
+};
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
@@ -68,8 +78,8 @@ constexpr int pick_waves(int wt, int ch, int maxw) {
   return best;
 }
 
-// Compile-time shape of the kernel for one d.
-template <int D>
+// Compile-time shape of the kernel for one d and bit width.
+template <int D, int BITS>
 struct Shape {
   static constexpr int H = D & -D;                    // Hadamard block
   static constexpr int S = H < 1024 ? H : 1024;       // slot: a block, or 1024 of one
@@ -87,9 +97,9 @@ struct Shape {
   static constexpr int CBITS = ilog2(S) - 5;          // chunk bits transformed in registers
   // LDS layout: tables first so their offsets fit instruction immediates
   static constexpr int CT_OFF = 0;                    // cell table, offsets are immediates
-  static constexpr int NP_OFF = CT_OFF + kCellBytes;  // [TB][W] partial sums of squares
-  static constexpr int LV_OFF = NP_OFF + ((TB * W * 4 + 15) / 16) * 16;  // 16 unit levels
-  static constexpr int YB_OFF = LV_OFF + 64;
+  static constexpr int NP_OFF = CT_OFF + Grid<BITS>::CELLB;  // [TB][W] partial sums of squares
+  static constexpr int LV_OFF = NP_OFF + ((TB * W * 4 + 15) / 16) * 16;  // 2^BITS unit levels
+  static constexpr int YB_OFF = LV_OFF + (4 << BITS);
   static constexpr int LDS = YB_OFF + TB * D * 2;
   // register budget of the one-batch-ahead prefetch
   static constexpr bool PREFETCH = (TB * CPT * 4) <= (W <= 8 ? 48 : 32);
@@ -107,13 +117,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // DQ: write bf16 s * level[code] at every coordinate (dq) instead of codes.
 // IDENT: the input is already in rotation order (x'_i = x_{pi(i)}); scat is
 // unused and smask holds the sign masks of the coordinates in place.
+// table: the device codebook table (cell grid, then levels).
 template <int D, int BITS, bool DQ, bool IDENT>
-__global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
+__global__ __launch_bounds__((64 * Shape<D, BITS>::W)) void rq_fast_kernel(
     const uint16_t *__restrict__ x, int64_t n_tok, const uint32_t *__restrict__ scat,
-    const uint32_t *__restrict__ smask, const uint32_t *__restrict__ cells, Thresholds th,
-    LevelsF32 lv, uint8_t *__restrict__ codes, uint16_t *__restrict__ dq,
-    float *__restrict__ norms) {
-  using SH = Shape<D>;
+    const uint32_t *__restrict__ smask, const uint32_t *__restrict__ table,
+    uint8_t *__restrict__ codes, uint16_t *__restrict__ dq, float *__restrict__ norms) {
+  using SH = Shape<D, BITS>;
+  constexpr int CELLB = Grid<BITS>::CELLB;
   constexpr int S = SH::S, P = SH::P, TB = SH::TB, WT = SH::WT, W = SH::W, CPT = SH::CPT;
   constexpr int G = SH::G;
   // a static array: its base is a compile-time constant, so every table and
@@ -122,11 +133,12 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float *npart = (float *)(lds + SH::NP_OFF);
 
-  // cell tables (all 4 copies) into LDS
-  for (int i = tid; i < kCellBytes / 16; i += W * 64)
-    ((u32x4 *)(lds + SH::CT_OFF))[i] = ((const u32x4 *)cells)[i];
+  // cell table (and the levels, for fake quantization) into LDS
+  for (int i = tid; i < CELLB / 16; i += W * 64)
+    ((u32x4 *)(lds + SH::CT_OFF))[i] = ((const u32x4 *)table)[i];
   if constexpr (DQ) {
-    if (tid < 16) ((float *)(lds + SH::LV_OFF))[tid] = lv.v[tid];
+    for (int i = tid; i < (1 << BITS); i += W * 64)
+      ((uint32_t *)(lds + SH::LV_OFF))[i] = table[table_levels_word(BITS) + i];
   }
 
   // per-thread staging: chunk c of every token covers x[8*pos, 8*pos+8)
@@ -222,8 +234,8 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
       for (int w = 0; w < W; w++) ss += npart[tko * W + w];
       const float s = sqrtf(ss);
       const float us = (s > 0.f) ? 1.0f / (s * scale_hd) : 0.f;  // v -> sqrt(d) z
-      const float a8 = us * 64.0f;                               // 8 bytes / (1/8 cell)
-      constexpr float m8 = kMagic + (float)(kCellBytes / 2);      // cell 64 at u = 0
+      const float a8 = us * Grid<BITS>::PER_UNIT;                // 8 bytes per cell
+      constexpr float m8 = kMagic + (float)(CELLB / 2);          // middle cell at u = 0
       // input side: MFMA row r = lane & 15 -> slot r>>2, chunk (r&3) of each group
       const int sig_i = 4 * q + ((lane & 15) >> 2);
       const int tki = sig_i / P, ji = sig_i - tki * P;
@@ -294,16 +306,17 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
       const float fs = s * (1.0f / __builtin_sqrtf((float)D));  // s / sqrt(d)
 #pragma unroll
       for (int g = 0; g < G; g++) {
-        uint32_t word = 0;
+        uint32_t word = 0, word1 = 0;  // word1: codes 4-7 at 8 bits
 #pragma unroll
         for (int w = 0; w < 2; w++)
 #pragma unroll
           for (int i = 0; i < 4; i++) {
             const float val = v[g][w][i];
-            // byte offset 8 floor(8u + 64 + 1/16) of the cell, u clamped to [-8, 8)
+            // byte offset 8 floor(u / step + C/2 + 1/16) of the cell, u clamped
+            // to the grid; the integer sits in the low mantissa bits of tq
             const float tq = __builtin_amdgcn_fmed3f(__builtin_fmaf(val, a8, m8), kMagic,
-                                                     kMagic + (float)(kCellBytes - 1));
-            const uint32_t off = __float_as_uint(tq) & (uint32_t)(kCellBytes - 8);
+                                                     kMagic + (float)(CELLB - 1));
+            const uint32_t off = __float_as_uint(tq) & Grid<BITS>::MASK;
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
             const u32x2 ent = *(const u32x2 *)(lds + SH::CT_OFF + off);  // {tau, base}
             const uint32_t code = ent[1] + (val * us >= __uint_as_float(ent[0]) ? 1u : 0u);
@@ -312,11 +325,19 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
               if (tok < n_tok)
                 dq0[(g & XM) * S + (g & ~XM) * 128 + 32 * i + 16 * w] = f32_to_bf16_rne(fs * lvv);
             }
-            word |= code << (BITS * (4 * w + i));
+            if constexpr (BITS == 8) {
+              if (w == 0) word |= code << (8 * i);
+              else word1 |= code << (8 * i);
+            } else {
+              word |= code << (BITS * (4 * w + i));
+            }
           }
         if (!DQ && tok < n_tok) {
           uint8_t *dst = dst0 + 16 * BITS * ((g & XM) * G + (g & ~XM));
-          if constexpr (BITS == 4) {
+          if constexpr (BITS == 8) {
+            typedef uint32_t u32x2s __attribute__((ext_vector_type(2)));
+            *(u32x2s *)dst = u32x2s{word, word1};
+          } else if constexpr (BITS == 4) {
             *(uint32_t *)dst = word;
           } else if constexpr (BITS == 2) {
             *(uint16_t *)dst = (uint16_t)word;
@@ -334,8 +355,8 @@ __global__ __launch_bounds__(64 * Shape<D>::W) void rq_fast_kernel(
 
 template <int D, int BITS>
 hipError_t launch_one(const RotateArgs &a, const uint32_t *scat, const uint32_t *smask,
-                      const uint32_t *cells, const Thresholds &th) {
-  using SH = Shape<D>;
+                      const uint32_t *table) {
+  using SH = Shape<D, BITS>;
   auto k = a.dequant_out ? (a.input_permuted ? rq_fast_kernel<D, BITS, true, true>
                                              : rq_fast_kernel<D, BITS, true, false>)
                          : (a.input_permuted ? rq_fast_kernel<D, BITS, false, true>
@@ -356,36 +377,37 @@ hipError_t launch_one(const RotateArgs &a, const uint32_t *scat, const uint32_t 
   uint8_t *codes = a.dequant_out ? nullptr : (uint8_t *)a.out;
   uint16_t *dq = a.dequant_out ? (uint16_t *)a.out : nullptr;
   hipLaunchKernelGGL(k, dim3(grid), dim3(64 * SH::W), 0, a.stream, (const uint16_t *)a.x,
-                     a.n_tok, scat, smask, cells, th, a.levels, codes, dq, a.norms);
+                     a.n_tok, scat, smask, table, codes, dq, a.norms);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const RotateArgs &a, const uint32_t *scat, const uint32_t *smask,
-                    const uint32_t *cells, const Thresholds &th) {
+                    const uint32_t *table) {
   switch (a.bits) {
-    case 2: return launch_one<D, 2>(a, scat, smask, cells, th);
-    case 3: return launch_one<D, 3>(a, scat, smask, cells, th);
-    default: return launch_one<D, 4>(a, scat, smask, cells, th);
+    case 2: return launch_one<D, 2>(a, scat, smask, table);
+    case 3: return launch_one<D, 3>(a, scat, smask, table);
+    case 8: return launch_one<D, 8>(a, scat, smask, table);
+    default: return launch_one<D, 4>(a, scat, smask, table);
   }
 }
 
 }  // namespace
 
 hipError_t launch_rotate_quantize_fast(const RotateArgs &a, const uint32_t *scat,
-                                       const uint32_t *smask, const uint32_t *cells,
-                                       const Thresholds &th, bool *handled) {
+                                       const uint32_t *smask, const uint32_t *table,
+                                       bool *handled) {
   *handled = false;
   if (a.dtype != 1 || a.rotated_out) return hipSuccess;
   *handled = true;
   switch (a.d) {
-    case 1024: return launch_d<1024>(a, scat, smask, cells, th);
-    case 2048: return launch_d<2048>(a, scat, smask, cells, th);
-    case 3072: return launch_d<3072>(a, scat, smask, cells, th);
-    case 4096: return launch_d<4096>(a, scat, smask, cells, th);
-    case 5120: return launch_d<5120>(a, scat, smask, cells, th);
-    case 12288: return launch_d<12288>(a, scat, smask, cells, th);
-    case 13824: return launch_d<13824>(a, scat, smask, cells, th);
+    case 1024: return launch_d<1024>(a, scat, smask, table);
+    case 2048: return launch_d<2048>(a, scat, smask, table);
+    case 3072: return launch_d<3072>(a, scat, smask, table);
+    case 4096: return launch_d<4096>(a, scat, smask, table);
+    case 5120: return launch_d<5120>(a, scat, smask, table);
+    case 12288: return launch_d<12288>(a, scat, smask, table);
+    case 13824: return launch_d<13824>(a, scat, smask, table);
     default: break;
   }
   *handled = false;

@@ -58,8 +58,8 @@ def test_host_codebook_properties(q, bits):
 
 def test_codebook_rejects(q):
     L = q.lib()
-    buf = np.zeros(16, np.float32)
-    assert L.oq_codebook(256, 5, buf.ctypes.data, buf.ctypes.data) == q.OQ_EUNSUPPORTED
+    buf = np.zeros(512, np.float32)
+    assert L.oq_codebook(256, 9, buf.ctypes.data, buf.ctypes.data) == q.OQ_EUNSUPPORTED
     assert L.oq_codebook(256, 0, buf.ctypes.data, buf.ctypes.data) == q.OQ_EUNSUPPORTED
     assert L.oq_codebook(0, 4, buf.ctypes.data, buf.ctypes.data) == q.OQ_EINVAL
     assert L.oq_codebook(256, 4, None, buf.ctypes.data) == q.OQ_EINVAL
