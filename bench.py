@@ -188,6 +188,54 @@ def fake_quant_path(q, x, W, seed, ba, bw, iters=10):
             "ms": round(ms, 4)}
 
 
+def w8a8_path(q, x, W, seed, iters=10):
+    """The same step at 8 bits on both sides (W8A8, the top of the pages'
+    bit range): weight prep, rotate + quantize to byte codes, W8A8 linear;
+    per-kernel times from events on the launch stream."""
+    import torch
+    M, K = x.shape
+    N = W.shape[0]
+    wc = torch.empty((N, K), dtype=torch.uint8, device=x.device)
+    ac = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    wn = torch.empty((N,), dtype=torch.float32, device=x.device)
+    an = torch.empty((M,), dtype=torch.float32, device=x.device)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters)]
+
+    def run(e=None):
+        if e is not None:
+            e[0].record(stream)
+        q.prepare_weights(W, seed, 8, out=wc, norms=wn)
+        if e is not None:
+            e[1].record(stream)
+        q.rotate_quantize(x, seed, 8, out=ac, norms=an)
+        if e is not None:
+            e[2].record(stream)
+        q.linear(ac, an, 8, wc, wn, 8, K, out=y)
+        if e is not None:
+            e[3].record(stream)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    for i in range(iters):
+        run(ev[i])
+    torch.cuda.synchronize()
+    t_step = float(np.median([e[0].elapsed_time(e[3]) for e in ev]))
+    t_rot = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+    t_lin = float(np.median([e[2].elapsed_time(e[3]) for e in ev]))
+    in_b = x.element_size()
+    rot_gbs = M * (K * in_b + K + 4) / (t_rot * 1e-3) / 1e9
+    lin_tf = 2.0 * M * N * K / (t_lin * 1e-3) / 1e12
+    return {"what": "W8A8 step on the same inputs (medians over launches)",
+            "step_ms": round(t_step, 4),
+            "linear": {"ms": round(t_lin, 4), "TFLOP/s": round(lin_tf, 1),
+                       "frac_of_mfma_fp16_peak": round(lin_tf / MFMA_FP16_PEAK_TFLOPS, 4)},
+            "rotate_quantize": {"ms": round(t_rot, 4), "GB/s": round(rot_gbs, 1),
+                                "frac_of_hbm_peak": round(rot_gbs / HBM_PEAK_GBS, 4)}}
+
+
 def adaln_rtn4(q, name, iters=50):
     """The AdaLN modulation projection of the same model size with INT4
     weight-only RTN weights (oq_rtn4_linear), HBM-bound: weight nibbles +
@@ -492,6 +540,7 @@ def main():
     ref_gemm = None if a.no_ref_gemm else library_fp16_gemm(M, N, K)
     fq_path = None if a.no_ref_gemm else fake_quant_path(q, xs[0], Ws[0], lin.seed, ba, bw)
     adaln = None if a.no_ref_gemm else adaln_rtn4(q, "image" if K == 3072 else "video")
+    w8 = None if a.no_ref_gemm else w8a8_path(q, xs[0], Ws[0], lin.seed)
 
     flops = 2.0 * M * N * K
     in_b = 2 if lin.act.dtype == wl.BF16 else 4
@@ -551,6 +600,8 @@ def main():
             ref_gemm["ms"] / t_lin, 3))
     if adaln is not None:
         out["adaln_rtn4"] = adaln
+    if w8 is not None:
+        out["w8a8"] = w8
     if fq_path is not None:
         out["fake_quant_path"] = dict(fq_path, native_step_speedup=round(
             fq_path["ms"] / ms_step, 3))
