@@ -12,12 +12,17 @@
 // Design (one 512-thread workgroup per 256 x 256 output tile):
 //   * every thread owns one row of the tile (waves 0-3 the 256 activation
 //     rows, waves 4-7 the 256 weight rows) and, per 64-slot K step, turns
-//     the row's 64 codes into fp16 levels with v_perm_b32 byte tables (the
-//     fp16 low and high bytes of the 2^b levels; no memory lookups);
+//     the row's 64 codes into fp16 levels.  With 4-bit codes on both sides
+//     a 1 KB LDS table maps each code byte (two slots) straight to the fp16
+//     pair, four 32-bit LDS reads per 8 slots and about one VALU instruction
+//     per MFMA; other bit pairs use v_perm_b32 byte tables (the fp16 low and
+//     high bytes of the 2^b levels; no memory lookups);
 //   * decoded tiles live in LDS, double buffered, as 8 planes of 256 rows x
 //     16 bytes (one plane per 8-slot chunk): the decode stores and the MFMA
 //     fragment loads both touch consecutive 16-byte words, so neither has
-//     bank conflicts and every offset is an instruction immediate;
+//     bank conflicts and every offset is an instruction immediate (the
+//     per-lane bases are kept opaque to the compiler so it cannot fold them
+//     into one register per fragment);
 //   * each of the 8 waves multiplies a 128 x 64 block with
 //     v_mfma_f32_16x16x32_f16 (fp32 accumulation), weight fragment first so
 //     every lane ends up with 4 consecutive output columns;
@@ -25,16 +30,20 @@
 //     MFMAs of step t, loads fragments for chunk c+1, decodes slot chunk c of
 //     step t+1 and stores it.  Scheduling fences between chunks keep the
 //     decode spread between the MFMAs, so both waves of a SIMD always have
-//     VALU work to issue while the matrix core runs; codes are loaded two
+//     other work to issue while the matrix core runs; codes are loaded two
 //     steps ahead into alternating registers;
-//   * epilogue: scale by s_m r_n / K, round once to bf16 (nearest even),
-//     8-byte stores;
-//   * workgroup -> tile order: contiguous per XCD, grouped along M so tiles
-//     resident together share activation rows in L2.
+//   * epilogue: scale by s_m r_n / K (the tile's norms were loaded at tile
+//     start and pass through LDS), round once to bf16 with the hardware's
+//     round to nearest even, 8-byte stores;
+//   * persistent workgroups (one per CU); workgroup -> tile order is
+//     contiguous per XCD and grouped along M, so tiles resident together
+//     share activation rows in L2, and a tile's stores drain while the next
+//     tile starts.
 //
-// Throughput is bound by the matrix core and the decode's VALU issue
-// together (about 3.1 VALU instructions per MFMA at 4 bits); the plain fp16
-// library GEMM of the same shape is the practical ceiling for comparison.
+// Throughput: about 40% of the fp16 matrix-core peak in the steady state at
+// these shapes, near the plain fp16 library GEMM of the same shape (which
+// does no decoding); a partial last round of tiles and the K loop's
+// barriers take most of the rest.
 //
 // 8-bit codes (W8A8) take the same path except for the decode: 256 levels do
 // not fit byte-permute tables, so each workgroup first converts the fp32
@@ -44,6 +53,8 @@
 // 2 * code.  The decoded tiles follow the table.
 #include <hip/hip_runtime.h>
 
+#include <cstring>
+
 #include "oq_internal.h"
 
 namespace oq {
@@ -52,6 +63,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int KS = 64;      // K step (slots)
 constexpr int GROUP_M = 8;  // tile rows per group of the tile order
@@ -69,6 +81,8 @@ struct Tile {
   static constexpr int STAGEB = 2 * OPB;          // A + B per stage
   static constexpr int LDS = 2 * STAGEB;          // double buffered
   static constexpr int LUT8 = 512;                 // 8 bits: level table before the tiles
+  static constexpr int LUTP = 1024;                // 4+4 bits: pair table before the tiles
+  static constexpr int NRM = 2 * TT * 4;           // after the tiles: the tile's row norms
 
   static_assert(WM * WN * 64 == THREADS, "one wave per 64 rows");
   static_assert(IB % 4 == 0 && JB >= 1, "4 chunks per K half");
@@ -167,16 +181,27 @@ __device__ __forceinline__ u32x4 decode_q8(const uint32_t *w, const uint16_t *lu
                lut_pair(lut, w1, 8, 24)};
 }
 
-// The decode of one role: byte-permute tables (2-4 bits) or an LDS level
-// table (8 bits).
+// 4 bits on both sides: one code byte holds slots 2k and 2k+1, and a 1 KB
+// LDS table maps the byte straight to the fp16 pair [F(lo), F(hi)], so
+// slots 8q .. 8q+7 (word w[q]) come out in natural order with four 32-bit
+// reads and no byte permutes.
+__device__ __forceinline__ u32x4 decode_pair4(const uint32_t *w, const uint32_t *lut, int q) {
+  const uint32_t v = w[q];
+  return u32x4{lut[v & 0xFFu], lut[(v >> 8) & 0xFFu], lut[(v >> 16) & 0xFFu], lut[v >> 24]};
+}
+
+// The decode of one role: byte-permute tables (2-4 bits), an LDS pair table
+// (4 bits on both sides) or an LDS level table (8 bits).
 struct Decoder {
   PermTab t;
   const uint16_t *lut;
+  const uint32_t *lut32;
 };
 
-template <int BITS>
+template <int BITS, bool PAIR>
 __device__ __forceinline__ u32x4 decode_chunk(const uint32_t *w, const Decoder &dc, int q) {
   if constexpr (BITS == 8) return decode_q8(w, dc.lut, q);
+  else if constexpr (PAIR) return decode_pair4(w, dc.lut32, q);
   else return decode_q<BITS>(w, dc.t, q);
 }
 
@@ -208,7 +233,7 @@ __device__ __forceinline__ void load_codes(const uint8_t *p, uint32_t *w) {
 
 // The K loop of one tile for a thread whose row has BITS-bit codes at `prow`
 // (activation or weight row; the MFMA work is the same for both roles).
-template <class TL, int BITS>
+template <class TL, int BITS, bool PAIR>
 __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[TL::JB][TL::IB],
                                        const uint8_t *prow, const Decoder &tt, int opoff, int row,
                                        int lane, int wm, int wn, int T) {
@@ -224,7 +249,7 @@ __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[TL::JB][TL::
   load_codes<BITS>(prow, cb0);
 #pragma unroll
   for (int q = 0; q < 8; q++)
-    *(u32x4 *)(wbase + chunk_off<TL>(row, q)) = decode_chunk<BITS>(cb0, tt, q);
+    *(u32x4 *)(wbase + chunk_off<TL>(row, q)) = decode_chunk<BITS, PAIR>(cb0, tt, q);
   if (T > 1) load_codes<BITS>(prow + RB, REFILL ? cb0 : cb1);
 
   // fragment lanes: rows + (lane & 15), 8-slot chunk (lane >> 4) of each
@@ -288,7 +313,7 @@ __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[TL::JB][TL::
             acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf1[j], af1[i], acc[j][i], 0, 0, 0);
         }
       }
-      if (decode) *(u32x4 *)(dst + c * TL::PLANE) = decode_chunk<BITS>(cur, tt, c);
+      if (decode) *(u32x4 *)(dst + c * TL::PLANE) = decode_chunk<BITS, PAIR>(cur, tt, c);
       if constexpr (REFILL) {
         if (decode && (c & 1)) {  // words 2c-2 .. 2c+1 are free: step t+2's bytes 8c-8 ..
           const u32x4 v = *(const u32x4 *)(prow + (int64_t)n2 * RB + 8 * (c - 1));
@@ -334,47 +359,19 @@ __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
     PermTab tw, const float *__restrict__ lv8, int vec_store, int first, int count) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_base[];
   static_assert(BA != 8 || BW == 8, "8-bit codes on both sides");
-  uint8_t *lds = lds_base + (BA == 8 ? TL::LUT8 : 0);  // decoded tiles
+  constexpr bool PAIR = BA == 4 && BW == 4;
+  uint8_t *lds = lds_base + (BA == 8 ? TL::LUT8 : PAIR ? TL::LUTP : 0);  // decoded tiles
   constexpr int TT = TL::T, IB = TL::IB, JB = TL::JB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn_count = TT / (16 * JB);
   const int wm = wave / wn_count, wn = wave % wn_count;
 
-  // ---- workgroup -> tile
   const int nbm = (M + BIG - 1) / BIG, nbn = (N + BIG - 1) / BIG;
-  int m0, n0;
-  if constexpr (TT == BIG) {
-    int bid = blockIdx.x;
-    const int xcd = bid & 7, local = bid >> 3, per = count >> 3, rem = count & 7;
-    bid = xcd * per + (xcd < rem ? xcd : rem) + local;
-    int tm, tn;
-    big_tile_of(first + bid, nbm, nbn, tm, tn);
-    m0 = tm * BIG;
-    n0 = tn * BIG;
-  } else {
-    int tm, tn;
-    big_tile_of(first + (int)(blockIdx.x >> 2), nbm, nbn, tm, tn);
-    const int sub = blockIdx.x & 3;
-    m0 = tm * BIG + (sub >> 1) * TT;
-    n0 = tn * BIG + (sub & 1) * TT;
-  }
-
-  // ---- the row this thread decodes (rows past the edge repeat the last row)
   const bool is_a = __builtin_amdgcn_readfirstlane(tid) < TT;  // wave-uniform
   const int row = tid % TT;
-  const int am = (m0 + row < M) ? m0 + row : M - 1;
-  const int wr = (n0 + row < N) ? n0 + row : N - 1;
-  const uint8_t *pa = A + (int64_t)am * ((int64_t)K * BA / 8);
-  const uint8_t *pw = Wc + (int64_t)wr * ((int64_t)K * BW / 8);
   const int T = K / KS;
 
-  floatx4 acc[JB][IB];
-#pragma unroll
-  for (int j = 0; j < JB; j++)
-#pragma unroll
-    for (int i = 0; i < IB; i++) acc[j][i] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  Decoder da{ta, nullptr}, dw{tw, nullptr};
+  Decoder da{ta, nullptr, nullptr}, dw{tw, nullptr, nullptr};
   if constexpr (BA == 8) {
     // fp16 level table (round to nearest even, as on the host) into LDS
     uint16_t *lut = (uint16_t *)lds_base;
@@ -384,39 +381,95 @@ __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
     da.lut = lut;
     dw.lut = lut;
   }
-
-  if constexpr (BA == BW) {
-    k_loop<TL, BA>(lds, acc, is_a ? pa : pw, is_a ? da : dw, is_a ? 0 : TL::OPB, row, lane, wm,
-                   wn, T);
-  } else {
-    // both branches run the same barriers; the branch is wave-uniform
-    if (is_a) k_loop<TL, BA>(lds, acc, pa, da, 0, row, lane, wm, wn, T);
-    else k_loop<TL, BW>(lds, acc, pw, dw, TL::OPB, row, lane, wm, wn, T);
+  if constexpr (PAIR) {
+    // pair table from the byte-permute tables of the shared codebook
+    uint32_t *lut = (uint32_t *)lds_base;
+    for (int b = tid; b < 256; b += TL::THREADS) {
+      const int e0 = b & 15, e1 = b >> 4;
+      const uint32_t f0 = ((ta.lo[e0 >> 2] >> (8 * (e0 & 3))) & 0xFFu) |
+                          (((ta.hi[e0 >> 2] >> (8 * (e0 & 3))) & 0xFFu) << 8);
+      const uint32_t f1 = ((ta.lo[e1 >> 2] >> (8 * (e1 & 3))) & 0xFFu) |
+                          (((ta.hi[e1 >> 2] >> (8 * (e1 & 3))) & 0xFFu) << 8);
+      lut[b] = f0 | (f1 << 16);
+    }
+    __syncthreads();
+    da.lut32 = lut;
+    dw.lut32 = lut;
   }
 
-  // ---- epilogue: lane holds rows m = .. + (lane & 15), cols n = .. + 4 (lane >> 4) + r
-  const float invk = 1.0f / (float)K;
+  // ---- tiles: TL = BigTile is persistent (one workgroup per CU, each
+  // walking its XCD's contiguous run of tiles, so a tile's output stores
+  // drain while the next tile computes); TL = SmallTile takes one tile
+  const int nv = (TT == BIG) ? count : 4 * count;
+  for (int v = blockIdx.x; v < nv; v += gridDim.x) {
+    int m0, n0;
+    if constexpr (TT == BIG) {
+      const int xcd = v & 7, local = v >> 3, per = count >> 3, rem = count & 7;
+      int tm, tn;
+      big_tile_of(first + xcd * per + (xcd < rem ? xcd : rem) + local, nbm, nbn, tm, tn);
+      m0 = tm * BIG;
+      n0 = tn * BIG;
+    } else {
+      int tm, tn;
+      big_tile_of(first + (v >> 2), nbm, nbn, tm, tn);
+      const int sub = v & 3;
+      m0 = tm * BIG + (sub >> 1) * TT;
+      n0 = tn * BIG + (sub & 1) * TT;
+    }
+
+    // the row this thread decodes (rows past the edge repeat the last row)
+    const int am = (m0 + row < M) ? m0 + row : M - 1;
+    const int wr = (n0 + row < N) ? n0 + row : N - 1;
+    const uint8_t *pa = A + (int64_t)am * ((int64_t)K * BA / 8);
+    const uint8_t *pw = Wc + (int64_t)wr * ((int64_t)K * BW / 8);
+    // this row's norm, loaded now and used after the K loop (latency hidden)
+    const float nrm = is_a ? sa[am] : sw[wr];
+
+    floatx4 acc[JB][IB];
 #pragma unroll
-  for (int i = 0; i < IB; i++) {
-    const int m = m0 + wm * (16 * IB) + 16 * i + (lane & 15);
-    if (m >= M) continue;
-    const float s = sa[m] * invk;
-    uint16_t *yrow = Y + (int64_t)m * N;
+    for (int j = 0; j < JB; j++)
 #pragma unroll
-    for (int j = 0; j < JB; j++) {
-      const int n = n0 + wn * (16 * JB) + 16 * j + 4 * (lane >> 4);
-      if (vec_store && n + 3 < N) {
-        const floatx4 r = *(const floatx4 *)(sw + n);
-        const uint32_t lo = f32_to_bf16_rne(acc[j][i][0] * s * r[0]) |
-                            (f32_to_bf16_rne(acc[j][i][1] * s * r[1]) << 16);
-        const uint32_t hi = f32_to_bf16_rne(acc[j][i][2] * s * r[2]) |
-                            (f32_to_bf16_rne(acc[j][i][3] * s * r[3]) << 16);
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        *(u32x2 *)(yrow + n) = u32x2{lo, hi};
-      } else {
+      for (int i = 0; i < IB; i++) acc[j][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();  // the previous tile's last step may still read stage 0
+
+    if constexpr (BA == BW) {
+      k_loop<TL, BA, PAIR>(lds, acc, is_a ? pa : pw, is_a ? da : dw, is_a ? 0 : TL::OPB, row,
+                           lane, wm, wn, T);
+    } else {
+      // both branches run the same barriers; the branch is wave-uniform
+      if (is_a) k_loop<TL, BA, false>(lds, acc, pa, da, 0, row, lane, wm, wn, T);
+      else k_loop<TL, BW, false>(lds, acc, pw, dw, TL::OPB, row, lane, wm, wn, T);
+    }
+
+    // ---- epilogue: lane holds rows m = .. + (lane & 15), cols n = .. + 4 (lane >> 4) + r.
+    // The tile's norms go through LDS (activation rows, then weight rows);
+    // bf16 rounding is the hardware's round to nearest even.
+    float *nl = (float *)(lds + TL::LDS);
+    nl[is_a ? row : TT + row] = nrm;
+    __syncthreads();
+    const float invk = 1.0f / (float)K;
 #pragma unroll
-        for (int r = 0; r < 4; r++)
-          if (n + r < N) yrow[n + r] = (uint16_t)f32_to_bf16_rne(acc[j][i][r] * s * sw[n + r]);
+    for (int i = 0; i < IB; i++) {
+      const int mr = wm * (16 * IB) + 16 * i + (lane & 15), m = m0 + mr;
+      if (m >= M) continue;
+      const float s = nl[mr] * invk;
+      uint16_t *yrow = Y + (int64_t)m * N;
+#pragma unroll
+      for (int j = 0; j < JB; j++) {
+        const int nr = wn * (16 * JB) + 16 * j + 4 * (lane >> 4), n = n0 + nr;
+        const floatx4 r = *(const floatx4 *)(nl + TT + nr);
+        const bf16x2 p0 = {(__bf16)(acc[j][i][0] * s * r[0]), (__bf16)(acc[j][i][1] * s * r[1])};
+        const bf16x2 p1 = {(__bf16)(acc[j][i][2] * s * r[2]), (__bf16)(acc[j][i][3] * s * r[3])};
+        const uint32_t lo = __builtin_bit_cast(uint32_t, p0), hi = __builtin_bit_cast(uint32_t, p1);
+        if (vec_store && n + 3 < N) {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          *(u32x2 *)(yrow + n) = u32x2{lo, hi};
+        } else {
+          const uint32_t w4[4] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16};
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            if (n + e < N) yrow[n + e] = (uint16_t)w4[e];
+        }
       }
     }
   }
@@ -434,7 +487,8 @@ PermTab make_tab(const LevelsF16 &lv) {
 template <class TL, int BA, int BW>
 hipError_t launch_tiles(const LinearArgs &a, const PermTab &ta, const PermTab &tw,
                         const float *lv8, int vec, int first, int count, unsigned grid) {
-  constexpr int lds = TL::LDS + (BA == 8 ? TL::LUT8 : 0);
+  constexpr int lds = TL::LDS + TL::NRM +
+                      (BA == 8 ? TL::LUT8 : (BA == 4 && BW == 4) ? TL::LUTP : 0);
   static bool attr_set = false;  // per instantiation; the attribute is per function
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void *)linear_kernel<TL, BA, BW>,
@@ -469,8 +523,11 @@ hipError_t launch_ab(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &
   }
   const int64_t full = (4 * tiles <= cus) ? 0 : tiles;
   if (full > 0) {
+    // persistent: at most one workgroup per CU (a multiple of 8 keeps each
+    // workgroup on one XCD's run of tiles)
+    const int64_t grid = full < cus ? full : cus;
     hipError_t e =
-        launch_tiles<BigTile, BA, BW>(a, ta, tw, lv8, vec, 0, (int)full, (unsigned)full);
+        launch_tiles<BigTile, BA, BW>(a, ta, tw, lv8, vec, 0, (int)full, (unsigned)grid);
     if (e != hipSuccess) return e;
   }
   if (full < tiles)
@@ -489,6 +546,9 @@ hipError_t launch_linear(const LinearArgs &a, const LevelsF16 &la, const LevelsF
     if (!ta || ta != tw) return hipErrorInvalidValue;
     return launch_ab<8, 8>(a, la, lw, (const float *)(ta + table_levels_word(8)));
   }
+  // 4 bits on both sides: one pair table serves both operands
+  if (a.a_bits == 4 && a.w_bits == 4 && std::memcmp(la.v, lw.v, sizeof(la.v)) != 0)
+    return hipErrorInvalidValue;
 #define OQ_CASE(x, y) \
   if (a.a_bits == x && a.w_bits == y) return launch_ab<x, y>(a, la, lw, nullptr);
   OQ_CASE(2, 2) OQ_CASE(2, 3) OQ_CASE(2, 4)
