@@ -13,10 +13,12 @@
 //   * every thread owns one row of the tile (waves 0-3 the 256 activation
 //     rows, waves 4-7 the 256 weight rows) and, per 64-slot K step, turns
 //     the row's 64 codes into fp16 levels.  With 4-bit codes on both sides
-//     a 1 KB LDS table maps each code byte (two slots) straight to the fp16
+//     an LDS table maps each code byte (two slots) straight to the fp16
 //     pair, four 32-bit LDS reads per 8 slots and about one VALU instruction
-//     per MFMA; other bit pairs use v_perm_b32 byte tables (the fp16 low and
-//     high bytes of the 2^b levels; no memory lookups);
+//     per MFMA (16 lane-interleaved copies of the table keep the random
+//     lookups from piling onto a few banks); other bit pairs use v_perm_b32
+//     byte tables (the fp16 low and high bytes of the 2^b levels; no memory
+//     lookups);
 //   * decoded tiles live in LDS, double buffered, as 8 planes of 256 rows x
 //     16 bytes (one plane per 8-slot chunk): the decode stores and the MFMA
 //     fragment loads both touch consecutive 16-byte words, so neither has
@@ -47,10 +49,11 @@
 //
 // 8-bit codes (W8A8) take the same path except for the decode: 256 levels do
 // not fit byte-permute tables, so each workgroup first converts the fp32
-// unit levels to an fp16 table at the start of LDS (512 bytes; activation
-// and weight codes of one linear share K, bit width and codebook family, so
-// they share the table) and a code becomes one 16-bit LDS read at address
-// 2 * code.  The decoded tiles follow the table.
+// unit levels to an fp16 table at the start of LDS (16 interleaved copies,
+// as for the 4-bit pairs; activation and weight codes of one linear share
+// K, bit width and codebook family, so they share the table) and a code
+// becomes one LDS read; these reads run one chunk ahead of their stores.
+// The decoded tiles follow the table.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -80,8 +83,6 @@ struct Tile {
   static constexpr int OPB = 8 * PLANE;           // bytes per operand tile
   static constexpr int STAGEB = 2 * OPB;          // A + B per stage
   static constexpr int LDS = 2 * STAGEB;          // double buffered
-  static constexpr int LUT8 = 512;                 // 8 bits: level table before the tiles
-  static constexpr int LUTP = 1024;                // 4+4 bits: pair table before the tiles
   static constexpr int NRM = 2 * TT * 4;           // after the tiles: the tile's row norms
 
   static_assert(WM * WN * 64 == THREADS, "one wave per 64 rows");
@@ -163,45 +164,52 @@ __device__ __forceinline__ u32x4 decode_q(const uint32_t *w, const PermTab &t, i
   return u32x4{a0, a1, b0, b1};
 }
 
+// LDS code tables (4 bits on both sides, and 8 bits): 256 32-bit entries,
+// stored as 16 interleaved copies (entry e of copy c at word 16 e + c) and
+// read by lane l from copy l mod 16, so the random lookups of a wave spread
+// over the banks instead of piling onto a few.  `lut` below already points
+// at the lane's copy.
+constexpr int kLutCopies = 16;
+constexpr int kLutBytes = 256 * kLutCopies * 4;
+
+__device__ __forceinline__ uint32_t lut_at(const uint32_t *lut, uint32_t e) {
+  return lut[e * kLutCopies];
+}
+
 // 8 bits: slots 8q .. 8q+7 are bytes 0-3 of w[2q] and w[2q+1]; each code
-// is a 16-bit read from the fp16 level table lut (in LDS), and the levels
-// come out in the same slot order as above.
-__device__ __forceinline__ uint32_t lut_pair(const uint16_t *lut, uint32_t v, int sh0, int sh1) {
-  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-  const _Float16 *l = (const _Float16 *)lut;
-  half2v r;
-  r[0] = l[(v >> sh0) & 0xFFu];  // 16-bit reads straight into the two halves
-  r[1] = l[(v >> sh1) & 0xFFu];
-  return __builtin_bit_cast(uint32_t, r);
+// reads its fp16 level (low half of the entry), and the levels come out in
+// the same slot order as above.
+__device__ __forceinline__ uint32_t lut_pair8(const uint32_t *lut, uint32_t v, int sh0, int sh1) {
+  return perm(lut_at(lut, (v >> sh1) & 0xFFu), lut_at(lut, (v >> sh0) & 0xFFu), 0x05040100u);
 }
 
-__device__ __forceinline__ u32x4 decode_q8(const uint32_t *w, const uint16_t *lut, int q) {
+__device__ __forceinline__ u32x4 decode_q8(const uint32_t *w, const uint32_t *lut, int q) {
   const uint32_t w0 = w[2 * q], w1 = w[2 * q + 1];
-  return u32x4{lut_pair(lut, w0, 0, 16), lut_pair(lut, w1, 0, 16), lut_pair(lut, w0, 8, 24),
-               lut_pair(lut, w1, 8, 24)};
+  return u32x4{lut_pair8(lut, w0, 0, 16), lut_pair8(lut, w1, 0, 16), lut_pair8(lut, w0, 8, 24),
+               lut_pair8(lut, w1, 8, 24)};
 }
 
-// 4 bits on both sides: one code byte holds slots 2k and 2k+1, and a 1 KB
-// LDS table maps the byte straight to the fp16 pair [F(lo), F(hi)], so
-// slots 8q .. 8q+7 (word w[q]) come out in natural order with four 32-bit
-// reads and no byte permutes.
+// 4 bits on both sides: one code byte holds slots 2k and 2k+1, and the
+// table maps the byte straight to the fp16 pair [F(lo), F(hi)], so slots
+// 8q .. 8q+7 (word w[q]) come out in natural order with four 32-bit reads
+// and no byte permutes.
 __device__ __forceinline__ u32x4 decode_pair4(const uint32_t *w, const uint32_t *lut, int q) {
   const uint32_t v = w[q];
-  return u32x4{lut[v & 0xFFu], lut[(v >> 8) & 0xFFu], lut[(v >> 16) & 0xFFu], lut[v >> 24]};
+  return u32x4{lut_at(lut, v & 0xFFu), lut_at(lut, (v >> 8) & 0xFFu),
+               lut_at(lut, (v >> 16) & 0xFFu), lut_at(lut, v >> 24)};
 }
 
-// The decode of one role: byte-permute tables (2-4 bits), an LDS pair table
-// (4 bits on both sides) or an LDS level table (8 bits).
+// The decode of one role: byte-permute tables (2-4 bits) or an LDS table
+// (4 bits on both sides: pairs; 8 bits: levels).
 struct Decoder {
   PermTab t;
-  const uint16_t *lut;
-  const uint32_t *lut32;
+  const uint32_t *lut;
 };
 
 template <int BITS, bool PAIR>
 __device__ __forceinline__ u32x4 decode_chunk(const uint32_t *w, const Decoder &dc, int q) {
   if constexpr (BITS == 8) return decode_q8(w, dc.lut, q);
-  else if constexpr (PAIR) return decode_pair4(w, dc.lut32, q);
+  else if constexpr (PAIR) return decode_pair4(w, dc.lut, q);
   else return decode_q<BITS>(w, dc.t, q);
 }
 
@@ -244,6 +252,9 @@ __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[TL::JB][TL::
   // a pair of chunks has been decoded from it (registers are too tight for
   // two), still about three quarters of a step ahead of use
   constexpr bool REFILL = BITS == 8;
+  // 8 bits: the decode (eight table reads per chunk) runs one chunk ahead;
+  // at 4+4 bits (four reads) that measured no better than decoding in place
+  constexpr bool PIPE = BITS == 8;
   uint32_t cb0[2 * BITS], cb1[REFILL ? 1 : 2 * BITS];
   uint8_t *wbase = lds + opoff;
   load_codes<BITS>(prow, cb0);
@@ -276,6 +287,10 @@ __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[TL::JB][TL::
     const uint8_t *sA = stg + aoff, *sB = stg + boff;
     uint8_t *dst = lds + ((t + 1) & 1) * TL::STAGEB + woff;
     half8 af0[IB], bf0[JB], af1[IB], bf1[JB];
+    // pipelined decodes: chunk c's lookups are issued in chunk c-1, so
+    // eight MFMAs cover their latency before the store
+    u32x4 pend = {0u, 0u, 0u, 0u};
+    if (PIPE && decode) pend = decode_chunk<BITS, PAIR>(cur, tt, 0);
 #pragma unroll
     for (int j = 0; j < JB; j++) bf0[j] = *(const half8 *)(sB + 256 * j);
 #pragma unroll
@@ -313,7 +328,16 @@ __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[TL::JB][TL::
             acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf1[j], af1[i], acc[j][i], 0, 0, 0);
         }
       }
-      if (decode) *(u32x4 *)(dst + c * TL::PLANE) = decode_chunk<BITS, PAIR>(cur, tt, c);
+      if (decode) {
+        if constexpr (PIPE) {
+          u32x4 nxt = pend;
+          if (c < 7) nxt = decode_chunk<BITS, PAIR>(cur, tt, c + 1);
+          *(u32x4 *)(dst + c * TL::PLANE) = pend;
+          pend = nxt;
+        } else {
+          *(u32x4 *)(dst + c * TL::PLANE) = decode_chunk<BITS, PAIR>(cur, tt, c);
+        }
+      }
       if constexpr (REFILL) {
         if (decode && (c & 1)) {  // words 2c-2 .. 2c+1 are free: step t+2's bytes 8c-8 ..
           const u32x4 v = *(const u32x4 *)(prow + (int64_t)n2 * RB + 8 * (c - 1));
@@ -360,7 +384,7 @@ __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_base[];
   static_assert(BA != 8 || BW == 8, "8-bit codes on both sides");
   constexpr bool PAIR = BA == 4 && BW == 4;
-  uint8_t *lds = lds_base + (BA == 8 ? TL::LUT8 : PAIR ? TL::LUTP : 0);  // decoded tiles
+  uint8_t *lds = lds_base + ((BA == 8 || PAIR) ? kLutBytes : 0);  // decoded tiles
   constexpr int TT = TL::T, IB = TL::IB, JB = TL::JB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn_count = TT / (16 * JB);
@@ -371,30 +395,30 @@ __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
   const int row = tid % TT;
   const int T = K / KS;
 
-  Decoder da{ta, nullptr, nullptr}, dw{tw, nullptr, nullptr};
-  if constexpr (BA == 8) {
-    // fp16 level table (round to nearest even, as on the host) into LDS
-    uint16_t *lut = (uint16_t *)lds_base;
-    for (int i = tid; i < 256; i += TL::THREADS)
-      lut[i] = __builtin_bit_cast(uint16_t, (_Float16)lv8[i]);
-    __syncthreads();
-    da.lut = lut;
-    dw.lut = lut;
-  }
-  if constexpr (PAIR) {
-    // pair table from the byte-permute tables of the shared codebook
+  Decoder da{ta, nullptr}, dw{tw, nullptr};
+  if constexpr (BA == 8 || PAIR) {
+    // the shared table, 16 interleaved copies: 8 bits, the fp16 levels
+    // (round to nearest even, as on the host); 4+4 bits, the fp16 pairs of
+    // every code byte, from the byte-permute tables
     uint32_t *lut = (uint32_t *)lds_base;
-    for (int b = tid; b < 256; b += TL::THREADS) {
-      const int e0 = b & 15, e1 = b >> 4;
-      const uint32_t f0 = ((ta.lo[e0 >> 2] >> (8 * (e0 & 3))) & 0xFFu) |
-                          (((ta.hi[e0 >> 2] >> (8 * (e0 & 3))) & 0xFFu) << 8);
-      const uint32_t f1 = ((ta.lo[e1 >> 2] >> (8 * (e1 & 3))) & 0xFFu) |
-                          (((ta.hi[e1 >> 2] >> (8 * (e1 & 3))) & 0xFFu) << 8);
-      lut[b] = f0 | (f1 << 16);
+    for (int i = tid; i < 256 * kLutCopies; i += TL::THREADS) {
+      const int b = i / kLutCopies;
+      uint32_t e;
+      if constexpr (BA == 8) {
+        e = __builtin_bit_cast(uint16_t, (_Float16)lv8[b]);
+      } else {
+        const int e0 = b & 15, e1 = b >> 4;
+        const uint32_t f0 = ((ta.lo[e0 >> 2] >> (8 * (e0 & 3))) & 0xFFu) |
+                            (((ta.hi[e0 >> 2] >> (8 * (e0 & 3))) & 0xFFu) << 8);
+        const uint32_t f1 = ((ta.lo[e1 >> 2] >> (8 * (e1 & 3))) & 0xFFu) |
+                            (((ta.hi[e1 >> 2] >> (8 * (e1 & 3))) & 0xFFu) << 8);
+        e = f0 | (f1 << 16);
+      }
+      lut[i] = e;
     }
     __syncthreads();
-    da.lut32 = lut;
-    dw.lut32 = lut;
+    da.lut = lut + (lane & (kLutCopies - 1));
+    dw.lut = da.lut;
   }
 
   // ---- tiles: TL = BigTile is persistent (one workgroup per CU, each
@@ -487,8 +511,7 @@ PermTab make_tab(const LevelsF16 &lv) {
 template <class TL, int BA, int BW>
 hipError_t launch_tiles(const LinearArgs &a, const PermTab &ta, const PermTab &tw,
                         const float *lv8, int vec, int first, int count, unsigned grid) {
-  constexpr int lds = TL::LDS + TL::NRM +
-                      (BA == 8 ? TL::LUT8 : (BA == 4 && BW == 4) ? TL::LUTP : 0);
+  constexpr int lds = TL::LDS + TL::NRM + ((BA == 8 || (BA == 4 && BW == 4)) ? kLutBytes : 0);
   static bool attr_set = false;  // per instantiation; the attribute is per function
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void *)linear_kernel<TL, BA, BW>,
