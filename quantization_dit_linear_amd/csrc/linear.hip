@@ -36,7 +36,8 @@
 //     steps ahead into alternating registers;
 //   * epilogue: scale by s_m r_n / K (the tile's norms were loaded at tile
 //     start and pass through LDS), round once to bf16 with the hardware's
-//     round to nearest even, 8-byte stores;
+//     round to nearest even, stage the bf16 tile in LDS (XOR-swizzled rows)
+//     and store whole rows in 16-byte pieces;
 //   * persistent workgroups (one per CU); workgroup -> tile order is
 //     contiguous per XCD and grouped along M, so tiles resident together
 //     share activation rows in L2, and a tile's stores drain while the next
@@ -465,35 +466,50 @@ __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
       else k_loop<TL, BW, false>(lds, acc, pw, dw, TL::OPB, row, lane, wm, wn, T);
     }
 
-    // ---- epilogue: lane holds rows m = .. + (lane & 15), cols n = .. + 4 (lane >> 4) + r.
-    // The tile's norms go through LDS (activation rows, then weight rows);
-    // bf16 rounding is the hardware's round to nearest even.
+    // ---- epilogue.  The tile's norms go through LDS (activation rows, then
+    // weight rows); bf16 rounding is the hardware's round to nearest even.
+    // The bf16 tile is staged in the (now idle) decoded-tile buffers, row r
+    // at byte 2 TT r with its 8-byte column chunks XOR-swizzled by row so
+    // neither the fragment-shaped writes nor the row reads conflict, then
+    // leaves as whole 16-byte row pieces: full cache lines instead of 16
+    // rows x 32 bytes per store instruction.
     float *nl = (float *)(lds + TL::LDS);
     nl[is_a ? row : TT + row] = nrm;
-    __syncthreads();
+    __syncthreads();  // every wave is past its last MFMA read of the tiles
+    constexpr int CPR = TT / 4;  // 8-byte chunks per staged row
+    auto sw = [](int r) { return (4 * r) & (CPR - 4); };
     const float invk = 1.0f / (float)K;
 #pragma unroll
     for (int i = 0; i < IB; i++) {
-      const int mr = wm * (16 * IB) + 16 * i + (lane & 15), m = m0 + mr;
-      if (m >= M) continue;
+      const int mr = wm * (16 * IB) + 16 * i + (lane & 15);
       const float s = nl[mr] * invk;
-      uint16_t *yrow = Y + (int64_t)m * N;
 #pragma unroll
       for (int j = 0; j < JB; j++) {
-        const int nr = wn * (16 * JB) + 16 * j + 4 * (lane >> 4), n = n0 + nr;
+        const int nr = wn * (16 * JB) + 16 * j + 4 * (lane >> 4);
         const floatx4 r = *(const floatx4 *)(nl + TT + nr);
         const bf16x2 p0 = {(__bf16)(acc[j][i][0] * s * r[0]), (__bf16)(acc[j][i][1] * s * r[1])};
         const bf16x2 p1 = {(__bf16)(acc[j][i][2] * s * r[2]), (__bf16)(acc[j][i][3] * s * r[3])};
-        const uint32_t lo = __builtin_bit_cast(uint32_t, p0), hi = __builtin_bit_cast(uint32_t, p1);
-        if (vec_store && n + 3 < N) {
-          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-          *(u32x2 *)(yrow + n) = u32x2{lo, hi};
-        } else {
-          const uint32_t w4[4] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16};
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        *(u32x2 *)(lds + 2 * TT * mr + 8 * ((nr >> 2) ^ sw(mr))) =
+            u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+      }
+    }
+    __syncthreads();
+    // row pieces: thread -> (row, 16-byte piece k = columns 8k .. 8k+7)
+    constexpr int PPR = TT / 8, RPI = TL::THREADS / PPR;  // pieces per row, rows per pass
+    const int k = tid % PPR;
+#pragma unroll 4
+    for (int rr = tid / PPR; rr < TT; rr += RPI) {
+      const int m = m0 + rr, n = n0 + 8 * k;
+      if (m >= M || n >= N) continue;
+      const u32x4 v = *(const u32x4 *)(lds + 2 * TT * rr + 8 * ((2 * k) ^ sw(rr)));
+      uint16_t *yp = Y + (int64_t)m * N + n;
+      if (vec_store && n + 7 < N) {
+        *(u32x4 *)yp = v;
+      } else {
 #pragma unroll
-          for (int e = 0; e < 4; e++)
-            if (n + e < N) yrow[n + e] = (uint16_t)w4[e];
-        }
+        for (int e = 0; e < 8; e++)
+          if (n + e < N) yp[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
       }
     }
   }
@@ -534,7 +550,7 @@ template <int BA, int BW>
 hipError_t launch_ab(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw,
                      const float *lv8) {
   const PermTab ta = make_tab(la), tw = make_tab(lw);
-  const int vec = (a.N % 4 == 0) && (((uintptr_t)a.y & 7) == 0) && (((uintptr_t)a.w_norms & 15) == 0);
+  const int vec = (a.N % 8 == 0) && (((uintptr_t)a.y & 15) == 0);
   const int64_t tiles = ((a.M + BIG - 1) / BIG) * ((a.N + BIG - 1) / BIG);
   if (tiles > (int64_t)(INT32_MAX / 4)) return hipErrorInvalidValue;
   int cus = 256;
