@@ -101,8 +101,14 @@ struct Shape {
   static constexpr int LV_OFF = NP_OFF + ((TB * W * 4 + 15) / 16) * 16;  // 2^BITS unit levels
   static constexpr int YB_OFF = LV_OFF + (4 << BITS);
   static constexpr int LDS = YB_OFF + TB * D * 2;
+  // d = 5120 (five 5-wave workgroups' worth of tiles, 2 resident at 3
+  // waves per SIMD) runs lean instead: no prefetch registers, 4 waves per
+  // SIMD, 3 workgroups per CU -- measured 6% faster there and slower at
+  // every other size
+  static constexpr bool LEAN = D == 5120;
+  static constexpr int MIN_WAVES_PER_SIMD = LEAN ? 4 : 1;
   // register budget of the one-batch-ahead prefetch
-  static constexpr bool PREFETCH = (TB * CPT * 4) <= (W <= 8 ? 48 : 32);
+  static constexpr bool PREFETCH = !LEAN && (TB * CPT * 4) <= (W <= 8 ? 48 : 32);
   static_assert(S <= 1024 && S >= 128, "slot size");
   static_assert(XB <= 2 && (1 << XB) <= G, "at most 4 slots per block");
   static_assert(LDS <= 160 * 1024, "LDS");
@@ -119,7 +125,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // unused and smask holds the sign masks of the coordinates in place.
 // table: the device codebook table (cell grid, then levels).
 template <int D, int BITS, bool DQ, bool IDENT>
-__global__ __launch_bounds__((64 * Shape<D, BITS>::W)) void rq_fast_kernel(
+__global__ __launch_bounds__((64 * Shape<D, BITS>::W))
+__attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void rq_fast_kernel(
     const uint16_t *__restrict__ x, int64_t n_tok, const uint32_t *__restrict__ scat,
     const uint32_t *__restrict__ smask, const uint32_t *__restrict__ table,
     uint8_t *__restrict__ codes, uint16_t *__restrict__ dq, float *__restrict__ norms) {
