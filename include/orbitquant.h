@@ -29,7 +29,10 @@
  *     hipStream_t passed as void*; NULL = the null stream) and is
  *     asynchronous: results are valid once the stream has reached them.
  *   - The library owns only its rotation-plan tables (a few tens of KB per
- *     (device, d, seed)); they live until oq_release_plans() or unload.
+ *     (device, d, seed)) and codebook tables (decision grid, levels and
+ *     thresholds: about 1 KB per (device, bits, family), 11 KB at 8 bits,
+ *     per d for the sphere family); they live until oq_release_plans() or
+ *     unload.
  *   - The rotation seed and flags of a layer's weights and of its
  *     activations must be the same; the library cannot check this.
  *   - Code layout ("storage order"): inside each group of 128 consecutive
@@ -174,9 +177,10 @@ int oq_linear_ex(const uint8_t *a_codes, const float *a_norms, int a_bits,
                  const uint8_t *w_codes, const float *w_norms, int w_bits,
                  int64_t M, int64_t N, int K, uint32_t flags, uint16_t *y, void *stream);
 
-/* Free every cached rotation plan on every device (the caller must ensure
- * no enqueued work still uses them, e.g. by synchronising first).  Handles
- * from oq_plan_create stay valid to destroy but name no tables any more. */
+/* Free every cached rotation plan and codebook table on every device (the
+ * caller must ensure no enqueued work still uses them, e.g. by
+ * synchronising first).  Handles from oq_plan_create stay valid to destroy
+ * but name no tables any more. */
 int oq_release_plans(void);
 
 /* INT4 weight-only round-to-nearest for the AdaLN modulation projections
