@@ -84,22 +84,15 @@ struct Tile {
   static constexpr int OPB = 8 * PLANE;           // bytes per operand tile
   static constexpr int STAGEB = 2 * OPB;          // A + B per stage
   static constexpr int LDS = 2 * STAGEB;          // double buffered
-  static constexpr int NRM = 2 * TT * 4;           // after the tiles: the tile's row norms
-
+  static constexpr int NRM = 2 * TT * 4;          // after the tiles: the tile's row norms
   static_assert(WM * WN * 64 == THREADS, "one wave per 64 rows");
   static_assert(IB % 4 == 0 && JB >= 1, "4 chunks per K half");
 };
-using BigTile = Tile<256, 2, 4>;    // 128 x 64 per wave, 128 KB LDS
-using SmallTile = Tile<128, 2, 2>;  // 64 x 64 per wave, 64 KB LDS
+using BigTile = Tile<256, 2, 4>;    // 128 x 64 per wave, 128 KB of tiles in LDS
+using SmallTile = Tile<128, 2, 2>;  // 64 x 64 per wave, 64 KB of tiles in LDS
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
 }
 
 // Byte tables of one codebook for v_perm: lo[j] / hi[j] hold the low / high
