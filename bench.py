@@ -236,6 +236,43 @@ def w8a8_path(q, x, W, seed, iters=10):
                                 "frac_of_hbm_peak": round(rot_gbs / HBM_PEAK_GBS, 4)}}
 
 
+def measured_ceilings(q):
+    """The ceilings measured on this GPU beside the datasheet peaks: the
+    library's matrix-core probe (back-to-back independent fp16 MFMAs, no
+    memory traffic) and a 1 GiB device-to-device copy (HBM read + write)."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 2 * cus
+    sink = torch.empty((blocks * 512,), dtype=torch.float32, device="cuda")
+    q.diag_mfma_f16(blocks, 100, sink)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    iters = 4000
+    e0.record()
+    flop = q.diag_mfma_f16(blocks, iters, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    mfma_tf = flop / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * (1 << 30) / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    del src, dst, sink
+    return {"mfma_f16_probe_TFLOP/s": round(mfma_tf, 1),
+            "copy_1GiB_GB/s": round(copy_gbs, 1),
+            "what": "fp16 MFMA probe (orbitquant_diag.h, 2 workgroups per CU, 32 independent "
+                    "accumulators per wave) and a 1 GiB device copy counted as read + write"}
+
+
 def adaln_rtn4(q, name, iters=50):
     """The AdaLN modulation projection of the same model size with INT4
     weight-only RTN weights (oq_rtn4_linear), HBM-bound: weight nibbles +
@@ -540,6 +577,7 @@ def main():
     ref_gemm = None if a.no_ref_gemm else library_fp16_gemm(M, N, K)
     fq_path = None if a.no_ref_gemm else fake_quant_path(q, xs[0], Ws[0], lin.seed, ba, bw)
     adaln = None if a.no_ref_gemm else adaln_rtn4(q, "image" if K == 3072 else "video")
+    ceil = None if a.no_ref_gemm else measured_ceilings(q)
     w8 = None if a.no_ref_gemm else w8a8_path(q, xs[0], Ws[0], lin.seed)
 
     flops = 2.0 * M * N * K
@@ -600,6 +638,10 @@ def main():
             ref_gemm["ms"] / t_lin, 3))
     if adaln is not None:
         out["adaln_rtn4"] = adaln
+    if ceil is not None:
+        out["measured_ceilings"] = dict(
+            ceil, linear_frac_of_probe=round(lin_tflops / ceil["mfma_f16_probe_TFLOP/s"], 4),
+            rotate_frac_of_copy=round(rot_gbs / ceil["copy_1GiB_GB/s"], 4))
     if w8 is not None:
         out["w8a8"] = w8
     if fq_path is not None:

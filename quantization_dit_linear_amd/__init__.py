@@ -56,6 +56,7 @@ _SIGS = {
                                                _P, _P, _P]),
     "oq_rtn4_linear": (ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int64, _P, _P, ctypes.c_int64,
                                       ctypes.c_int, _P, _P]),
+    "oq_diag_mfma_f16": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _P, _P]),
 }
 
 _lib = None
@@ -304,3 +305,13 @@ class Plan:
 
     def __exit__(self, *exc):
         self.close()
+
+
+def diag_mfma_f16(blocks, iters, sink, stream=None):
+    """Enqueue the matrix-core probe (orbitquant_diag.h); returns its flop
+    count.  sink: float32 CUDA tensor of at least blocks * 512 elements."""
+    if sink.numel() < blocks * 512:
+        raise ValueError("sink too small")
+    _check(lib().oq_diag_mfma_f16(blocks, iters, _dev_ptr(sink, "sink"), _stream(stream)),
+           "oq_diag_mfma_f16")
+    return blocks * 8 * iters * 32 * 16384

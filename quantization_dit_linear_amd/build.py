@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liborbitquant.so")
 SOURCES = ["oq_host.cpp", "rotate_quantize.hip", "rotate_quantize_fast.hip", "linear.hip",
-           "adaln_rtn4.hip"]
+           "adaln_rtn4.hip", "diag.hip"]
 # per-source extra flags: the rotate kernel keeps its MFMA results in
 # ordinary VGPRs (no accumulation-register round trip per value)
 PER_SOURCE = {"rotate_quantize_fast.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}

@@ -22,14 +22,19 @@ def q():
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "orbitquant.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(oq_[a-z_0-9]+)\s*\(", src)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(oq_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol(q):
     names = _declared()
-    assert "oq_linear" in names and "oq_rotate_quantize" in names
+    assert "oq_linear" in names and "oq_rotate_quantize" in names and "oq_diag_mfma_f16" in names
     lib = ctypes.CDLL(q.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
