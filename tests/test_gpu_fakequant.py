@@ -42,7 +42,8 @@ def test_tiny_fp32(q, bits, signs):
 
 
 @pytest.mark.parametrize("cfg,name,bits", [("image_qkv", "qkv", 4), ("image_mlp", "down", 4),
-                                           ("video_block", "down", 3), ("stress", "proj", 2)])
+                                           ("video_block", "qkv", 4), ("video_block", "down", 3),
+                                           ("stress", "proj", 2)])
 def test_workload_rows(q, cfg, name, bits):
     lin = wl.get_linear(cfg, name)
     x = wl.activations(cfg, name, np.arange(0, 150))
