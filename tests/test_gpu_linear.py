@@ -155,3 +155,17 @@ def test_end_to_end_sampled(q, cfg, name):
     owc, own, _ = oracle.rotate_quantize(W, lin.weight.dtype, K, lin.seed, bw)
     ref = oracle.linear(oac, oan, ba, owc, own, bw, K)
     assert parity.rel_fro(y, ref) <= parity.LINEAR_FRO
+
+
+@pytest.mark.parametrize("ba,bw", [(4, 4), (2, 3), (8, 8)])
+def test_maximum_k(q, ba, bw):
+    """K = 16384, the largest dimension the path takes (256 K steps per
+    tile), on a ragged 300 x 270 output."""
+    M, N, K = 300, 270, 16384
+    ac, an = wl.random_codes(M, K, ba, 61)
+    wc, wn = wl.random_codes(N, K, bw, 62)
+    say("linear max K", M, N, K, ba, bw)
+    y = _run(q, ac, an, ba, wc, wn, bw, K)
+    ref = oracle.linear(ac, an, ba, wc, wn, bw, K)
+    assert parity.rel_fro(y, ref) <= parity.LINEAR_FRO
+    assert np.all(np.abs(y - ref) <= 1e-2 * np.abs(ref).max() + 1e-30)
