@@ -502,8 +502,8 @@ def main():
     if a.summarize_profiles:
         return summarize_profiles(a)
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): this build has no "
-              "multi-GPU path; see the sharding notes in DESIGN.md", flush=True)
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): the library has no "
+              "multi-GPU path; its kernels run one GPU's share of the work", flush=True)
         return 2
     import torch
     import quantization_dit_linear_amd as q
