@@ -205,13 +205,9 @@ hipError_t launch_rtn4_linear(const void *x, int dtype, int64_t M, const uint8_t
   if (mb < 1) return hipErrorInvalidValue;
   if (mb > kMaxMB) mb = kMaxMB;
   if (mb > M) mb = (int)M;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void *)rtn4_linear_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kXBytes);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_lds_limit((const void *)rtn4_linear_kernel, kXBytes, lds_set);
+  if (e != hipSuccess) return e;
   int dev = 0, cus = 0;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

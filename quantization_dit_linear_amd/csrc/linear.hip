@@ -521,13 +521,9 @@ template <class TL, int BA, int BW>
 hipError_t launch_tiles(const LinearArgs &a, const PermTab &ta, const PermTab &tw,
                         const float *lv8, int vec, int first, int count, unsigned grid) {
   constexpr int lds = TL::LDS + TL::NRM + ((BA == 8 || (BA == 4 && BW == 4)) ? kLutBytes : 0);
-  static bool attr_set = false;  // per instantiation; the attribute is per function
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)linear_kernel<TL, BA, BW>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};  // per instantiation and device
+  hipError_t e = ensure_lds_limit((const void *)linear_kernel<TL, BA, BW>, lds, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((linear_kernel<TL, BA, BW>), dim3(grid), dim3(TL::THREADS), lds, a.stream,
                      a.a_codes, a.a_norms, a.w_codes, a.w_norms, (int)a.M, (int)a.N, a.K, a.y, ta,
                      tw, lv8, vec, first, count);

@@ -4,7 +4,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace oq {
+
+// Raise a kernel's dynamic-LDS limit on the current device, once per device
+// (`done` holds one bit per device id; setting the attribute twice from two
+// threads is harmless).
+inline hipError_t ensure_lds_limit(const void *fn, int bytes, std::atomic<uint64_t> &done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  if (bit) done.fetch_or(bit, std::memory_order_release);
+  return hipSuccess;
+}
 
 constexpr int kMaxD = 16384;
 constexpr int kGroup = 128;  // coordinates per storage-order group

@@ -192,9 +192,11 @@ hipError_t launch_generic_bits(const RotateArgs &a, const int32_t *sc, int sign_
                                uint8_t *codes, float *zout, uint16_t *dq) {
   const size_t lds = sizeof(float) * (a.d + (BITS == 8 ? 512 : 0));
   if (lds > 32768) {
-    // tokens above 8192 fp32 need more than the default dynamic-LDS cap
-    hipError_t e = hipFuncSetAttribute((const void *)rq_generic_kernel<BITS>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    // tokens above 8192 fp32 need more than the default dynamic-LDS cap (set
+    // once per device at the largest token size the path takes)
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = ensure_lds_limit((const void *)rq_generic_kernel<BITS>,
+                                    (int)sizeof(float) * (kMaxD + 512), lds_set);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(rq_generic_kernel<BITS>, dim3(grid), dim3(kThreads), lds, a.stream, a.x,
