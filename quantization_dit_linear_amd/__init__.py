@@ -106,9 +106,24 @@ def _dev_ptr(t, name):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if t.device.index is not None and t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} lives on {t.device}, not on the current device "
+                         f"cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _expect(t, shape, dtype, name):
+    """The shape and dtype a buffer must have for the call (the library
+    trusts its sizes): checked before anything touches the device."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
 
 
 # ------------------------------------------------------------------- API --
@@ -150,6 +165,8 @@ def rotate_quantize(x, seed, bits, *, signs=True, permuted=False, sphere=False, 
         out = torch.empty((M, d * bits // 8), dtype=torch.uint8, device=x.device)
     if norms is None:
         norms = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _expect(out, (M, d * bits // 8), torch.uint8, "out")
+    _expect(norms, (M,), torch.float32, "norms")
     flags = ((0 if signs else OQ_ROT_NO_SIGNS) | (OQ_ROT_INPUT_PERMUTED if permuted else 0)
              | (OQ_CODEBOOK_SPHERE if sphere else 0))
     rc = lib().oq_rotate_quantize(_dev_ptr(x, "x"), _dtype_code(x), M, d, seed, flags, bits,
@@ -186,6 +203,8 @@ def fake_quantize(x, seed, bits, *, signs=True, sphere=False, out=None, norms=No
         out = torch.empty((M, d), dtype=torch.bfloat16, device=x.device)
     if norms is None:
         norms = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _expect(out, (M, d), torch.bfloat16, "out")
+    _expect(norms, (M,), torch.float32, "norms")
     flags = (OQ_OUT_BF16_DEQUANT | (0 if signs else OQ_ROT_NO_SIGNS)
              | (OQ_CODEBOOK_SPHERE if sphere else 0))
     rc = lib().oq_rotate_quantize(_dev_ptr(x, "x"), _dtype_code(x), M, d, seed, flags, bits,
@@ -206,6 +225,8 @@ def prepare_weights(W, seed, bits, *, signs=True, sphere=False, out=None, norms=
         out = torch.empty((N, K * bits // 8), dtype=torch.uint8, device=W.device)
     if norms is None:
         norms = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _expect(out, (N, K * bits // 8), torch.uint8, "out")
+    _expect(norms, (N,), torch.float32, "norms")
     flags = (0 if signs else OQ_ROT_NO_SIGNS) | (OQ_CODEBOOK_SPHERE if sphere else 0)
     rc = lib().oq_prepare_weights(_dev_ptr(W, "W"), _dtype_code(W), N, K, seed, flags, bits,
                                   _dev_ptr(out, "w_codes"), _dev_ptr(norms, "row_norms"),
@@ -219,10 +240,17 @@ def linear(a_codes, a_norms, a_bits, w_codes, w_norms, w_bits, K, *, sphere=Fals
     """bf16 y [M, N] = s_m r_n sum_k C_w[p_nk] C_a[q_mk] (sphere: the
     exact-sphere-marginal codebooks, oq_linear_ex)."""
     import torch
+    if a_codes.dim() != 2 or w_codes.dim() != 2:
+        raise ValueError("a_codes and w_codes must be [rows, K*bits/8]")
     M = a_codes.shape[0]
     N = w_codes.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a_codes.device)
+    _expect(a_codes, (M, K * a_bits // 8), torch.uint8, "a_codes")
+    _expect(w_codes, (N, K * w_bits // 8), torch.uint8, "w_codes")
+    _expect(a_norms, (M,), torch.float32, "a_norms")
+    _expect(w_norms, (N,), torch.float32, "w_norms")
+    _expect(out, (M, N), torch.bfloat16, "out")
     if sphere:
         rc = lib().oq_linear_ex(_dev_ptr(a_codes, "a_codes"), _dev_ptr(a_norms, "a_norms"),
                                 a_bits, _dev_ptr(w_codes, "w_codes"), _dev_ptr(w_norms, "w_norms"),
@@ -245,6 +273,8 @@ def rtn4_prepare_weights(W, *, out=None, scales=None, stream=None):
         out = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
     if scales is None:
         scales = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _expect(out, (N, K // 2), torch.uint8, "out")
+    _expect(scales, (N,), torch.float32, "scales")
     rc = lib().oq_rtn4_prepare_weights(_dev_ptr(W, "W"), _dtype_code(W), N, K,
                                        _dev_ptr(out, "q4"), _dev_ptr(scales, "scales"),
                                        _stream(stream))
@@ -259,6 +289,9 @@ def rtn4_linear(x, q4, scales, *, out=None, stream=None):
     N = q4.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _expect(q4, (N, K // 2), torch.uint8, "q4")
+    _expect(scales, (N,), torch.float32, "scales")
+    _expect(out, (M, N), torch.bfloat16, "out")
     rc = lib().oq_rtn4_linear(_dev_ptr(x, "x"), _dtype_code(x), M, _dev_ptr(q4, "q4"),
                               _dev_ptr(scales, "scales"), N, K, _dev_ptr(out, "y"),
                               _stream(stream))
@@ -272,6 +305,7 @@ def permute_rows(src, seed, *, out=None, stream=None):
     import torch
     if out is None:
         out = torch.empty_like(src)
+    _expect(out, tuple(src.shape), src.dtype, "out")
     rows = src.shape[0]
     row_bytes = src[0].numel() * src.element_size() if rows else 0
     rc = lib().oq_permute_rows(_dev_ptr(src, "src"), _dev_ptr(out, "dst"), rows, row_bytes,
