@@ -96,9 +96,9 @@ def test_oracle_codes_realistic_distribution(q):
     assert parity.rel_fro(y, ref) <= parity.LINEAR_FRO
 
 
-FULL = [("image_qkv", "qkv", 4, 4), ("image_mlp", "up", 4, 4), ("image_mlp", "down", 2, 4),
-        ("video_block", "qkv", 4, 4), ("video_block", "up", 3, 4),
-        ("video_block", "down", 4, 4), ("stress", "proj", 2, 3)]
+# every (config, linear, W bits, A bits) the workloads name, at full size
+FULL = [(cfg, lin.name, bw, ba) for cfg in wl.CONFIGS if cfg != "tiny"
+        for lin in wl.CONFIGS[cfg]["linears"] for bw, ba in lin.bit_pairs]
 
 
 @pytest.mark.parametrize("cfg,name,bw,ba", FULL)
