@@ -114,18 +114,18 @@ def test_weight_prep_rows(q, cfg, name, bits):
     parity.assert_norms_match(host(rn), rr, f"W {cfg}/{name}")
 
 
-FULL = [("image_qkv", "qkv"), ("image_mlp", "up"), ("image_mlp", "down"),
-        ("video_block", "qkv"), ("video_block", "up"), ("video_block", "down"),
-        ("stress", "proj")]
+# every activation (config, linear, A bits) the workloads name
+FULL = sorted({(cfg, lin.name, ba) for cfg in wl.CONFIGS if cfg != "tiny"
+               for lin in wl.CONFIGS[cfg]["linears"] for _, ba in lin.bit_pairs})
 
 
-@pytest.mark.parametrize("cfg,name", FULL)
-def test_full_size_sampled_rows(q, cfg, name):
+@pytest.mark.parametrize("cfg,name,bits", FULL)
+def test_full_size_sampled_rows(q, cfg, name, bits):
     """The whole activation matrix at its real size, in the launch the
     benchmark times; the oracle checks a seeded sample of rows."""
     import torch
     lin = wl.get_linear(cfg, name)
-    d, bits = lin.act.d, lin.bit_pairs[0][1]
+    d = lin.act.d
     x = wl.activations(cfg, name)
     say("full", cfg, name, x.shape)
     xd = to_device(x)
