@@ -158,3 +158,25 @@ def test_explicit_plan_handles(q):
     assert torch.equal(c1, c2) and torch.equal(c1, c3) and torch.equal(n1, n2)
     rc, rn, rz = oracle.rotate_quantize(x, wl.BF16, d, 1234, 4, want_z=True)
     parity.assert_codes_match(host(c1), rc, rz, d, 4, _thr(4), "plan handles")
+
+
+# every weight (config, linear, W bits) the workloads name
+FULL_W = sorted({(cfg, lin.name, bw) for cfg in wl.CONFIGS if cfg != "tiny"
+                 for lin in wl.CONFIGS[cfg]["linears"] for bw, _ in lin.bit_pairs})
+
+
+@pytest.mark.parametrize("cfg,name,bits", FULL_W)
+def test_weight_prep_full_size_sampled_rows(q, cfg, name, bits):
+    """The whole weight matrix prepared at once; a seeded sample of rows
+    checked against the oracle."""
+    import torch
+    lin = wl.get_linear(cfg, name)
+    K, N = lin.weight.K, lin.weight.N
+    W = wl.weights(cfg, name)
+    say("prepare_weights full", cfg, name, W.shape, bits)
+    codes, rn = q.prepare_weights(to_device(W), lin.seed, bits)
+    torch.cuda.synchronize()
+    rows = wl.sample_rows(N, 64, 4)
+    rc, rr, rz = oracle.rotate_quantize(W[rows], lin.weight.dtype, K, lin.seed, bits, want_z=True)
+    parity.assert_codes_match(host(codes)[rows], rc, rz, K, bits, _thr(bits), f"W {cfg}/{name}")
+    parity.assert_norms_match(host(rn)[rows], rr, f"W {cfg}/{name}")
