@@ -41,12 +41,17 @@
 //   * persistent workgroups (one per CU); workgroup -> tile order is
 //     contiguous per XCD and grouped along M, so tiles resident together
 //     share activation rows in L2, and a tile's stores drain while the next
-//     tile starts.
+//     tile starts;
+//   * a sparse last round (at most a quarter of the CUs' worth of tiles)
+//     would leave one CU per tile running a whole K loop alone; those tiles
+//     run first instead, as 128 x 128 sub-tiles cut into K ranges that fill
+//     every CU, with their fp32 partial sums parked in output rows that the
+//     full rounds overwrite afterwards, and a small kernel sums them.
 //
 // Throughput: about 40% of the fp16 matrix-core peak in the steady state at
 // these shapes, near the plain fp16 library GEMM of the same shape (which
-// does no decoding); a partial last round of tiles and the K loop's
-// barriers take most of the rest.
+// does no decoding); the K loop's LDS traffic and barriers take most of
+// the rest.
 //
 // 8-bit codes (W8A8) take the same path except for the decode: 256 levels do
 // not fit byte-permute tables, so each workgroup first converts the fp32
@@ -358,7 +363,7 @@ __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[TL::JB][TL::
 
 // Group-major tile order: index g -> 256 x 256 tile (tm, tn), GROUP_M tile
 // rows per group, column-major inside a group.
-__device__ __forceinline__ void big_tile_of(int g, int nbm, int nbn, int &tm, int &tn) {
+__host__ __device__ __forceinline__ void big_tile_of(int g, int nbm, int nbn, int &tm, int &tn) {
   const int gsz = GROUP_M * nbn, grp = g / gsz, first_m = grp * GROUP_M;
   const int gm = (nbm - first_m) < GROUP_M ? (nbm - first_m) : GROUP_M;
   tm = first_m + (g % gsz) % gm;
@@ -368,13 +373,18 @@ __device__ __forceinline__ void big_tile_of(int g, int nbm, int nbn, int &tm, in
 // One workgroup per output tile.  TL = BigTile: `count` tiles of the
 // group-major order from index `first` (block ids spread so each XCD takes a
 // contiguous run).  TL = SmallTile: each 256 x 256 tile from index `first`
-// on is split into four 128 x 128 tiles, one workgroup each.
+// on is split into four 128 x 128 tiles, one workgroup each; with
+// splits > 1 each of those is further cut into `splits` contiguous K ranges
+// (piece v: sub-tile v mod 4 count, range v div 4 count), and a piece
+// writes its raw fp32 accumulators, in fragment order, to part + 128^2 v
+// instead of the epilogue (tail_reduce_kernel finishes the tile).
 // lv8 (8 bits only): fp32 unit levels of the shared codebook.
 template <class TL, int BA, int BW>
 __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
     const uint8_t *__restrict__ A, const float *__restrict__ sa, const uint8_t *__restrict__ Wc,
     const float *__restrict__ sw, int M, int N, int K, uint16_t *__restrict__ Y, PermTab ta,
-    PermTab tw, const float *__restrict__ lv8, int vec_store, int first, int count) {
+    PermTab tw, const float *__restrict__ lv8, int vec_store, int first, int count, int splits,
+    float *__restrict__ part) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_base[];
   static_assert(BA != 8 || BW == 8, "8-bit codes on both sides");
   constexpr bool PAIR = BA == 4 && BW == 4;
@@ -418,9 +428,11 @@ __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
   // ---- tiles: TL = BigTile is persistent (one workgroup per CU, each
   // walking its XCD's contiguous run of tiles, so a tile's output stores
   // drain while the next tile computes); TL = SmallTile takes one tile
-  const int nv = (TT == BIG) ? count : 4 * count;
+  const int nv = (TT == BIG) ? count : 4 * count * splits;
   for (int v = blockIdx.x; v < nv; v += gridDim.x) {
     int m0, n0;
+    int kb = 0, ke = T;  // K steps of this piece
+    float *pdst = nullptr;
     if constexpr (TT == BIG) {
       const int xcd = v & 7, local = v >> 3, per = count >> 3, rem = count & 7;
       int tm, tn;
@@ -429,19 +441,25 @@ __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
       n0 = tn * BIG;
     } else {
       int tm, tn;
-      big_tile_of(first + (v >> 2), nbm, nbn, tm, tn);
-      const int sub = v & 3;
+      const int nsub = 4 * count, u = v % nsub, s = v / nsub;
+      big_tile_of(first + (u >> 2), nbm, nbn, tm, tn);
+      const int sub = u & 3;
       m0 = tm * BIG + (sub >> 1) * TT;
       n0 = tn * BIG + (sub & 1) * TT;
+      if (splits > 1) {
+        kb = s * T / splits;
+        ke = (s + 1) * T / splits;
+        pdst = part + (int64_t)v * (TT * TT);
+      }
     }
 
     // the row this thread decodes (rows past the edge repeat the last row)
     const int am = (m0 + row < M) ? m0 + row : M - 1;
     const int wr = (n0 + row < N) ? n0 + row : N - 1;
-    const uint8_t *pa = A + (int64_t)am * ((int64_t)K * BA / 8);
-    const uint8_t *pw = Wc + (int64_t)wr * ((int64_t)K * BW / 8);
+    const uint8_t *pa = A + (int64_t)am * ((int64_t)K * BA / 8) + kb * (8 * BA);
+    const uint8_t *pw = Wc + (int64_t)wr * ((int64_t)K * BW / 8) + kb * (8 * BW);
     // this row's norm, loaded now and used after the K loop (latency hidden)
-    const float nrm = is_a ? sa[am] : sw[wr];
+    const float nrm = pdst ? 0.f : (is_a ? sa[am] : sw[wr]);
 
     floatx4 acc[JB][IB];
 #pragma unroll
@@ -452,11 +470,22 @@ __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
 
     if constexpr (BA == BW) {
       k_loop<TL, BA, PAIR>(lds, acc, is_a ? pa : pw, is_a ? da : dw, is_a ? 0 : TL::OPB, row,
-                           lane, wm, wn, T);
+                           lane, wm, wn, ke - kb);
     } else {
       // both branches run the same barriers; the branch is wave-uniform
-      if (is_a) k_loop<TL, BA, false>(lds, acc, pa, da, 0, row, lane, wm, wn, T);
-      else k_loop<TL, BW, false>(lds, acc, pw, dw, TL::OPB, row, lane, wm, wn, T);
+      if (is_a) k_loop<TL, BA, false>(lds, acc, pa, da, 0, row, lane, wm, wn, ke - kb);
+      else k_loop<TL, BW, false>(lds, acc, pw, dw, TL::OPB, row, lane, wm, wn, ke - kb);
+    }
+
+    if (pdst) {
+      // K-range piece: raw accumulators, one 16-byte fragment per lane and
+      // (wave, j, i), consecutive lanes adjacent (fully coalesced)
+#pragma unroll
+      for (int j = 0; j < JB; j++)
+#pragma unroll
+        for (int i = 0; i < IB; i++)
+          *(floatx4 *)(pdst + 4 * (((wave * JB + j) * IB + i) * 64 + lane)) = acc[j][i];
+      continue;  // uniform across the workgroup
     }
 
     // ---- epilogue.  The tile's norms go through LDS (activation rows, then
@@ -508,6 +537,39 @@ __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
   }
 }
 
+// Finishes the tiles cut into K-range pieces: for every fragment of every
+// 128 x 128 sub-tile, the sum of its `splits` partial accumulators (in
+// range order), scaled and rounded exactly as the tile epilogue does, one
+// 8-byte store of 4 bf16 outputs.  Requires N % 8 == 0 and a 16-byte
+// aligned y (the launcher checks).
+__global__ __launch_bounds__(256) void tail_reduce_kernel(
+    const float *__restrict__ part, int splits, int count, int first, int M, int N, int K,
+    const float *__restrict__ sa, const float *__restrict__ sw, uint16_t *__restrict__ Y) {
+  using TL = SmallTile;
+  constexpr int IB = TL::IB, JB = TL::JB, FR = TL::THREADS * TL::IB * TL::JB;  // per sub-tile
+  const int nsub = 4 * count;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= (int64_t)nsub * FR) return;
+  const int u = (int)(g / FR), f = (int)(g % FR);
+  const int lane = f & 63, i = (f >> 6) % IB, j = (f >> 6) / IB % JB, wave = (f >> 6) / (IB * JB);
+  const int wn_count = TL::T / (16 * JB), wm = wave / wn_count, wn = wave % wn_count;
+  const int nbm = (M + BIG - 1) / BIG, nbn = (N + BIG - 1) / BIG;
+  int tm, tn;
+  big_tile_of(first + (u >> 2), nbm, nbn, tm, tn);
+  const int m = tm * BIG + ((u & 3) >> 1) * TL::T + wm * (16 * IB) + 16 * i + (lane & 15);
+  const int n = tn * BIG + (u & 1) * TL::T + wn * (16 * JB) + 16 * j + 4 * (lane >> 4);
+  if (m >= M || n >= N) return;
+  floatx4 acc = *(const floatx4 *)(part + 4 * (int64_t)g);
+  for (int s = 1; s < splits; s++) acc += *(const floatx4 *)(part + 4 * ((int64_t)s * nsub * FR + g));
+  const float sc = sa[m] * (1.0f / (float)K);
+  const floatx4 r = {sw[n], sw[n + 1], sw[n + 2], sw[n + 3]};
+  const bf16x2 p0 = {(__bf16)(acc[0] * sc * r[0]), (__bf16)(acc[1] * sc * r[1])};
+  const bf16x2 p1 = {(__bf16)(acc[2] * sc * r[2]), (__bf16)(acc[3] * sc * r[3])};
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  *(u32x2 *)(Y + (int64_t)m * N + n) =
+      u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+}
+
 PermTab make_tab(const LevelsF16 &lv) {
   PermTab t{};
   for (int e = 0; e < 16; e++) {
@@ -519,28 +581,36 @@ PermTab make_tab(const LevelsF16 &lv) {
 
 template <class TL, int BA, int BW>
 hipError_t launch_tiles(const LinearArgs &a, const PermTab &ta, const PermTab &tw,
-                        const float *lv8, int vec, int first, int count, unsigned grid) {
+                        const float *lv8, int vec, int first, int count, unsigned grid,
+                        int splits = 1, float *part = nullptr) {
   constexpr int lds = TL::LDS + TL::NRM + ((BA == 8 || (BA == 4 && BW == 4)) ? kLutBytes : 0);
   static std::atomic<uint64_t> lds_set{0};  // per instantiation and device
   hipError_t e = ensure_lds_limit((const void *)linear_kernel<TL, BA, BW>, lds, lds_set);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((linear_kernel<TL, BA, BW>), dim3(grid), dim3(TL::THREADS), lds, a.stream,
                      a.a_codes, a.a_norms, a.w_codes, a.w_norms, (int)a.M, (int)a.N, a.K, a.y, ta,
-                     tw, lv8, vec, first, count);
+                     tw, lv8, vec, first, count, splits, part);
   return hipGetLastError();
 }
 
 // Tiles of 256 x 256, one workgroup per CU at a time.  A problem too small
 // to fill a quarter of the CUs runs as 128 x 128 tiles instead (four times
-// the workgroups).  A sparse last round of a large problem stays as it is:
-// workgroups finish staggered, so it costs far less than a full round, and
-// 128 x 128 tiles (one wave per SIMD) take about half a round's time anyway.
+// the workgroups).  A large problem whose last round would leave at most a
+// quarter of the CUs busy (R leftover tiles, each alone on its CU for a
+// whole K loop) runs those R tiles first as 128 x 128 sub-tiles, each cut
+// into S = CUs / 4R K ranges so that every CU takes one piece; the pieces'
+// fp32 partial sums go to rows of y that belong to the full rounds (they
+// are overwritten later in stream order, so no extra memory is needed),
+// tail_reduce_kernel sums them into the R tiles, and then the full rounds
+// run as before.  Tails of more than a quarter of the CUs stay whole 256 x
+// 256 tiles.
 template <int BA, int BW>
 hipError_t launch_ab(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw,
                      const float *lv8) {
   const PermTab ta = make_tab(la), tw = make_tab(lw);
   const int vec = (a.N % 8 == 0) && (((uintptr_t)a.y & 15) == 0);
-  const int64_t tiles = ((a.M + BIG - 1) / BIG) * ((a.N + BIG - 1) / BIG);
+  const int nbm = (int)((a.M + BIG - 1) / BIG), nbn = (int)((a.N + BIG - 1) / BIG);
+  const int64_t tiles = (int64_t)nbm * nbn;
   if (tiles > (int64_t)(INT32_MAX / 4)) return hipErrorInvalidValue;
   int cus = 256;
   {
@@ -549,19 +619,45 @@ hipError_t launch_ab(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &
       (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (cus <= 0) cus = 256;
   }
-  const int64_t full = (4 * tiles <= cus) ? 0 : tiles;
-  if (full > 0) {
+  if (4 * tiles <= cus)
+    return launch_tiles<SmallTile, BA, BW>(a, ta, tw, lv8, vec, 0, (int)tiles,
+                                           (unsigned)(4 * tiles));
+  const int64_t rounds = tiles / cus, rem = tiles % cus;
+  if (rounds == 0 || rem == 0 || 4 * rem > cus)
     // persistent: at most one workgroup per CU (a multiple of 8 keeps each
     // workgroup on one XCD's run of tiles)
-    const int64_t grid = full < cus ? full : cus;
-    hipError_t e =
-        launch_tiles<BigTile, BA, BW>(a, ta, tw, lv8, vec, 0, (int)full, (unsigned)grid);
+    return launch_tiles<BigTile, BA, BW>(a, ta, tw, lv8, vec, 0, (int)tiles,
+                                         (unsigned)(tiles < cus ? tiles : cus));
+
+  const int first = (int)(rounds * cus), R = (int)rem, T = a.K / KS;
+  int S = cus / (4 * R);
+  if (S > T / 3) S = T / 3;  // at least three K steps per piece
+  if (S > 1 && !vec) S = 1;
+  if (S > 1) {
+    // scratch: y rows above the highest leftover tile row, all full-round tiles
+    int top = nbm;
+    for (int g = first; g < (int)tiles; g++) {
+      int tm, tn;
+      big_tile_of(g, nbm, nbn, tm, tn);
+      if (tm < top) top = tm;
+    }
+    const int64_t need = (int64_t)S * 4 * R * SmallTile::T * SmallTile::T * 4;
+    if (need > (int64_t)top * BIG * a.N * 2) S = 1;
+  }
+  if (S < 1) S = 1;
+  float *part = S > 1 ? (float *)a.y : nullptr;
+  hipError_t e = launch_tiles<SmallTile, BA, BW>(a, ta, tw, lv8, vec, first, R,
+                                                 (unsigned)(4 * R * S), S, part);
+  if (e != hipSuccess) return e;
+  if (S > 1) {
+    const int64_t work = (int64_t)4 * R * SmallTile::THREADS * SmallTile::IB * SmallTile::JB;
+    hipLaunchKernelGGL(tail_reduce_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0,
+                       a.stream, part, S, R, first, (int)a.M, (int)a.N, a.K, a.a_norms, a.w_norms,
+                       a.y);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (full < tiles)
-    return launch_tiles<SmallTile, BA, BW>(a, ta, tw, lv8, vec, (int)full,
-                                           (int)(tiles - full), (unsigned)(4 * (tiles - full)));
-  return hipSuccess;
+  return launch_tiles<BigTile, BA, BW>(a, ta, tw, lv8, vec, 0, first, (unsigned)cus);
 }
 
 }  // namespace
