@@ -315,6 +315,9 @@ def adaln_rtn4(q, name, iters=50):
             "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+LINEAR_KERNELS = ("linear_kernel", "tail_reduce_kernel")  # the kernels of one linear call
+
+
 def _short_kernel_name(name):
     n = name.replace("(anonymous namespace)::", "").replace("oq::", "")
     if "(" in n:
@@ -347,7 +350,10 @@ def summarize_profiles(a):
     for r in rows:
         lines.append((_short_kernel_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
                       float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
-    lin_name = next(n for n, *_ in lines if n.startswith("linear_kernel"))
+    # one linear call: the full-round kernel, plus (when a sparse last round
+    # of tiles is cut into K ranges) the pieces' kernel and their reduction
+    lin_parts = [n for n, *_ in lines if n.startswith(LINEAR_KERNELS)]
+    lin_name = " + ".join(lin_parts)
     rot_name = next(n for n, *_ in lines if n.startswith("rq_"))
     with open(os.path.join(ROOT, "profiles", f"{tag}_kernel_stats.txt"), "w") as f:
         f.write(f"Kernel timing on one MI355X (gfx950), workload {cfg}/{lin.name}: {M} tokens, "
@@ -357,16 +363,17 @@ def summarize_profiles(a):
                 f"{'pct':>6s}\n")
         for n, c, av, mn, mx, pc in lines:
             f.write(f"{n[:70]:70s} {c:6d} {av:9.1f} {mn:9.1f} {mx:9.1f} {pc:6.2f}\n")
-        f.write(f"\n{lin_name}: 2*{M}*{N}*{K} = {2.0 * M * N * K:.4g} flop per launch\n")
+        lin_sum = sum(av for n, c, av, *_ in lines if n in lin_parts)
+        f.write(f"\nlinear call = {lin_name}: {lin_sum:.1f} us per call; 2*{M}*{N}*{K} = "
+                f"{2.0 * M * N * K:.4g} flop per call\n")
         f.write(f"{rot_name}: rows*(d*{in_b} + d*b/8 + 4) algorithmic bytes per launch "
                 f"({M} activation rows at {ba} bits, {N} weight rows at {bw} bits)\n")
         if a.profile_bench_log:
             line = [l for l in open(a.profile_bench_log) if l.startswith("{")][-1]
             kb = json.loads(line)["kernels"]
-            lin_us = next(av for n, c, av, *_ in lines if n == lin_name)
             f.write(f"\nAgreement: in the traced run bench.py's own HIP events (on the stream "
                     f"the kernels run on) averaged {kb['linear']['ms'] * 1e3:.1f} us per linear "
-                    f"launch vs {lin_us:.1f} us in the trace; rotate+quantize "
+                    f"call vs {lin_sum:.1f} us of its kernels in the trace; rotate+quantize "
                     f"{kb['rotate_quantize']['ms'] * 1e3:.1f} us (events include the gaps "
                     f"between launches).\n")
 
@@ -391,13 +398,14 @@ def summarize_profiles(a):
     copy_kib = 1024 * 1024  # 1 GiB read and written by the calibration copy
     f_scale, w_scale = copy_kib / f_ref, copy_kib / w_ref
 
-    def kib(per, prefix, grid=None):
-        vals = [v for k, vs in per.items() if _short_kernel_name(k).startswith(prefix)
-                for (gsz, v) in vs]
-        return float(np.mean(vals))
+    def kib_per_call(per, prefixes):
+        # every kernel of a call runs once per call: the sum of their means
+        names = {_short_kernel_name(k) for k in per if _short_kernel_name(k).startswith(prefixes)}
+        return sum(float(np.mean([v for k, vs in per.items() if _short_kernel_name(k) == n
+                                  for (gsz, v) in vs])) for n in names)
 
-    lin_fetch = kib(fetch, "linear_kernel") * 1024 * f_scale
-    lin_write = kib(write, "linear_kernel") * 1024 * w_scale
+    lin_fetch = kib_per_call(fetch, LINEAR_KERNELS) * 1024 * f_scale
+    lin_write = kib_per_call(write, LINEAR_KERNELS) * 1024 * w_scale
     # activation launches only (the weight-preparation launches have N rows)
     rot_f = [v for k, vs in fetch.items() if _short_kernel_name(k).startswith("rq_")
              for (g, v) in vs]
@@ -439,12 +447,12 @@ def summarize_profiles(a):
                     f"{e['write_bytes'] / 1e6:.1f} MB (algorithmic writes "
                     f"{e['algorithmic_write_bytes'] / 1e6:.1f} MB)\n")
     if a.profile_counters:
-        write_counter_summary(a, tag, lin_name, rot_name, M, N, K, ba, bw, in_b)
+        write_counter_summary(a, tag, lin_parts, rot_name, M, N, K, ba, bw, in_b)
     print(json.dumps(table))
     return 0
 
 
-def write_counter_summary(a, tag, lin_name, rot_name, M, N, K, ba, bw, in_b):
+def write_counter_summary(a, tag, lin_parts, rot_name, M, N, K, ba, bw, in_b):
     """Per-kernel averages of SQ/GRBM counters from rocprofv3 --pmc runs,
     with the derived rates the kernels are tuned by."""
     import csv
@@ -454,7 +462,7 @@ def write_counter_summary(a, tag, lin_name, rot_name, M, N, K, ba, bw, in_b):
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 k = _short_kernel_name(r["Kernel_Name"])
-                if k not in (lin_name, rot_name):
+                if k not in lin_parts and k != rot_name:
                     continue
                 per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
                     float(r["Counter_Value"]))
@@ -462,7 +470,9 @@ def write_counter_summary(a, tag, lin_name, rot_name, M, N, K, ba, bw, in_b):
              f"({M} x {K} -> {N}).", "Commands (repository root on the GPU host):",
              a.profile_command, ""]
     n_mfma = 2.0 * M * N * K / 16384  # 16x16x32 f16 MFMAs of the linear
-    for k in (lin_name, rot_name):
+    mfma_call = sum(float(np.mean(per[k]["SQ_INSTS_MFMA"])) for k in lin_parts
+                    if "SQ_INSTS_MFMA" in per.get(k, {}))
+    for k in (*lin_parts, rot_name):
         c = {n: float(np.mean(v)) for n, v in per.get(k, {}).items()}
         if not c:
             continue
@@ -470,18 +480,18 @@ def write_counter_summary(a, tag, lin_name, rot_name, M, N, K, ba, bw, in_b):
         for n in sorted(c):
             lines.append(f"  {n:30s} {c[n]:.6g}")
         gui = c.get("GRBM_GUI_ACTIVE")
-        if k == lin_name:
+        if k in lin_parts and k.startswith("linear_kernel"):
             if "SQ_VALU_MFMA_BUSY_CYCLES" in c and gui:
                 lines.append(f"  MFMA busy per SIMD (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / "
                              f"(GRBM_GUI_ACTIVE / 8 XCDs)): "
                              f"{c['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / (gui / 8):.3f}")
             if "SQ_INSTS_MFMA" in c:
-                lines.append(f"  MFMA instructions: {c['SQ_INSTS_MFMA']:.4g} "
-                             f"(2MNK/16384 = {n_mfma:.4g})")
+                lines.append(f"  MFMA instructions: {c['SQ_INSTS_MFMA']:.4g}; all kernels of "
+                             f"the call: {mfma_call:.4g} (2MNK/16384 = {n_mfma:.4g})")
             if "SQ_INSTS_VALU" in c and "SQ_INSTS_MFMA" in c:
                 lines.append(f"  non-MFMA VALU instructions per MFMA: "
                              f"{(c['SQ_INSTS_VALU'] - c['SQ_INSTS_MFMA']) / c['SQ_INSTS_MFMA']:.2f}")
-        else:
+        elif k == rot_name:
             elems = (M + N) / 2.0 * K  # mean over activation and weight launches
             for n in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
                       "SQ_LDS_IDX_ACTIVE"):
