@@ -15,7 +15,7 @@
 //     the row's 64 codes into fp16 levels.  With 4-bit codes on both sides
 //     an LDS table maps each code byte (two slots) straight to the fp16
 //     pair, four 32-bit LDS reads per 8 slots and about one VALU instruction
-//     per MFMA (16 lane-interleaved copies of the table keep the random
+//     per MFMA (32 lane-interleaved copies of the table keep the random
 //     lookups from piling onto a few banks); other bit pairs use v_perm_b32
 //     byte tables (the fp16 low and high bytes of the 2^b levels; no memory
 //     lookups);
@@ -55,7 +55,7 @@
 //
 // 8-bit codes (W8A8) take the same path except for the decode: 256 levels do
 // not fit byte-permute tables, so each workgroup first converts the fp32
-// unit levels to an fp16 table at the start of LDS (16 interleaved copies,
+// unit levels to an fp16 table at the start of LDS (32 interleaved copies,
 // as for the 4-bit pairs; activation and weight codes of one linear share
 // K, bit width and codebook family, so they share the table) and a code
 // becomes one LDS read; these reads run one chunk ahead of their stores.
@@ -89,7 +89,6 @@ struct Tile {
   static constexpr int OPB = 8 * PLANE;           // bytes per operand tile
   static constexpr int STAGEB = 2 * OPB;          // A + B per stage
   static constexpr int LDS = 2 * STAGEB;          // double buffered
-  static constexpr int NRM = 2 * TT * 4;          // after the tiles: the tile's row norms
   static_assert(WM * WN * 64 == THREADS, "one wave per 64 rows");
   static_assert(IB % 4 == 0 && JB >= 1, "4 chunks per K half");
 };
@@ -164,11 +163,12 @@ __device__ __forceinline__ u32x4 decode_q(const uint32_t *w, const PermTab &t, i
 }
 
 // LDS code tables (4 bits on both sides, and 8 bits): 256 32-bit entries,
-// stored as 16 interleaved copies (entry e of copy c at word 16 e + c) and
-// read by lane l from copy l mod 16, so the random lookups of a wave spread
-// over the banks instead of piling onto a few.  `lut` below already points
-// at the lane's copy.
-constexpr int kLutCopies = 16;
+// stored as 32 interleaved copies (entry e of copy c at word 32 e + c) and
+// read by lane l from copy l mod 32, so the random lookups of a wave spread
+// over the banks instead of piling onto a few (measured 2-4% faster than 16
+// copies; 32 KB, which with the two 64 KB stages of 256 x 256 tiles fills
+// the CU's 160 KB exactly).  `lut` below already points at the lane's copy.
+constexpr int kLutCopies = 32;
 constexpr int kLutBytes = 256 * kLutCopies * 4;
 
 __device__ __forceinline__ uint32_t lut_at(const uint32_t *lut, uint32_t e) {
@@ -488,27 +488,36 @@ __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
       continue;  // uniform across the workgroup
     }
 
-    // ---- epilogue.  The tile's norms go through LDS (activation rows, then
-    // weight rows); bf16 rounding is the hardware's round to nearest even.
-    // The bf16 tile is staged in the (now idle) decoded-tile buffers, row r
-    // at byte 2 TT r with its 8-byte column chunks XOR-swizzled by row so
-    // neither the fragment-shaped writes nor the row reads conflict, then
+    // ---- epilogue.  The tile's norms go through LDS into registers
+    // (activation rows, then weight rows, in the pipeline stage the last K
+    // step left idle); bf16 rounding is the hardware's round to nearest
+    // even.  The bf16 tile is staged in the (now idle) decoded-tile buffers,
+    // row r at byte 2 TT r with its 8-byte column chunks XOR-swizzled by row
+    // so neither the fragment-shaped writes nor the row reads conflict, then
     // leaves as whole 16-byte row pieces: full cache lines instead of 16
     // rows x 32 bytes per store instruction.
-    float *nl = (float *)(lds + TL::LDS);
+    float *nl = (float *)(lds + ((ke - kb) & 1) * TL::STAGEB);
     nl[is_a ? row : TT + row] = nrm;
-    __syncthreads();  // every wave is past its last MFMA read of the tiles
+    __syncthreads();  // norms visible; every wave is past its last MFMA read of the tiles
+    const float invk = 1.0f / (float)K;
+    float sn[IB];
+    floatx4 rn[JB];
+#pragma unroll
+    for (int i = 0; i < IB; i++) sn[i] = nl[wm * (16 * IB) + 16 * i + (lane & 15)] * invk;
+#pragma unroll
+    for (int j = 0; j < JB; j++)
+      rn[j] = *(const floatx4 *)(nl + TT + wn * (16 * JB) + 16 * j + 4 * (lane >> 4));
+    __syncthreads();  // every norm read before the staged tile overwrites them
     constexpr int CPR = TT / 4;  // 8-byte chunks per staged row
     auto sw = [](int r) { return (4 * r) & (CPR - 4); };
-    const float invk = 1.0f / (float)K;
 #pragma unroll
     for (int i = 0; i < IB; i++) {
       const int mr = wm * (16 * IB) + 16 * i + (lane & 15);
-      const float s = nl[mr] * invk;
+      const float s = sn[i];
 #pragma unroll
       for (int j = 0; j < JB; j++) {
         const int nr = wn * (16 * JB) + 16 * j + 4 * (lane >> 4);
-        const floatx4 r = *(const floatx4 *)(nl + TT + nr);
+        const floatx4 r = rn[j];
         const bf16x2 p0 = {(__bf16)(acc[j][i][0] * s * r[0]), (__bf16)(acc[j][i][1] * s * r[1])};
         const bf16x2 p1 = {(__bf16)(acc[j][i][2] * s * r[2]), (__bf16)(acc[j][i][3] * s * r[3])};
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -583,7 +592,8 @@ template <class TL, int BA, int BW>
 hipError_t launch_tiles(const LinearArgs &a, const PermTab &ta, const PermTab &tw,
                         const float *lv8, int vec, int first, int count, unsigned grid,
                         int splits = 1, float *part = nullptr) {
-  constexpr int lds = TL::LDS + TL::NRM + ((BA == 8 || (BA == 4 && BW == 4)) ? kLutBytes : 0);
+  constexpr int lds = TL::LDS + ((BA == 8 || (BA == 4 && BW == 4)) ? kLutBytes : 0);
+  static_assert(lds <= 160 * 1024, "LDS of one CU");
   static std::atomic<uint64_t> lds_set{0};  // per instantiation and device
   hipError_t e = ensure_lds_limit((const void *)linear_kernel<TL, BA, BW>, lds, lds_set);
   if (e != hipSuccess) return e;
