@@ -108,6 +108,32 @@ def test_leftover_tiles_split(q, M, N, K, ba, bw):
     assert np.all(np.abs(y[rows] - ref) <= 1e-2 * np.abs(ref).max() + 1e-30)
 
 
+@pytest.mark.parametrize("offset", [8, 1])
+def test_leftover_tiles_output_bounds(q, offset):
+    """y inside a larger buffer with sentinels on both sides: offset 8 keeps
+    y 16-byte aligned (the K-split leftover path parks its partial sums in
+    y), offset 1 does not (the leftover sub-tiles run whole, scalar stores).
+    Nothing outside y may change, and the leftover band and the scratch rows
+    must match the oracle."""
+    import torch
+    M, N, K = 4352, 4096, 768
+    ac, an = wl.random_codes(M, K, 4, 71)
+    wc, wn = wl.random_codes(N, K, 4, 72)
+    say("linear leftover tiles, y offset", offset)
+    buf = torch.full((M * N + offset + 8,), -7.0, dtype=torch.bfloat16, device="cuda")
+    y = buf[offset:offset + M * N].view(M, N)
+    q.linear(to_device(ac), to_device(an), 4, to_device(wc), to_device(wn), 4, K, out=y)
+    torch.cuda.synchronize()
+    guard = torch.cat([buf[:offset], buf[offset + M * N:]]).float().cpu().numpy()
+    assert np.all(guard == -7.0)
+    yn = bf16_to_np(y)
+    rows = np.unique(np.concatenate([np.linspace(0, 2047, 24).astype(np.int64),
+                                     np.arange(4096, M, 2)]))
+    ref = oracle.linear(ac, an, 4, wc, wn, 4, K, rows=rows)
+    assert parity.rel_fro(yn[rows], ref) <= parity.LINEAR_FRO
+    assert np.all(np.abs(yn[rows] - ref) <= 1e-2 * np.abs(ref).max() + 1e-30)
+
+
 def test_oracle_codes_realistic_distribution(q):
     """Codes produced by the oracle's own quantizer on workload inputs (the
     Lloyd-Max cell frequencies, not uniform), fed to both sides."""
