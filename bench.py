@@ -96,37 +96,72 @@ def to_dev(x):
     return torch.from_numpy(x).cuda()
 
 
-def cpu_baseline(cfg, lin, bw, ba, rows_n):
-    """The fp64 oracle, as it stands, on a bounded sample: weight prep of all
-    N weight rows, rotate + quantize and the linear for `rows_n` of the M
-    token rows; the full step is extrapolated linearly in token rows."""
+def _oracle_stages(cfg, lin, bw, ba, w_rows, x_rows, lin_rows):
+    """Seconds of the oracle's three stages on seeded samples: weight prep
+    of w_rows weight rows, rotate + quantize of x_rows token rows, and the
+    linear of the first lin_rows of those token rows against all N rows."""
     import oracle
     import workloads as wl
     M, N, K = lin.act.M, lin.weight.N, lin.act.d
-    rows = wl.sample_rows(M, rows_n, 5)
+    rows = wl.sample_rows(M, x_rows, 5)
     x = wl.activations(cfg, lin.name, rows)
     W = wl.weights(cfg, lin.name)
+    Wp = W if w_rows >= N else W[:w_rows]
     t0 = time.perf_counter()
-    wc, wn, _ = oracle.rotate_quantize(W, lin.weight.dtype, K, lin.seed, bw)
+    wc, wn, _ = oracle.rotate_quantize(Wp, lin.weight.dtype, K, lin.seed, bw)
     t1 = time.perf_counter()
     ac, an, _ = oracle.rotate_quantize(x, lin.act.dtype, K, lin.seed, ba)
     t2 = time.perf_counter()
-    oracle.linear(ac, an, ba, wc, wn, bw, K)
+    if wc.shape[0] < N:  # the linear needs every weight row: tile the sample
+        reps = -(-N // wc.shape[0])
+        wc, wn = np.tile(wc, (reps, 1))[:N], np.tile(wn, reps)[:N]
+    oracle.linear(ac, an, ba, wc, wn, bw, K, rows=np.arange(min(lin_rows, len(rows))))
     t3 = time.perf_counter()
-    scale = M / len(rows)
-    t_step = (t1 - t0) + ((t2 - t1) + (t3 - t2)) * scale
-    flops = 2.0 * M * N * K
-    return {
-        "value": flops / t_step / 1e12,
+    return len(Wp), len(rows), min(lin_rows, len(rows)), t1 - t0, t2 - t1, t3 - t2
+
+
+def cpu_baseline(cfg, lin, bw, ba, rows_n):
+    """The fp64 oracle, as it stands, on a bounded sample: weight prep of all
+    N weight rows, rotate + quantize and the linear for `rows_n` of the M
+    token rows; the full step is extrapolated linearly in token rows.  Also
+    the per-stage rates (rotate + quantize GB/s over the same algorithmic
+    bytes as the GPU figure, linear GFLOP/s), and the same on one thread on
+    a smaller sample."""
+    import oracle
+    import workloads as wl
+    M, N, K = lin.act.M, lin.weight.N, lin.act.d
+    e_w = 2 if lin.weight.dtype == wl.BF16 else 4
+    e_a = 2 if lin.act.dtype == wl.BF16 else 4
+
+    def rates(nw, nx, nl, tw, tx, tl):
+        return {"prepare_weights_GB/s": round(nw * (K * e_w + K * bw / 8 + 4) / tw / 1e9, 3),
+                "rotate_quantize_GB/s": round(nx * (K * e_a + K * ba / 8 + 4) / tx / 1e9, 3),
+                "linear_GFLOP/s": round(2.0 * nl * N * K / tl / 1e9, 2)}
+
+    nw, nx, nl, tw, tx, tl = _oracle_stages(cfg, lin, bw, ba, N, rows_n, rows_n)
+    t_step = tw + (tx + tl) * (M / nx)
+    out = {
+        "value": 2.0 * M * N * K / t_step / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": (f"weight prep of all {N} weight rows + rotate-quantize and linear of "
-                   f"{len(rows)} of {M} token rows (seeded sample), fp64; full step "
+                   f"{nx} of {M} token rows (seeded sample), fp64; full step "
                    f"extrapolated linearly in token rows"),
-        "seconds_measured": round(t3 - t0, 3),
+        "seconds_measured": round(tw + tx + tl, 3),
         "step_seconds_extrapolated": round(t_step, 3),
+        "stages": rates(nw, nx, nl, tw, tx, tl),
     }
+    threads = oracle.num_threads()
+    try:
+        oracle.set_threads(1)
+        one = _oracle_stages(cfg, lin, bw, ba, min(N, 1024), min(M, 256), 16)
+    finally:
+        oracle.set_threads(threads)
+    out["one_thread"] = dict(rates(*one), sample=(
+        f"{one[0]} weight rows, {one[1]} token rows rotated, {one[2]} token rows through "
+        f"the linear"), seconds_measured=round(sum(one[3:]), 3))
+    return out
 
 
 def library_fp16_gemm(M, N, K, iters=10):

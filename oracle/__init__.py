@@ -84,6 +84,8 @@ def _load():
                                     ctypes.c_int, P]
     lib.oqo_num_threads.restype = ctypes.c_int
     lib.oqo_num_threads.argtypes = []
+    lib.oqo_set_threads.restype = None
+    lib.oqo_set_threads.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
 
@@ -293,3 +295,9 @@ def rtn4_linear(x, dtype, q, scales):
 def num_threads():
     """OpenMP threads the oracle's parallel loops use."""
     return _load().oqo_num_threads()
+
+
+def set_threads(n):
+    """Threads for the oracle's later parallel loops (n <= 0: all
+    processors); for timing only, results do not depend on it."""
+    _load().oqo_set_threads(int(n))

@@ -627,3 +627,7 @@ int oqo_linear(const uint8_t *a_codes, const double *a_norms, int ba,
 
 /* Threads an OpenMP region of this oracle uses (for reporting). */
 int oqo_num_threads(void) { return omp_get_max_threads(); }
+
+/* Threads for the following OpenMP regions (n <= 0: every processor).
+   Timing only; no result depends on it. */
+void oqo_set_threads(int n) { omp_set_num_threads(n > 0 ? n : omp_get_num_procs()); }

@@ -45,4 +45,5 @@ int oqo_rtn4_quantize(const void *W, int dtype, int64_t rows, int d, int8_t *q, 
 int oqo_rtn4_linear(const void *x, int dtype, int64_t M, const int8_t *q, const float *scales,
                     int64_t N, int K, double *y);
 int oqo_num_threads(void);
+void oqo_set_threads(int n);
 #endif
