@@ -64,6 +64,9 @@ def parse():
     p.add_argument("--profile-bench-log", default=None,
                    help="with --summarize-profiles: output of the traced bench.py run, whose "
                         "own per-kernel event timings are compared with the trace")
+    p.add_argument("--sweep", action="store_true",
+                   help="no step benchmark: time rotate+quantize and the linear of every "
+                        "workload instance and bit pair at full size, one JSON line each")
     return p.parse_args()
 
 
@@ -542,6 +545,77 @@ def write_counter_summary(a, tag, lin_parts, rot_name, M, N, K, ba, bw, in_b):
         f.write("\n".join(lines))
 
 
+def _median_ms(fn, n_sets, iters):
+    """Median of per-call HIP event times (current stream), cycling buffer
+    sets, after two untimed rounds."""
+    import torch
+    for i in range(2 * n_sets):
+        fn(i % n_sets)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record()
+        fn(i % n_sets)
+        e1.record()
+    torch.cuda.synchronize()
+    return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+
+def sweep(q, iters=20):
+    """Every workload instance at full size: rotate+quantize of its
+    activations (synthetic bf16 tokens; enough buffer sets to exceed twice
+    the 256 MB Infinity Cache) and the linear for each of its bit pairs on
+    the codes the library itself makes from synthetic tokens and weights
+    (so the codes follow the Lloyd-Max cell frequencies, as in use), against
+    the HBM and fp16 MFMA peaks."""
+    import torch
+    import workloads as wl
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    for cfg, c in wl.CONFIGS.items():
+        if cfg == "tiny":
+            continue
+        for lin in c["linears"]:
+            M, N, K = lin.act.M, lin.weight.N, lin.act.d
+            e_in = 2 if lin.act.dtype == wl.BF16 else 4
+            dt = torch.bfloat16 if e_in == 2 else torch.float32
+            sets = max(1, min(4, -(-(512 << 20) // (M * K * e_in))))
+            xs = [torch.randn((M, K), generator=g, device="cuda").to(dt) for _ in range(sets)]
+            W = (0.02 * torch.randn((N, K), generator=g, device="cuda")).to(dt)
+            rec = {"instance": f"{cfg}/{lin.name}", "M": M, "N": N, "K": K, "rotate_quantize": [],
+                   "linear": []}
+            acodes = {}
+            for ba in sorted({b for _, b in lin.bit_pairs}):
+                codes = [torch.empty((M, K * ba // 8), dtype=torch.uint8, device="cuda")
+                         for _ in range(sets)]
+                norms = [torch.empty((M,), dtype=torch.float32, device="cuda") for _ in range(sets)]
+                ms = _median_ms(lambda i: q.rotate_quantize(xs[i], lin.seed, ba, out=codes[i],
+                                                            norms=norms[i]), sets, iters)
+                gbs = M * (K * e_in + K * ba / 8 + 4) / (ms * 1e-3) / 1e9
+                rec["rotate_quantize"].append({"a_bits": ba, "us": round(ms * 1e3, 1),
+                                               "GB/s": round(gbs, 1),
+                                               "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+                acodes[ba] = (codes[0], norms[0])
+                del codes[1:], norms[1:]
+            del xs
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            for bw, ba in lin.bit_pairs:
+                wc, wn = q.prepare_weights(W, lin.seed, bw)
+                ac, an = acodes[ba]
+                ms = _median_ms(lambda i: q.linear(ac, an, ba, wc, wn, bw, K, out=y), 1, iters)
+                tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+                rec["linear"].append({"w_bits": bw, "a_bits": ba, "ms": round(ms, 4),
+                                      "TFLOP/s": round(tf, 1),
+                                      "frac_of_mfma_fp16_peak": round(tf / MFMA_FP16_PEAK_TFLOPS,
+                                                                      4)})
+                del wc, wn
+            del y, W, acodes
+            torch.cuda.empty_cache()
+            print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main():
     a = parse()
     if a.summarize_profiles:
@@ -550,6 +624,11 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): the library has no "
               "multi-GPU path; its kernels run one GPU's share of the work", flush=True)
         return 2
+    if a.sweep:
+        import torch
+        import quantization_dit_linear_amd as q
+        torch.cuda.set_device(0)
+        return sweep(q)
     import torch
     import quantization_dit_linear_amd as q
     import workloads as wl
