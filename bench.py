@@ -78,15 +78,15 @@ def src_digest(*names):
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kernel, digest):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
+def stored_traffic(tag, kernel, digest):
+    """HBM bytes per launch from the committed counter summary of workload
+    `tag`, if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    e = t.get(kernel)
+    e = t.get(tag, {}).get(kernel)
     if not e or e.get("source_digest") != digest:
         return None
     return e.get("bytes_per_launch")
@@ -469,9 +469,18 @@ def summarize_profiles(a):
                             "algorithmic_read_bytes": int(rot_alg_r),
                             "algorithmic_write_bytes": int(rot_alg_w),
                             "note": "mean over the activation and weight-preparation launches"},
-        "workload": tag, "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
-        json.dump(table, f, indent=1)
+        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
+    # one entry per workload, so summaries of several workloads coexist
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    allt = {}
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            allt = json.load(f)
+        if "workload" in allt:  # older single-workload layout
+            allt = {}
+    allt[tag] = table
+    with open(tpath, "w") as f:
+        json.dump(allt, f, indent=1)
     with open(os.path.join(ROOT, "profiles", f"{tag}_traffic.txt"), "w") as f:
         f.write(f"HBM-side traffic per launch from rocprofv3 counters, workload {cfg}/{lin.name} "
                 f"({M} x {K} -> {N}, W{bw}A{ba}).\nCommands (repository root on the GPU host):\n"
@@ -637,6 +646,7 @@ def main():
     lin = wl.CONFIGS[cfg]["linears"][0] if a.linear is None else wl.get_linear(cfg, a.linear)
     bw, ba = lin.bit_pairs[0] if a.bits is None else tuple(int(v) for v in a.bits.split(","))
     M, N, K = lin.act.M, lin.weight.N, lin.act.d
+    tag = f"{cfg}_w{bw}a{ba}"
     torch.cuda.set_device(0)
 
     x_np = wl.activations(cfg, lin.name)
@@ -751,11 +761,12 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(lin_tflops, 2),
                      "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(lin_tflops / MFMA_FP16_PEAK_TFLOPS, 4),
-                     "traffic": stored_traffic("linear", lin_digest)},
+                     "traffic": stored_traffic(tag, "linear", lin_digest)},
         "roofline_rotate_quantize": {"bound": "hbm", "achieved": round(rot_gbs, 1),
                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                      "frac": round(rot_gbs / HBM_PEAK_GBS, 4),
-                                     "traffic": stored_traffic("rotate_quantize", rot_digest)},
+                                     "traffic": stored_traffic(tag, "rotate_quantize",
+                                                               rot_digest)},
     }
     if ref_gemm is not None:
         out["reference_fp16_gemm"] = dict(ref_gemm, linear_over_reference=round(
