@@ -81,26 +81,29 @@ def test_tile_paths(q, M, N, K, ba, bw):
     assert np.all(np.abs(y[rows] - ref) <= 1e-2 * np.abs(ref).max() + 1e-30)
 
 
-@pytest.mark.parametrize("M,N,K,ba,bw", [
-    (4352, 4096, 768, 4, 4),    # 272 tiles: 16 leftover, 4 K ranges each
-    (4312, 4088, 768, 4, 4),    # the same tile grid, ragged bottom and right edges
-    (4352, 4096, 3072, 4, 4),   # 48 K steps in 4 ranges of 12
-    (4352, 4096, 768, 3, 2),    # mixed widths
-    (4352, 4096, 768, 8, 8),    # W8A8
-    (4352, 4352, 256, 4, 4),    # 289 tiles: 33 leftover, too short a K to cut
-    (4352, 4092, 768, 4, 4),    # N % 8 != 0: leftover tiles not cut
+@pytest.mark.parametrize("M,N,K,ba,bw,band0", [
+    (4352, 4096, 768, 4, 4, 4096),    # 272 tiles: 16 leftover, 4 K ranges each
+    (4312, 4088, 768, 4, 4, 4096),    # the same tile grid, ragged bottom and right edges
+    (4352, 4096, 3072, 4, 4, 4096),   # 48 K steps in 4 ranges of 12
+    (4352, 4096, 640, 4, 4, 4096),    # 10 K steps in 3 uneven ranges (3, 3, 4)
+    (3072, 5888, 768, 4, 4, 2048),    # 276 tiles: 20 leftover (rows 8-11), 3 ranges
+    (4352, 4096, 768, 3, 2, 4096),    # mixed widths
+    (4352, 4096, 768, 8, 8, 4096),    # W8A8
+    (4352, 4352, 256, 4, 4, 4096),    # 289 tiles: 33 leftover, too short a K to cut
+    (4352, 4092, 768, 4, 4, 4096),    # N % 8 != 0: leftover tiles not cut
 ])
-def test_leftover_tiles_split(q, M, N, K, ba, bw):
+def test_leftover_tiles_split(q, M, N, K, ba, bw, band0):
     """A partial last round of at most a quarter of the CUs runs as 128 x 128
     sub-tiles cut into K ranges, with the partial sums parked in y rows of
-    the full rounds.  Checks every row of the leftover band (tile row 16)
-    and the rows used as scratch, which the full rounds must overwrite."""
+    the full rounds.  Checks every row of the leftover band (from row
+    band0) and the rows used as scratch, which the full rounds must
+    overwrite."""
     ac, an = wl.random_codes(M, K, ba, M + 11)
     wc, wn = wl.random_codes(N, K, bw, N + 13)
     say("linear leftover tiles", M, N, K, ba, bw)
     y = _run(q, ac, an, ba, wc, wn, bw, K)
     scratch_rows = np.linspace(0, 2047, 40).astype(np.int64)
-    band = np.arange(4096, M) if K <= 768 else np.arange(4096, M, 3)
+    band = np.arange(band0, M) if K <= 768 else np.arange(band0, M, 3)
     rows = np.unique(np.concatenate([scratch_rows, band, wl.sample_rows(M, 8, 5)]))
     ref = oracle.linear(ac, an, ba, wc, wn, bw, K, rows=rows)
     assert np.all(np.isfinite(y[rows]))
