@@ -48,10 +48,11 @@
 //     every CU, with their fp32 partial sums parked in output rows that the
 //     full rounds overwrite afterwards, and a small kernel sums them.
 //
-// Throughput: about 40% of the fp16 matrix-core peak in the steady state at
-// these shapes, near the plain fp16 library GEMM of the same shape (which
-// does no decoding); the K loop's LDS traffic and barriers take most of
-// the rest.
+// Throughput: 40-50% of the fp16 matrix-core peak at these shapes (about
+// 42% at 9216 x 9216 x 3072, 48-50% with 32760 tokens), on par with the
+// plain fp16 library GEMM of the same shape (which does no decoding); the
+// K loop's LDS traffic (fragment loads, table lookups, decoded stores) and
+// barriers take most of the rest.
 //
 // 8-bit codes (W8A8) take the same path except for the decode: 256 levels do
 // not fit byte-permute tables, so each workgroup first converts the fp32
@@ -401,7 +402,7 @@ __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
 
   Decoder da{ta, nullptr}, dw{tw, nullptr};
   if constexpr (BA == 8 || PAIR) {
-    // the shared table, 16 interleaved copies: 8 bits, the fp16 levels
+    // the shared table, kLutCopies interleaved copies: 8 bits, the fp16 levels
     // (round to nearest even, as on the host); 4+4 bits, the fp16 pairs of
     // every code byte, from the byte-permute tables
     uint32_t *lut = (uint32_t *)lds_base;
