@@ -71,10 +71,17 @@ def parse():
 
 
 def src_digest(*names):
+    """Digest of kernel sources with comments and blank lines dropped, so
+    stored counter data stays valid across comment-only edits and goes
+    stale on any code change."""
+    import re
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "quantization_dit_linear_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "quantization_dit_linear_amd", "csrc", n)) as f:
+            txt = f.read()
+        txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+        txt = re.sub(r"//[^\n]*", "", txt)
+        h.update("\n".join(l.rstrip() for l in txt.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 
