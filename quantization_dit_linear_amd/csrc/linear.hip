@@ -80,9 +80,11 @@ constexpr int GROUP_M = 8;  // tile rows per group of the tile order
 constexpr int BIG = 256;    // main tile edge
 
 // Tile shape: TT x TT output tile, WM x WN waves, one decoded row per thread.
-template <int TT, int WM, int WN>
+template <int TT, int WM, int WN, int LUTC_, int WGS_>
 struct Tile {
   static constexpr int T = TT;
+  static constexpr int LUTC = LUTC_;              // interleaved copies of an LDS code table
+  static constexpr int WGS = WGS_;                // workgroups meant to share a CU
   static constexpr int THREADS = 2 * TT;          // TT activation + TT weight rows
   static constexpr int IB = TT / WM / 16;         // 16-row activation blocks per wave
   static constexpr int JB = TT / WN / 16;         // 16-row weight blocks per wave
@@ -93,8 +95,11 @@ struct Tile {
   static_assert(WM * WN * 64 == THREADS, "one wave per 64 rows");
   static_assert(IB % 4 == 0 && JB >= 1, "4 chunks per K half");
 };
-using BigTile = Tile<256, 2, 4>;    // 128 x 64 per wave, 128 KB of tiles in LDS
-using SmallTile = Tile<128, 2, 2>;  // 64 x 64 per wave, 64 KB of tiles in LDS
+// 256 x 256: 128 x 64 per wave, 128 KB of tiles + a 32 KB table fill the
+// CU.  128 x 128: 64 x 64 per wave (one wave per SIMD per workgroup), 64 KB
+// of tiles + a 16 KB table, so two workgroups share a CU.
+using BigTile = Tile<256, 2, 4, 32, 1>;
+using SmallTile = Tile<128, 2, 2, 16, 2>;
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
@@ -164,39 +169,41 @@ __device__ __forceinline__ u32x4 decode_q(const uint32_t *w, const PermTab &t, i
 }
 
 // LDS code tables (4 bits on both sides, and 8 bits): 256 32-bit entries,
-// stored as 32 interleaved copies (entry e of copy c at word 32 e + c) and
-// read by lane l from copy l mod 32, so the random lookups of a wave spread
-// over the banks instead of piling onto a few (measured 2-4% faster than 16
-// copies; 32 KB, which with the two 64 KB stages of 256 x 256 tiles fills
-// the CU's 160 KB exactly).  `lut` below already points at the lane's copy.
-constexpr int kLutCopies = 32;
-constexpr int kLutBytes = 256 * kLutCopies * 4;
-
+// stored as C interleaved copies (entry e of copy c at word C e + c) and
+// read by lane l from copy l mod C, so the random lookups of a wave spread
+// over the banks instead of piling onto a few (C = 32 for 256 x 256 tiles:
+// 2-4% faster than 16, and 32 KB with the two 64 KB tile stages fills the
+// CU's 160 KB exactly).  `lut` below already points at the lane's copy.
+template <int C>
 __device__ __forceinline__ uint32_t lut_at(const uint32_t *lut, uint32_t e) {
-  return lut[e * kLutCopies];
+  return lut[e * C];
 }
 
 // 8 bits: slots 8q .. 8q+7 are bytes 0-3 of w[2q] and w[2q+1]; each code
 // reads its fp16 level (low half of the entry), and the levels come out in
 // the same slot order as above.
+template <int C>
 __device__ __forceinline__ uint32_t lut_pair8(const uint32_t *lut, uint32_t v, int sh0, int sh1) {
-  return perm(lut_at(lut, (v >> sh1) & 0xFFu), lut_at(lut, (v >> sh0) & 0xFFu), 0x05040100u);
+  return perm(lut_at<C>(lut, (v >> sh1) & 0xFFu), lut_at<C>(lut, (v >> sh0) & 0xFFu),
+              0x05040100u);
 }
 
+template <int C>
 __device__ __forceinline__ u32x4 decode_q8(const uint32_t *w, const uint32_t *lut, int q) {
   const uint32_t w0 = w[2 * q], w1 = w[2 * q + 1];
-  return u32x4{lut_pair8(lut, w0, 0, 16), lut_pair8(lut, w1, 0, 16), lut_pair8(lut, w0, 8, 24),
-               lut_pair8(lut, w1, 8, 24)};
+  return u32x4{lut_pair8<C>(lut, w0, 0, 16), lut_pair8<C>(lut, w1, 0, 16),
+               lut_pair8<C>(lut, w0, 8, 24), lut_pair8<C>(lut, w1, 8, 24)};
 }
 
 // 4 bits on both sides: one code byte holds slots 2k and 2k+1, and the
 // table maps the byte straight to the fp16 pair [F(lo), F(hi)], so slots
 // 8q .. 8q+7 (word w[q]) come out in natural order with four 32-bit reads
 // and no byte permutes.
+template <int C>
 __device__ __forceinline__ u32x4 decode_pair4(const uint32_t *w, const uint32_t *lut, int q) {
   const uint32_t v = w[q];
-  return u32x4{lut_at(lut, v & 0xFFu), lut_at(lut, (v >> 8) & 0xFFu),
-               lut_at(lut, (v >> 16) & 0xFFu), lut_at(lut, v >> 24)};
+  return u32x4{lut_at<C>(lut, v & 0xFFu), lut_at<C>(lut, (v >> 8) & 0xFFu),
+               lut_at<C>(lut, (v >> 16) & 0xFFu), lut_at<C>(lut, v >> 24)};
 }
 
 // The decode of one role: byte-permute tables (2-4 bits) or an LDS table
@@ -206,10 +213,10 @@ struct Decoder {
   const uint32_t *lut;
 };
 
-template <int BITS, bool PAIR>
+template <int BITS, bool PAIR, int C>
 __device__ __forceinline__ u32x4 decode_chunk(const uint32_t *w, const Decoder &dc, int q) {
-  if constexpr (BITS == 8) return decode_q8(w, dc.lut, q);
-  else if constexpr (PAIR) return decode_pair4(w, dc.lut, q);
+  if constexpr (BITS == 8) return decode_q8<C>(w, dc.lut, q);
+  else if constexpr (PAIR) return decode_pair4<C>(w, dc.lut, q);
   else return decode_q<BITS>(w, dc.t, q);
 }
 
@@ -260,7 +267,7 @@ __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[TL::JB][TL::
   load_codes<BITS>(prow, cb0);
 #pragma unroll
   for (int q = 0; q < 8; q++)
-    *(u32x4 *)(wbase + chunk_off<TL>(row, q)) = decode_chunk<BITS, PAIR>(cb0, tt, q);
+    *(u32x4 *)(wbase + chunk_off<TL>(row, q)) = decode_chunk<BITS, PAIR, TL::LUTC>(cb0, tt, q);
   if (T > 1) load_codes<BITS>(prow + RB, REFILL ? cb0 : cb1);
 
   // fragment lanes: rows + (lane & 15), 8-slot chunk (lane >> 4) of each
@@ -290,7 +297,7 @@ __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[TL::JB][TL::
     // pipelined decodes: chunk c's lookups are issued in chunk c-1, so
     // eight MFMAs cover their latency before the store
     u32x4 pend = {0u, 0u, 0u, 0u};
-    if (PIPE && decode) pend = decode_chunk<BITS, PAIR>(cur, tt, 0);
+    if (PIPE && decode) pend = decode_chunk<BITS, PAIR, TL::LUTC>(cur, tt, 0);
 #pragma unroll
     for (int j = 0; j < JB; j++) bf0[j] = *(const half8 *)(sB + 256 * j);
 #pragma unroll
@@ -331,11 +338,11 @@ __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[TL::JB][TL::
       if (decode) {
         if constexpr (PIPE) {
           u32x4 nxt = pend;
-          if (c < 7) nxt = decode_chunk<BITS, PAIR>(cur, tt, c + 1);
+          if (c < 7) nxt = decode_chunk<BITS, PAIR, TL::LUTC>(cur, tt, c + 1);
           *(u32x4 *)(dst + c * TL::PLANE) = pend;
           pend = nxt;
         } else {
-          *(u32x4 *)(dst + c * TL::PLANE) = decode_chunk<BITS, PAIR>(cur, tt, c);
+          *(u32x4 *)(dst + c * TL::PLANE) = decode_chunk<BITS, PAIR, TL::LUTC>(cur, tt, c);
         }
       }
       if constexpr (REFILL) {
@@ -381,7 +388,7 @@ __host__ __device__ __forceinline__ void big_tile_of(int g, int nbm, int nbn, in
 // instead of the epilogue (tail_reduce_kernel finishes the tile).
 // lv8 (8 bits only): fp32 unit levels of the shared codebook.
 template <class TL, int BA, int BW>
-__global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
+__global__ __launch_bounds__(TL::THREADS, TL::WGS) void linear_kernel(
     const uint8_t *__restrict__ A, const float *__restrict__ sa, const uint8_t *__restrict__ Wc,
     const float *__restrict__ sw, int M, int N, int K, uint16_t *__restrict__ Y, PermTab ta,
     PermTab tw, const float *__restrict__ lv8, int vec_store, int first, int count, int splits,
@@ -389,7 +396,8 @@ __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_base[];
   static_assert(BA != 8 || BW == 8, "8-bit codes on both sides");
   constexpr bool PAIR = BA == 4 && BW == 4;
-  uint8_t *lds = lds_base + ((BA == 8 || PAIR) ? kLutBytes : 0);  // decoded tiles
+  constexpr int LUTB = 256 * TL::LUTC * 4;                       // table bytes
+  uint8_t *lds = lds_base + ((BA == 8 || PAIR) ? LUTB : 0);  // decoded tiles
   constexpr int TT = TL::T, IB = TL::IB, JB = TL::JB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn_count = TT / (16 * JB);
@@ -402,12 +410,12 @@ __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
 
   Decoder da{ta, nullptr}, dw{tw, nullptr};
   if constexpr (BA == 8 || PAIR) {
-    // the shared table, kLutCopies interleaved copies: 8 bits, the fp16 levels
+    // the shared table, TL::LUTC interleaved copies: 8 bits, the fp16 levels
     // (round to nearest even, as on the host); 4+4 bits, the fp16 pairs of
     // every code byte, from the byte-permute tables
     uint32_t *lut = (uint32_t *)lds_base;
-    for (int i = tid; i < 256 * kLutCopies; i += TL::THREADS) {
-      const int b = i / kLutCopies;
+    for (int i = tid; i < 256 * TL::LUTC; i += TL::THREADS) {
+      const int b = i / TL::LUTC;
       uint32_t e;
       if constexpr (BA == 8) {
         e = __builtin_bit_cast(uint16_t, (_Float16)lv8[b]);
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(TL::THREADS, 1) void linear_kernel(
       lut[i] = e;
     }
     __syncthreads();
-    da.lut = lut + (lane & (kLutCopies - 1));
+    da.lut = lut + (lane & (TL::LUTC - 1));
     dw.lut = da.lut;
   }
 
@@ -593,8 +601,8 @@ template <class TL, int BA, int BW>
 hipError_t launch_tiles(const LinearArgs &a, const PermTab &ta, const PermTab &tw,
                         const float *lv8, int vec, int first, int count, unsigned grid,
                         int splits = 1, float *part = nullptr) {
-  constexpr int lds = TL::LDS + ((BA == 8 || (BA == 4 && BW == 4)) ? kLutBytes : 0);
-  static_assert(lds <= 160 * 1024, "LDS of one CU");
+  constexpr int lds = TL::LDS + ((BA == 8 || (BA == 4 && BW == 4)) ? 256 * TL::LUTC * 4 : 0);
+  static_assert(lds * TL::WGS <= 160 * 1024, "LDS of one CU");
   static std::atomic<uint64_t> lds_set{0};  // per instantiation and device
   hipError_t e = ensure_lds_limit((const void *)linear_kernel<TL, BA, BW>, lds, lds_set);
   if (e != hipSuccess) return e;
@@ -609,7 +617,8 @@ hipError_t launch_tiles(const LinearArgs &a, const PermTab &ta, const PermTab &t
 // the workgroups).  A large problem whose last round would leave at most a
 // quarter of the CUs busy (R leftover tiles, each alone on its CU for a
 // whole K loop) runs those R tiles first as 128 x 128 sub-tiles, each cut
-// into S = CUs / 4R K ranges so that every CU takes one piece; the pieces'
+// into S = 2 CUs / 4R K ranges so that every CU takes two pieces (two
+// 128 x 128 workgroups share a CU); the pieces'
 // fp32 partial sums go to rows of y that belong to the full rounds (they
 // are overwritten later in stream order, so no extra memory is needed),
 // tail_reduce_kernel sums them into the R tiles, and then the full rounds
@@ -641,7 +650,7 @@ hipError_t launch_ab(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &
                                          (unsigned)(tiles < cus ? tiles : cus));
 
   const int first = (int)(rounds * cus), R = (int)rem, T = a.K / KS;
-  int S = cus / (4 * R);
+  int S = SmallTile::WGS * cus / (4 * R);  // pieces fill every CU's 128 x 128 slots
   if (S > T / 3) S = T / 3;  // at least three K steps per piece
   if (S > 1 && !vec) S = 1;
   if (S > 1) {
