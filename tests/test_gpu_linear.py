@@ -82,11 +82,11 @@ def test_tile_paths(q, M, N, K, ba, bw):
 
 
 @pytest.mark.parametrize("M,N,K,ba,bw,band0", [
-    (4352, 4096, 768, 4, 4, 4096),    # 272 tiles: 16 leftover, 4 K ranges each
+    (4352, 4096, 768, 4, 4, 4096),    # 272 tiles: 16 leftover, 4 K ranges of 3 steps
     (4312, 4088, 768, 4, 4, 4096),    # the same tile grid, ragged bottom and right edges
-    (4352, 4096, 3072, 4, 4, 4096),   # 48 K steps in 4 ranges of 12
+    (4352, 4096, 3072, 4, 4, 4096),   # 48 K steps in 8 ranges of 6
     (4352, 4096, 640, 4, 4, 4096),    # 10 K steps in 3 uneven ranges (3, 3, 4)
-    (3072, 5888, 768, 4, 4, 2048),    # 276 tiles: 20 leftover (rows 8-11), 3 ranges
+    (3072, 5888, 768, 4, 4, 2048),    # 276 tiles: 20 leftover (rows 8-11), 320 pieces
     (4352, 4096, 768, 3, 2, 4096),    # mixed widths
     (4352, 4096, 768, 8, 8, 4096),    # W8A8
     (4352, 4352, 256, 4, 4, 4096),    # 289 tiles: 33 leftover, too short a K to cut
