@@ -57,7 +57,8 @@ def test_small_and_ragged_shapes(q, M, N, K):
 @pytest.mark.parametrize("M,N,K,ba,bw", [
     (1000, 700, 256, 4, 4),    # 12 tiles: run as 128 x 128 tiles
     (1000, 700, 256, 3, 2),    # the same with mixed widths
-    (2600, 2344, 384, 4, 4),   # 110 tiles of 256 x 256, ragged edges
+    (2600, 2344, 384, 4, 4),   # 110 tiles: 128 x 128 tiles, two per CU, ragged edges
+    (3600, 3300, 384, 4, 4),   # 195 tiles of 256 x 256 in one partial round, ragged edges
     (7387, 2204, 512, 4, 4),   # 261 tiles: a 5-tile last round
     (7387, 2204, 512, 2, 4),   # the same with mixed widths
 ])
