@@ -615,16 +615,16 @@ hipError_t launch_tiles(const LinearArgs &a, const PermTab &ta, const PermTab &t
 // Tiles of 256 x 256, one workgroup per CU at a time.  A problem too small
 // to fill half of the CUs runs as 128 x 128 tiles instead (four times the
 // workgroups, two per CU; 10-15% faster there than 256 x 256 tiles on part
-// of the CUs).  A large problem whose last round would leave at most a
-// quarter of the CUs busy (R leftover tiles, each alone on its CU for a
-// whole K loop) runs those R tiles first as 128 x 128 sub-tiles, each cut
-// into S = 2 CUs / 4R K ranges so that every CU takes two pieces (two
-// 128 x 128 workgroups share a CU); the pieces'
+// of the CUs).  A large problem whose last round would leave at most half
+// of the CUs busy (R leftover tiles, each alone on its CU for a whole K
+// loop) runs those R tiles first as 128 x 128 sub-tiles, each cut into
+// S = 2 CUs / 4R K ranges (when that is 2 or more) so that every CU takes
+// two pieces (two 128 x 128 workgroups share a CU); the pieces'
 // fp32 partial sums go to rows of y that belong to the full rounds (they
 // are overwritten later in stream order, so no extra memory is needed),
 // tail_reduce_kernel sums them into the R tiles, and then the full rounds
-// run as before.  Tails of more than a quarter of the CUs stay whole 256 x
-// 256 tiles.
+// run as before.  Tails of more than half of the CUs stay whole 256 x 256
+// tiles.
 template <int BA, int BW>
 hipError_t launch_ab(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &lw,
                      const float *lv8) {
@@ -644,7 +644,7 @@ hipError_t launch_ab(const LinearArgs &a, const LevelsF16 &la, const LevelsF16 &
     return launch_tiles<SmallTile, BA, BW>(a, ta, tw, lv8, vec, 0, (int)tiles,
                                            (unsigned)(4 * tiles));
   const int64_t rounds = tiles / cus, rem = tiles % cus;
-  if (rounds == 0 || rem == 0 || 4 * rem > cus)
+  if (rounds == 0 || rem == 0 || 4 * rem > SmallTile::WGS * cus)
     // persistent: at most one workgroup per CU (a multiple of 8 keeps each
     // workgroup on one XCD's run of tiles)
     return launch_tiles<BigTile, BA, BW>(a, ta, tw, lv8, vec, 0, (int)tiles,

@@ -91,6 +91,7 @@ def test_tile_paths(q, M, N, K, ba, bw):
     (4352, 4096, 768, 3, 2, 4096),    # mixed widths
     (4352, 4096, 768, 8, 8, 4096),    # W8A8
     (4352, 4352, 256, 4, 4, 4096),    # 289 tiles: 33 leftover, too short a K to cut
+    (4608, 5120, 384, 4, 4, 2048),    # 360 tiles: 104 leftover, 128 x 128 tiles uncut
     (4352, 4092, 768, 4, 4, 4096),    # N % 8 != 0: leftover tiles not cut
 ])
 def test_leftover_tiles_split(q, M, N, K, ba, bw, band0):
