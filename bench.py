@@ -64,6 +64,8 @@ def parse():
     p.add_argument("--profile-bench-log", default=None,
                    help="with --summarize-profiles: output of the traced bench.py run, whose "
                         "own per-kernel event timings are compared with the trace")
+    p.add_argument("--profile-out", default=os.path.join(ROOT, "profiles"),
+                   help="with --summarize-profiles: folder for the summaries and traffic.json")
     p.add_argument("--sweep", action="store_true",
                    help="no step benchmark: time rotate+quantize and the linear of every "
                         "workload instance and bit pair at full size, one JSON line each")
@@ -400,7 +402,7 @@ def summarize_profiles(a):
     lin_parts = [n for n, *_ in lines if n.startswith(LINEAR_KERNELS)]
     lin_name = " + ".join(lin_parts)
     rot_name = next(n for n, *_ in lines if n.startswith("rq_"))
-    with open(os.path.join(ROOT, "profiles", f"{tag}_kernel_stats.txt"), "w") as f:
+    with open(os.path.join(a.profile_out, f"{tag}_kernel_stats.txt"), "w") as f:
         f.write(f"Kernel timing on one MI355X (gfx950), workload {cfg}/{lin.name}: {M} tokens, "
                 f"d_in {K} -> d_out {N}, W{bw}A{ba}.\nCommands (repository root on the GPU "
                 f"host):\n{a.profile_command}\n\n")
@@ -478,7 +480,7 @@ def summarize_profiles(a):
                             "note": "mean over the activation and weight-preparation launches"},
         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
     # one entry per workload, so summaries of several workloads coexist
-    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    tpath = os.path.join(a.profile_out, "traffic.json")
     allt = {}
     if os.path.exists(tpath):
         with open(tpath) as f:
@@ -488,7 +490,7 @@ def summarize_profiles(a):
     allt[tag] = table
     with open(tpath, "w") as f:
         json.dump(allt, f, indent=1)
-    with open(os.path.join(ROOT, "profiles", f"{tag}_traffic.txt"), "w") as f:
+    with open(os.path.join(a.profile_out, f"{tag}_traffic.txt"), "w") as f:
         f.write(f"HBM-side traffic per launch from rocprofv3 counters, workload {cfg}/{lin.name} "
                 f"({M} x {K} -> {N}, W{bw}A{ba}).\nCommands (repository root on the GPU host):\n"
                 f"{a.profile_command}\n\n")
@@ -557,7 +559,7 @@ def write_counter_summary(a, tag, lin_parts, rot_name, M, N, K, ba, bw, in_b):
                 lines.append(f"  VALU busy per SIMD: "
                              f"{c['SQ_ACTIVE_INST_VALU'] * 4 / 1024 / (gui / 8):.3f}")
         lines.append("")
-    with open(os.path.join(ROOT, "profiles", f"{tag}_counters.txt"), "w") as f:
+    with open(os.path.join(a.profile_out, f"{tag}_counters.txt"), "w") as f:
         f.write("\n".join(lines))
 
 
