@@ -139,6 +139,35 @@ def test_leftover_tiles_output_bounds(q, offset):
     assert np.all(np.abs(yn[rows] - ref) <= 1e-2 * np.abs(ref).max() + 1e-30)
 
 
+# seeded random shapes, three per launch path (persistent rounds with and
+# without leftovers of each kind, one partial round of 256 x 256 tiles,
+# 128 x 128 tiles), bit pairs in rotation
+_PATH_SHAPES = [(2295, 6416, 128), (1925, 4419, 128), (3494, 2600, 896),      # one round
+                (2036, 8632, 896), (3537, 9376, 1024), (9291, 8904, 896),     # K-split leftovers
+                (747, 1352, 896), (748, 8680, 384), (1231, 1960, 896),        # 128 x 128 tiles
+                (4356, 5592, 896), (5860, 4632, 640), (9268, 4896, 640),      # 256 x 256 leftovers
+                (7436, 4439, 1024), (3455, 4629, 512), (3172, 5771, 256),     # 128 x 128 leftovers
+                (8181, 5952, 384), (5900, 8026, 896), (7997, 3896, 256)]      # full rounds only
+_PAIRS = [(4, 4), (2, 4), (3, 4), (2, 3), (4, 2), (3, 3), (8, 8), (2, 2), (4, 3)]
+
+
+@pytest.mark.parametrize("idx", range(len(_PATH_SHAPES)))
+def test_random_shapes_every_path(q, idx):
+    M, N, K = _PATH_SHAPES[idx]
+    ba, bw = _PAIRS[idx % len(_PAIRS)]
+    ac, an = wl.random_codes(M, K, ba, 100 + idx)
+    wc, wn = wl.random_codes(N, K, bw, 200 + idx)
+    say("linear random shape", M, N, K, ba, bw)
+    y = _run(q, ac, an, ba, wc, wn, bw, K)
+    last = (M - 1) // 256 * 256
+    rows = np.unique(np.concatenate([wl.sample_rows(M, 10, 300 + idx),
+                                     np.linspace(last, M - 1, 6).astype(np.int64)]))
+    ref = oracle.linear(ac, an, ba, wc, wn, bw, K, rows=rows)
+    assert np.all(np.isfinite(y))
+    assert parity.rel_fro(y[rows], ref) <= parity.LINEAR_FRO
+    assert np.all(np.abs(y[rows] - ref) <= 1e-2 * np.abs(ref).max() + 1e-30)
+
+
 def test_oracle_codes_realistic_distribution(q):
     """Codes produced by the oracle's own quantizer on workload inputs (the
     Lloyd-Max cell frequencies, not uniform), fed to both sides."""
