@@ -298,30 +298,82 @@ static double sphere_moment(double a, double b, int d)
     return exp(lc) * (pa - pb) / (d - 1);
 }
 
+/* Density of T: c_d (1 - t^2)^((d-3)/2) on (-1, 1). */
+static double sphere_pdf(double t, int d)
+{
+    if (t <= -1.0 || t >= 1.0) return 0.0;
+    const double lc = lgamma(0.5 * d) - 0.5 * log(M_PI) - lgamma(0.5 * (d - 1));
+    return exp(lc + 0.5 * (d - 3) * log1p(-t * t));
+}
+
+/* Newton's method on the Lloyd-Max conditions for the sphere marginal: the
+ * same conditions, Jacobian and stopping rule as lloyd_max_newton (there
+ * for N(0,1)), with f_d's density, cell masses and first moments, the
+ * outer cells ending at -1 and 1 (fixed ends: no derivative), and steps
+ * measured in units of sigma = 1/sqrt(d).  Returns the number of steps. */
+static int sphere_newton(int d, int L, double *c)
+{
+    double t[256 + 1], lo[256], di[256], up[256], rhs[256];
+    const double unit = sqrt((double)d);
+    double prev = INFINITY;
+    int it;
+    for (it = 1; it <= 100; it++) {
+        t[0] = -1.0;
+        t[L] = 1.0;
+        for (int k = 1; k < L; k++) t[k] = 0.5 * (c[k - 1] + c[k]);
+        for (int k = 0; k < L; k++) {
+            const double a = t[k], b = t[k + 1];
+            const double m = sphere_mass(a, b, d);
+            const double mu = sphere_moment(a, b, d) / m;
+            const double da = (k == 0) ? 0.0 : sphere_pdf(a, d) * (mu - a) / m;
+            const double db = (k == L - 1) ? 0.0 : sphere_pdf(b, d) * (b - mu) / m;
+            lo[k] = -0.5 * da;
+            up[k] = -0.5 * db;
+            di[k] = 1.0 - 0.5 * da - 0.5 * db;
+            rhs[k] = -(c[k] - mu);
+        }
+        for (int k = 1; k < L; k++) {
+            const double f = lo[k] / di[k - 1];
+            di[k] -= f * up[k - 1];
+            rhs[k] -= f * rhs[k - 1];
+        }
+        rhs[L - 1] /= di[L - 1];
+        for (int k = L - 2; k >= 0; k--) rhs[k] = (rhs[k] - up[k] * rhs[k + 1]) / di[k];
+        double move = 0.0;
+        for (int k = 0; k < L; k++) {
+            c[k] += rhs[k];
+            if (fabs(rhs[k]) * unit > move) move = fabs(rhs[k]) * unit;
+        }
+        if (move < 1e-14 || (it >= 3 && move > 0.5 * prev)) break;
+        prev = move;
+    }
+    return it;
+}
+
 /* Lloyd-Max quantizer for the exact marginal of one coordinate of a uniform
  * point on S^{d-1} (pith.science: the referee's minor comment 1 asks for
  * this closed-form marginal; the Figure 2 caption uses its Gaussian limit
  * N(0, 1/d)): Lloyd's alternation as for the Gaussian, with the cell masses
- * and first moments of f_d.  Writes levels and thresholds in units of z
- * (the sigma = 1/sqrt(d) scale is built in).  d >= 3. */
+ * and first moments of f_d, started from the Gaussian codebook scaled by
+ * sigma; from 5 bits on (8 bits: the top of the llmdb.app bit range) a
+ * short alternation is followed by Newton's method (sphere_newton), as for
+ * the Gaussian.  Writes levels and thresholds in units of z (the sigma =
+ * 1/sqrt(d) scale is built in).  d >= 3. */
 int oqo_codebook_sphere(int d, int bits, double *levels, double *thresholds)
 {
     if (d < 3 || bits < 1 || bits > 8) return -1;
     const int L = 1 << bits;
     double t[257];
     double ul[256], ut[255];
-    oqo_codebook_unit(bits <= 4 ? bits : 4, ul, ut); /* a start near the fixed point */
-    if (bits <= 4) {
-        for (int k = 0; k < L; k++) levels[k] = ul[k] / sqrt((double)d);
-    } else {
-        for (int k = 0; k < L; k++) levels[k] = (-1.0 + (2.0 * k + 1.0) / L) * 2.5 / sqrt((double)d);
-    }
+    oqo_codebook_unit(bits, ul, ut); /* a start near the fixed point */
+    for (int k = 0; k < L; k++) levels[k] = ul[k] / sqrt((double)d);
     for (int k = 0; k < L; k++) { /* keep the start inside (-1, 1) */
         if (levels[k] <= -1.0) levels[k] = -1.0 + (k + 0.5) / L;
         if (levels[k] >= 1.0) levels[k] = 1.0 - (L - k - 0.5) / L;
     }
+    const int max_iter = bits <= 4 ? 400000 : 200;
     int it;
-    for (it = 1; it <= 400000; it++) {
+    for (it = 1; it <= max_iter; it++) {
         double move = 0.0;
         t[0] = -1.0;
         t[L] = 1.0;
@@ -334,6 +386,7 @@ int oqo_codebook_sphere(int d, int bits, double *levels, double *thresholds)
         }
         if (move < 1e-13) break; /* the incomplete beta is good to about 1e-15 */
     }
+    if (bits > 4) it += sphere_newton(d, L, levels);
     for (int k = 1; k < L; k++) thresholds[k - 1] = 0.5 * (levels[k - 1] + levels[k]);
     return it;
 }

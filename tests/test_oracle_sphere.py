@@ -11,7 +11,11 @@ pages use).
 * cell masses of the oracle's incomplete beta against SciPy's numerical
   integration of the density c_d (1 - t^2)^((d-3)/2);
 * the centroid condition for every cell, by SciPy quadrature;
-* antisymmetry.
+* antisymmetry;
+* 8 bits (where Lloyd's alternation is followed by Newton's method): the
+  d = 3 uniform quantizer, every centroid condition, antisymmetry, and a
+  gap to the Gaussian codebook that shrinks like 1/d (the marginal's
+  first-order correction to N(0, 1/d) is O(1/d)).
 """
 import math
 
@@ -28,7 +32,7 @@ def _density(d):
     return lambda t: c * (1.0 - t * t) ** ((d - 3) / 2)
 
 
-@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
 def test_d3_is_the_uniform_quantizer(bits):
     L = 1 << bits
     lv, th, _ = oracle.codebook_sphere(3, bits)
@@ -61,7 +65,7 @@ def test_cell_masses_against_quadrature(d):
         assert abs(oracle.sphere_mass(a, b, d) - ref) <= 1e-11 * max(ref, 1e-3), (a, b)
 
 
-@pytest.mark.parametrize("d,bits", [(5, 3), (256, 4), (3072, 2)])
+@pytest.mark.parametrize("d,bits", [(5, 3), (256, 4), (3072, 2), (256, 8), (3072, 8)])
 def test_centroid_condition(d, bits):
     f = _density(d)
     lv, th, _ = oracle.codebook_sphere(d, bits)
@@ -78,3 +82,22 @@ def test_antisymmetric():
     lv, th, _ = oracle.codebook_sphere(384, 4)
     np.testing.assert_allclose(lv, -lv[::-1], atol=1e-15)
     np.testing.assert_allclose(th, -th[::-1], atol=1e-15)
+    # 8 bits: Newton stops at the incomplete beta's rounding noise
+    for d in (384, 13824):
+        lv, th, _ = oracle.codebook_sphere(d, 8)
+        np.testing.assert_allclose(lv, -lv[::-1], atol=1e-11)
+        np.testing.assert_allclose(th, -th[::-1], atol=1e-11)
+        assert np.all(np.diff(lv) > 0)
+
+
+def test_gaussian_limit_8bit_scales_like_one_over_d():
+    ul, _, _ = oracle.codebook_unit(8)
+    ds = (256, 3072, 13824)
+    gaps = []
+    for d in ds:
+        lv, _, _ = oracle.codebook_sphere(d, 8)
+        gaps.append(np.max(np.abs(lv * math.sqrt(d) - ul) / np.abs(ul)))
+    assert gaps[0] > gaps[1] > gaps[2]
+    for i in range(2):
+        ratio = gaps[i] / gaps[i + 1]
+        assert abs(ratio / (ds[i + 1] / ds[i]) - 1) < 0.15, (gaps, ratio)
