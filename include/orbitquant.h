@@ -43,7 +43,7 @@
  *     indices 0..2^b-1 in ascending level order.
  *     At 8 bits this is plain byte addressing: byte slot(i) holds code i.
  *   - Limits: d (and K) a multiple of 128, 128 <= d <= 16384; bits in
- *     {2, 3, 4, 8} (1..8 for oq_codebook; the exact-sphere family up to 4).
+ *     {2, 3, 4, 8} (1..8 for oq_codebook; the exact-sphere family 1..4 and 8).
  *     Zero rows are valid (a zero token gets norm 0 and every code
  *     2^(b-1)).  NaN/Inf inputs give unspecified codes and no error.
  */
@@ -106,8 +106,12 @@ int oq_codebook(int d, int bits, float *levels, float *thresholds);
  * c_d (1 - t^2)^((d-3)/2) of one coordinate of a uniform point on S^{d-1}
  * (pith.science: the referee's minor comment 1 asks for this closed-form
  * marginal), defined for the dimensions the kernels take (d % 128 == 0,
- * d <= 16384) and bits 1..4 (else OQ_EUNSUPPORTED).  It differs from the Gaussian one by
- * 0.8% of a level at d = 256 and 0.015% at d = 13824 (4 bits). */
+ * d <= 16384) and bits 1..4 and 8 (else OQ_EUNSUPPORTED).  It differs from
+ * the Gaussian one by 0.8% of a level at d = 256 and 0.015% at d = 13824
+ * (4 bits).  Up to 4 bits the solver is Max's shooting method; at 8 bits
+ * Newton's method on the Lloyd-Max conditions from the Gaussian codebook
+ * (the conditions fix the 8-bit levels to about 1e-7 of the unit scale in
+ * double precision). */
 int oq_codebook_ex(int d, int bits, uint32_t flags, float *levels, float *thresholds);
 
 /* Bytes of a packed code matrix: rows * d * bits / 8 (-1 on bad input). */
@@ -176,7 +180,7 @@ int oq_linear(const uint8_t *a_codes, const float *a_norms, int a_bits,
 /* oq_linear with a codebook family for both operands (flags 0 or
  * OQ_CODEBOOK_SPHERE; the codes must come from rotate/prepare calls with
  * the same family).  Same layout, limits and errors; flags outside the
- * family bit give OQ_EINVAL; the sphere family at 8 bits, OQ_EUNSUPPORTED. */
+ * family bit give OQ_EINVAL.  W8A8 takes either family. */
 int oq_linear_ex(const uint8_t *a_codes, const float *a_norms, int a_bits,
                  const uint8_t *w_codes, const float *w_norms, int w_bits,
                  int64_t M, int64_t N, int K, uint32_t flags, uint16_t *y, void *stream);

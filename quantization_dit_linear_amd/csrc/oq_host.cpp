@@ -221,6 +221,52 @@ void shoot_codebook(int bits, double top, const Mean &mean, double *lv, double *
   th[P - 1] = 0.0;
 }
 
+// Newton's method on the Lloyd-Max conditions of a symmetric density over
+// the upper half-line: unknowns the P positive levels c_0 < ... < c_{P-1}
+// (lv on entry: a start close to the solution), cells [e_k, e_{k+1}) with
+// e_0 = 0, e_k = (c_{k-1} + c_k) / 2, e_P = top; conditions
+// F_k = c_k - mean(e_k, e_{k+1}) = 0.  With m the cell mass and g the
+// density, d mean / d e_k = g(e_k)(mean - e_k)/m and
+// d mean / d e_{k+1} = g(e_{k+1})(e_{k+1} - mean)/m, so the Jacobian is
+// tridiagonal (each inner edge moves with both neighbouring levels by 1/2).
+// Used where shooting loses accuracy (8 bits: its forward sweep magnifies
+// the first level's rounding across 128 cells).  Stops after a step below
+// 1e-14 or once steps stop shrinking.
+template <class Dist>
+void newton_upper_half(int P, const Dist &dist, double *c) {
+  std::vector<double> e(P + 1), lo(P), di(P), up(P), rhs(P);
+  double prev = INFINITY;
+  for (int it = 0; it < 60; it++) {
+    e[0] = 0.0;
+    e[P] = dist.top();
+    for (int k = 1; k < P; k++) e[k] = 0.5 * (c[k - 1] + c[k]);
+    for (int k = 0; k < P; k++) {
+      const double a = e[k], b = e[k + 1], m = dist.mass(a, b);
+      const double mu = dist.moment(a, b) / m;
+      const double da = (k == 0) ? 0.0 : dist.g(a) * (mu - a) / m;
+      const double db = (k == P - 1) ? 0.0 : dist.g(b) * (b - mu) / m;
+      lo[k] = -0.5 * da;
+      up[k] = -0.5 * db;
+      di[k] = 1.0 - 0.5 * da - 0.5 * db;
+      rhs[k] = mu - c[k];
+    }
+    for (int k = 1; k < P; k++) {  // Thomas algorithm
+      const double f = lo[k] / di[k - 1];
+      di[k] -= f * up[k - 1];
+      rhs[k] -= f * rhs[k - 1];
+    }
+    rhs[P - 1] /= di[P - 1];
+    for (int k = P - 2; k >= 0; k--) rhs[k] = (rhs[k] - up[k] * rhs[k + 1]) / di[k];
+    double move = 0.0;
+    for (int k = 0; k < P; k++) {
+      c[k] += rhs[k];
+      move = std::max(move, std::fabs(rhs[k]));
+    }
+    if (move < 1e-14 || (it >= 2 && move > 0.5 * prev)) break;
+    prev = move;
+  }
+}
+
 // Unit-variance codebook of a family: Gaussian (d-independent) or the exact
 // sphere marginal of dimension d (cached per (d, bits)).
 void family_codebook(int d, int bits, bool sphere, double *levels, double *thresholds) {
@@ -236,8 +282,24 @@ void family_codebook(int d, int bits, bool sphere, double *levels, double *thres
   if (it == cache.end()) {
     SphereDist dist(d);
     std::vector<double> v(2 * L);
-    shoot_codebook(bits, dist.top(), [&](double a, double b) { return dist.mean(a, b); },
-                   v.data(), v.data() + L);
+    if (bits <= 4) {
+      shoot_codebook(bits, dist.top(), [&](double a, double b) { return dist.mean(a, b); },
+                     v.data(), v.data() + L);
+    } else {
+      // from the Gaussian codebook (the d -> infinity limit, within a few
+      // percent at d = 128), Newton on the sphere conditions
+      const int P = L / 2;
+      double gl[256], gt[255];
+      unit_codebook(bits, gl, gt);
+      std::vector<double> c(gl + P, gl + L);
+      newton_upper_half(P, dist, c.data());
+      for (int k = 0; k < P; k++) {
+        v[P + k] = c[k];
+        v[P - 1 - k] = -c[k];
+      }
+      for (int k = 0; k < L - 1; k++) v[L + k] = 0.5 * (v[k] + v[k + 1]);
+      v[L + P - 1] = 0.0;
+    }
     it = cache.emplace(std::make_pair(d, bits), v).first;
   }
   std::memcpy(levels, it->second.data(), sizeof(double) * L);
@@ -455,7 +517,6 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
   if ((flags & outs) == outs) return OQ_EINVAL;
   int rc = check_d_bits(d, bits);
   if (rc != OQ_OK) return rc;
-  if (sphere && bits > 4) return OQ_EUNSUPPORTED;
   if (n_tok == 0) return OQ_OK;  // empty input: nothing to do, pointers may be null
   if (!x || !out || !norms) return OQ_EINVAL;
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(norms, 4)) return OQ_EINVAL;
@@ -507,7 +568,7 @@ const char *oq_strerror(int status) {
   switch (status) {
     case OQ_OK: return "success";
     case OQ_EINVAL: return "invalid argument (null or misaligned pointer, bad size, dtype or flag)";
-    case OQ_EUNSUPPORTED: return "unsupported configuration (d must be a multiple of 128 in [128, 16384]; bits in {2,3,4,8}; 8 bits on both sides of a linear; the sphere codebook up to 4 bits)";
+    case OQ_EUNSUPPORTED: return "unsupported configuration (d must be a multiple of 128 in [128, 16384]; bits in {2,3,4,8}; 8 bits on both sides of a linear; the sphere codebook at 1-4 and 8 bits)";
     case OQ_ENOMEM: return "out of device memory for the rotation plan";
     case OQ_EDEVICE: return "HIP runtime or kernel launch failure";
     default: return "unknown status";
@@ -521,7 +582,8 @@ int oq_codebook_ex(int d, int bits, uint32_t flags, float *levels, float *thresh
   if (flags & ~OQ_CODEBOOK_SPHERE) return OQ_EINVAL;
   if (bits < 1 || bits > 8) return OQ_EUNSUPPORTED;
   const bool sphere = (flags & OQ_CODEBOOK_SPHERE) != 0;
-  if (sphere && (d % oq::kGroup != 0 || d > oq::kMaxD || bits > 4)) return OQ_EUNSUPPORTED;
+  if (sphere && (d % oq::kGroup != 0 || d > oq::kMaxD || (bits > 4 && bits != 8)))
+    return OQ_EUNSUPPORTED;
   double lv[256], th[255];
   family_codebook(d, bits, sphere, lv, th);
   const double sigma = 1.0 / std::sqrt((double)d);
@@ -563,7 +625,6 @@ int oq_linear_ex(const uint8_t *a_codes, const float *a_norms, int a_bits, const
   rc = check_d_bits(K, w_bits);
   if (rc != OQ_OK) return rc;
   if ((a_bits == 8) != (w_bits == 8)) return OQ_EUNSUPPORTED;  // W8A8 only, no mixed pair
-  if (sphere && a_bits == 8) return OQ_EUNSUPPORTED;
   if (M == 0 || N == 0) return OQ_OK;  // empty output: pointers may be null
   if (!a_codes || !a_norms || !w_codes || !w_norms || !y) return OQ_EINVAL;
   if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_norms, 4) ||

@@ -24,6 +24,22 @@ def test_library_sphere_codebook_matches_oracle(q, d, bits):
     np.testing.assert_allclose(th, rt, rtol=2e-7, atol=1e-9 / np.sqrt(d))
 
 
+@pytest.mark.parametrize("d", [128, 256, 3072, 5120, 12288, 13824, 16384])
+def test_library_sphere_codebook_8bit(q, d):
+    """8 bits: the library runs Newton from the Gaussian codebook, the
+    oracle Lloyd then Newton from it; at 8 bits the Lloyd-Max conditions
+    pin the levels only to about 1e-7 sigma in double precision (one nearly
+    flat direction), so the two agree to that, which stays well inside the
+    1e-6 window around each threshold that the code parity exempts."""
+    lv, th = q.codebook(d, 8, sphere=True)
+    rl, rt, _ = oracle.codebook_sphere(d, 8)
+    s = np.sqrt(d)
+    window = 1e-6 * np.maximum(np.abs(rt * s), 1.0)
+    assert np.max(np.abs(th.astype(np.float64) * s - rt * s) / window) <= 0.8
+    np.testing.assert_allclose(lv * s, rl * s, rtol=0, atol=1e-6)
+    assert np.all(np.diff(lv) > 0)
+
+
 def test_family_flag_validation(q):
     import ctypes
     lv = np.zeros(16, np.float32)

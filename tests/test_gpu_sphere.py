@@ -28,7 +28,9 @@ def _thr_unit(d, bits):
 
 
 @pytest.mark.parametrize("cfg,name,bits", [("image_qkv", "qkv", 4), ("image_mlp", "down", 3),
-                                           ("video_block", "down", 2), ("tiny", "tiny", 4)])
+                                           ("video_block", "down", 2), ("tiny", "tiny", 4),
+                                           ("image_qkv", "qkv", 8), ("video_block", "down", 8),
+                                           ("tiny", "tiny", 8)])
 def test_rotate_quantize_sphere(q, cfg, name, bits):
     import torch
     lin = wl.get_linear(cfg, name)
@@ -57,7 +59,7 @@ def test_sphere_codes_differ_from_gaussian_where_expected(q):
     assert np.abs(a.astype(int) - b.astype(int)).max() == 1
 
 
-@pytest.mark.parametrize("bw,ba", [(4, 4), (2, 4)])
+@pytest.mark.parametrize("bw,ba", [(4, 4), (2, 4), (8, 8)])
 def test_linear_sphere(q, bw, ba):
     import torch
     lin = wl.get_linear("image_qkv", "qkv")
