@@ -39,7 +39,10 @@ def test_eight_bit_validation(q):
     L = q.lib()
     lv = np.zeros(256, np.float32)
     th = np.zeros(256, np.float32)
+    # the sphere family: 1-4 and 8 bits
     assert L.oq_codebook_ex(3072, 8, q.OQ_CODEBOOK_SPHERE, lv.ctypes.data,
+                            th.ctypes.data) == q.OQ_OK
+    assert L.oq_codebook_ex(3072, 6, q.OQ_CODEBOOK_SPHERE, lv.ctypes.data,
                             th.ctypes.data) == q.OQ_EUNSUPPORTED
     assert L.oq_codebook_ex(3072, 9, 0, lv.ctypes.data, th.ctypes.data) == q.OQ_EUNSUPPORTED
     assert L.oq_codes_bytes(10, 3072, 8) == 10 * 3072
@@ -49,10 +52,10 @@ def test_eight_bit_validation(q):
     assert L.oq_linear(None, None, 8, None, None, 8, 0, 5, 3072, None, None) == q.OQ_OK
     assert L.oq_linear(None, None, 5, None, None, 5, 0, 5, 3072, None, None) == q.OQ_EUNSUPPORTED
     assert L.oq_linear_ex(None, None, 8, None, None, 8, 0, 5, 3072, q.OQ_CODEBOOK_SPHERE, None,
-                          None) == q.OQ_EUNSUPPORTED
-    # rotate: 8 bits accepted (empty input is a no-op), sphere family only to 4 bits
+                          None) == q.OQ_OK
+    # rotate: 8 bits accepted in both families (empty input is a no-op)
     assert L.oq_rotate_quantize(None, q.OQ_BF16, 0, 3072, 1, 0, 8, None, None, None) == q.OQ_OK
     assert L.oq_rotate_quantize(None, q.OQ_BF16, 0, 3072, 1, q.OQ_CODEBOOK_SPHERE, 8, None, None,
-                                None) == q.OQ_EUNSUPPORTED
+                                None) == q.OQ_OK
     assert L.oq_rotate_quantize(None, q.OQ_BF16, 0, 3072, 1, 0, 6, None, None,
                                 None) == q.OQ_EUNSUPPORTED
