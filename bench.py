@@ -19,6 +19,13 @@ projection (2 CFG branches x 4608 tokens, d = 3072 -> 9216, 1% outlier
 channels x50, per-token log-normal(0, 1.5) scale) and N(0, 0.02^2) weights,
 drawn by the `workloads` generators.  Four input buffer sets are cycled so
 the working set exceeds the 256 MB Infinity Cache.
+
+Other modes:
+    python bench.py --sweep           every workload instance and bit pair at
+                                      full size, one JSON line each
+    python bench.py --summarize-profiles KT FETCH WRITE [--profile-counters ...]
+                                      rocprofv3 output -> profiles/ summaries
+                                      and the workload's traffic.json entry
 """
 import argparse
 import hashlib
