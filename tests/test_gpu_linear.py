@@ -168,6 +168,36 @@ def test_random_shapes_every_path(q, idx):
     assert np.all(np.abs(y[rows] - ref) <= 1e-2 * np.abs(ref).max() + 1e-30)
 
 
+@pytest.mark.parametrize("M,N,K,ba,bw", [(4352, 4096, 768, 4, 4),   # split leftover tiles
+                                         (1000, 700, 256, 3, 2),    # 128 x 128 tiles only
+                                         (4352, 4096, 768, 8, 8)])  # W8A8, split leftovers
+def test_linear_in_a_hip_graph(q, M, N, K, ba, bw):
+    """The whole linear call (up to three kernels; no memory fills) captured
+    in a HIP graph: every replay, with eager work and synchronisations in
+    between, gives the eager result bit for bit."""
+    import torch
+    ac, an = wl.random_codes(M, K, ba, 41)
+    wc, wn = wl.random_codes(N, K, bw, 42)
+    say("linear graph", M, N, K, ba, bw)
+    a, sa, w, sw = to_device(ac), to_device(an), to_device(wc), to_device(wn)
+    eager = q.linear(a, sa, ba, w, sw, bw, K)
+    torch.cuda.synchronize()
+    ref = eager.clone()
+    y = torch.empty_like(eager)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        q.linear(a, sa, ba, w, sw, bw, K, out=y)
+    for _ in range(3):
+        y.fill_(7.0)                                  # stale contents must not leak through
+        q.linear(a, sa, ba, w, sw, bw, K, out=eager)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)
+        assert torch.equal(eager, ref)
+
+
 def test_oracle_codes_realistic_distribution(q):
     """Codes produced by the oracle's own quantizer on workload inputs (the
     Lloyd-Max cell frequencies, not uniform), fed to both sides."""
