@@ -180,3 +180,33 @@ def test_weight_prep_full_size_sampled_rows(q, cfg, name, bits):
     rc, rr, rz = oracle.rotate_quantize(W[rows], lin.weight.dtype, K, lin.seed, bits, want_z=True)
     parity.assert_codes_match(host(codes)[rows], rc, rz, K, bits, _thr(bits), f"W {cfg}/{name}")
     parity.assert_norms_match(host(rn)[rows], rr, f"W {cfg}/{name}")
+
+
+@pytest.mark.parametrize("cfg,name,bits", [("image_qkv", "qkv", 4), ("tiny", "tiny", 4),
+                                           ("video_block", "down", 8)])
+def test_rotate_quantize_in_a_hip_graph(q, cfg, name, bits):
+    """rotate+quantize (the bf16 fast kernel, and the general kernel for the
+    fp32 tiny workload) captured in a HIP graph: every replay, with eager
+    work and synchronisations in between, gives the eager codes and norms
+    bit for bit."""
+    import torch
+    lin = wl.get_linear(cfg, name)
+    x = to_device(wl.activations(cfg, name, np.arange(0, min(lin.act.M, 256))))
+    say("rotate graph", cfg, name, bits)
+    c0, n0 = q.rotate_quantize(x, lin.seed, bits)
+    torch.cuda.synchronize()
+    rc, rn = c0.clone(), n0.clone()
+    c, n = torch.empty_like(c0), torch.empty_like(n0)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        q.rotate_quantize(x, lin.seed, bits, out=c, norms=n)
+    for _ in range(3):
+        c.fill_(0xAB)
+        n.fill_(-1.0)
+        q.rotate_quantize(x, lin.seed, bits, out=c0, norms=n0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(c, rc) and torch.equal(n, rn)
+        assert torch.equal(c0, rc) and torch.equal(n0, rn)
