@@ -186,8 +186,9 @@ int oq_linear_ex(const uint8_t *a_codes, const float *a_norms, int a_bits,
                  int64_t M, int64_t N, int K, uint32_t flags, uint16_t *y, void *stream);
 
 /* Free every cached rotation plan and codebook table on every device (the
- * caller must ensure no enqueued work still uses them, e.g. by
- * synchronising first).  Handles from oq_plan_create stay valid to destroy
+ * caller must ensure that no enqueued work still uses them, e.g. by
+ * synchronising first, and that no other thread is inside a library call
+ * meanwhile).  Handles from oq_plan_create stay valid to destroy
  * but name no tables any more. */
 int oq_release_plans(void);
 
@@ -239,8 +240,9 @@ int oq_permute_rows(const void *src, void *dst, int64_t rows, int64_t row_bytes,
  * (pith.science Supplementary A setup) as device tables -- on first use and
  * cache it.  oq_plan_create builds it now (no first-call latency) and pins
  * it; oq_plan_destroy drops the pin and frees the tables when no other
- * handle pins them (the caller must ensure no enqueued work still uses
- * them).  A later compute call with the same (d, seed) rebuilds the plan.
+ * handle pins them (the caller must ensure that no enqueued work still
+ * uses them and that no other thread's call on the same (d, seed) is in
+ * progress).  A later compute call with the same (d, seed) rebuilds the plan.
  *   d:     128 <= d <= 16384, d % 128 == 0   (else OQ_EUNSUPPORTED)
  *   flags: 0 or OQ_ROT_NO_SIGNS (one plan serves both sign modes)
  *   plan:  receives an opaque handle (NULL on error)

@@ -358,14 +358,16 @@ void free_plan_tables(const oq::DevicePlan &p) {
     if (ptr) (void)hipFree(ptr);
 }
 
-int get_plan(int d, uint64_t seed, hipStream_t stream, const oq::DevicePlan **out) {
+// Returns a copy of the cached entry, taken under the lock: another thread's
+// oq_plan_destroy or oq_release_plans may erase the entry right after.
+int get_plan(int d, uint64_t seed, hipStream_t stream, oq::DevicePlan *out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return OQ_EDEVICE;
   std::lock_guard<std::mutex> g(g_plan_mu);
   PlanKey key{dev, d, seed};
   auto it = g_plans.find(key);
   if (it != g_plans.end()) {
-    *out = &it->second;
+    *out = it->second;
     return OQ_OK;
   }
   std::vector<int32_t> perm;
@@ -417,8 +419,8 @@ int get_plan(int d, uint64_t seed, hipStream_t stream, const oq::DevicePlan **ou
     return rc;
   }
   (void)stream;
-  auto res = g_plans.emplace(key, p);
-  *out = &res.first->second;
+  g_plans.emplace(key, p);
+  *out = p;
   return OQ_OK;
 }
 
@@ -520,7 +522,7 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
   if (n_tok == 0) return OQ_OK;  // empty input: nothing to do, pointers may be null
   if (!x || !out || !norms) return OQ_EINVAL;
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(norms, 4)) return OQ_EINVAL;
-  const oq::DevicePlan *plan = nullptr;
+  oq::DevicePlan plan;
   rc = get_plan(d, seed, (hipStream_t)stream, &plan);
   if (rc != OQ_OK) return rc;
   double lv[256], th[255];
@@ -548,13 +550,12 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
   if (rc != OQ_OK) return rc;
   if (a.dtype == OQ_BF16 && !a.rotated_out) {
     bool handled = false;
-    const uint32_t *smask = a.input_permuted ? (a.signs ? plan->fast_signs_id : plan->fast_nosigns)
-                                             : (a.signs ? plan->fast_signs : plan->fast_nosigns);
-    hipError_t e =
-        oq::launch_rotate_quantize_fast(a, plan->fast_scatter, smask, table, &handled);
+    const uint32_t *smask = a.input_permuted ? (a.signs ? plan.fast_signs_id : plan.fast_nosigns)
+                                             : (a.signs ? plan.fast_signs : plan.fast_nosigns);
+    hipError_t e = oq::launch_rotate_quantize_fast(a, plan.fast_scatter, smask, table, &handled);
     if (handled) return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
   }
-  hipError_t e = oq::launch_rotate_quantize_generic(a, *plan, t, table);
+  hipError_t e = oq::launch_rotate_quantize_generic(a, plan, t, table);
   return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
 }
 
@@ -687,11 +688,11 @@ int oq_permute_rows(const void *src, void *dst, int64_t rows, int64_t row_bytes,
                     void *stream) {
   if (!src || !dst || src == dst || row_bytes < 1 || rows <= 0) return OQ_EINVAL;
   if (rows % oq::kGroup != 0 || rows > oq::kMaxD) return OQ_EUNSUPPORTED;
-  const oq::DevicePlan *plan = nullptr;
+  oq::DevicePlan plan;
   int rc = get_plan((int)rows, seed, (hipStream_t)stream, &plan);
   if (rc != OQ_OK) return rc;
   hipError_t e =
-      oq::launch_permute_rows(src, dst, rows, row_bytes, plan->perm_inv, (hipStream_t)stream);
+      oq::launch_permute_rows(src, dst, rows, row_bytes, plan.perm_inv, (hipStream_t)stream);
   return e == hipSuccess ? OQ_OK : OQ_EDEVICE;
 }
 
@@ -711,7 +712,7 @@ int oq_plan_create(int d, uint64_t seed, uint32_t flags, void **plan) {
   if (flags & ~OQ_ROT_NO_SIGNS) return OQ_EINVAL;
   if (d <= 0) return OQ_EINVAL;
   if (d % oq::kGroup != 0 || d > oq::kMaxD) return OQ_EUNSUPPORTED;
-  const oq::DevicePlan *p = nullptr;
+  oq::DevicePlan p;
   int rc = get_plan(d, seed, nullptr, &p);
   if (rc != OQ_OK) return rc;
   int dev = 0;
