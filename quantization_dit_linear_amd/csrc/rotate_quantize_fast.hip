@@ -104,9 +104,11 @@ struct Shape {
   // d = 5120 (five 5-wave workgroups' worth of tiles, 2 resident at 3
   // waves per SIMD) runs lean instead: no prefetch registers, 4 waves per
   // SIMD, 3 workgroups per CU -- measured 6% faster there and slower at
-  // every other size
+  // every other size.  d = 4096 (about 175 registers, 2 waves per SIMD)
+  // is held to 3 waves per SIMD: a few spilled registers, 7-8% faster;
+  // the same at d = 12288 spills about 80 (18% slower without prefetch)
   static constexpr bool LEAN = D == 5120;
-  static constexpr int MIN_WAVES_PER_SIMD = LEAN ? 4 : 1;
+  static constexpr int MIN_WAVES_PER_SIMD = LEAN ? 4 : (D == 4096 ? 3 : 1);
   // register budget of the one-batch-ahead prefetch
   static constexpr bool PREFETCH = !LEAN && (TB * CPT * 4) <= (W <= 8 ? 48 : 32);
   static_assert(S <= 1024 && S >= 128, "slot size");
