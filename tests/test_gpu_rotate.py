@@ -210,3 +210,44 @@ def test_rotate_quantize_in_a_hip_graph(q, cfg, name, bits):
         torch.cuda.synchronize()
         assert torch.equal(c, rc) and torch.equal(n, rn)
         assert torch.equal(c0, rc) and torch.equal(n0, rn)
+
+
+def _rotated_basis_token(d, seed, ks, coefs):
+    """A token whose rotation is sum_j coefs[j] e_{ks[j]} (before bf16
+    rounding of x): in rotation order y = sum_j c_j H_h e_k / sqrt(h), and
+    x_{pi(i)} = D_i y_i undoes the permutation and the signs."""
+    perm, sign = oracle.plan(d, seed)
+    h = oracle.block_size(d)
+    i = np.arange(h)
+    y = np.zeros(d)
+    for k, c in zip(ks, coefs):
+        b0, kk = (k // h) * h, k % h
+        par = np.array([bin(v).count("1") & 1 for v in (i & kk)])
+        y[b0:b0 + h] += c * (1.0 - 2.0 * par) / np.sqrt(h)
+    x = np.zeros(d)
+    x[perm] = sign * y
+    return x
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("d", [1024, 2048, 3072, 4096, 5120, 12288, 13824])
+def test_rotated_basis_tokens(q, d, bits):
+    """Tokens whose energy lands on one or a few rotated coordinates, so
+    sqrt(d) z reaches +-sqrt(d), far outside the central Lloyd-Max cells:
+    the codes there must be the extreme ones, as the oracle says."""
+    seed = 31
+    h = oracle.block_size(d)
+    other = h + 1 if d > h else 1
+    rows = [([5], [1.0]), ([d - 1], [-3.0]), ([0, other], [0.8, 0.6]),
+            ([7, 9, 11], [0.9, -0.3, 0.3]), ([d // 2], [1e-3]), ([d - 2, 3], [-0.6, 0.8])]
+    x = np.stack([_rotated_basis_token(d, seed, ks, cs) for ks, cs in rows])
+    rng = np.random.default_rng(d + bits)
+    x = np.concatenate([x, rng.standard_normal((3, d))]).astype(np.float32)
+    xb = wl.f32_to_bf16_bits(x)
+    _check_rows(q, xb, wl.BF16, d, seed, bits, True, f"basis d={d} b={bits}")
+    import torch
+    codes, _ = q.rotate_quantize(to_device(xb), seed, bits)
+    torch.cuda.synchronize()
+    c = parity.unpack_codes(host(codes), d, bits)
+    top = (1 << bits) - 1
+    assert c[0, 5] == top and c[1, d - 1] == 0, "extreme coordinates take the extreme codes"
