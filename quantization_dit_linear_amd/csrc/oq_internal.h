@@ -90,8 +90,11 @@ hipError_t launch_rotate_quantize_fast(const RotateArgs &a, const uint32_t *scat
 // Device codebook table of one (bits, family, d): the fast path's cell grid
 // ({tau, base} per cell), then the 2^bits unit levels (fp32), then the
 // 2^bits - 1 unit thresholds (fp32), all as 32-bit words.  The grid is 1/8
-// of a unit over [-8, 8) up to 4 bits and 1/128 over [-5, 5) at 8 bits.
-constexpr int kFastCells = 128;
+// of a unit over [-130, 130) up to 4 bits -- every sqrt(d) z of a unit
+// vector with d <= 16384 lies inside, so a kernel needs no clamp -- and
+// 1/128 over [-5, 5) at 8 bits.
+constexpr int kFastHalfUnits = 130;
+constexpr int kFastCells = 16 * kFastHalfUnits;
 constexpr int kFastCells8 = 1280;
 constexpr __host__ __device__ int cells_for_bits(int bits) {
   return bits == 8 ? kFastCells8 : kFastCells;

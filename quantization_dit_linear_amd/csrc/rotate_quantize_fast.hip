@@ -58,18 +58,35 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kMagic = 12582912.0f;        // 1.5 * 2^23
 
-// Cell grid of a bit width: bytes of the {float tau, uint base} table, and
-// the fma scale from a unit-space value to bytes (8 bytes per cell).
-template <int BITS>
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+constexpr int isqrt_ceil(int v) {
+  int r = 0;
+  while (r * r < v) r++;
+  return r;
+}
+constexpr int pow2_ceil(int v) { return v <= 1 ? 1 : 2 * pow2_ceil((v + 1) / 2); }
+
+// Cell grid of one token length and bit width, in LDS: {float tau, uint
+// base} per 8-byte cell and the fma scale from a unit-space value to bytes.
+// Up to 4 bits the kernel takes the window of the device grid that holds
+// every possible sqrt(d) z (|sqrt(d) z| <= sqrt(d) for a unit vector, plus
+// two units of margin), so no value needs clamping; at 8 bits the grid
+// spans [-5, 5) and values beyond are clamped onto its end cells.
+template <int D, int BITS>
 struct Grid {
-  static constexpr int CELLB = 8 * cells_for_bits(BITS);
-  static constexpr float PER_UNIT = BITS == 8 ? 1024.0f : 64.0f;  // 8 / step
+  static constexpr bool CLAMP = BITS == 8;
+  static constexpr int R = CLAMP ? 0 : isqrt_ceil(D) + 2;           // half-range, units
+  static constexpr int CELLS = CLAMP ? kFastCells8 : 16 * R;       // step 1/8 up to 4 bits
+  static constexpr int FIRST = CLAMP ? 0 : kFastCells / 2 - 8 * R;  // first device cell
+  static constexpr int CELLB = 8 * CELLS;
+  static constexpr float PER_UNIT = CLAMP ? 1024.0f : 64.0f;  // 8 / step
   // offset mask: keeps every offset inside the workgroup's LDS even for a NaN
-  static constexpr uint32_t MASK = BITS == 8 ? 0x3FF8u : 0x3F8u;
-  static_assert(CELLB <= (int)MASK + 8, "mask covers the table");
+  static constexpr uint32_t MASK = (uint32_t)pow2_ceil(CELLB) - 8u;
+  static_assert(CLAMP || R <= kFastHalfUnits, "window inside the device grid");
+  static_assert(FIRST % 2 == 0, "16-byte aligned window");
 };
 
-constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
 
 constexpr int pick_waves(int wt, int ch, int maxw) {
   int best = 1;
@@ -97,7 +114,7 @@ struct Shape {
   static constexpr int CBITS = ilog2(S) - 5;          // chunk bits transformed in registers
   // LDS layout: tables first so their offsets fit instruction immediates
   static constexpr int CT_OFF = 0;                    // cell table, offsets are immediates
-  static constexpr int NP_OFF = CT_OFF + Grid<BITS>::CELLB;  // [TB][W] partial sums of squares
+  static constexpr int NP_OFF = CT_OFF + Grid<D, BITS>::CELLB;  // [TB][W] partial sums of squares
   static constexpr int LV_OFF = NP_OFF + ((TB * W * 4 + 15) / 16) * 16;  // 2^BITS unit levels
   static constexpr int YB_OFF = LV_OFF + (4 << BITS);
   static constexpr int LDS = YB_OFF + TB * D * 2;
@@ -114,6 +131,7 @@ struct Shape {
   static_assert(S <= 1024 && S >= 128, "slot size");
   static_assert(XB <= 2 && (1 << XB) <= G, "at most 4 slots per block");
   static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert((int)Grid<D, BITS>::MASK + 8 <= LDS, "masked offsets stay in the workgroup's LDS");
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -133,7 +151,8 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
     const uint32_t *__restrict__ smask, const uint32_t *__restrict__ table,
     uint8_t *__restrict__ codes, uint16_t *__restrict__ dq, float *__restrict__ norms) {
   using SH = Shape<D, BITS>;
-  constexpr int CELLB = Grid<BITS>::CELLB;
+  using GR = Grid<D, BITS>;
+  constexpr int CELLB = GR::CELLB;
   constexpr int S = SH::S, P = SH::P, TB = SH::TB, WT = SH::WT, W = SH::W, CPT = SH::CPT;
   constexpr int G = SH::G;
   // a static array: its base is a compile-time constant, so every table and
@@ -144,7 +163,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
 
   // cell table (and the levels, for fake quantization) into LDS
   for (int i = tid; i < CELLB / 16; i += W * 64)
-    ((u32x4 *)(lds + SH::CT_OFF))[i] = ((const u32x4 *)table)[i];
+    ((u32x4 *)(lds + SH::CT_OFF))[i] = ((const u32x4 *)(table + 2 * GR::FIRST))[i];
   if constexpr (DQ) {
     for (int i = tid; i < (1 << BITS); i += W * 64)
       ((uint32_t *)(lds + SH::LV_OFF))[i] = table[table_levels_word(BITS) + i];
@@ -254,7 +273,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       for (int w = 0; w < W; w++) ss += npart[tko * W + w];
       const float s = sqrtf(ss);
       const float us = (s > 0.f) ? 1.0f / (s * scale_hd) : 0.f;  // v -> sqrt(d) z
-      const float a8 = us * Grid<BITS>::PER_UNIT;                // 8 bytes per cell
+      const float a8 = us * GR::PER_UNIT;                        // 8 bytes per cell
       constexpr float m8 = kMagic + (float)(CELLB / 2);          // middle cell at u = 0
       // input side: MFMA row r = lane & 15 -> slot r>>2, chunk (r&3) of each group
       const int sig_i = 4 * q + ((lane & 15) >> 2);
@@ -332,16 +351,19 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
 #pragma unroll
           for (int i = 0; i < 4; i++) {
             const float val = v[g][w][i];
-            // byte offset 8 floor(u / step + C/2 + 1/16) of the cell, u clamped
-            // to the grid; the integer sits in the low mantissa bits of tq
-            const float tq = __builtin_amdgcn_fmed3f(__builtin_fmaf(val, a8, m8), kMagic,
-                                                     kMagic + (float)(CELLB - 1));
-            const uint32_t off = __float_as_uint(tq) & Grid<BITS>::MASK;
+            // byte offset 8 floor(u / step + C/2 + 1/16) of the cell (u clamped
+            // to the grid at 8 bits); the integer sits in the low mantissa bits
+            const float fq = __builtin_fmaf(val, a8, m8);
+            const float tq = GR::CLAMP ? __builtin_amdgcn_fmed3f(fq, kMagic, kMagic + (float)(CELLB - 1))
+                                       : fq;
+            const uint32_t off = __float_as_uint(tq) & GR::MASK;
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
             const u32x2 ent = *(const u32x2 *)(lds + SH::CT_OFF + off);  // {tau, base}
             const uint32_t code = ent[1] + (val * us >= __uint_as_float(ent[0]) ? 1u : 0u);
             if constexpr (DQ) {
-              const float lvv = *(const float *)(lds + SH::LV_OFF + 4 * code);
+              // (code masked: a u outside the window -- only from a norm
+              // that underflowed -- reads an arbitrary entry)
+              const float lvv = *(const float *)(lds + SH::LV_OFF + 4 * (code & ((1u << BITS) - 1)));
               if (tok < n_tok)
                 dq0[(g & XM) * S + (g & ~XM) * 128 + 32 * i + 16 * w] = f32_to_bf16_rne(fs * lvv);
             }
