@@ -500,11 +500,14 @@ __global__ __launch_bounds__(TL::THREADS, TL::WGS) void linear_kernel(
     // ---- epilogue.  The tile's norms go through LDS into registers
     // (activation rows, then weight rows, in the pipeline stage the last K
     // step left idle); bf16 rounding is the hardware's round to nearest
-    // even.  The bf16 tile is staged in the (now idle) decoded-tile buffers,
-    // row r at byte 2 TT r with its 8-byte column chunks XOR-swizzled by row
-    // so neither the fragment-shaped writes nor the row reads conflict, then
-    // leaves as whole 16-byte row pieces: full cache lines instead of 16
-    // rows x 32 bytes per store instruction.
+    // even.  Each wave stages its own (16 IB) x (16 JB) bf16 block in a
+    // region of the (now idle) decoded-tile buffers -- rows of 32 JB bytes
+    // (128: one cache line), 8-byte column chunks XOR-swizzled by an even
+    // row mask so neither the fragment-shaped writes nor the row reads
+    // conflict -- and writes it out as 16-byte row pieces: whole cache lines
+    // instead of 16 rows x 32 bytes per store instruction, and no
+    // workgroup barrier between staging and stores (measured 0.5-1% faster
+    // at K = 3072, 6% at K = 128, than staging the whole tile).
     float *nl = (float *)(lds + ((ke - kb) & 1) * TL::STAGEB);
     nl[is_a ? row : TT + row] = nrm;
     __syncthreads();  // norms visible; every wave is past its last MFMA read of the tiles
@@ -517,32 +520,36 @@ __global__ __launch_bounds__(TL::THREADS, TL::WGS) void linear_kernel(
     for (int j = 0; j < JB; j++)
       rn[j] = *(const floatx4 *)(nl + TT + wn * (16 * JB) + 16 * j + 4 * (lane >> 4));
     __syncthreads();  // every norm read before the staged tile overwrites them
-    constexpr int CPR = TT / 4;  // 8-byte chunks per staged row
-    auto sw = [](int r) { return (4 * r) & (CPR - 4); };
+    constexpr int WR = 16 * IB, WCB = 32 * JB, WCH = WCB / 8;  // rows, row bytes, chunks
+    static_assert((TL::THREADS / 64) * WR * WCB <= 2 * TL::STAGEB, "regions fit the idle stages");
+    uint8_t *reg = lds + wave * (WR * WCB);
+    auto swz = [](int r) { return (2 * r) & (WCH - 2); };
 #pragma unroll
     for (int i = 0; i < IB; i++) {
-      const int mr = wm * (16 * IB) + 16 * i + (lane & 15);
+      const int rr = 16 * i + (lane & 15);
       const float s = sn[i];
 #pragma unroll
       for (int j = 0; j < JB; j++) {
-        const int nr = wn * (16 * JB) + 16 * j + 4 * (lane >> 4);
+        const int ch = 4 * j + (lane >> 4);
         const floatx4 r = rn[j];
         const bf16x2 p0 = {(__bf16)(acc[j][i][0] * s * r[0]), (__bf16)(acc[j][i][1] * s * r[1])};
         const bf16x2 p1 = {(__bf16)(acc[j][i][2] * s * r[2]), (__bf16)(acc[j][i][3] * s * r[3])};
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        *(u32x2 *)(lds + 2 * TT * mr + 8 * ((nr >> 2) ^ sw(mr))) =
+        *(u32x2 *)(reg + WCB * rr + 8 * (ch ^ swz(rr))) =
             u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
       }
     }
-    __syncthreads();
-    // row pieces: thread -> (row, 16-byte piece k = columns 8k .. 8k+7)
-    constexpr int PPR = TT / 8, RPI = TL::THREADS / PPR;  // pieces per row, rows per pass
-    const int k = tid % PPR;
+    // the row reads take values other lanes of this wave wrote: wait for
+    // the wave's LDS writes (lgkmcnt(0)); no other wave touches the region
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+    constexpr int PPR = WCB / 16, RPI = 64 / PPR;  // 16-byte pieces per row, rows per pass
+    const int k = lane % PPR;
 #pragma unroll 4
-    for (int rr = tid / PPR; rr < TT; rr += RPI) {
-      const int m = m0 + rr, n = n0 + 8 * k;
+    for (int rr = lane / PPR; rr < WR; rr += RPI) {
+      const int m = m0 + wm * WR + rr, n = n0 + wn * (16 * JB) + 8 * k;
+      const u32x4 v = *(const u32x4 *)(reg + WCB * rr + 8 * ((2 * k) ^ swz(rr)));
       if (m >= M || n >= N) continue;
-      const u32x4 v = *(const u32x4 *)(lds + 2 * TT * rr + 8 * ((2 * k) ^ sw(rr)));
       uint16_t *yp = Y + (int64_t)m * N + n;
       if (vec_store && n + 7 < N) {
         *(u32x4 *)yp = v;
