@@ -36,8 +36,9 @@
 //     steps ahead into alternating registers;
 //   * epilogue: scale by s_m r_n / K (the tile's norms were loaded at tile
 //     start and pass through LDS), round once to bf16 with the hardware's
-//     round to nearest even, stage the bf16 tile in LDS (XOR-swizzled rows)
-//     and store whole rows in 16-byte pieces;
+//     round to nearest even; each wave stages its bf16 block in its own LDS
+//     region (XOR-swizzled 128-byte rows) and stores whole rows in 16-byte
+//     pieces;
 //   * persistent workgroups (one per CU); workgroup -> tile order is
 //     contiguous per XCD and grouped along M, so tiles resident together
 //     share activation rows in L2, and a tile's stores drain while the next
@@ -519,7 +520,7 @@ __global__ __launch_bounds__(TL::THREADS, TL::WGS) void linear_kernel(
 #pragma unroll
     for (int j = 0; j < JB; j++)
       rn[j] = *(const floatx4 *)(nl + TT + wn * (16 * JB) + 16 * j + 4 * (lane >> 4));
-    __syncthreads();  // every norm read before the staged tile overwrites them
+    __syncthreads();  // every norm read before the staging regions overwrite them
     constexpr int WR = 16 * IB, WCB = 32 * JB, WCH = WCB / 8;  // rows, row bytes, chunks
     static_assert((TL::THREADS / 64) * WR * WCB <= 2 * TL::STAGEB, "regions fit the idle stages");
     uint8_t *reg = lds + wave * (WR * WCB);
