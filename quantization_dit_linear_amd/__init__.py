@@ -176,13 +176,18 @@ def rotate_quantize(x, seed, bits, *, signs=True, permuted=False, sphere=False, 
     return out, norms
 
 
-def rotate(x, seed, *, signs=True, stream=None):
-    """Rotated unit vectors z (float32 [M, d], coordinate order) and norms."""
+def rotate(x, seed, *, signs=True, permuted=False, stream=None):
+    """Rotated unit vectors z (float32 [M, d], coordinate order) and norms.
+    bf16 tokens of the fast-path sizes run through the same kernel as the
+    codes; permuted=True: x's columns are already in rotation order."""
     import torch
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, d]")
     M, d = x.shape
     z = torch.empty((M, d), dtype=torch.float32, device=x.device)
     norms = torch.empty((M,), dtype=torch.float32, device=x.device)
-    flags = OQ_OUT_F32_ROTATED | (0 if signs else OQ_ROT_NO_SIGNS)
+    flags = (OQ_OUT_F32_ROTATED | (0 if signs else OQ_ROT_NO_SIGNS)
+             | (OQ_ROT_INPUT_PERMUTED if permuted else 0))
     rc = lib().oq_rotate_quantize(_dev_ptr(x, "x"), _dtype_code(x), M, d, seed, flags, 4,
                                   _dev_ptr(z, "z"), _dev_ptr(norms, "norms"), _stream(stream))
     _check(rc, "oq_rotate_quantize")

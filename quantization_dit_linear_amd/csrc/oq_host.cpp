@@ -500,6 +500,15 @@ int get_cells(int d, int bits, bool sphere, const uint32_t **out) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Byte ranges [p, p + pb) and [q, q + qb) share at least one byte.
+bool overlaps(const void *p, int64_t pb, const void *q, int64_t qb) {
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + (uintptr_t)qb && b < a + (uintptr_t)pb;
+}
+
+// Largest row count of either linear operand (tile indices stay in int).
+constexpr int64_t kMaxRows = (int64_t)1 << 30;
+
 int check_d_bits(int d, int bits) {
   if (d <= 0) return OQ_EINVAL;
   if ((bits < 2 || bits > 4) && bits != 8) return OQ_EUNSUPPORTED;
@@ -548,7 +557,7 @@ int rotate_common(const void *x, int dtype, int64_t n_tok, int d, uint64_t seed,
   const uint32_t *table = nullptr;
   rc = get_cells(d, bits, sphere, &table);
   if (rc != OQ_OK) return rc;
-  if (a.dtype == OQ_BF16 && !a.rotated_out) {
+  if (a.dtype == OQ_BF16) {
     bool handled = false;
     const uint32_t *smask = a.input_permuted ? (a.signs ? plan.fast_signs_id : plan.fast_nosigns)
                                              : (a.signs ? plan.fast_signs : plan.fast_nosigns);
@@ -626,10 +635,20 @@ int oq_linear_ex(const uint8_t *a_codes, const float *a_norms, int a_bits, const
   rc = check_d_bits(K, w_bits);
   if (rc != OQ_OK) return rc;
   if ((a_bits == 8) != (w_bits == 8)) return OQ_EUNSUPPORTED;  // W8A8 only, no mixed pair
+  if (M > kMaxRows || N > kMaxRows) return OQ_EUNSUPPORTED;
   if (M == 0 || N == 0) return OQ_OK;  // empty output: pointers may be null
   if (!a_codes || !a_norms || !w_codes || !w_norms || !y) return OQ_EINVAL;
   if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_norms, 4) ||
       !aligned(w_norms, 4) || !aligned(y, 2))
+    return OQ_EINVAL;
+  // y must not share a byte with any input: a sparse last round of tiles
+  // parks fp32 partial sums in y's first rows before the other tiles have
+  // read their codes, so an overlap would corrupt the call's own inputs
+  const int64_t y_bytes = M * N * 2;
+  if (overlaps(y, y_bytes, a_codes, M * (int64_t)K * a_bits / 8) ||
+      overlaps(y, y_bytes, a_norms, M * 4) ||
+      overlaps(y, y_bytes, w_codes, N * (int64_t)K * w_bits / 8) ||
+      overlaps(y, y_bytes, w_norms, N * 4))
     return OQ_EINVAL;
   oq::LevelsF16 la{}, lw{};
   const uint32_t *ta = nullptr, *tw = nullptr;

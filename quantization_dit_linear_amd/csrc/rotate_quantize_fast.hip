@@ -36,15 +36,19 @@
 //    a group bit in the lane, which the store addressing follows.
 //  * Quantize.  A magic-number fma turns v into the byte offset of its cell
 //    in a uniform grid over sqrt(d) z (narrower than any threshold gap:
-//    step 1/8 over [-8, 8) up to 4 bits, 1/128 over [-5, 5) at 8 bits;
-//    clamped to the grid, whose ends lie beyond every threshold); one 8-byte
-//    LDS read gives the code at the cell's lower edge and the only threshold
-//    that can fall inside the cell; one exact fp32 compare of sqrt(d) z with
-//    it settles the code.  The table (1 KB, or 10 KB at 8 bits) does not
-//    depend on the token, so it is loaded once per workgroup.
+//    step 1/8 up to 4 bits, over +-(ceil(sqrt(d)) + 2) units, which holds
+//    every value a unit vector can take, so nothing is clamped; step 1/128
+//    over [-5, 5) at 8 bits, values beyond clamped onto the end cells, which
+//    lie beyond every threshold); one 8-byte LDS read gives the code at the
+//    cell's lower edge and the only threshold that can fall inside the cell;
+//    one exact fp32 compare of sqrt(d) z with it settles the code.  The
+//    table window (4-15 KB, or 10 KB at 8 bits) does not depend on the
+//    token, so it is loaded once per workgroup.
 //  * Pack.  A lane's 8 codes per group are exactly 8 consecutive storage
 //    slots, so they pack into one b-byte word per lane (8 bytes at 8 bits).  (Fake-quantization
-//    mode instead stores bf16 s * level[code] at every coordinate.)
+//    mode instead stores bf16 s * level[code] at every coordinate, and the
+//    rotated-value mode the fp32 unit vector z itself, both in coordinate
+//    order.)
 #include <hip/hip_runtime.h>
 
 #include "oq_internal.h"
@@ -140,18 +144,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// DQ: write bf16 s * level[code] at every coordinate (dq) instead of codes.
+// What the kernel writes besides the norms.
+enum OutMode { kCodes = 0, kDequant = 1, kRotated = 2 };
+
+// MODE: kCodes packs codes; kDequant writes bf16 s * level[code] at every
+// coordinate (dq); kRotated writes the fp32 unit vector z = H_h y / (s
+// sqrt(h)) at every coordinate (zout) and skips the quantizer.
 // IDENT: the input is already in rotation order (x'_i = x_{pi(i)}); scat is
 // unused and smask holds the sign masks of the coordinates in place.
 // table: the device codebook table (cell grid, then levels).
-template <int D, int BITS, bool DQ, bool IDENT>
+template <int D, int BITS, int MODE, bool IDENT>
 __global__ __launch_bounds__((64 * Shape<D, BITS>::W))
 __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void rq_fast_kernel(
     const uint16_t *__restrict__ x, int64_t n_tok, const uint32_t *__restrict__ scat,
     const uint32_t *__restrict__ smask, const uint32_t *__restrict__ table,
-    uint8_t *__restrict__ codes, uint16_t *__restrict__ dq, float *__restrict__ norms) {
+    uint8_t *__restrict__ codes, uint16_t *__restrict__ dq, float *__restrict__ zout,
+    float *__restrict__ norms) {
   using SH = Shape<D, BITS>;
   using GR = Grid<D, BITS>;
+  constexpr bool DQ = MODE == kDequant, ZO = MODE == kRotated;
   constexpr int CELLB = GR::CELLB;
   constexpr int S = SH::S, P = SH::P, TB = SH::TB, WT = SH::WT, W = SH::W, CPT = SH::CPT;
   constexpr int G = SH::G;
@@ -162,8 +173,10 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
   float *npart = (float *)(lds + SH::NP_OFF);
 
   // cell table (and the levels, for fake quantization) into LDS
-  for (int i = tid; i < CELLB / 16; i += W * 64)
-    ((u32x4 *)(lds + SH::CT_OFF))[i] = ((const u32x4 *)(table + 2 * GR::FIRST))[i];
+  if constexpr (!ZO) {
+    for (int i = tid; i < CELLB / 16; i += W * 64)
+      ((u32x4 *)(lds + SH::CT_OFF))[i] = ((const u32x4 *)(table + 2 * GR::FIRST))[i];
+  }
   if constexpr (DQ) {
     for (int i = tid; i < (1 << BITS); i += W * 64)
       ((uint32_t *)(lds + SH::LV_OFF))[i] = table[table_levels_word(BITS) + i];
@@ -343,6 +356,21 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       // (jo + (g & XM)) S + ((g & ~XM) | (rl & XM)) 128 + 32 i + 16 w + (lane & 15)
       uint16_t *dq0 = dq + tok * D + jo * S + (rl & XM) * 128 + (lane & 15);
       const float fs = s * (1.0f / __builtin_sqrtf((float)D));  // s / sqrt(d)
+      if constexpr (ZO) {
+        // rotated values: z = v / (s sqrt(h)), same coordinates as above
+        const float zs = (s > 0.f) ? 1.0f / (s * __builtin_sqrtf((float)SH::H)) : 0.f;
+        float *z0 = zout + tok * D + jo * S + (rl & XM) * 128 + (lane & 15);
+        if (tok < n_tok) {
+#pragma unroll
+          for (int g = 0; g < G; g++)
+#pragma unroll
+            for (int w = 0; w < 2; w++)
+#pragma unroll
+              for (int i = 0; i < 4; i++)
+                z0[(g & XM) * S + (g & ~XM) * 128 + 32 * i + 16 * w] = v[g][w][i] * zs;
+        }
+        continue;  // wave-uniform: no codes in this mode
+      }
 #pragma unroll
       for (int g = 0; g < G; g++) {
         uint32_t word = 0, word1 = 0;  // word1: codes 4-7 at 8 bits
@@ -395,14 +423,12 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
   }
 }
 
-template <int D, int BITS>
+template <int D, int BITS, int MODE>
 hipError_t launch_one(const RotateArgs &a, const uint32_t *scat, const uint32_t *smask,
                       const uint32_t *table) {
   using SH = Shape<D, BITS>;
-  auto k = a.dequant_out ? (a.input_permuted ? rq_fast_kernel<D, BITS, true, true>
-                                             : rq_fast_kernel<D, BITS, true, false>)
-                         : (a.input_permuted ? rq_fast_kernel<D, BITS, false, true>
-                                             : rq_fast_kernel<D, BITS, false, false>);
+  auto k = a.input_permuted ? rq_fast_kernel<D, BITS, MODE, true>
+                            : rq_fast_kernel<D, BITS, MODE, false>;
   int dev = 0, cus = 0;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -416,21 +442,31 @@ hipError_t launch_one(const RotateArgs &a, const uint32_t *scat, const uint32_t 
   const int64_t nb = (a.n_tok + SH::TB - 1) / SH::TB;
   const int64_t want = (int64_t)(cus > 0 ? cus : 256) * per_cu;
   const int grid = (int)(nb < want ? nb : want);
-  uint8_t *codes = a.dequant_out ? nullptr : (uint8_t *)a.out;
-  uint16_t *dq = a.dequant_out ? (uint16_t *)a.out : nullptr;
+  uint8_t *codes = MODE == kCodes ? (uint8_t *)a.out : nullptr;
+  uint16_t *dq = MODE == kDequant ? (uint16_t *)a.out : nullptr;
+  float *zout = MODE == kRotated ? (float *)a.out : nullptr;
   hipLaunchKernelGGL(k, dim3(grid), dim3(64 * SH::W), 0, a.stream, (const uint16_t *)a.x,
-                     a.n_tok, scat, smask, table, codes, dq, a.norms);
+                     a.n_tok, scat, smask, table, codes, dq, zout, a.norms);
   return hipGetLastError();
+}
+
+template <int D, int BITS>
+hipError_t launch_mode(const RotateArgs &a, const uint32_t *scat, const uint32_t *smask,
+                       const uint32_t *table) {
+  return a.dequant_out ? launch_one<D, BITS, kDequant>(a, scat, smask, table)
+                       : launch_one<D, BITS, kCodes>(a, scat, smask, table);
 }
 
 template <int D>
 hipError_t launch_d(const RotateArgs &a, const uint32_t *scat, const uint32_t *smask,
                     const uint32_t *table) {
+  // rotated values do not depend on the bit width: one instantiation
+  if (a.rotated_out) return launch_one<D, 4, kRotated>(a, scat, smask, table);
   switch (a.bits) {
-    case 2: return launch_one<D, 2>(a, scat, smask, table);
-    case 3: return launch_one<D, 3>(a, scat, smask, table);
-    case 8: return launch_one<D, 8>(a, scat, smask, table);
-    default: return launch_one<D, 4>(a, scat, smask, table);
+    case 2: return launch_mode<D, 2>(a, scat, smask, table);
+    case 3: return launch_mode<D, 3>(a, scat, smask, table);
+    case 8: return launch_mode<D, 8>(a, scat, smask, table);
+    default: return launch_mode<D, 4>(a, scat, smask, table);
   }
 }
 
@@ -440,7 +476,7 @@ hipError_t launch_rotate_quantize_fast(const RotateArgs &a, const uint32_t *scat
                                        const uint32_t *smask, const uint32_t *table,
                                        bool *handled) {
   *handled = false;
-  if (a.dtype != 1 || a.rotated_out) return hipSuccess;
+  if (a.dtype != 1) return hipSuccess;
   *handled = true;
   switch (a.d) {
     case 1024: return launch_d<1024>(a, scat, smask, table);

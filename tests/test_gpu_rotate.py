@@ -137,6 +137,67 @@ def test_full_size_sampled_rows(q, cfg, name, bits):
     parity.assert_norms_match(host(norms)[rows], rn, f"{cfg}/{name}")
 
 
+# token sizes the bf16 fast kernel is built for, each at a full-size shape:
+# the workload activations where one has that size, else a custom batch of
+# outlier-laden tokens (token count not a multiple of the batch)
+FAST_FULL = [(1024, None, None), (2048, None, None), (3072, "image_qkv", "qkv"),
+             (4096, None, None), (5120, "video_block", "qkv"),
+             (12288, "image_mlp", "down"), (13824, "video_block", "down")]
+
+
+@pytest.mark.parametrize("d,cfg,name", FAST_FULL)
+def test_rotated_values_fast_kernel_full_size(q, d, cfg, name):
+    """The fp32 rotated unit vectors and norms of the bf16 fast kernel (the
+    one that makes every workload's codes) at full size, checked on a seeded
+    sample of rows against the oracle's fp64 z = H_h D Pi x / (s sqrt(h)):
+    per token ||dz|| <= 1e-5, every |dz_i| <= 1e-5 max|z|, norms to 1e-5
+    relative (pith.science, Supplementary A setup)."""
+    import torch
+    if cfg is None:
+        M, seed = 12003, 57
+        x = wl.custom_activations(M, d, wl.BF16, d + 5, n_out=max(1, d // 100),
+                                  out_factor=50.0, sigma_s=1.5, zero_rows=(M - 2,))
+    else:
+        lin = wl.get_linear(cfg, name)
+        assert lin.act.d == d
+        M, seed = lin.act.M, lin.seed
+        x = wl.activations(cfg, name)
+    say("rotated full", d, cfg, name, x.shape)
+    xd = to_device(x)
+    z, n = q.rotate(xd, seed)
+    torch.cuda.synchronize()
+    rows = wl.sample_rows(M, 64, 3)
+    if cfg is None:
+        rows = np.unique(np.concatenate([rows, [M - 2]]))  # the zero token
+    zs = host(z[torch.from_numpy(rows).cuda()])
+    ns = host(n)[rows]
+    del z
+    rc, rn, rz = oracle.rotate_quantize(x[rows], wl.BF16, d, seed, 4, want_z=True)
+    parity.assert_rotated_match(zs, rz, f"z d={d}")
+    nz = rn > 0
+    parity.assert_norms_match(ns[nz], rn[nz], f"norms d={d}")
+    assert (ns[~nz] == 0).all() and (zs[~nz] == 0).all()
+
+
+@pytest.mark.parametrize("d", [1024, 3072, 4096, 5120, 12288, 13824])
+@pytest.mark.parametrize("signs", [True, False])
+def test_rotated_values_fast_kernel_permuted_input(q, d, signs):
+    """Rotated values of input already in rotation order (the fast kernel's
+    scatter-free form): the same z as the unpermuted input, to fp32
+    rounding, and within the tolerance of the oracle."""
+    import torch
+    M, seed = 203, 77
+    x = wl.custom_activations(M, d, wl.BF16, d + 11, n_out=3, out_factor=40.0, sigma_s=1.0)
+    perm, _ = oracle.plan(d, seed)
+    say("rotated permuted", d, signs)
+    z, n = q.rotate(to_device(np.ascontiguousarray(x[:, perm])), seed, signs=signs,
+                    permuted=True)
+    torch.cuda.synchronize()
+    rc, rn, rz = oracle.rotate_quantize(x, wl.BF16, d, seed, 4, use_signs=signs, want_z=True)
+    parity.assert_rotated_match(host(z), rz, f"z permuted d={d}")
+    parity.assert_norms_match(host(n), rn, f"norms permuted d={d}")
+
+
 def test_explicit_plan_handles(q):
     """oq_plan_create / oq_plan_destroy: results are the same with a pinned
     plan, after it is freed (rebuilt lazily), and with two handles."""
