@@ -1,24 +1,27 @@
 """Benchmark of the OrbitQuant online quantized-linear path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload image_qkv]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload video_block]
 
-A step is one pass of the whole path over one batch of synthetic input
-resident in HBM: offline weight preparation of W (rotate + quantize the
-weight rows), online rotate + quantize of the activation tokens, and the
-W4A4 low-bit linear.  The codebook and rotation plan are host-side
-precomputations cached by the library after the first call (warmup).
+A step is one pass of the online path over one batch of synthetic input
+resident in HBM: rotate + quantize of the activation tokens, then the W4A4
+low-bit linear against weight codes prepared offline.  Weight preparation
+(rotate + quantize of the weight rows) runs once before the timed region,
+as it would when a layer is loaded, and is timed on its own.  The codebook
+and rotation plan are host-side precomputations cached by the library after
+the first call.
 
-Prints ONE JSON line with the throughput of the whole step (in the linear's
+Prints ONE JSON line with the throughput of the step (in the linear's
 FLOP-equivalent TFLOP/s), per-kernel rates, the roofline of the dominant
 kernel (the linear, bound by fp16 MFMA) and of rotate + quantize (bound by
-HBM), and the fp64 CPU oracle timed on a bounded sample of the same
-workload on this host's cores.
+HBM), the same step on the image-DiT QKV shape, and the fp64 CPU oracle
+timed on a bounded sample of the same workload on this host's cores.
 
-Inputs: seeded synthetic activations shaped like an image-DiT fused QKV
-projection (2 CFG branches x 4608 tokens, d = 3072 -> 9216, 1% outlier
-channels x50, per-token log-normal(0, 1.5) scale) and N(0, 0.02^2) weights,
-drawn by the `workloads` generators.  Four input buffer sets are cycled so
-the working set exceeds the 256 MB Infinity Cache.
+Inputs: seeded synthetic activations shaped like a video-DiT block's fused
+QKV projection (21 x 30 x 52 = 32760 latent tokens, d = 5120 -> 15360, 1%
+outlier channels x50, per-token log-normal(0, 2) scale) and N(0, 0.02^2)
+weights, drawn by the `workloads` generators.  Activation buffer sets are
+cycled so rotate + quantize reads its input from HBM, not the 256 MB
+Infinity Cache (the linear's 1 GB output also evicts it every step).
 
 Other modes:
     python bench.py --sweep           every workload instance and bit pair at
@@ -48,12 +51,15 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="image_qkv")
+    p.add_argument("--workload", default="video_block")
     p.add_argument("--linear", default=None, help="linear name inside the workload")
     p.add_argument("--bits", default=None, help="w,a bits (default: the workload's first pair)")
-    p.add_argument("--sets", type=int, default=4, help="input buffer sets cycled")
+    p.add_argument("--sets", type=int, default=2, help="activation buffer sets cycled")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=9216)
+    p.add_argument("--cpu-rows", type=int, default=3072,
+                   help="token rows of the oracle's sample (rotate + quantize and the linear)")
+    p.add_argument("--no-second-shape", action="store_true",
+                   help="skip the same step on the image-DiT QKV shape")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="before the steps, copy a buffer of this many MiB once (untimed), "
                         "as the known-size reference for HBM byte counters")
@@ -71,6 +77,9 @@ def parse():
     p.add_argument("--profile-bench-log", default=None,
                    help="with --summarize-profiles: output of the traced bench.py run, whose "
                         "own per-kernel event timings are compared with the trace")
+    p.add_argument("--prep-launches", type=int, default=None,
+                   help="with --summarize-profiles: leading rotate-kernel dispatches that "
+                        "prepared weights (default: what bench.py launches, 1 + 5)")
     p.add_argument("--profile-out", default=os.path.join(ROOT, "profiles"),
                    help="with --summarize-profiles: folder for the summaries and traffic.json")
     p.add_argument("--sweep", action="store_true",
@@ -140,12 +149,14 @@ def _oracle_stages(cfg, lin, bw, ba, w_rows, x_rows, lin_rows):
 
 
 def cpu_baseline(cfg, lin, bw, ba, rows_n):
-    """The fp64 oracle, as it stands, on a bounded sample: weight prep of all
-    N weight rows, rotate + quantize and the linear for `rows_n` of the M
-    token rows; the full step is extrapolated linearly in token rows.  Also
-    the per-stage rates (rotate + quantize GB/s over the same algorithmic
-    bytes as the GPU figure, linear GFLOP/s), and the same on one thread on
-    a smaller sample."""
+    """The fp64 oracle, as it stands, on a bounded sample of the same
+    workload: weight prep of all N weight rows (offline, reported on its
+    own), then rotate + quantize and the linear for a seeded sample of
+    `rows_n` of the M token rows; the online step is extrapolated linearly
+    in token rows.  Also the per-stage rates (weight prep and rotate +
+    quantize in GB/s over the same algorithmic bytes as the GPU figures,
+    the linear in GFLOP/s), and the same on one thread on a smaller
+    sample."""
     import oracle
     import workloads as wl
     M, N, K = lin.act.M, lin.weight.N, lin.act.d
@@ -158,23 +169,24 @@ def cpu_baseline(cfg, lin, bw, ba, rows_n):
                 "linear_GFLOP/s": round(2.0 * nl * N * K / tl / 1e9, 2)}
 
     nw, nx, nl, tw, tx, tl = _oracle_stages(cfg, lin, bw, ba, N, rows_n, rows_n)
-    t_step = tw + (tx + tl) * (M / nx)
+    t_step = tx * (M / nx) + tl * (M / nl)
     out = {
         "value": 2.0 * M * N * K / t_step / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": (f"weight prep of all {N} weight rows + rotate-quantize and linear of "
-                   f"{nx} of {M} token rows (seeded sample), fp64; full step "
-                   f"extrapolated linearly in token rows"),
+        "sample": (f"rotate-quantize and linear (against all {N} weight rows) of {nx} of "
+                   f"{M} token rows (seeded sample), fp64; the online step extrapolated "
+                   f"linearly in token rows; weight prep of all {N} rows timed apart"),
         "seconds_measured": round(tw + tx + tl, 3),
         "step_seconds_extrapolated": round(t_step, 3),
+        "prepare_weights_seconds": round(tw, 3),
         "stages": rates(nw, nx, nl, tw, tx, tl),
     }
     threads = oracle.num_threads()
     try:
         oracle.set_threads(1)
-        one = _oracle_stages(cfg, lin, bw, ba, min(N, 1024), min(M, 256), 16)
+        one = _oracle_stages(cfg, lin, bw, ba, min(N, 1024), min(M, 256), 8)
     finally:
         oracle.set_threads(threads)
     out["one_thread"] = dict(rates(*one), sample=(
@@ -209,21 +221,20 @@ def library_fp16_gemm(M, N, K, iters=10):
 
 
 def fake_quant_path(q, x, W, seed, ba, bw, iters=10):
-    """Context: the pages' own evaluation path on the same inputs -- both
-    operands fake-quantized to bf16 by the library (oq_rotate_quantize with
-    OQ_OUT_BF16_DEQUANT), then the vendor bf16 GEMM -- timed per step."""
+    """Context: the pages' own evaluation path on the same inputs -- the
+    weights fake-quantized offline to bf16 by the library (oq_rotate_quantize
+    with OQ_OUT_BF16_DEQUANT, then transposed once), and per step the tokens
+    fake-quantized the same way followed by the vendor bf16 GEMM."""
     import torch
     M, K = x.shape
     N = W.shape[0]
     xh = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
-    wh = torch.empty((N, K), dtype=torch.bfloat16, device=x.device)
     xn = torch.empty((M,), dtype=torch.float32, device=x.device)
-    wn = torch.empty((N,), dtype=torch.float32, device=x.device)
-    wt = torch.empty((K, N), dtype=torch.bfloat16, device=x.device)
+    wh, _ = q.fake_quantize(W, seed, bw)
+    wt = wh.t().contiguous()
+    del wh
 
     def run():
-        q.fake_quantize(W, seed, bw, out=wh, norms=wn)
-        wt.copy_(wh.t())
         q.fake_quantize(x, seed, ba, out=xh, norms=xn)
         return torch.mm(xh, wt)
 
@@ -238,37 +249,36 @@ def fake_quant_path(q, x, W, seed, ba, bw, iters=10):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters
-    return {"what": "fake-quantize W and x to bf16 (library), transpose W, vendor bf16 GEMM",
+    del wt, xh, xn
+    return {"what": "fake-quantize x to bf16 (library) and a vendor bf16 GEMM against the "
+                    "weights fake-quantized and transposed offline",
             "ms": round(ms, 4)}
 
 
 def w8a8_path(q, x, W, seed, iters=10):
-    """The same step at 8 bits on both sides (W8A8, the top of the pages'
-    bit range): weight prep, rotate + quantize to byte codes, W8A8 linear;
-    per-kernel times from events on the launch stream."""
+    """The same online step at 8 bits on both sides (W8A8, the top of the
+    pages' bit range): rotate + quantize to byte codes and the W8A8 linear
+    against weights prepared offline; per-kernel times from events on the
+    launch stream."""
     import torch
     M, K = x.shape
     N = W.shape[0]
-    wc = torch.empty((N, K), dtype=torch.uint8, device=x.device)
     ac = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-    wn = torch.empty((N,), dtype=torch.float32, device=x.device)
     an = torch.empty((M,), dtype=torch.float32, device=x.device)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    wc, wn = q.prepare_weights(W, seed, 8)
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(iters)]
 
     def run(e=None):
         if e is not None:
             e[0].record(stream)
-        q.prepare_weights(W, seed, 8, out=wc, norms=wn)
-        if e is not None:
-            e[1].record(stream)
         q.rotate_quantize(x, seed, 8, out=ac, norms=an)
         if e is not None:
-            e[2].record(stream)
+            e[1].record(stream)
         q.linear(ac, an, 8, wc, wn, 8, K, out=y)
         if e is not None:
-            e[3].record(stream)
+            e[2].record(stream)
 
     for _ in range(2):
         run()
@@ -276,13 +286,14 @@ def w8a8_path(q, x, W, seed, iters=10):
     for i in range(iters):
         run(ev[i])
     torch.cuda.synchronize()
-    t_step = float(np.median([e[0].elapsed_time(e[3]) for e in ev]))
-    t_rot = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
-    t_lin = float(np.median([e[2].elapsed_time(e[3]) for e in ev]))
+    t_step = float(np.median([e[0].elapsed_time(e[2]) for e in ev]))
+    t_rot = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    t_lin = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
     in_b = x.element_size()
     rot_gbs = M * (K * in_b + K + 4) / (t_rot * 1e-3) / 1e9
     lin_tf = 2.0 * M * N * K / (t_lin * 1e-3) / 1e12
-    return {"what": "W8A8 step on the same inputs (medians over launches)",
+    del ac, an, y, wc, wn
+    return {"what": "W8A8 online step on the same inputs (medians over launches)",
             "step_ms": round(t_step, 4),
             "linear": {"ms": round(t_lin, 4), "TFLOP/s": round(lin_tf, 1),
                        "frac_of_mfma_fp16_peak": round(lin_tf / MFMA_FP16_PEAK_TFLOPS, 4)},
@@ -379,6 +390,19 @@ def _short_kernel_name(name):
     return n.replace("void ", "").strip()
 
 
+def _split_rotate(rows, n_prep):
+    """Rotate-kernel rows of a rocprofv3 csv in dispatch order -> (weight
+    preparation rows, activation rows): the first n_prep dispatches of the
+    workload's rotate kernel prepared the weights (bench.py launches them
+    before any activation)."""
+    order = sorted(rows, key=lambda r: int(r.get("Dispatch_Id") or 0))
+    disp = sorted({int(r.get("Dispatch_Id") or i) for i, r in enumerate(order)})
+    prep_ids = set(disp[:n_prep])
+    prep = [r for i, r in enumerate(order) if int(r.get("Dispatch_Id") or i) in prep_ids]
+    act = [r for i, r in enumerate(order) if int(r.get("Dispatch_Id") or i) not in prep_ids]
+    return prep, act
+
+
 def summarize_profiles(a):
     """Write profiles/<workload>_kernel_stats.txt, _traffic.txt and the
     traffic table bench.py reads, from rocprofv3 csv output."""
@@ -391,12 +415,15 @@ def summarize_profiles(a):
     M, N, K = lin.act.M, lin.weight.N, lin.act.d
     in_b = 2 if lin.act.dtype == wl.BF16 else 4
     tag = f"{cfg}_w{bw}a{ba}"
+    n_prep = (1 + PREP_TIMED) if a.prep_launches is None else a.prep_launches
     kt_dir, f_dir, w_dir = a.summarize_profiles
 
-    def one(pattern, d):
+    def one(pattern, d, required=True):
         files = glob.glob(os.path.join(d, "**", pattern), recursive=True)
         if not files:
-            raise SystemExit(f"no {pattern} under {d}")
+            if required:
+                raise SystemExit(f"no {pattern} under {d}")
+            return None
         return files[0]
 
     rows = list(csv.DictReader(open(one("*kernel_stats.csv", kt_dir))))
@@ -408,7 +435,20 @@ def summarize_profiles(a):
     # of tiles is cut into K ranges) the pieces' kernel and their reduction
     lin_parts = [n for n, *_ in lines if n.startswith(LINEAR_KERNELS)]
     lin_name = " + ".join(lin_parts)
-    rot_name = next(n for n, *_ in lines if n.startswith("rq_"))
+    rot_name = next(n for n, *_ in lines if n.startswith(f"rq_fast_kernel<{K},")
+                    or n.startswith("rq_"))
+    # per-dispatch durations of the rotate kernel: weight preparation apart
+    trace = one("*kernel_trace.csv", kt_dir, required=False)
+    rot_act_us = rot_prep_us = None
+    if trace:
+        tr = [r for r in csv.DictReader(open(trace))
+              if _short_kernel_name(r["Kernel_Name"]) == rot_name]
+        prep, act = _split_rotate(tr, n_prep)
+        dur = lambda rs: [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
+        if act:
+            rot_act_us = float(np.mean(dur(act)))
+        if prep:
+            rot_prep_us = float(np.mean(dur(prep)))
     with open(os.path.join(a.profile_out, f"{tag}_kernel_stats.txt"), "w") as f:
         f.write(f"Kernel timing on one MI355X (gfx950), workload {cfg}/{lin.name}: {M} tokens, "
                 f"d_in {K} -> d_out {N}, W{bw}A{ba}.\nCommands (repository root on the GPU "
@@ -419,31 +459,41 @@ def summarize_profiles(a):
             f.write(f"{n[:70]:70s} {c:6d} {av:9.1f} {mn:9.1f} {mx:9.1f} {pc:6.2f}\n")
         lin_sum = sum(av for n, c, av, *_ in lines if n in lin_parts)
         f.write(f"\nlinear call = {lin_name}: {lin_sum:.1f} us per call; 2*{M}*{N}*{K} = "
-                f"{2.0 * M * N * K:.4g} flop per call\n")
-        f.write(f"{rot_name}: rows*(d*{in_b} + d*b/8 + 4) algorithmic bytes per launch "
-                f"({M} activation rows at {ba} bits, {N} weight rows at {bw} bits)\n")
+                f"{2.0 * M * N * K:.4g} flop per call -> "
+                f"{2.0 * M * N * K / (lin_sum * 1e-6) / 1e12:.1f} TFLOP/s\n")
+        rot_alg = M * (K * in_b + K * ba / 8 + 4)
+        f.write(f"{rot_name}: {M} activation rows x ({K}*{in_b} + {K}*{ba}/8 + 4) = "
+                f"{rot_alg:.4g} algorithmic bytes per launch")
+        if rot_act_us is not None:
+            f.write(f"; activation launches (all but the first {n_prep} dispatches, which "
+                    f"prepared the {N} weight rows) average {rot_act_us:.1f} us -> "
+                    f"{rot_alg / (rot_act_us * 1e-6) / 1e9:.1f} GB/s")
+            if rot_prep_us is not None:
+                f.write(f"; weight preparation {rot_prep_us:.1f} us")
+        f.write("\n")
         if a.profile_bench_log:
             line = [l for l in open(a.profile_bench_log) if l.startswith("{")][-1]
             kb = json.loads(line)["kernels"]
             f.write(f"\nAgreement: in the traced run bench.py's own HIP events (on the stream "
                     f"the kernels run on) averaged {kb['linear']['ms'] * 1e3:.1f} us per linear "
                     f"call vs {lin_sum:.1f} us of its kernels in the trace; rotate+quantize "
-                    f"{kb['rotate_quantize']['ms'] * 1e3:.1f} us (events include the gaps "
-                    f"between launches).\n")
+                    f"{kb['rotate_quantize']['ms'] * 1e3:.1f} us"
+                    + (f" vs {rot_act_us:.1f} us" if rot_act_us is not None else "")
+                    + " (events include the gaps between launches).\n")
 
     def counters(d, cname):
         per = {}
         for r in csv.DictReader(open(one("*counter_collection.csv", d))):
             if r["Counter_Name"] != cname:
                 continue
-            per.setdefault(r["Kernel_Name"], []).append(
-                (int(r["Grid_Size"]), float(r["Counter_Value"])))
+            per.setdefault(r["Kernel_Name"], []).append(r)
         return per
 
     fetch, write = counters(f_dir, "FETCH_SIZE"), counters(w_dir, "WRITE_SIZE")
 
     def calib(per):
-        copies = [v for k, vals in per.items() if "copyBuffer" in k for v in vals]
+        copies = [(int(r["Grid_Size"]), float(r["Counter_Value"]))
+                  for k, vals in per.items() if "copyBuffer" in k for r in vals]
         if not copies:
             raise SystemExit("no copy kernel in the counter run (use --calib-copy-mib)")
         return max(copies)[1]  # the largest copy: the calibration buffer
@@ -455,23 +505,22 @@ def summarize_profiles(a):
     def kib_per_call(per, prefixes):
         # every kernel of a call runs once per call: the sum of their means
         names = {_short_kernel_name(k) for k in per if _short_kernel_name(k).startswith(prefixes)}
-        return sum(float(np.mean([v for k, vs in per.items() if _short_kernel_name(k) == n
-                                  for (gsz, v) in vs])) for n in names)
+        return sum(float(np.mean([float(r["Counter_Value"]) for k, vs in per.items()
+                                  if _short_kernel_name(k) == n for r in vs])) for n in names)
+
+    def rot_act(per):
+        rs = [r for k, vs in per.items() if _short_kernel_name(k) == rot_name for r in vs]
+        return float(np.mean([float(r["Counter_Value"])
+                              for r in _split_rotate(rs, n_prep)[1]]))
 
     lin_fetch = kib_per_call(fetch, LINEAR_KERNELS) * 1024 * f_scale
     lin_write = kib_per_call(write, LINEAR_KERNELS) * 1024 * w_scale
-    # activation launches only (the weight-preparation launches have N rows)
-    rot_f = [v for k, vs in fetch.items() if _short_kernel_name(k).startswith("rq_")
-             for (g, v) in vs]
-    rot_w = [v for k, vs in write.items() if _short_kernel_name(k).startswith("rq_")
-             for (g, v) in vs]
-    rot_fetch = float(np.mean(rot_f)) * 1024 * f_scale
-    rot_write = float(np.mean(rot_w)) * 1024 * w_scale
+    rot_fetch = rot_act(fetch) * 1024 * f_scale
+    rot_write = rot_act(write) * 1024 * w_scale
     lin_alg_r = M * K * ba / 8 + N * K * bw / 8 + 4 * (M + N)
     lin_alg_w = 2 * M * N
-    rot_rows = (M + N) / 2.0  # mean over the activation and weight launches
-    rot_alg_r = rot_rows * K * in_b
-    rot_alg_w = (M * (K * ba / 8 + 4) + N * (K * bw / 8 + 4)) / 2.0
+    rot_alg_r = M * K * in_b
+    rot_alg_w = M * (K * ba / 8 + 4)
     lin_digest = src_digest("linear.hip")
     rot_digest = src_digest("rotate_quantize.hip", "rotate_quantize_fast.hip")
     table = {
@@ -484,7 +533,8 @@ def summarize_profiles(a):
                             "fetch_bytes": int(rot_fetch), "write_bytes": int(rot_write),
                             "algorithmic_read_bytes": int(rot_alg_r),
                             "algorithmic_write_bytes": int(rot_alg_w),
-                            "note": "mean over the activation and weight-preparation launches"},
+                            "note": f"activation launches only (the first {n_prep} "
+                                    f"dispatches prepared the weights)"},
         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
     # one entry per workload, so summaries of several workloads coexist
     tpath = os.path.join(a.profile_out, "traffic.json")
@@ -510,12 +560,12 @@ def summarize_profiles(a):
                     f"{e['write_bytes'] / 1e6:.1f} MB (algorithmic writes "
                     f"{e['algorithmic_write_bytes'] / 1e6:.1f} MB)\n")
     if a.profile_counters:
-        write_counter_summary(a, tag, lin_parts, rot_name, M, N, K, ba, bw, in_b)
+        write_counter_summary(a, tag, lin_parts, rot_name, M, N, K, ba, bw, in_b, n_prep)
     print(json.dumps(table))
     return 0
 
 
-def write_counter_summary(a, tag, lin_parts, rot_name, M, N, K, ba, bw, in_b):
+def write_counter_summary(a, tag, lin_parts, rot_name, M, N, K, ba, bw, in_b, n_prep):
     """Per-kernel averages of SQ/GRBM counters from rocprofv3 --pmc runs,
     with the derived rates the kernels are tuned by."""
     import csv
@@ -523,9 +573,14 @@ def write_counter_summary(a, tag, lin_parts, rot_name, M, N, K, ba, bw, in_b):
     per = {}
     for d in a.profile_counters:
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            for r in csv.DictReader(open(f)):
+            rows = [r for r in csv.DictReader(open(f))
+                    if _short_kernel_name(r["Kernel_Name"]) in (*lin_parts, rot_name)]
+            rot = [r for r in rows if _short_kernel_name(r["Kernel_Name"]) == rot_name]
+            # activation launches of the rotate kernel only (weight prep apart)
+            keep = {id(r) for r in _split_rotate(rot, n_prep)[1]}
+            for r in rows:
                 k = _short_kernel_name(r["Kernel_Name"])
-                if k not in lin_parts and k != rot_name:
+                if k == rot_name and id(r) not in keep:
                     continue
                 per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
                     float(r["Counter_Value"]))
@@ -555,7 +610,7 @@ def write_counter_summary(a, tag, lin_parts, rot_name, M, N, K, ba, bw, in_b):
                 lines.append(f"  non-MFMA VALU instructions per MFMA: "
                              f"{(c['SQ_INSTS_VALU'] - c['SQ_INSTS_MFMA']) / c['SQ_INSTS_MFMA']:.2f}")
         elif k == rot_name:
-            elems = (M + N) / 2.0 * K  # mean over activation and weight launches
+            elems = float(M) * K  # activation launches
             for n in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
                       "SQ_LDS_IDX_ACTIVE"):
                 if n in c:
@@ -641,6 +696,107 @@ def sweep(q, iters=20):
     return 0
 
 
+PREP_TIMED = 5  # timed weight-preparation launches after the first one
+
+
+def online_step(q, lin, cfg, bw, ba, steps, warmup, sets, calib_copy_mib=0):
+    """Times the online step of one linear: weight codes prepared once
+    (offline; 1 + PREP_TIMED launches, the first untimed, before anything
+    else touches the rotate kernel), then `warmup` untimed and `steps` timed
+    steps of rotate + quantize (activation set i mod sets) followed by the
+    linear, with HIP events on the launch stream around each kernel and the
+    whole timed region bracketed by device synchronisations."""
+    import torch
+    import workloads as wl
+    M, N, K = lin.act.M, lin.weight.N, lin.act.d
+    x_np = wl.activations(cfg, lin.name)
+    xs = [to_dev(x_np)]
+    del x_np
+    for i in range(1, sets):
+        # distinct buffers with the same distribution: circular row shifts
+        xs.append(torch.roll(xs[0], shifts=97 * i, dims=0).contiguous())
+    W = to_dev(wl.weights(cfg, lin.name))
+    dev = xs[0].device
+    stream = torch.cuda.current_stream()
+    wc = torch.empty((N, K * bw // 8), dtype=torch.uint8, device=dev)
+    wn = torch.empty((N,), dtype=torch.float32, device=dev)
+    ac = [torch.empty((M, K * ba // 8), dtype=torch.uint8, device=dev) for _ in range(sets)]
+    an = [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(sets)]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    if calib_copy_mib > 0:  # known-size reference for the HBM byte counters
+        n = calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # offline weight preparation
+    q.prepare_weights(W, lin.seed, bw, out=wc, norms=wn)
+    torch.cuda.synchronize()
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(PREP_TIMED)]
+    for e0, e1 in pev:
+        e0.record(stream)
+        q.prepare_weights(W, lin.seed, bw, out=wc, norms=wn)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t_prep = float(np.median([e0.elapsed_time(e1) for e0, e1 in pev]))
+
+    def step(i, ev=None):
+        s = i % sets
+        if ev is not None:
+            ev[0].record(stream)
+        q.rotate_quantize(xs[s], lin.seed, ba, out=ac[s], norms=an[s])
+        if ev is not None:
+            ev[1].record(stream)
+        q.linear(ac[s], an[s], ba, wc, wn, bw, K, out=y)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        step(i, evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    r = {
+        "ms_step": total_ms / steps,
+        "t_rot": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+        "t_lin": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
+        "per_step": np.array([e[0].elapsed_time(e[2]) for e in evs]),
+        "lin_steps": np.array([e[1].elapsed_time(e[2]) for e in evs]),
+        "rot_steps": np.array([e[0].elapsed_time(e[1]) for e in evs]),
+        "t_prep": t_prep,
+        "prep_launches": 1 + PREP_TIMED,
+    }
+    r["x0"], r["W"] = xs[0], W
+    del xs[1:], ac, an, y, wc, wn
+    return r
+
+
+def step_rates(lin, bw, ba, r):
+    import workloads as wl
+    M, N, K = lin.act.M, lin.weight.N, lin.act.d
+    in_b = 2 if lin.act.dtype == wl.BF16 else 4
+    flops = 2.0 * M * N * K
+    rot_bytes = M * (K * in_b + K * ba / 8 + 4)
+    prep_bytes = N * (K * (2 if lin.weight.dtype == wl.BF16 else 4) + K * bw / 8 + 4)
+    return {"lin_tflops": flops / (r["t_lin"] * 1e-3) / 1e12,
+            "rot_gbs": rot_bytes / (r["t_rot"] * 1e-3) / 1e9,
+            "prep_gbs": prep_bytes / (r["t_prep"] * 1e-3) / 1e9,
+            "value": flops / (r["ms_step"] * 1e-3) / 1e12}
+
+
 def main():
     a = parse()
     if a.summarize_profiles:
@@ -665,92 +821,46 @@ def main():
     tag = f"{cfg}_w{bw}a{ba}"
     torch.cuda.set_device(0)
 
-    x_np = wl.activations(cfg, lin.name)
-    W_np = wl.weights(cfg, lin.name)
-    xs = [to_dev(x_np)]
-    Ws = [to_dev(W_np)]
-    for i in range(1, a.sets):
-        # distinct buffers with the same distribution: circular row shifts
-        xs.append(torch.roll(xs[0], shifts=97 * i, dims=0).contiguous())
-        Ws.append(torch.roll(Ws[0], shifts=89 * i, dims=0).contiguous())
-    dev = xs[0].device
-    wc = [torch.empty((N, K * bw // 8), dtype=torch.uint8, device=dev) for _ in range(a.sets)]
-    wn = [torch.empty((N,), dtype=torch.float32, device=dev) for _ in range(a.sets)]
-    ac = [torch.empty((M, K * ba // 8), dtype=torch.uint8, device=dev) for _ in range(a.sets)]
-    an = [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(a.sets)]
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
-        s = i % a.sets
-        if ev is not None:
-            ev[0].record(stream)
-        q.prepare_weights(Ws[s], lin.seed, bw, out=wc[s], norms=wn[s])
-        if ev is not None:
-            ev[1].record(stream)
-        q.rotate_quantize(xs[s], lin.seed, ba, out=ac[s], norms=an[s])
-        if ev is not None:
-            ev[2].record(stream)
-        q.linear(ac[s], an[s], ba, wc[s], wn[s], bw, K, out=y)
-        if ev is not None:
-            ev[3].record(stream)
-
-    if a.calib_copy_mib > 0:
-        n = a.calib_copy_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    for i in range(a.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(a.steps):
-        step(i, evs[i])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / a.steps
-    t_prep = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    t_rot = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    t_lin = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    per_step = np.array([e[0].elapsed_time(e[3]) for e in evs])
-    lin_steps = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    r = online_step(q, lin, cfg, bw, ba, a.steps, a.warmup, a.sets, a.calib_copy_mib)
+    rt = step_rates(lin, bw, ba, r)
+    x0, W0 = r.pop("x0"), r.pop("W")
     ref_gemm = None if a.no_ref_gemm else library_fp16_gemm(M, N, K)
-    fq_path = None if a.no_ref_gemm else fake_quant_path(q, xs[0], Ws[0], lin.seed, ba, bw)
+    fq_path = None if a.no_ref_gemm else fake_quant_path(q, x0, W0, lin.seed, ba, bw)
+    w8 = None if a.no_ref_gemm else w8a8_path(q, x0, W0, lin.seed)
     adaln = None if a.no_ref_gemm else adaln_rtn4(q, "image" if K == 3072 else "video")
     ceil = None if a.no_ref_gemm else measured_ceilings(q)
-    w8 = None if a.no_ref_gemm else w8a8_path(q, xs[0], Ws[0], lin.seed)
-
-    flops = 2.0 * M * N * K
-    in_b = 2 if lin.act.dtype == wl.BF16 else 4
-    rot_bytes = M * (K * in_b + K * ba / 8 + 4)
-    prep_bytes = N * (K * (2 if lin.weight.dtype == wl.BF16 else 4) + K * bw / 8 + 4)
-    lin_tflops = flops / (t_lin * 1e-3) / 1e12
-    rot_gbs = rot_bytes / (t_rot * 1e-3) / 1e9
-    prep_gbs = prep_bytes / (t_prep * 1e-3) / 1e9
+    del x0, W0
+    torch.cuda.empty_cache()
+    second = None
+    if not a.no_second_shape and cfg != "image_qkv":
+        l2 = wl.CONFIGS["image_qkv"]["linears"][0]
+        r2 = online_step(q, l2, "image_qkv", 4, 4, max(a.steps, 20), max(a.warmup, 3), 4)
+        r2.pop("x0"), r2.pop("W")
+        rt2 = step_rates(l2, 4, 4, r2)
+        second = {
+            "workload": f"image_qkv/qkv: {l2.act.M} tokens, d_in {l2.act.d} -> d_out "
+                        f"{l2.weight.N}, W4A4, activations bf16 (4 activation sets)",
+            "ms_per_step": round(r2["ms_step"], 4), "value": round(rt2["value"], 3),
+            "linear": {"ms": round(r2["t_lin"], 4), "TFLOP/s": round(rt2["lin_tflops"], 2),
+                       "frac_of_mfma_fp16_peak": round(rt2["lin_tflops"] / MFMA_FP16_PEAK_TFLOPS,
+                                                       4)},
+            "rotate_quantize": {"ms": round(r2["t_rot"], 4), "GB/s": round(rt2["rot_gbs"], 1),
+                                "frac_of_hbm_peak": round(rt2["rot_gbs"] / HBM_PEAK_GBS, 4)},
+            "prepare_weights": {"ms": round(r2["t_prep"], 4), "GB/s": round(rt2["prep_gbs"], 1)},
+        }
+        torch.cuda.empty_cache()
 
     lin_digest = src_digest("linear.hip")
-    rot_digest = src_digest("rotate_quantize.hip", "rotate_quantize_fast.hip") if os.path.exists(
-        os.path.join(ROOT, "quantization_dit_linear_amd", "csrc", "rotate_quantize_fast.hip")) \
-        else src_digest("rotate_quantize.hip")
-
+    rot_digest = src_digest("rotate_quantize.hip", "rotate_quantize_fast.hip")
+    lin_tflops, rot_gbs, prep_gbs = rt["lin_tflops"], rt["rot_gbs"], rt["prep_gbs"]
     out = {
         "metric": "rotate+quant GB/s and W4A4 linear TFLOP/s, as % of HBM / MFMA peak",
-        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "value": round(rt["value"], 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(r["ms_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -760,20 +870,26 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg}/{lin.name}: {M} tokens, d_in {K} -> d_out {N}, "
                                f"W{bw}A{ba}, activations "
-                               f"{'bf16' if lin.act.dtype == wl.BF16 else 'fp32'}",
+                               f"{'bf16' if lin.act.dtype == wl.BF16 else 'fp32'}; step = "
+                               f"rotate+quantize + linear, weights prepared offline",
                    "M": M, "N": N, "K": K, "w_bits": bw, "a_bits": ba},
-        "step_ms_median": round(float(np.median(per_step)), 4),
-        "step_ms_iqr": [round(float(np.percentile(per_step, 25)), 4),
-                        round(float(np.percentile(per_step, 75)), 4)],
+        "step_ms_median": round(float(np.median(r["per_step"])), 4),
+        "step_ms_iqr": [round(float(np.percentile(r["per_step"], 25)), 4),
+                        round(float(np.percentile(r["per_step"], 75)), 4)],
         "kernels": {
-            "linear": {"ms": round(t_lin, 4), "TFLOP/s": round(lin_tflops, 2),
-                       "ms_median": round(float(np.median(lin_steps)), 4),
+            "linear": {"ms": round(r["t_lin"], 4), "TFLOP/s": round(lin_tflops, 2),
+                       "ms_median": round(float(np.median(r["lin_steps"])), 4),
                        "frac_of_mfma_fp16_peak": round(lin_tflops / MFMA_FP16_PEAK_TFLOPS, 4)},
-            "rotate_quantize": {"ms": round(t_rot, 4), "GB/s": round(rot_gbs, 1),
+            "rotate_quantize": {"ms": round(r["t_rot"], 4), "GB/s": round(rot_gbs, 1),
+                                "ms_median": round(float(np.median(r["rot_steps"])), 4),
                                 "frac_of_hbm_peak": round(rot_gbs / HBM_PEAK_GBS, 4)},
-            "prepare_weights": {"ms": round(t_prep, 4), "GB/s": round(prep_gbs, 1),
-                                "frac_of_hbm_peak": round(prep_gbs / HBM_PEAK_GBS, 4)},
         },
+        "prepare_weights": {"what": "offline, once per layer: not in the step; median of "
+                                    f"{PREP_TIMED} launches",
+                            "ms": round(r["t_prep"], 4), "GB/s": round(prep_gbs, 1),
+                            "frac_of_hbm_peak": round(prep_gbs / HBM_PEAK_GBS, 4),
+                            "launches": r["prep_launches"],
+                            "step_ms_with_it": round(r["ms_step"] + r["t_prep"], 4)},
         "roofline": {"bound": "mfma", "achieved": round(lin_tflops, 2),
                      "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(lin_tflops / MFMA_FP16_PEAK_TFLOPS, 4),
@@ -784,9 +900,11 @@ def main():
                                      "traffic": stored_traffic(tag, "rotate_quantize",
                                                                rot_digest)},
     }
+    if second is not None:
+        out["image_qkv"] = second
     if ref_gemm is not None:
         out["reference_fp16_gemm"] = dict(ref_gemm, linear_over_reference=round(
-            ref_gemm["ms"] / t_lin, 3))
+            ref_gemm["ms"] / r["t_lin"], 3))
     if adaln is not None:
         out["adaln_rtn4"] = adaln
     if ceil is not None:
@@ -797,7 +915,7 @@ def main():
         out["w8a8"] = w8
     if fq_path is not None:
         out["fake_quant_path"] = dict(fq_path, native_step_speedup=round(
-            fq_path["ms"] / ms_step, 3))
+            fq_path["ms"] / r["ms_step"], 3))
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, lin, bw, ba, a.cpu_rows)
     print(json.dumps(out), flush=True)

@@ -3,6 +3,7 @@
 Every HIP source is compiled with packed-fp32 instruction selection turned
 off (no v_pk_{add,mul,fma}_f32 in the output).
 """
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -42,12 +43,14 @@ def build(verbose: bool = False, extra=()) -> str:
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
               "-Wall", "-Wno-unused-function",
               "-I", os.path.join(ROOT, "include"), "-I", CSRC, *extra]
-    objs = []
-    for s in SOURCES:
-        src = os.path.join(CSRC, s)
-        obj = os.path.join(BUILD_DIR, s + ".o")
-        _run(common + PER_SOURCE.get(s, []) + ["-c", src, "-o", obj], verbose)
-        objs.append(obj)
+    objs = [os.path.join(BUILD_DIR, s + ".o") for s in SOURCES]
+    cmds = [common + PER_SOURCE.get(s, []) + ["-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
+    # the sources compile independently: one hipcc per source, in parallel
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "8"))))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", OUT + ".tmp"],
          verbose)
     os.replace(OUT + ".tmp", OUT)

@@ -30,11 +30,15 @@ def _write(path, header, rows):
 
 
 def _counters(path, name, per_kernel):
+    """One row per dispatch; dispatch ids follow the listing order."""
     rows = []
+    did = 0
     for kernel, values in per_kernel.items():
         for v in values:
-            rows.append([kernel, name, float(v), 1024])
-    _write(path, ["Kernel_Name", "Counter_Name", "Counter_Value", "Grid_Size"], rows)
+            did += 1
+            rows.append([did, kernel, name, float(v), 1024])
+    _write(path, ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Grid_Size"],
+           rows)
 
 
 @pytest.fixture
@@ -48,14 +52,20 @@ def runs(tmp_path):
             [LIN_SMALL, 12, 240000.0, 20000.0, 3.0, 19000.0, 21000.0, 1.0],
             [REDUCE, 12, 96000.0, 8000.0, 1.0, 7000.0, 9000.0, 1.0],
             [COPY, 9, 30000.0, 3333.0, 0.4, 2000.0, 5000.0, 1.0]])
+    # per-dispatch trace of the rotate kernel: one weight-preparation launch
+    # (30 us) first, then activation launches of 25 and 27 us
+    _write(str(kt / "kt_kernel_trace.csv"),
+           ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+           [[5, ROT, 1000, 31000], [9, ROT, 50000, 75000], [12, ROT, 90000, 117000],
+            [7, LIN_BIG, 40000, 45000]])
     # KiB per dispatch; the 1 GiB calibration copy reads 524288 and writes
     # 1048576, so the scales are 2.0 and 1.0
     _counters(str(tmp_path / "f" / "f_counter_collection.csv"), "FETCH_SIZE",
               {COPY: [1.0, 524288.0], LIN_BIG: [100000.0, 100000.0], LIN_SMALL: [8000.0],
-               REDUCE: [16000.0], ROT: [27000.0, 29000.0]})
+               REDUCE: [16000.0], ROT: [27000.0, 29000.0, 30000.0]})
     _counters(str(tmp_path / "w" / "w_counter_collection.csv"), "WRITE_SIZE",
               {COPY: [1.0, 1048576.0], LIN_BIG: [170000.0], LIN_SMALL: [16000.0],
-               REDUCE: [2000.0], ROT: [7000.0]})
+               REDUCE: [2000.0], ROT: [9000.0, 7000.0]})
     _counters(str(tmp_path / "s" / "s_counter_collection.csv"), "SQ_INSTS_MFMA",
               {LIN_BIG: [3.0e7], LIN_SMALL: [1.5e6], REDUCE: [0.0]})
     out = tmp_path / "out"
@@ -67,7 +77,8 @@ def runs(tmp_path):
 
 
 def _summarize(tmp_path, monkeypatch):
-    argv = ["bench.py", "--summarize-profiles", str(tmp_path / "kt"), str(tmp_path / "f"),
+    argv = ["bench.py", "--workload", "image_qkv", "--prep-launches", "1",
+            "--summarize-profiles", str(tmp_path / "kt"), str(tmp_path / "f"),
             str(tmp_path / "w"), "--profile-counters", str(tmp_path / "s"),
             "--profile-out", str(tmp_path / "out"), "--profile-command", "cmd"]
     monkeypatch.setattr(sys, "argv", argv)
@@ -93,12 +104,21 @@ def test_traffic_per_call_and_scaling(runs, monkeypatch):
     assert lin["bytes_per_launch"] == lin["fetch_bytes"] + lin["write_bytes"]
     assert lin["source_digest"] == bench.src_digest("linear.hip")
     rot = e["rotate_quantize"]
-    assert rot["fetch_bytes"] == int(28000 * 1024 * 2.0)
+    # the first dispatch prepared the weights: activation launches only
+    assert rot["fetch_bytes"] == int(29500 * 1024 * 2.0)
+    assert rot["write_bytes"] == int(7000 * 1024 * 1.0)
+    assert rot["algorithmic_read_bytes"] == 9216 * 3072 * 2
     # algorithmic bytes of the workload: codes and norms in, bf16 out
     M = N = 9216
     K = 3072
     assert lin["algorithmic_read_bytes"] == M * K // 2 + N * K // 2 + 4 * (M + N)
     assert lin["algorithmic_write_bytes"] == 2 * M * N
+
+
+def test_rotate_time_excludes_weight_preparation(runs, monkeypatch):
+    _summarize(runs, monkeypatch)
+    txt = (runs / "out" / "image_qkv_w4a4_kernel_stats.txt").read_text()
+    assert "average 26.0 us" in txt and "weight preparation 30.0 us" in txt
 
 
 def test_mfma_count_sums_the_call(runs, monkeypatch):
