@@ -163,15 +163,17 @@ int oq_prepare_weights(const void *W, int dtype, int64_t n_out, int d_in, uint64
  *   a_codes [M][K*a_bits/8], a_norms [M], w_codes [N][K*w_bits/8],
  *   w_norms [N]: device, as produced by oq_rotate_quantize /
  *   oq_prepare_weights with the same seed, flags and K
- *   y: device bf16 bit patterns, [M][N] row-major, 2-byte aligned; it must
- *      not overlap the inputs.  Until the call completes on the stream, y
+ *   y: device bf16 bit patterns, [M][N] row-major, 2-byte aligned; a y
+ *      that shares a byte with any of the four inputs is rejected
+ *      (OQ_EINVAL).  Until the call completes on the stream, y
  *      may hold intermediate values (a sparse last round of output tiles
  *      parks fp32 partial sums in y's first rows, which are then
  *      overwritten), so nothing may read it concurrently.
  * a_bits, w_bits in {2, 3, 4}, any pair, or both 8 (W8A8: the codes are
  * decoded through an fp16 table of the 256 levels; a pair with only one
- * side at 8 bits is OQ_EUNSUPPORTED).  M = 0 or N = 0 is a no-op that succeeds
- * (the pointers may then be NULL).  Errors:
+ * side at 8 bits is OQ_EUNSUPPORTED).  M and N up to 2^30 (OQ_EUNSUPPORTED
+ * beyond).  M = 0 or N = 0 is a no-op that succeeds (the pointers may then
+ * be NULL).  Errors:
  * OQ_EINVAL, OQ_EUNSUPPORTED, OQ_EDEVICE. */
 int oq_linear(const uint8_t *a_codes, const float *a_norms, int a_bits,
               const uint8_t *w_codes, const float *w_norms, int w_bits,

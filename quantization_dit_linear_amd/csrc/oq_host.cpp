@@ -375,10 +375,14 @@ int get_plan(int d, uint64_t seed, hipStream_t stream, oq::DevicePlan *out) {
   build_plan(d, seed, perm, neg);
   std::vector<int32_t> sc(d), sc0(d), sid(d);
   std::vector<uint32_t> fsc(d), fsg(d / 2), fz(d / 2, 0u), fsid(d / 2);
+  // fast path: slots of min(h, 1024) coordinates, each followed by 8
+  // elements of padding in the kernel's LDS copy of a token
+  const int slot = oq::fast_slot(d);
   for (int i = 0; i < d; i++) {
     sc[perm[i]] = i | (neg[i] ? (int32_t)0x80000000 : 0);
     sc0[perm[i]] = i;
-    fsc[perm[i]] = 2u * (uint32_t)i;  // source j = pi(i) goes to byte 2i
+    // source j = pi(i) goes to element i of the padded copy
+    fsc[perm[i]] = 2u * (uint32_t)(i + 8 * (i / slot));
     sid[i] = i | (neg[i] ? (int32_t)0x80000000 : 0);
   }
   for (int j = 0; j < d; j += 2) {

@@ -92,6 +92,23 @@ struct Grid {
 
 
 
+// Per token size d, measured on MI355X (32760 x 5120, 9216 x 12288, 65536 x
+// 3072, 16384 x 4096 tokens):
+//  * mfma_group_bits: group bits of a slot (coordinate bits 7 .. 7+MB-1)
+//    transformed on the matrix cores together with the five in-chunk bits:
+//    the MFMA then applies a 2^(5+MB)-point Hadamard (the H_32 operand and
+//    the +-1 signs of H_(2^MB) over 2^MB accumulated k-blocks), 2^(2MB+1)
+//    MFMAs per 16 x 2^(5+MB) block instead of MB register butterfly stages.
+//    One bit: 8-10% faster at d = 12288 and 5120, equal at 1024, 3072 and
+//    13824, 12% slower at 4096 (more MFMA chains than the register stages
+//    they replace); two or three bits were slower everywhere.
+//  * d = 5120 runs 512-coordinate slots (one permlane stage joins the two
+//    halves of each 1024 block) so that a batch of two tokens still tiles
+//    the five waves: half the staging registers, which leaves room for the
+//    one-batch-ahead prefetch at 4 waves per SIMD (5% faster than four
+//    tokens of 1024-coordinate slots without prefetch).
+constexpr int mfma_group_bits(int d) { return (d == 2048 || d == 4096) ? 0 : 1; }
+
 constexpr int pick_waves(int wt, int ch, int maxw) {
   int best = 1;
   for (int w = 1; w <= maxw; w++)
@@ -103,11 +120,11 @@ constexpr int pick_waves(int wt, int ch, int maxw) {
 template <int D, int BITS>
 struct Shape {
   static constexpr int H = D & -D;                    // Hadamard block
-  static constexpr int S = H < 1024 ? H : 1024;       // slot: a block, or 1024 of one
+  static constexpr int S = fast_slot(D);              // slot: a block, or 1024 (512) of one
   static constexpr int XB = ilog2(H / S);             // butterfly stages across slots
   static constexpr int P = D / S;                     // slots per token
   // tokens per batch: 4, or 2 for long tokens when the slots still tile
-  static constexpr int TB = (D * 2 * 4 > 64 * 1024 && (2 * P) % 4 == 0) ? 2 : 4;
+  static constexpr int TB = ((D * 2 * 4 > 64 * 1024 || D == 5120) && (2 * P) % 4 == 0) ? 2 : 4;
   static constexpr int WT = TB * P / 4;               // wave tiles per batch
   static constexpr int CH = D / 512;                  // 8-element chunks per token per 64 threads
   // waves per workgroup: divide both the wave tiles and the staging chunks;
@@ -115,23 +132,30 @@ struct Shape {
   static constexpr int W = pick_waves(WT, CH, XB > 0 ? 8 : 16);
   static constexpr int CPT = CH / W;                  // chunks per thread per token
   static constexpr int G = S / 128;                   // 128-coordinate groups per slot
-  static constexpr int CBITS = ilog2(S) - 5;          // chunk bits transformed in registers
+  static constexpr int CBITS = ilog2(S) - 5;          // chunk bits (above the 32-element chunk)
+  // group bits (coordinate bits 7 .. 7+MB-1) transformed on the matrix cores
+  // together with the five in-chunk bits; the other chunk bits are register
+  // butterflies
+  static constexpr int MB = mfma_group_bits(D) < ilog2(G) ? mfma_group_bits(D) : ilog2(G);
+  // a slot takes SP elements of LDS: 8 of padding shift the next slot by one
+  // 16-byte bank group, so the 16 operand rows of an MFMA (4 slots x 4
+  // chunks) fall on 16 different bank groups
+  static constexpr int SP = S + 8;
+  static constexpr int TOKB = P * SP * 2;             // bytes per token in LDS
   // LDS layout: tables first so their offsets fit instruction immediates
   static constexpr int CT_OFF = 0;                    // cell table, offsets are immediates
   static constexpr int NP_OFF = CT_OFF + Grid<D, BITS>::CELLB;  // [TB][W] partial sums of squares
   static constexpr int LV_OFF = NP_OFF + ((TB * W * 4 + 15) / 16) * 16;  // 2^BITS unit levels
   static constexpr int YB_OFF = LV_OFF + (4 << BITS);
-  static constexpr int LDS = YB_OFF + TB * D * 2;
-  // d = 5120 (five 5-wave workgroups' worth of tiles, 2 resident at 3
-  // waves per SIMD) runs lean instead: no prefetch registers, 4 waves per
-  // SIMD, 3 workgroups per CU -- measured 6% faster there and slower at
-  // every other size.  d = 4096 (about 175 registers, 2 waves per SIMD)
-  // is held to 3 waves per SIMD: a few spilled registers, 7-8% faster;
-  // the same at d = 12288 spills about 80 (18% slower without prefetch)
-  static constexpr bool LEAN = D == 5120;
-  static constexpr int MIN_WAVES_PER_SIMD = LEAN ? 4 : (D == 4096 ? 3 : 1);
+  static constexpr int LDS = YB_OFF + TB * TOKB;
+  // register target (waves per SIMD): d = 5120 (two tokens of 512-coordinate
+  // slots, about 126 registers) is held to 4, three 5-wave workgroups per
+  // CU; d = 4096 (about 175 registers, 2 waves per SIMD) to 3: a few
+  // spilled registers, 7-8% faster; the same at d = 12288 spills about 80
+  // (18% slower without prefetch)
+  static constexpr int MIN_WAVES_PER_SIMD = D == 5120 ? 4 : (D == 4096 ? 3 : 1);
   // register budget of the one-batch-ahead prefetch
-  static constexpr bool PREFETCH = !LEAN && (TB * CPT * 4) <= (W <= 8 ? 48 : 32);
+  static constexpr bool PREFETCH = (TB * CPT * 4) <= (W <= 8 ? 48 : 32);
   static_assert(S <= 1024 && S >= 128, "slot size");
   static_assert(XB <= 2 && (1 << XB) <= G, "at most 4 slots per block");
   static_assert(LDS <= 160 * 1024, "LDS");
@@ -197,12 +221,16 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
   (void)saddr;
 
   // H_32 operands: lane holds H[k][n] for k = 8(lane>>4)+e, n = lane&15 (+16)
-  bf16x8 hb0, hb1;
+  // (nhb: the same negated, for the -1 entries of H_(2^MB))
+  bf16x8 hb0, hb1, nhb0, nhb1;
 #pragma unroll
   for (int e = 0; e < 8; e++) {
     const int k = 8 * (lane >> 4) + e, n = lane & 15;
-    hb0[e] = (__builtin_popcount(k & n) & 1) ? (__bf16)-1.0f : (__bf16)1.0f;
-    hb1[e] = (__builtin_popcount(k & (n + 16)) & 1) ? (__bf16)-1.0f : (__bf16)1.0f;
+    const bool n0 = __builtin_popcount(k & n) & 1, n1 = __builtin_popcount(k & (n + 16)) & 1;
+    hb0[e] = n0 ? (__bf16)-1.0f : (__bf16)1.0f;
+    hb1[e] = n1 ? (__bf16)-1.0f : (__bf16)1.0f;
+    nhb0[e] = n0 ? (__bf16)1.0f : (__bf16)-1.0f;
+    nhb1[e] = n1 ? (__bf16)1.0f : (__bf16)-1.0f;
   }
   const float scale_hd = sqrtf((float)SH::H / (float)D);  // v-space threshold = tau s sqrt(h/d)
   constexpr int64_t row_bytes = (int64_t)D * BITS / 8;
@@ -230,13 +258,15 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
 #pragma unroll
     for (int tk = 0; tk < TB; tk++) {
       floatx4 gram = {0.f, 0.f, 0.f, 0.f};
-      uint8_t *yb = lds + SH::YB_OFF + tk * D * 2;
+      uint8_t *yb = lds + SH::YB_OFF + tk * SH::TOKB;
 #pragma unroll
       for (int c = 0; c < CPT; c++) {
         const bf16x8 xv = __builtin_bit_cast(bf16x8, stg[tk][c]);
         gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, xv, gram, 0, 0, 0);
         if constexpr (IDENT) {
-          *(u32x4 *)(yb + 16 * (tid + c * W * 64)) =
+          // chunk pos of the token: slot pos / (S/8), 16 bytes of padding per slot
+          const int pos = tid + c * W * 64;
+          *(u32x4 *)(yb + 16 * (pos + pos / (S / 8))) =
               u32x4{stg[tk][c][0] ^ smk[c][0], stg[tk][c][1] ^ smk[c][1],
                     stg[tk][c][2] ^ smk[c][2], stg[tk][c][3] ^ smk[c][3]};
         } else {
@@ -291,25 +321,56 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       // input side: MFMA row r = lane & 15 -> slot r>>2, chunk (r&3) of each group
       const int sig_i = 4 * q + ((lane & 15) >> 2);
       const int tki = sig_i / P, ji = sig_i - tki * P;
-      const uint8_t *ya = lds + SH::YB_OFF + tki * D * 2 +
-                          2 * (ji * S + 32 * (lane & 3) + 8 * (lane >> 4));
+      const uint8_t *ya = lds + SH::YB_OFF + tki * SH::TOKB +
+                          2 * (ji * SH::SP + 32 * (lane & 3) + 8 * (lane >> 4));
 
+      // Matrix cores: MFMA row r = (slot r>>2, chunk (r&3) of a group), k =
+      // the 32 elements of the chunk.  Accumulating the k-blocks of GA
+      // consecutive groups with the signs of H_GA applies the Hadamard over
+      // the in-chunk bits and the low MB group bits at once (the Sylvester
+      // matrix is a Kronecker product over the coordinate bits, so its
+      // factors can be applied in any order and any grouping).  Output
+      // block b of group block gb lands in register group gb GA + b.
+      constexpr int GA = 1 << SH::MB, GB = G / GA;
       float v[G][2][4];
 #pragma unroll
-      for (int g = 0; g < G; g++) {
-        const bf16x8 a = *(const bf16x8 *)(ya + 256 * g);
-        floatx4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hb0, c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hb1, c1, 0, 0, 0);
+      for (int gb = 0; gb < GB; gb++) {
+        floatx4 acc[GA][2];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          v[g][0][i] = c0[i];
-          v[g][1][i] = c1[i];
+        for (int b = 0; b < GA; b++) acc[b][0] = acc[b][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int a = 0; a < GA; a++) {
+          const bf16x8 av = *(const bf16x8 *)(ya + 256 * (gb * GA + a));
+#pragma unroll
+          for (int b = 0; b < GA; b++) {
+            const bool neg = __builtin_popcount(a & b) & 1;
+            acc[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, neg ? nhb0 : hb0, acc[b][0],
+                                                                0, 0, 0);
+            acc[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, neg ? nhb1 : hb1, acc[b][1],
+                                                                0, 0, 0);
+          }
         }
-      }
-      // chunk stages: chunk = 4g + i
 #pragma unroll
-      for (int bit = 0; bit < SH::CBITS; bit++) {
+        for (int b = 0; b < GA; b++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            v[gb * GA + b][0][i] = acc[b][0][i];
+            v[gb * GA + b][1][i] = acc[b][1][i];
+          }
+      }
+      // butterfly (scaling comes later: an fma(p0, us, -p1 us) would turn an
+      // exact cancellation p0 = p1 into a rounding residue of either sign,
+      // and an exact zero sits on a decision threshold)
+      auto bfly = [](float &x0, float &x1, float p0, float p1) {
+        x0 = p0 + p1;
+        x1 = p0 - p1;
+      };
+      // register stages over the chunk bits the matrix cores did not take:
+      // chunk = 4g + i, bits 0-1 are i, bits 2.. are g
+      constexpr int NCB = SH::CBITS - SH::MB;  // register chunk stages
+#pragma unroll
+      for (int st = 0; st < NCB; st++) {
+        const int bit = st < 2 ? st : st + SH::MB;
 #pragma unroll
         for (int g = 0; g < G; g++)
 #pragma unroll
@@ -317,11 +378,8 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
 #pragma unroll
             for (int i = 0; i < 4; i++) {
               const int ci = 4 * g + i, pi = ci ^ (1 << bit);
-              if (ci < pi) {
-                const float p0 = v[g][w][i], p1 = v[pi >> 2][w][pi & 3];
-                v[g][w][i] = p0 + p1;
-                v[pi >> 2][w][pi & 3] = p0 - p1;
-              }
+              if (ci < pi)
+                bfly(v[g][w][i], v[pi >> 2][w][pi & 3], v[g][w][i], v[pi >> 2][w][pi & 3]);
             }
       }
       // stages across the tile's slots: slot bit x pairs lane rows r, r ^ (1 << x)
@@ -340,9 +398,8 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
               // register; rows with bit x clear keep register g, the others g2
               const auto sw = (x == 0) ? __builtin_amdgcn_permlane16_swap(a, c, false, false)
                                        : __builtin_amdgcn_permlane32_swap(a, c, false, false);
-              const float lo = __uint_as_float(sw[0]), hi = __uint_as_float(sw[1]);
-              v[g][w][i] = lo + hi;   // slot bit x = 0
-              v[g2][w][i] = lo - hi;  // slot bit x = 1
+              // slot bit x = 0 / 1
+              bfly(v[g][w][i], v[g2][w][i], __uint_as_float(sw[0]), __uint_as_float(sw[1]));
             }
         }
       }
@@ -357,8 +414,8 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       uint16_t *dq0 = dq + tok * D + jo * S + (rl & XM) * 128 + (lane & 15);
       const float fs = s * (1.0f / __builtin_sqrtf((float)D));  // s / sqrt(d)
       if constexpr (ZO) {
-        // rotated values: z = v / (s sqrt(h)), same coordinates as above
-        const float zs = (s > 0.f) ? 1.0f / (s * __builtin_sqrtf((float)SH::H)) : 0.f;
+        // rotated values: z = v us / sqrt(d), same coordinates as above
+        const float rsd = us / __builtin_sqrtf((float)D);
         float *z0 = zout + tok * D + jo * S + (rl & XM) * 128 + (lane & 15);
         if (tok < n_tok) {
 #pragma unroll
@@ -367,7 +424,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
             for (int w = 0; w < 2; w++)
 #pragma unroll
               for (int i = 0; i < 4; i++)
-                z0[(g & XM) * S + (g & ~XM) * 128 + 32 * i + 16 * w] = v[g][w][i] * zs;
+                z0[(g & XM) * S + (g & ~XM) * 128 + 32 * i + 16 * w] = v[g][w][i] * rsd;
         }
         continue;  // wave-uniform: no codes in this mode
       }

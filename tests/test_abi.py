@@ -78,7 +78,7 @@ def test_codes_bytes(q):
 
 # Fake but aligned, non-null "device" addresses: every call below must be
 # rejected by validation before the library touches the GPU.
-A16, B16, C16 = 0x100000, 0x200000, 0x300000
+A16, B16, C16, D16 = 0x100000, 0x200000, 0x300000, 0x10000000
 
 
 @pytest.mark.parametrize("fn", ["oq_rotate_quantize", "oq_prepare_weights"])
@@ -118,7 +118,7 @@ def test_rotate_validation_rejects_before_hip(q, fn):
 
 def test_linear_validation_rejects_before_hip(q):
     f = q.lib().oq_linear
-    base = dict(a=A16, sa=C16, ba=4, w=B16, sw=C16, bw=4, M=16, N=16, K=3072, y=A16)
+    base = dict(a=A16, sa=C16, ba=4, w=B16, sw=C16 + 64, bw=4, M=16, N=16, K=3072, y=D16)
 
     def call(**kw):
         a = dict(base, **kw)
@@ -130,7 +130,9 @@ def test_linear_validation_rejects_before_hip(q):
     assert call(y=None) == q.OQ_EINVAL
     assert call(sa=None) == q.OQ_EINVAL
     assert call(a=A16 + 8) == q.OQ_EINVAL
-    assert call(y=A16 + 1) == q.OQ_EINVAL
+    assert call(y=D16 + 1) == q.OQ_EINVAL
+    assert call(M=1 << 31) == q.OQ_EUNSUPPORTED
+    assert call(N=(1 << 30) + 1) == q.OQ_EUNSUPPORTED
     assert call(M=-1) == q.OQ_EINVAL
     assert call(K=100) == q.OQ_EUNSUPPORTED
     assert call(ba=5) == q.OQ_EUNSUPPORTED
@@ -138,6 +140,29 @@ def test_linear_validation_rejects_before_hip(q):
     assert call(M=0) == q.OQ_OK
     assert call(N=0) == q.OQ_OK
     assert call(M=0, a=None, y=None) == q.OQ_OK
+
+
+def test_linear_rejects_an_output_overlapping_its_inputs(q):
+    """y [M][N] bf16 may not share a byte with a_codes [M][K b_a/8],
+    a_norms [M], w_codes [N][K b_w/8] or w_norms [N]: the call returns
+    OQ_EINVAL before any device work."""
+    f = q.lib().oq_linear
+    M, N, K = 16, 32, 3072
+    a_b, w_b, y_b = M * K // 2, N * K // 2, M * N * 2
+    A, SA, W, SW, Y = 0x1000000, 0x2000000, 0x3000000, 0x4000000, 0x5000000
+
+    def call(a=A, sa=SA, w=W, sw=SW, y=Y):
+        return f(a, sa, 4, w, sw, 4, M, N, K, y, None)
+
+    # y starting inside, ending inside, or covering each input range
+    for base, nb in ((A, a_b), (SA, 4 * M), (W, w_b), (SW, 4 * N)):
+        assert call(y=base) == q.OQ_EINVAL
+        assert call(y=base + nb - 16) == q.OQ_EINVAL
+        assert call(y=base - y_b + 16) == q.OQ_EINVAL
+    assert call(a=Y + 16) == q.OQ_EINVAL
+    assert call(sa=Y + y_b - 4) == q.OQ_EINVAL
+    assert call(w=Y) == q.OQ_EINVAL
+    assert call(sw=Y + 64) == q.OQ_EINVAL
 
 
 def test_binding_fails_loudly_without_gpu_tensors(q):
