@@ -218,17 +218,40 @@ FULL = [(cfg, lin.name, bw, ba) for cfg in wl.CONFIGS if cfg != "tiny"
         for lin in wl.CONFIGS[cfg]["linears"] for bw, ba in lin.bit_pairs]
 
 
+def _tile_spanning_rows(M, n, seed):
+    """A seeded sample of about n rows: the first and last rows, rows of
+    many 256-row tiles, and the first and last rows of the last (possibly
+    ragged) tile."""
+    last = (M - 1) // 256 * 256
+    edge = np.concatenate([np.arange(last, min(last + 4, M)), np.arange(max(M - 4, 0), M)])
+    return np.unique(np.concatenate([wl.sample_rows(M, n - 8, seed), edge])).astype(np.int64)
+
+
 @pytest.mark.parametrize("cfg,name,bw,ba", FULL)
-def test_full_size_sampled_rows(q, cfg, name, bw, ba):
+def test_full_size_library_codes(q, cfg, name, bw, ba):
+    """Every workload linear at full size, in the launch the benchmark
+    times, on the codes and norms the library itself makes from the
+    workload's x and W (Lloyd-Max cell frequencies, as in use).  The oracle
+    recomputes a seeded sample of 64 output rows spanning many tile rows and
+    the ragged last tile from those same codes: relative Frobenius error
+    <= 2e-3 and every checked element within 1e-2 of the largest."""
+    import torch
     lin = wl.get_linear(cfg, name)
     M, N, K = lin.act.M, lin.weight.N, lin.act.d
-    ac, an = wl.random_codes(M, K, ba, 31)
-    wc, wn = wl.random_codes(N, K, bw, 32)
-    say("linear full", cfg, name, M, N, K)
-    y = _run(q, ac, an, ba, wc, wn, bw, K)
-    rows = wl.sample_rows(M, 24, 2)
-    ref = oracle.linear(ac, an, ba, wc, wn, bw, K, rows=rows)
-    assert parity.rel_fro(y[rows], ref) <= parity.LINEAR_FRO
+    say("linear full (library codes)", cfg, name, M, N, K, "w", bw, "a", ba)
+    wc, wn = q.prepare_weights(to_device(wl.weights(cfg, name)), lin.seed, bw)
+    ac, an = q.rotate_quantize(to_device(wl.activations(cfg, name)), lin.seed, ba)
+    y = q.linear(ac, an, ba, wc, wn, bw, K)
+    torch.cuda.synchronize()
+    rows = _tile_spanning_rows(M, 64, 2)
+    ridx = torch.as_tensor(rows, device="cuda")
+    ys = bf16_to_np(y[ridx])
+    ac_s, an_s = host(ac[ridx]), host(an[ridx])
+    wc_h, wn_h = host(wc), host(wn)
+    del y, ac, an, wc, wn
+    ref = oracle.linear(ac_s, an_s, ba, wc_h, wn_h, bw, K)
+    assert parity.rel_fro(ys, ref) <= parity.LINEAR_FRO
+    assert np.all(np.abs(ys - ref) <= 1e-2 * np.abs(ref).max() + 1e-30)
 
 
 def test_end_to_end_tiny(q):
