@@ -28,11 +28,11 @@ constexpr int kGroup = 128;  // coordinates per storage-order group
 
 // Slot size of the bf16 fast rotate kernel for token size d: the Hadamard
 // block, at most 1024 coordinates (a block of 2048 or 4096 spans several
-// slots), 512 at d = 5120 (a batch of two tokens then tiles the kernel's
-// five waves).  The host lays out the kernel's LDS copy of a token by
-// slots, so both sides take the size from here.
+// slots), 512 at d = 5120 and 3072 (a batch of two tokens then tiles the
+// kernel's compute waves).  The host lays out the kernel's LDS copy of a
+// token by slots, so both sides take the size from here.
 constexpr __host__ __device__ int fast_slot(int d) {
-  const int h = d & -d, cap = d == 5120 ? 512 : 1024;
+  const int h = d & -d, cap = (d == 5120 || d == 3072) ? 512 : 1024;
   return h < cap ? h : cap;
 }
 

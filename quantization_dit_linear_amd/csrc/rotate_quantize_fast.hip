@@ -53,6 +53,7 @@
 
 #include "oq_internal.h"
 
+
 namespace oq {
 namespace {
 
@@ -108,6 +109,18 @@ struct Grid {
 //    one-batch-ahead prefetch at 4 waves per SIMD (5% faster than four
 //    tokens of 1024-coordinate slots without prefetch).
 constexpr int mfma_group_bits(int d) { return (d == 2048 || d == 4096) ? 0 : 1; }
+// Staging waves per workgroup (0: every wave stages and computes in turn).
+// With staging waves, W compute waves transform and quantize batch b from
+// one token buffer while the staging waves load batch b+2 and scatter
+// batch b+1 into the other, one barrier per batch: the LDS-bound scatter
+// and the VALU-bound transform run at the same time on different waves
+// instead of one after the other.  d = 5120: 130 -> 96 us for 32760 tokens
+// (two workgroups of 5 + 5 waves per CU, 70 registers); d = 3072 (512
+// slots, two tokens per batch, 3 + 3 waves, four workgroups per CU): 3-6%
+// faster, already close to the device's copy rate at 65536 tokens.  At d =
+// 12288 (one token per batch, 3 + 6 waves) it measured equal, and d = 13824
+// has no batch shape that fits two token buffers and 1024 threads.
+constexpr int staging_waves(int d) { return d == 5120 ? 5 : (d == 3072 ? 3 : 0); }
 
 constexpr int pick_waves(int wt, int ch, int maxw) {
   int best = 1;
@@ -124,13 +137,22 @@ struct Shape {
   static constexpr int XB = ilog2(H / S);             // butterfly stages across slots
   static constexpr int P = D / S;                     // slots per token
   // tokens per batch: 4, or 2 for long tokens when the slots still tile
-  static constexpr int TB = ((D * 2 * 4 > 64 * 1024 || D == 5120) && (2 * P) % 4 == 0) ? 2 : 4;
+  static constexpr int TB = ((D * 2 * 4 > 64 * 1024 || staging_waves(D)) && (2 * P) % 4 == 0) ? 2 : 4;
   static constexpr int WT = TB * P / 4;               // wave tiles per batch
   static constexpr int CH = D / 512;                  // 8-element chunks per token per 64 threads
   // waves per workgroup: divide both the wave tiles and the staging chunks;
-  // with stages across slots at most 2 waves per SIMD (register budget)
-  static constexpr int W = pick_waves(WT, CH, XB > 0 ? 8 : 16);
+  // with stages across slots at most 2 waves per SIMD (register budget);
+  // with staging waves, one compute wave per tile
+  static constexpr int W = staging_waves(D) ? WT : pick_waves(WT, CH, XB > 0 ? 8 : 16);
   static constexpr int CPT = CH / W;                  // chunks per thread per token
+  // split roles: W compute waves and WS staging waves (loads, norm partials,
+  // scatter into the other of two token buffers)
+  static constexpr int WS = staging_waves(D);
+  static constexpr bool SPLIT = WS > 0;
+  static constexpr int WTOT = W + WS;
+  static constexpr int WSTG = SPLIT ? WS : W;          // waves that stage
+  static constexpr int CPTS = CH / WSTG;               // staged chunks per thread per token
+  static constexpr int NBUF = SPLIT ? 2 : 1;
   static constexpr int G = S / 128;                   // 128-coordinate groups per slot
   static constexpr int CBITS = ilog2(S) - 5;          // chunk bits (above the 32-element chunk)
   // group bits (coordinate bits 7 .. 7+MB-1) transformed on the matrix cores
@@ -144,18 +166,17 @@ struct Shape {
   static constexpr int TOKB = P * SP * 2;             // bytes per token in LDS
   // LDS layout: tables first so their offsets fit instruction immediates
   static constexpr int CT_OFF = 0;                    // cell table, offsets are immediates
-  static constexpr int NP_OFF = CT_OFF + Grid<D, BITS>::CELLB;  // [TB][W] partial sums of squares
-  static constexpr int LV_OFF = NP_OFF + ((TB * W * 4 + 15) / 16) * 16;  // 2^BITS unit levels
+  static constexpr int NP_OFF = CT_OFF + Grid<D, BITS>::CELLB;  // [NBUF][TB][WSTG] sums of squares
+  static constexpr int LV_OFF = NP_OFF + ((NBUF * TB * WSTG * 4 + 15) / 16) * 16;  // unit levels
   static constexpr int YB_OFF = LV_OFF + (4 << BITS);
-  static constexpr int LDS = YB_OFF + TB * TOKB;
-  // register target (waves per SIMD): d = 5120 (two tokens of 512-coordinate
-  // slots, about 126 registers) is held to 4, three 5-wave workgroups per
-  // CU; d = 4096 (about 175 registers, 2 waves per SIMD) to 3: a few
-  // spilled registers, 7-8% faster; the same at d = 12288 spills about 80
-  // (18% slower without prefetch)
-  static constexpr int MIN_WAVES_PER_SIMD = D == 5120 ? 4 : (D == 4096 ? 3 : 1);
+  static constexpr int LDS = YB_OFF + NBUF * TB * TOKB;
+  // register target (waves per SIMD): 5 with staging waves (about 70
+  // registers); d = 4096 (about 175 registers, 2 waves per SIMD) is held to
+  // 3: a few spilled registers, 7-8% faster; the same at d = 12288 spills
+  // about 80 (18% slower without prefetch)
+  static constexpr int MIN_WAVES_PER_SIMD = SPLIT ? 5 : (D == 4096 ? 3 : 1);
   // register budget of the one-batch-ahead prefetch
-  static constexpr bool PREFETCH = (TB * CPT * 4) <= (W <= 8 ? 48 : 32);
+  static constexpr bool PREFETCH = SPLIT || (TB * CPT * 4) <= (W <= 8 ? 48 : 32);
   static_assert(S <= 1024 && S >= 128, "slot size");
   static_assert(XB <= 2 && (1 << XB) <= G, "at most 4 slots per block");
   static_assert(LDS <= 160 * 1024, "LDS");
@@ -178,7 +199,7 @@ enum OutMode { kCodes = 0, kDequant = 1, kRotated = 2 };
 // unused and smask holds the sign masks of the coordinates in place.
 // table: the device codebook table (cell grid, then levels).
 template <int D, int BITS, int MODE, bool IDENT>
-__global__ __launch_bounds__((64 * Shape<D, BITS>::W))
+__global__ __launch_bounds__((64 * Shape<D, BITS>::WTOT))
 __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void rq_fast_kernel(
     const uint16_t *__restrict__ x, int64_t n_tok, const uint32_t *__restrict__ scat,
     const uint32_t *__restrict__ smask, const uint32_t *__restrict__ table,
@@ -188,21 +209,25 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
   using GR = Grid<D, BITS>;
   constexpr bool DQ = MODE == kDequant, ZO = MODE == kRotated;
   constexpr int CELLB = GR::CELLB;
-  constexpr int S = SH::S, P = SH::P, TB = SH::TB, WT = SH::WT, W = SH::W, CPT = SH::CPT;
+  constexpr int S = SH::S, P = SH::P, TB = SH::TB, WT = SH::WT, W = SH::W, CPT = SH::CPTS;
+  constexpr int WSTG = SH::WSTG, WTOT = SH::WTOT;
   constexpr int G = SH::G;
   // a static array: its base is a compile-time constant, so every table and
   // token-buffer offset below folds into the LDS instructions' immediates
   __shared__ __attribute__((aligned(16))) uint8_t lds[SH::LDS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid0 = threadIdx.x, lane = tid0 & 63, wave = tid0 >> 6;
+  const bool stager = !SH::SPLIT || wave >= W;    // this wave stages
+  const int swave = SH::SPLIT ? wave - W : wave;   // index among the staging waves
+  const int tid = swave * 64 + lane;               // staging thread index
   float *npart = (float *)(lds + SH::NP_OFF);
 
   // cell table (and the levels, for fake quantization) into LDS
   if constexpr (!ZO) {
-    for (int i = tid; i < CELLB / 16; i += W * 64)
+    for (int i = tid0; i < CELLB / 16; i += WTOT * 64)
       ((u32x4 *)(lds + SH::CT_OFF))[i] = ((const u32x4 *)(table + 2 * GR::FIRST))[i];
   }
   if constexpr (DQ) {
-    for (int i = tid; i < (1 << BITS); i += W * 64)
+    for (int i = tid0; i < (1 << BITS); i += WTOT * 64)
       ((uint32_t *)(lds + SH::LV_OFF))[i] = table[table_levels_word(BITS) + i];
   }
 
@@ -210,7 +235,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
   uint32_t saddr[IDENT ? 1 : CPT][8], smk[CPT][4];
 #pragma unroll
   for (int c = 0; c < CPT; c++) {
-    const int pos = tid + c * W * 64;
+    const int pos = (stager ? tid : 0) + c * WSTG * 64;
     if constexpr (!IDENT) {
 #pragma unroll
       for (int e = 0; e < 8; e++) saddr[c][e] = scat[pos * 8 + e];
@@ -243,29 +268,24 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       const int64_t t = b * TB + tk;
 #pragma unroll
       for (int c = 0; c < CPT; c++)
-        stg[tk][c] = (t < n_tok) ? *(const u32x4 *)(x + t * D + 8 * (tid + c * W * 64))
+        stg[tk][c] = (t < n_tok) ? *(const u32x4 *)(x + t * D + 8 * (tid + c * WSTG * 64))
                                  : u32x4{0, 0, 0, 0};
     }
   };
-  if constexpr (SH::PREFETCH) {
-    if ((int64_t)blockIdx.x < nbatch) load_batch(blockIdx.x);
-  }
-  __syncthreads();
-
-  for (int64_t b = blockIdx.x; b < nbatch; b += gridDim.x) {
-    // ---- stage: norms by Gram MFMA, sign, scatter
-    if constexpr (!SH::PREFETCH) load_batch(b);
+  // staging of the batch held in stg into token buffer nb: norms by Gram
+  // MFMA, signs, scatter
+  auto stage_batch = [&](int nb) {
 #pragma unroll
     for (int tk = 0; tk < TB; tk++) {
       floatx4 gram = {0.f, 0.f, 0.f, 0.f};
-      uint8_t *yb = lds + SH::YB_OFF + tk * SH::TOKB;
+      uint8_t *yb = lds + SH::YB_OFF + (nb * TB + tk) * SH::TOKB;
 #pragma unroll
       for (int c = 0; c < CPT; c++) {
         const bf16x8 xv = __builtin_bit_cast(bf16x8, stg[tk][c]);
         gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, xv, gram, 0, 0, 0);
         if constexpr (IDENT) {
           // chunk pos of the token: slot pos / (S/8), 16 bytes of padding per slot
-          const int pos = tid + c * W * 64;
+          const int pos = tid + c * WSTG * 64;
           *(u32x4 *)(yb + 16 * (pos + pos / (S / 8))) =
               u32x4{stg[tk][c][0] ^ smk[c][0], stg[tk][c][1] ^ smk[c][1],
                     stg[tk][c][2] ^ smk[c][2], stg[tk][c][3] ^ smk[c][3]};
@@ -294,12 +314,46 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       const float q1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(dgi, 20));
       const float q2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(dgi, 40));
       const float q3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(dgi, 60));
-      if (lane == 0) npart[tk * W + wave] = (q0 + q1) + (q2 + q3);
+      if (lane == 0) npart[(nb * TB + tk) * WSTG + swave] = (q0 + q1) + (q2 + q3);
     }
-    if constexpr (SH::PREFETCH) {
-      if (b + gridDim.x < nbatch) load_batch(b + gridDim.x);
+  };
+  if constexpr (SH::SPLIT) {
+    if (stager) {
+      // staging waves: their own loop (its registers are not live in the
+      // compute waves' loop): batch b+1 into the other buffer while the
+      // compute waves work on batch b, one barrier per batch
+      if ((int64_t)blockIdx.x < nbatch) {
+        load_batch(blockIdx.x);
+        stage_batch(0);
+        if ((int64_t)(blockIdx.x + gridDim.x) < nbatch) load_batch(blockIdx.x + gridDim.x);
+      }
+      __syncthreads();
+      int its = 0;
+      for (int64_t b = blockIdx.x; b < nbatch; b += gridDim.x, its++) {
+        if (b + gridDim.x < nbatch) {
+          stage_batch((its & 1) ^ 1);
+          if (b + 2 * (int64_t)gridDim.x < nbatch) load_batch(b + 2 * gridDim.x);
+        }
+        __syncthreads();
+      }
+      return;
     }
-    __syncthreads();
+  } else if constexpr (SH::PREFETCH) {
+    if ((int64_t)blockIdx.x < nbatch) load_batch(blockIdx.x);
+  }
+  __syncthreads();
+
+  int it = 0;
+  for (int64_t b = blockIdx.x; b < nbatch; b += gridDim.x, it++) {
+    const int cur = SH::SPLIT ? (it & 1) : 0;
+    if constexpr (!SH::SPLIT) {
+      if constexpr (!SH::PREFETCH) load_batch(b);
+      stage_batch(0);
+      if constexpr (SH::PREFETCH) {
+        if (b + gridDim.x < nbatch) load_batch(b + gridDim.x);
+      }
+      __syncthreads();
+    }
 
     // ---- compute: wave tiles q = wave, wave + W, ...
     for (int q = wave; q < WT; q += W) {
@@ -313,7 +367,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       const int tko = sig_o / P, jo = sig_o - tko * P;
       float ss = 0.f;
 #pragma unroll
-      for (int w = 0; w < W; w++) ss += npart[tko * W + w];
+      for (int w = 0; w < WSTG; w++) ss += npart[(cur * TB + tko) * WSTG + w];
       const float s = sqrtf(ss);
       const float us = (s > 0.f) ? 1.0f / (s * scale_hd) : 0.f;  // v -> sqrt(d) z
       const float a8 = us * GR::PER_UNIT;                        // 8 bytes per cell
@@ -321,7 +375,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       // input side: MFMA row r = lane & 15 -> slot r>>2, chunk (r&3) of each group
       const int sig_i = 4 * q + ((lane & 15) >> 2);
       const int tki = sig_i / P, ji = sig_i - tki * P;
-      const uint8_t *ya = lds + SH::YB_OFF + tki * SH::TOKB +
+      const uint8_t *ya = lds + SH::YB_OFF + (cur * TB + tki) * SH::TOKB +
                           2 * (ji * SH::SP + 32 * (lane & 3) + 8 * (lane >> 4));
 
       // Matrix cores: MFMA row r = (slot r>>2, chunk (r&3) of a group), k =
@@ -493,7 +547,7 @@ hipError_t launch_one(const RotateArgs &a, const uint32_t *scat, const uint32_t 
   // (registers and LDS decide), each looping over batches, so no second
   // partial round of workgroups and each pays its table set-up once
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 64 * SH::W, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 64 * SH::WTOT, 0) != hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
   const int64_t nb = (a.n_tok + SH::TB - 1) / SH::TB;
@@ -502,7 +556,7 @@ hipError_t launch_one(const RotateArgs &a, const uint32_t *scat, const uint32_t 
   uint8_t *codes = MODE == kCodes ? (uint8_t *)a.out : nullptr;
   uint16_t *dq = MODE == kDequant ? (uint16_t *)a.out : nullptr;
   float *zout = MODE == kRotated ? (float *)a.out : nullptr;
-  hipLaunchKernelGGL(k, dim3(grid), dim3(64 * SH::W), 0, a.stream, (const uint16_t *)a.x,
+  hipLaunchKernelGGL(k, dim3(grid), dim3(64 * SH::WTOT), 0, a.stream, (const uint16_t *)a.x,
                      a.n_tok, scat, smask, table, codes, dq, zout, a.norms);
   return hipGetLastError();
 }
