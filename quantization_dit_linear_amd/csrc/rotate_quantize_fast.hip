@@ -7,9 +7,15 @@
 // Supplementary A setup).  This path is built around the VALU budget of an
 // HBM-bound kernel (about a dozen lane operations per coordinate):
 //
-//  * Staging.  A workgroup handles TB tokens per batch.  Each thread owns
-//    CPT fixed 8-element chunks of every token: one 16-byte load per chunk
-//    (issued one batch ahead when registers allow), the Rademacher signs
+//  * Roles.  A workgroup handles TB tokens per batch.  At d = 3072 and
+//    5120 its waves have fixed roles: staging waves load and scatter batch
+//    b+1 into one of two token buffers while compute waves transform and
+//    quantize batch b from the other, so the LDS-bound scatter and the
+//    VALU-bound transform run at the same time; elsewhere every wave stages
+//    and then computes, with one token buffer.
+//  * Staging.  Each staging thread owns CPT fixed 8-element chunks of every
+//    token: one 16-byte load per chunk (issued one batch ahead when
+//    registers allow), the Rademacher signs
 //    applied as an XOR (D moved onto the source index: D_i x_{pi(i)} =
 //    (D_{pi^-1(j)} x_j) at j = pi(i)), and every element scattered with
 //    ds_write_b16 to its permuted position pi^-1(j) in LDS.  Scatter
@@ -23,14 +29,16 @@
 //  * Walsh-Hadamard, stages 0-4.  bf16 values are exact MFMA operands and
 //    H_32 is +-1, so v_mfma_f32_16x16x32_bf16 applies the 32-point
 //    transform of every 32-element chunk with fp32 accumulation.  The 16
-//    rows of one MFMA are 4 chunks of 4 slots (a slot = one Hadamard block,
-//    h <= 1024 here), so each lane ends up holding 4 chunks x 2 positions
-//    of one slot per 128-coordinate group.
+//    rows of one MFMA are 4 chunks of 4 slots (a slot = one Hadamard block
+//    of at most 1024 coordinates, 512 at d = 3072 and 5120), so each lane
+//    ends up holding 4 chunks x 2 positions of one slot per 128-coordinate
+//    group.  The lowest group bit is usually transformed there too (two
+//    accumulated k-blocks with the signs of H_2).
 //  * Remaining stages (chunk bits) are register butterflies.
-//  * Blocks of 2048 or 4096: the transform runs on 1024-element slots as
-//    above, and the four slots of a wave tile (one per 16-lane row of the
-//    MFMA output) are the 1024-element quarters of one block (or halves of
-//    two blocks).  The last one or two butterfly stages pair the rows:
+//  * Blocks larger than a slot (2048 or 4096, and the 1024 blocks of the
+//    512-slot sizes): the four slots of a wave tile (one per 16-lane row of
+//    the MFMA output) are the quarters of one block (or halves of two
+//    blocks).  The last one or two butterfly stages pair the rows:
 //    v_permlane16_swap / v_permlane32_swap hand each lane its partner's
 //    value, and the butterfly leaves the slot bit in the register index and
 //    a group bit in the lane, which the store addressing follows.
