@@ -336,11 +336,20 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
         if ((int64_t)(blockIdx.x + gridDim.x) < nbatch) load_batch(blockIdx.x + gridDim.x);
       }
       __syncthreads();
-      int its = 0;
-      for (int64_t b = blockIdx.x; b < nbatch; b += gridDim.x, its++) {
-        if (b + gridDim.x < nbatch) {
-          stage_batch((its & 1) ^ 1);
-          if (b + 2 * (int64_t)gridDim.x < nbatch) load_batch(b + 2 * gridDim.x);
+      // two batches per iteration, so the token buffer (and with it every
+      // scatter address offset) is a compile-time constant: the offsets go
+      // into the LDS stores' immediate field instead of one add per element
+      const int64_t g = gridDim.x;
+      for (int64_t b = blockIdx.x; b < nbatch; b += 2 * g) {
+        if (b + g < nbatch) {
+          stage_batch(1);
+          if (b + 2 * g < nbatch) load_batch(b + 2 * g);
+        }
+        __syncthreads();
+        if (b + g >= nbatch) break;
+        if (b + 2 * g < nbatch) {
+          stage_batch(0);
+          if (b + 3 * g < nbatch) load_batch(b + 3 * g);
         }
         __syncthreads();
       }
@@ -376,8 +385,14 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       float ss = 0.f;
 #pragma unroll
       for (int w = 0; w < WSTG; w++) ss += npart[(cur * TB + tko) * WSTG + w];
-      const float s = sqrtf(ss);
-      const float us = (s > 0.f) ? 1.0f / (s * scale_hd) : 0.f;  // v -> sqrt(d) z
+      // hardware square root and reciprocal (1 ulp each; a sum of squares
+      // below 2^-64 is scaled by 2^64 first, away from the range where the
+      // square root loses accuracy): a few instructions per tile instead of
+      // the correctly rounded sequences, and the codes only move inside the
+      // decision windows that rounding of the transform already leaves
+      const bool tiny = ss < 0x1p-64f;
+      const float s = __builtin_amdgcn_sqrtf(tiny ? ss * 0x1p64f : ss) * (tiny ? 0x1p-32f : 1.0f);
+      const float us = (s > 0.f) ? __builtin_amdgcn_rcpf(s * scale_hd) : 0.f;  // v -> sqrt(d) z
       const float a8 = us * GR::PER_UNIT;                        // 8 bytes per cell
       constexpr float m8 = kMagic + (float)(CELLB / 2);          // middle cell at u = 0
       // input side: MFMA row r = lane & 15 -> slot r>>2, chunk (r&3) of each group
