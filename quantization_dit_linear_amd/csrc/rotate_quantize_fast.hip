@@ -7,12 +7,14 @@
 // Supplementary A setup).  This path is built around the VALU budget of an
 // HBM-bound kernel (about a dozen lane operations per coordinate):
 //
-//  * Roles.  A workgroup handles TB tokens per batch.  At d = 3072 and
-//    5120 its waves have fixed roles: staging waves load and scatter batch
-//    b+1 into one of two token buffers while compute waves transform and
-//    quantize batch b from the other, so the LDS-bound scatter and the
+//  * Roles.  A workgroup handles TB tokens per batch.  At d = 3072, 5120
+//    and 13824 its waves have fixed roles: staging waves load and scatter
+//    batch b+1 into one of two token buffers while compute waves transform
+//    and quantize batch b from the other, so the LDS-bound scatter and the
 //    VALU-bound transform run at the same time; elsewhere every wave stages
-//    and then computes, with one token buffer.
+//    and then computes, with one token buffer.  A wave tile is 4 slots; at
+//    d = 13824 (27 slots per token, one token per batch) the last tile
+//    holds 3, and its fourth row works on a copy that is never stored.
 //  * Staging.  Each staging thread owns CPT fixed 8-element chunks of every
 //    token: one 16-byte load per chunk (issued one batch ahead when
 //    registers allow), the Rademacher signs
@@ -125,10 +127,14 @@ constexpr int mfma_group_bits(int d) { return (d == 2048 || d == 4096) ? 0 : 1; 
 // instead of one after the other.  d = 5120: 130 -> 96 us for 32760 tokens
 // (two workgroups of 5 + 5 waves per CU, 70 registers); d = 3072 (512
 // slots, two tokens per batch, 3 + 3 waves, four workgroups per CU): 3-6%
-// faster, already close to the device's copy rate at 65536 tokens.  At d =
-// 12288 (one token per batch, 3 + 6 waves) it measured equal, and d = 13824
-// has no batch shape that fits two token buffers and 1024 threads.
-constexpr int staging_waves(int d) { return d == 5120 ? 5 : (d == 3072 ? 3 : 0); }
+// faster, already close to the device's copy rate at 65536 tokens.  d =
+// 13824 (27 slots of 512 per token): one token per batch in 7 wave tiles,
+// the last holding 3 slots (the slots transform alone, so the missing one
+// is a copy whose results are never stored), 7 + 9 waves, two workgroups
+// per CU at 64 registers: 334 -> 223 us for 32760 tokens (four tokens per
+// batch, the tile-aligned shape, left room for one 112 KB token buffer
+// only).  At d = 12288 (one token per batch, 3 + 6 waves) it measured equal.
+constexpr int staging_waves(int d) { return d == 5120 ? 5 : (d == 3072 ? 3 : (d == 13824 ? 9 : 0)); }
 
 constexpr int pick_waves(int wt, int ch, int maxw) {
   int best = 1;
@@ -145,8 +151,10 @@ struct Shape {
   static constexpr int XB = ilog2(H / S);             // butterfly stages across slots
   static constexpr int P = D / S;                     // slots per token
   // tokens per batch: 4, or 2 for long tokens when the slots still tile
-  static constexpr int TB = ((D * 2 * 4 > 64 * 1024 || staging_waves(D)) && (2 * P) % 4 == 0) ? 2 : 4;
-  static constexpr int WT = TB * P / 4;               // wave tiles per batch
+  static constexpr int TB = D == 13824 ? 1
+                            : ((D * 2 * 4 > 64 * 1024 || staging_waves(D)) && (2 * P) % 4 == 0) ? 2 : 4;
+  static constexpr int NSLOT = TB * P;                // slots per batch
+  static constexpr int WT = (NSLOT + 3) / 4;          // wave tiles per batch (the last may be partial)
   static constexpr int CH = D / 512;                  // 8-element chunks per token per 64 threads
   // waves per workgroup: divide both the wave tiles and the staging chunks;
   // with stages across slots at most 2 waves per SIMD (register budget);
@@ -179,14 +187,16 @@ struct Shape {
   static constexpr int YB_OFF = LV_OFF + (4 << BITS);
   static constexpr int LDS = YB_OFF + NBUF * TB * TOKB;
   // register target (waves per SIMD): 5 with staging waves (about 70
-  // registers); d = 4096 (about 175 registers, 2 waves per SIMD) is held to
-  // 3: a few spilled registers, 7-8% faster; the same at d = 12288 spills
-  // about 80 (18% slower without prefetch)
-  static constexpr int MIN_WAVES_PER_SIMD = SPLIT ? 5 : (D == 4096 ? 3 : 1);
+  // registers); 8 at d = 13824 (64 registers, so two 16-wave workgroups
+  // share a CU: 3% faster than one); d = 4096 (about 175 registers, 2 waves
+  // per SIMD) is held to 3: a few spilled registers, 7-8% faster; the same
+  // at d = 12288 spills about 80 (18% slower without prefetch)
+  static constexpr int MIN_WAVES_PER_SIMD = D == 13824 ? 8 : SPLIT ? 5 : (D == 4096 ? 3 : 1);
   // register budget of the one-batch-ahead prefetch
   static constexpr bool PREFETCH = SPLIT || (TB * CPT * 4) <= (W <= 8 ? 48 : 32);
   static_assert(S <= 1024 && S >= 128, "slot size");
   static_assert(XB <= 2 && (1 << XB) <= G, "at most 4 slots per block");
+  static_assert(NSLOT % 4 == 0 || XB == 0, "a partial last tile needs slots that transform alone");
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert((int)Grid<D, BITS>::MASK + 8 <= LDS, "masked offsets stay in the workgroup's LDS");
 };
@@ -380,7 +390,11 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       // XB bits of rl are group bits.  All slots a lane ends up with belong
       // to one token.
       const int rl = lane >> 4;
-      const int sig_o = 4 * q + (rl & ~((1 << SH::XB) - 1));
+      // rows past the batch's last slot (a partial last tile; only without
+      // stages across slots) compute on a copy of that slot and store nothing
+      const int sig_r = 4 * q + (rl & ~((1 << SH::XB) - 1));
+      const bool row_ok = SH::NSLOT % 4 == 0 || sig_r < SH::NSLOT;
+      const int sig_o = row_ok ? sig_r : SH::NSLOT - 1;
       const int tko = sig_o / P, jo = sig_o - tko * P;
       float ss = 0.f;
 #pragma unroll
@@ -396,7 +410,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       const float a8 = us * GR::PER_UNIT;                        // 8 bytes per cell
       constexpr float m8 = kMagic + (float)(CELLB / 2);          // middle cell at u = 0
       // input side: MFMA row r = lane & 15 -> slot r>>2, chunk (r&3) of each group
-      const int sig_i = 4 * q + ((lane & 15) >> 2);
+      const int sig_i = min(4 * q + ((lane & 15) >> 2), SH::NSLOT - 1);
       const int tki = sig_i / P, ji = sig_i - tki * P;
       const uint8_t *ya = lds + SH::YB_OFF + (cur * TB + tki) * SH::TOKB +
                           2 * (ji * SH::SP + 32 * (lane & 3) + 8 * (lane >> 4));
@@ -483,8 +497,10 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       // quantize + pack + store.  Register group g holds slot jo + (g & m)
       // and group (g & ~m) | (rl & m) of that slot, m = 2^XB - 1.
       constexpr int XM = (1 << SH::XB) - 1;
-      const int64_t tok = b * TB + tko;
-      if ((lane & 15) == 0 && (rl & XM) == 0 && jo == 0 && tok < n_tok) norms[tok] = s;
+      // tok_end: stores happen for tok < tok_end (n_tok, or 0 for rows past
+      // the batch's last slot)
+      const int64_t tok = b * TB + tko, tok_end = row_ok ? n_tok : 0;
+      if ((lane & 15) == 0 && (rl & XM) == 0 && jo == 0 && tok < tok_end) norms[tok] = s;
       uint8_t *dst0 = codes + tok * row_bytes + 16 * BITS * (jo * G + (rl & XM)) + BITS * (lane & 15);
       // fake quantization: coordinate of register (g, w, i) is
       // (jo + (g & XM)) S + ((g & ~XM) | (rl & XM)) 128 + 32 i + 16 w + (lane & 15)
@@ -494,7 +510,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
         // rotated values: z = v us / sqrt(d), same coordinates as above
         const float rsd = us / __builtin_sqrtf((float)D);
         float *z0 = zout + tok * D + jo * S + (rl & XM) * 128 + (lane & 15);
-        if (tok < n_tok) {
+        if (tok < tok_end) {
 #pragma unroll
           for (int g = 0; g < G; g++)
 #pragma unroll
@@ -526,7 +542,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
               // (code masked: a u outside the window -- only from a norm
               // that underflowed -- reads an arbitrary entry)
               const float lvv = *(const float *)(lds + SH::LV_OFF + 4 * (code & ((1u << BITS) - 1)));
-              if (tok < n_tok)
+              if (tok < tok_end)
                 dq0[(g & XM) * S + (g & ~XM) * 128 + 32 * i + 16 * w] = f32_to_bf16_rne(fs * lvv);
             }
             if constexpr (BITS == 8) {
@@ -536,7 +552,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
               word |= code << (BITS * (4 * w + i));
             }
           }
-        if (!DQ && tok < n_tok) {
+        if (!DQ && tok < tok_end) {
           uint8_t *dst = dst0 + 16 * BITS * ((g & XM) * G + (g & ~XM));
           if constexpr (BITS == 8) {
             typedef uint32_t u32x2s __attribute__((ext_vector_type(2)));
