@@ -279,6 +279,16 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
   constexpr int64_t row_bytes = (int64_t)D * BITS / 8;
   const int64_t nbatch = (n_tok + TB - 1) / TB;
 
+  // the lane's diagonal Gram register as one-hot weights (all zero off
+  // the diagonal lanes), made once: selecting the term is then a product
+  // and three multiply-adds of exact zeros and ones, no compares per token
+  float dsel[4];
+  {
+    const int r = lane & 15;
+    const bool on_diag = (r >> 2) == (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; i++) dsel[i] = (on_diag && (r & 3) == i) ? 1.f : 0.f;
+  }
   u32x4 stg[TB][CPT];
   auto load_batch = [&](int64_t b) {
 #pragma unroll
@@ -321,12 +331,11 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       // 40-43 and 60-63.  Two DPP swaps sum each quad, four lane reads
       // gather the quad sums: no LDS traffic (a 64-lane shuffle tree cost
       // 6 LDS permutes per token; d = 5120 ran 13% faster without them)
-      const int r = lane & 15;
-      float dg = ((r >> 2) == (lane >> 4)) ? gram[r & 3] : 0.f;
-      dg += __builtin_bit_cast(
-          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, dg), 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
-      dg += __builtin_bit_cast(
-          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, dg), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+      float dg = gram[0] * dsel[0] + gram[1] * dsel[1] + gram[2] * dsel[2] + gram[3] * dsel[3];
+      dg += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                          0, __builtin_bit_cast(int, dg), 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+      dg += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                          0, __builtin_bit_cast(int, dg), 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
       const int dgi = __builtin_bit_cast(int, dg);
       const float q0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(dgi, 0));
       const float q1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(dgi, 20));
