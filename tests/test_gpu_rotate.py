@@ -92,6 +92,19 @@ def test_empty_input_is_noop(q):
     assert codes.shape == (0, 128) and norms.shape == (0,)
 
 
+@pytest.mark.parametrize("M", [1, 2, 7, 513])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_partial_last_tile_token_counts(q, M, bits):
+    """d = 13824 runs one token (27 slots) per batch in 7 wave tiles, the
+    last holding 3 slots: every code, norm and rotated value of 1, 2, 7 and
+    513 tokens (more batches than one per workgroup for 513) against the
+    oracle, so the tile's missing fourth slot never shows up in an output."""
+    d = 13824
+    x = wl.custom_activations(M, d, wl.BF16, d + M, n_out=max(1, d // 100), out_factor=50.0,
+                              sigma_s=1.5, zero_rows=(M - 1,) if M > 2 else ())
+    _check_rows(q, x, wl.BF16, d, 123, bits, True, f"d=13824 M={M}")
+
+
 @pytest.mark.parametrize("d", [128, 384, 640, 1024, 1152, 2048, 4096, 8192, 16384])
 def test_other_dimensions(q, d):
     """Block sizes 128..16384 and odd block counts."""
