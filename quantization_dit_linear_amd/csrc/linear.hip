@@ -16,9 +16,11 @@
 //     an LDS table maps each code byte (two slots) straight to the fp16
 //     pair, four 32-bit LDS reads per 8 slots and about one VALU instruction
 //     per MFMA (32 lane-interleaved copies of the table keep the random
-//     lookups from piling onto a few banks); other bit pairs use v_perm_b32
-//     byte tables (the fp16 low and high bytes of the 2^b levels; no memory
-//     lookups);
+//     lookups from piling onto a few banks); 4-bit activations use the same
+//     table against weights of another width, regrouped into the slot order
+//     of the weights' decode (two byte permutes per 8 slots); every other
+//     row uses v_perm_b32 byte tables (the fp16 low and high bytes of the
+//     2^b levels; no memory lookups);
 //   * decoded tiles live in LDS, double buffered, as 8 planes of 256 rows x
 //     16 bytes (one plane per 8-slot chunk): the decode stores and the MFMA
 //     fragment loads both touch consecutive 16-byte words, so neither has
@@ -207,6 +209,19 @@ __device__ __forceinline__ u32x4 decode_pair4(const uint32_t *w, const uint32_t 
                lut_at<C>(lut, (v >> 16) & 0xFFu), lut_at<C>(lut, v >> 24)};
 }
 
+// The same pair-table decode with the levels regrouped into the slot order
+// of the byte-permute decoder (8q + {0,2,4,6,1,3,5,7}), for 4-bit
+// activations against weights of another width: low halves of the pairs
+// (even slots) first, then the high halves (odd slots).
+template <int C>
+__device__ __forceinline__ u32x4 decode_pair4_ilv(const uint32_t *w, const uint32_t *lut, int q) {
+  const uint32_t v = w[q];
+  const uint32_t p0 = lut_at<C>(lut, v & 0xFFu), p1 = lut_at<C>(lut, (v >> 8) & 0xFFu);
+  const uint32_t p2 = lut_at<C>(lut, (v >> 16) & 0xFFu), p3 = lut_at<C>(lut, v >> 24);
+  return u32x4{perm(p1, p0, 0x05040100u), perm(p3, p2, 0x05040100u),
+               perm(p1, p0, 0x07060302u), perm(p3, p2, 0x07060302u)};
+}
+
 // The decode of one role: byte-permute tables (2-4 bits) or an LDS table
 // (4 bits on both sides: pairs; 8 bits: levels).
 struct Decoder {
@@ -214,10 +229,11 @@ struct Decoder {
   const uint32_t *lut;
 };
 
-template <int BITS, bool PAIR, int C>
+template <int BITS, int PAIR, int C>
 __device__ __forceinline__ u32x4 decode_chunk(const uint32_t *w, const Decoder &dc, int q) {
   if constexpr (BITS == 8) return decode_q8<C>(w, dc.lut, q);
-  else if constexpr (PAIR) return decode_pair4<C>(w, dc.lut, q);
+  else if constexpr (PAIR == 2) return decode_pair4_ilv<C>(w, dc.lut, q);
+  else if constexpr (PAIR == 1) return decode_pair4<C>(w, dc.lut, q);
   else return decode_q<BITS>(w, dc.t, q);
 }
 
@@ -249,7 +265,7 @@ __device__ __forceinline__ void load_codes(const uint8_t *p, uint32_t *w) {
 
 // The K loop of one tile for a thread whose row has BITS-bit codes at `prow`
 // (activation or weight row; the MFMA work is the same for both roles).
-template <class TL, int BITS, bool PAIR>
+template <class TL, int BITS, int PAIR>
 __device__ __forceinline__ void k_loop(uint8_t *lds, floatx4 (&acc)[TL::JB][TL::IB],
                                        const uint8_t *prow, const Decoder &tt, int opoff, int row,
                                        int lane, int wm, int wn, int T) {
@@ -397,8 +413,11 @@ __global__ __launch_bounds__(TL::THREADS, TL::WGS) void linear_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_base[];
   static_assert(BA != 8 || BW == 8, "8-bit codes on both sides");
   constexpr bool PAIR = BA == 4 && BW == 4;
+  // 4-bit activations always decode through the pair table (with other
+  // weight widths the weight rows keep the byte permutes)
+  constexpr bool TAB_A = BA == 4;
   constexpr int LUTB = 256 * TL::LUTC * 4;                       // table bytes
-  uint8_t *lds = lds_base + ((BA == 8 || PAIR) ? LUTB : 0);  // decoded tiles
+  uint8_t *lds = lds_base + ((BA == 8 || TAB_A) ? LUTB : 0);  // decoded tiles
   constexpr int TT = TL::T, IB = TL::IB, JB = TL::JB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn_count = TT / (16 * JB);
@@ -410,7 +429,7 @@ __global__ __launch_bounds__(TL::THREADS, TL::WGS) void linear_kernel(
   const int T = K / KS;
 
   Decoder da{ta, nullptr}, dw{tw, nullptr};
-  if constexpr (BA == 8 || PAIR) {
+  if constexpr (BA == 8 || TAB_A) {
     // the shared table, TL::LUTC interleaved copies: 8 bits, the fp16 levels
     // (round to nearest even, as on the host); 4+4 bits, the fp16 pairs of
     // every code byte, from the byte-permute tables
@@ -483,8 +502,8 @@ __global__ __launch_bounds__(TL::THREADS, TL::WGS) void linear_kernel(
                            lane, wm, wn, ke - kb);
     } else {
       // both branches run the same barriers; the branch is wave-uniform
-      if (is_a) k_loop<TL, BA, false>(lds, acc, pa, da, 0, row, lane, wm, wn, ke - kb);
-      else k_loop<TL, BW, false>(lds, acc, pw, dw, TL::OPB, row, lane, wm, wn, ke - kb);
+      if (is_a) k_loop<TL, BA, TAB_A ? 2 : 0>(lds, acc, pa, da, 0, row, lane, wm, wn, ke - kb);
+      else k_loop<TL, BW, 0>(lds, acc, pw, dw, TL::OPB, row, lane, wm, wn, ke - kb);
     }
 
     if (pdst) {
@@ -609,7 +628,7 @@ template <class TL, int BA, int BW>
 hipError_t launch_tiles(const LinearArgs &a, const PermTab &ta, const PermTab &tw,
                         const float *lv8, int vec, int first, int count, unsigned grid,
                         int splits = 1, float *part = nullptr) {
-  constexpr int lds = TL::LDS + ((BA == 8 || (BA == 4 && BW == 4)) ? 256 * TL::LUTC * 4 : 0);
+  constexpr int lds = TL::LDS + ((BA == 8 || BA == 4) ? 256 * TL::LUTC * 4 : 0);
   static_assert(lds * TL::WGS <= 160 * 1024, "LDS of one CU");
   static std::atomic<uint64_t> lds_set{0};  // per instantiation and device
   hipError_t e = ensure_lds_limit((const void *)linear_kernel<TL, BA, BW>, lds, lds_set);
