@@ -390,16 +390,19 @@ def _short_kernel_name(name):
     return n.replace("void ", "").strip()
 
 
-def _split_rotate(rows, n_prep):
+def _split_rotate(rows, n_prep, n_act=None):
     """Rotate-kernel rows of a rocprofv3 csv in dispatch order -> (weight
     preparation rows, activation rows): the first n_prep dispatches of the
     workload's rotate kernel prepared the weights (bench.py launches them
-    before any activation)."""
+    before any activation); with n_act, only the next n_act dispatches (the
+    steps' own launches, not the back-to-back ones timed after them) count
+    as activation rows."""
     order = sorted(rows, key=lambda r: int(r.get("Dispatch_Id") or 0))
     disp = sorted({int(r.get("Dispatch_Id") or i) for i, r in enumerate(order)})
     prep_ids = set(disp[:n_prep])
+    act_ids = set(disp[n_prep:] if n_act is None else disp[n_prep:n_prep + n_act])
     prep = [r for i, r in enumerate(order) if int(r.get("Dispatch_Id") or i) in prep_ids]
-    act = [r for i, r in enumerate(order) if int(r.get("Dispatch_Id") or i) not in prep_ids]
+    act = [r for i, r in enumerate(order) if int(r.get("Dispatch_Id") or i) in act_ids]
     return prep, act
 
 
@@ -443,7 +446,12 @@ def summarize_profiles(a):
     if trace:
         tr = [r for r in csv.DictReader(open(trace))
               if _short_kernel_name(r["Kernel_Name"]) == rot_name]
-        prep, act = _split_rotate(tr, n_prep)
+        n_act = None
+        if a.profile_bench_log:  # the steps' own launches: warm-up + timed steps
+            jl = json.loads([l for l in open(a.profile_bench_log) if l.startswith("{")][-1])
+            if "steps" in jl and "warmup" in jl:
+                n_act = int(jl["steps"]) + int(jl["warmup"])
+        prep, act = _split_rotate(tr, n_prep, n_act)
         dur = lambda rs: [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
         if act:
             rot_act_us = float(np.mean(dur(act)))
@@ -465,8 +473,9 @@ def summarize_profiles(a):
         f.write(f"{rot_name}: {M} activation rows x ({K}*{in_b} + {K}*{ba}/8 + 4) = "
                 f"{rot_alg:.4g} algorithmic bytes per launch")
         if rot_act_us is not None:
-            f.write(f"; activation launches (all but the first {n_prep} dispatches, which "
-                    f"prepared the {N} weight rows) average {rot_act_us:.1f} us -> "
+            f.write(f"; activation launches of the steps (after the first {n_prep} "
+                    f"dispatches, which prepared the {N} weight rows) average "
+                    f"{rot_act_us:.1f} us -> "
                     f"{rot_alg / (rot_act_us * 1e-6) / 1e9:.1f} GB/s")
             if rot_prep_us is not None:
                 f.write(f"; weight preparation {rot_prep_us:.1f} us")
@@ -697,6 +706,7 @@ def sweep(q, iters=20):
 
 
 PREP_TIMED = 5  # timed weight-preparation launches after the first one
+BACK_TO_BACK = 20  # rotate+quantize launches timed alone after the steps
 
 
 def online_step(q, lin, cfg, bw, ba, steps, warmup, sets, calib_copy_mib=0):
@@ -769,7 +779,21 @@ def online_step(q, lin, cfg, bw, ba, steps, warmup, sets, calib_copy_mib=0):
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
+    # after the timed region, not part of the step: the rotate+quantize
+    # launch alone, BACK_TO_BACK times back to back (one event pair), so its
+    # rate without a linear's output write-back beside it is on record too
+    for i in range(2):
+        q.rotate_quantize(xs[i % sets], lin.seed, ba, out=ac[i % sets], norms=an[i % sets])
+    torch.cuda.synchronize()
+    b0 = torch.cuda.Event(enable_timing=True)
+    b1 = torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for i in range(BACK_TO_BACK):
+        q.rotate_quantize(xs[i % sets], lin.seed, ba, out=ac[i % sets], norms=an[i % sets])
+    b1.record(stream)
+    torch.cuda.synchronize()
     r = {
+        "t_rot_b2b": b0.elapsed_time(b1) / BACK_TO_BACK,
         "ms_step": total_ms / steps,
         "t_rot": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
         "t_lin": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
@@ -784,6 +808,14 @@ def online_step(q, lin, cfg, bw, ba, steps, warmup, sets, calib_copy_mib=0):
     return r
 
 
+def b2b_entry(r, rt):
+    """The rotate+quantize launch timed alone (after the steps, not in them)."""
+    return {"what": f"the same launch {BACK_TO_BACK} times back to back after the timed "
+                    "steps (one event pair): no linear's output write-back beside it",
+            "ms": round(r["t_rot_b2b"], 4), "GB/s": round(rt["rot_b2b_gbs"], 1),
+            "frac_of_hbm_peak": round(rt["rot_b2b_gbs"] / HBM_PEAK_GBS, 4)}
+
+
 def step_rates(lin, bw, ba, r):
     import workloads as wl
     M, N, K = lin.act.M, lin.weight.N, lin.act.d
@@ -793,6 +825,7 @@ def step_rates(lin, bw, ba, r):
     prep_bytes = N * (K * (2 if lin.weight.dtype == wl.BF16 else 4) + K * bw / 8 + 4)
     return {"lin_tflops": flops / (r["t_lin"] * 1e-3) / 1e12,
             "rot_gbs": rot_bytes / (r["t_rot"] * 1e-3) / 1e9,
+            "rot_b2b_gbs": rot_bytes / (r["t_rot_b2b"] * 1e-3) / 1e9,
             "prep_gbs": prep_bytes / (r["t_prep"] * 1e-3) / 1e9,
             "value": flops / (r["ms_step"] * 1e-3) / 1e12}
 
@@ -845,7 +878,8 @@ def main():
                        "frac_of_mfma_fp16_peak": round(rt2["lin_tflops"] / MFMA_FP16_PEAK_TFLOPS,
                                                        4)},
             "rotate_quantize": {"ms": round(r2["t_rot"], 4), "GB/s": round(rt2["rot_gbs"], 1),
-                                "frac_of_hbm_peak": round(rt2["rot_gbs"] / HBM_PEAK_GBS, 4)},
+                                "frac_of_hbm_peak": round(rt2["rot_gbs"] / HBM_PEAK_GBS, 4),
+                                "back_to_back": b2b_entry(r2, rt2)},
             "prepare_weights": {"ms": round(r2["t_prep"], 4), "GB/s": round(rt2["prep_gbs"], 1)},
         }
         torch.cuda.empty_cache()
@@ -882,7 +916,8 @@ def main():
                        "frac_of_mfma_fp16_peak": round(lin_tflops / MFMA_FP16_PEAK_TFLOPS, 4)},
             "rotate_quantize": {"ms": round(r["t_rot"], 4), "GB/s": round(rot_gbs, 1),
                                 "ms_median": round(float(np.median(r["rot_steps"])), 4),
-                                "frac_of_hbm_peak": round(rot_gbs / HBM_PEAK_GBS, 4)},
+                                "frac_of_hbm_peak": round(rot_gbs / HBM_PEAK_GBS, 4),
+                                "back_to_back": b2b_entry(r, rt)},
         },
         "prepare_weights": {"what": "offline, once per layer: not in the step; median of "
                                     f"{PREP_TIMED} launches",
