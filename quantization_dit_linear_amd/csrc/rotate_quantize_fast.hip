@@ -150,7 +150,8 @@ struct Shape {
   static constexpr int S = fast_slot(D);              // slot: a block, or 1024 (512) of one
   static constexpr int XB = ilog2(H / S);             // butterfly stages across slots
   static constexpr int P = D / S;                     // slots per token
-  // tokens per batch: 4, or 2 for long tokens when the slots still tile
+  // tokens per batch: 4, or 2 for long tokens when the slots still tile;
+  // 1 at d = 13824, whose 27 slots leave the last wave tile partial
   static constexpr int TB = D == 13824 ? 1
                             : ((D * 2 * 4 > 64 * 1024 || staging_waves(D)) && (2 * P) % 4 == 0) ? 2 : 4;
   static constexpr int NSLOT = TB * P;                // slots per batch
@@ -197,6 +198,8 @@ struct Shape {
   static_assert(S <= 1024 && S >= 128, "slot size");
   static_assert(XB <= 2 && (1 << XB) <= G, "at most 4 slots per block");
   static_assert(NSLOT % 4 == 0 || XB == 0, "a partial last tile needs slots that transform alone");
+  static_assert(CH % WSTG == 0, "every staging thread owns whole chunks");
+  static_assert(!SPLIT || W == WT, "one compute wave per wave tile");
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert((int)Grid<D, BITS>::MASK + 8 <= LDS, "masked offsets stay in the workgroup's LDS");
 };
