@@ -137,3 +137,15 @@ def test_source_digest_ignores_comments(tmp_path, monkeypatch):
     assert bench.src_digest("k.hip") == d0
     (src / "k.hip").write_text("int f() {\n  return 2;  // one\n}\n")
     assert bench.src_digest("k.hip") != d0
+
+
+def test_split_rotate_counts_only_the_steps_launches():
+    """Rotate dispatches in launch order: the first n_prep prepared the
+    weights, the next n_act belong to the steps, and any later ones (the
+    launches timed back to back after the steps) are left out of both."""
+    rows = [{"Dispatch_Id": str(i), "v": i} for i in (7, 3, 11, 5, 9, 1, 13, 15, 2)]
+    prep, act = bench._split_rotate(rows, 2, 4)
+    assert [int(r["Dispatch_Id"]) for r in prep] == [1, 2]
+    assert [int(r["Dispatch_Id"]) for r in act] == [3, 5, 7, 9]
+    prep, act = bench._split_rotate(rows, 2)
+    assert [int(r["Dispatch_Id"]) for r in act] == [3, 5, 7, 9, 11, 13, 15]
