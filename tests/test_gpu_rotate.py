@@ -325,3 +325,45 @@ def test_rotated_basis_tokens(q, d, bits):
     c = parity.unpack_codes(host(codes), d, bits)
     top = (1 << bits) - 1
     assert c[0, 5] == top and c[1, d - 1] == 0, "extreme coordinates take the extreme codes"
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_partial_last_tile_writes_nothing_past_the_outputs(q, M):
+    """d = 13824: the fourth row of each token's last wave tile works on a
+    copy and must store nothing.  Codes, fake-quantized values, rotated
+    values and norms go into the front of buffers two rows longer, filled
+    with a sentinel: the extra rows keep it, and the front matches a call
+    into buffers of the exact size."""
+    import ctypes
+    import torch
+    d, seed, bits = 13824, 123, 4
+    x = to_device(wl.custom_activations(M, d, wl.BF16, d + 7, n_out=30, out_factor=50.0,
+                                        sigma_s=1.0))
+    say("guard rows", M)
+
+    def guarded(shape, dtype):
+        t = torch.empty((M + 2,) + shape, dtype=dtype, device="cuda")
+        t.view(torch.uint8).fill_(0xAB)
+        return t
+
+    def untouched(t):
+        return bool((t[M:].contiguous().view(torch.uint8) == 0xAB).all().item())
+
+    codes, norms = guarded((d * bits // 8,), torch.uint8), guarded((), torch.float32)
+    q.rotate_quantize(x, seed, bits, out=codes[:M], norms=norms[:M])
+    c_ref, n_ref = q.rotate_quantize(x, seed, bits)
+    dq, dn = guarded((d,), torch.bfloat16), guarded((), torch.float32)
+    q.fake_quantize(x, seed, bits, out=dq[:M], norms=dn[:M])
+    dq_ref, _ = q.fake_quantize(x, seed, bits)
+    z, zn = guarded((d,), torch.float32), guarded((), torch.float32)
+    rc = q.lib().oq_rotate_quantize(ctypes.c_void_p(x.data_ptr()), q.OQ_BF16, M, d, seed,
+                                    q.OQ_OUT_F32_ROTATED, bits, ctypes.c_void_p(z.data_ptr()),
+                                    ctypes.c_void_p(zn.data_ptr()),
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    z_ref, _ = q.rotate(x, seed)
+    torch.cuda.synchronize()
+    for t in (codes, norms, dq, dn, z, zn):
+        assert untouched(t), "a store landed past the last row"
+    assert torch.equal(codes[:M], c_ref) and torch.equal(norms[:M], n_ref)
+    assert torch.equal(dq[:M], dq_ref) and torch.equal(z[:M], z_ref)
