@@ -43,7 +43,11 @@
 //    blocks).  The last one or two butterfly stages pair the rows:
 //    v_permlane16_swap / v_permlane32_swap hand each lane its partner's
 //    value, and the butterfly leaves the slot bit in the register index and
-//    a group bit in the lane, which the store addressing follows.
+//    a group bit in the lane, which the store addressing follows.  A 4096
+//    block (4 slots of 1024, 64 values per lane) is split over two waves:
+//    each produces the half of the groups with one value of the top group
+//    bit, whose H_2 the matrix cores apply by accumulating both input
+//    halves with its signs, so a wave holds 32 values per lane.
 //  * Quantize.  A magic-number fma turns v into the byte offset of its cell
 //    in a uniform grid over sqrt(d) z (narrower than any threshold gap:
 //    step 1/8 up to 4 bits, over +-(ceil(sqrt(d)) + 2) units, which holds
@@ -72,6 +76,12 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kMagic = 12582912.0f;        // 1.5 * 2^23
+
+// compile-time half index of a split wave tile
+template <int V>
+struct Half {
+  static constexpr int value = V;
+};
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 constexpr int isqrt_ceil(int v) {
@@ -133,8 +143,20 @@ constexpr int mfma_group_bits(int d) { return (d == 2048 || d == 4096) ? 0 : 1; 
 // is a copy whose results are never stored), 7 + 9 waves, two workgroups
 // per CU at 64 registers: 334 -> 223 us for 32760 tokens (four tokens per
 // batch, the tile-aligned shape, left room for one 112 KB token buffer
-// only).  At d = 12288 (one token per batch, 3 + 6 waves) it measured equal.
+// only).  d = 12288 keeps one role per wave (below).
 constexpr int staging_waves(int d) { return d == 5120 ? 5 : (d == 3072 ? 3 : (d == 13824 ? 9 : 0)); }
+// Compute waves per wave tile: 2 where the wave tile is a whole 4096 block
+// (h = 4096: 4 slots of 1024).  Each of the two takes the half of the
+// output groups with one value of the top group bit; the matrix cores
+// apply that bit's H_2 too (its two input halves accumulated with signs),
+// so a wave holds 32 values per lane instead of 64.  d = 12288 (two tokens
+// per batch): 12 waves that each stage and compute, three per SIMD at 140
+// registers, 91 -> 76-81 us for 9216 tokens (one wave per tile at 197
+// registers left 1.5 waves per SIMD; split roles, 6 + 6 waves with one
+// token per batch, spilled at the 80 registers two workgroups per CU
+// allow and ran 13% slower than one wave per tile).  d = 4096: 114
+// registers instead of 168 with spills, 2-4% faster for 16384 tokens.
+constexpr int tile_split(int d) { return (d == 12288 || d == 4096) ? 2 : 1; }
 
 constexpr int pick_waves(int wt, int ch, int maxw) {
   int best = 1;
@@ -155,12 +177,14 @@ struct Shape {
   static constexpr int TB = D == 13824 ? 1
                             : ((D * 2 * 4 > 64 * 1024 || staging_waves(D)) && (2 * P) % 4 == 0) ? 2 : 4;
   static constexpr int NSLOT = TB * P;                // slots per batch
-  static constexpr int WT = (NSLOT + 3) / 4;          // wave tiles per batch (the last may be partial)
+  static constexpr int GS = tile_split(D);            // compute waves per 4-slot tile
+  static constexpr int WT = (NSLOT + 3) / 4 * GS;     // wave tiles per batch (the last may be partial)
   static constexpr int CH = D / 512;                  // 8-element chunks per token per 64 threads
   // waves per workgroup: divide both the wave tiles and the staging chunks;
-  // with stages across slots at most 2 waves per SIMD (register budget);
-  // with staging waves, one compute wave per tile
-  static constexpr int W = staging_waves(D) ? WT : pick_waves(WT, CH, XB > 0 ? 8 : 16);
+  // with stages across slots on unsplit tiles at most 2 waves per SIMD
+  // (register budget); with staging waves, one compute wave per tile
+  static constexpr int W =
+      staging_waves(D) ? WT : pick_waves(WT, CH, (XB > 0 && tile_split(D) == 1) ? 8 : 16);
   static constexpr int CPT = CH / W;                  // chunks per thread per token
   // split roles: W compute waves and WS staging waves (loads, norm partials,
   // scatter into the other of two token buffers)
@@ -171,6 +195,7 @@ struct Shape {
   static constexpr int CPTS = CH / WSTG;               // staged chunks per thread per token
   static constexpr int NBUF = SPLIT ? 2 : 1;
   static constexpr int G = S / 128;                   // 128-coordinate groups per slot
+  static constexpr int GW = G / GS;                   // groups of a slot one wave holds
   static constexpr int CBITS = ilog2(S) - 5;          // chunk bits (above the 32-element chunk)
   // group bits (coordinate bits 7 .. 7+MB-1) transformed on the matrix cores
   // together with the five in-chunk bits; the other chunk bits are register
@@ -189,14 +214,15 @@ struct Shape {
   static constexpr int LDS = YB_OFF + NBUF * TB * TOKB;
   // register target (waves per SIMD): 5 with staging waves (about 70
   // registers); 8 at d = 13824 (64 registers, so two 16-wave workgroups
-  // share a CU: 3% faster than one); d = 4096 (about 175 registers, 2 waves
-  // per SIMD) is held to 3: a few spilled registers, 7-8% faster; the same
-  // at d = 12288 spills about 80 (18% slower without prefetch)
-  static constexpr int MIN_WAVES_PER_SIMD = D == 13824 ? 8 : SPLIT ? 5 : (D == 4096 ? 3 : 1);
+  // share a CU: 3% faster than one); with split tiles 3 at d = 12288 (one
+  // 12-wave workgroup per CU) and 4 at d = 4096 (two 8-wave workgroups)
+  static constexpr int MIN_WAVES_PER_SIMD =
+      D == 13824 ? 8 : D == 12288 ? 3 : SPLIT ? 5 : (D == 4096 ? 4 : 1);
   // register budget of the one-batch-ahead prefetch
   static constexpr bool PREFETCH = SPLIT || (TB * CPT * 4) <= (W <= 8 ? 48 : 32);
   static_assert(S <= 1024 && S >= 128, "slot size");
-  static_assert(XB <= 2 && (1 << XB) <= G, "at most 4 slots per block");
+  static_assert(XB <= 2 && (1 << XB) <= GW, "at most 4 slots per block, held by one wave");
+  static_assert(GS == 1 || (GS == 2 && (1 << MB) <= GW), "a split tile keeps the low group bits");
   static_assert(NSLOT % 4 == 0 || XB == 0, "a partial last tile needs slots that transform alone");
   static_assert(CH % WSTG == 0, "every staging thread owns whole chunks");
   static_assert(!SPLIT || W == WT, "one compute wave per wave tile");
@@ -232,7 +258,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
   constexpr int CELLB = GR::CELLB;
   constexpr int S = SH::S, P = SH::P, TB = SH::TB, WT = SH::WT, W = SH::W, CPT = SH::CPTS;
   constexpr int WSTG = SH::WSTG, WTOT = SH::WTOT;
-  constexpr int G = SH::G;
+  constexpr int G = SH::G, GW = SH::GW;
   // a static array: its base is a compile-time constant, so every table and
   // token-buffer offset below folds into the LDS instructions' immediates
   __shared__ __attribute__((aligned(16))) uint8_t lds[SH::LDS];
@@ -394,8 +420,11 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       __syncthreads();
     }
 
-    // ---- compute: wave tiles q = wave, wave + W, ...
+    // ---- compute: wave tiles q = wave, wave + W, ...; wave tile q is half
+    // hh of 4-slot tile qt when a tile is split over two waves
     for (int q = wave; q < WT; q += W) {
+      const int qt = q / SH::GS;
+      const int hh = SH::GS == 1 ? 0 : __builtin_amdgcn_readfirstlane(q % SH::GS);
       // output side: row rl = lane >> 4 of the tile.  Before the stages
       // across slots it holds slot 4q + rl; after them the low XB bits of
       // the slot are register-index bits (group bits, see below) and the low
@@ -404,7 +433,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       const int rl = lane >> 4;
       // rows past the batch's last slot (a partial last tile; only without
       // stages across slots) compute on a copy of that slot and store nothing
-      const int sig_r = 4 * q + (rl & ~((1 << SH::XB) - 1));
+      const int sig_r = 4 * qt + (rl & ~((1 << SH::XB) - 1));
       const bool row_ok = SH::NSLOT % 4 == 0 || sig_r < SH::NSLOT;
       const int sig_o = row_ok ? sig_r : SH::NSLOT - 1;
       const int tko = sig_o / P, jo = sig_o - tko * P;
@@ -422,7 +451,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       const float a8 = us * GR::PER_UNIT;                        // 8 bytes per cell
       constexpr float m8 = kMagic + (float)(CELLB / 2);          // middle cell at u = 0
       // input side: MFMA row r = lane & 15 -> slot r>>2, chunk (r&3) of each group
-      const int sig_i = min(4 * q + ((lane & 15) >> 2), SH::NSLOT - 1);
+      const int sig_i = min(4 * qt + ((lane & 15) >> 2), SH::NSLOT - 1);
       const int tki = sig_i / P, ji = sig_i - tki * P;
       const uint8_t *ya = lds + SH::YB_OFF + (cur * TB + tki) * SH::TOKB +
                           2 * (ji * SH::SP + 32 * (lane & 3) + 8 * (lane >> 4));
@@ -433,34 +462,44 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       // the in-chunk bits and the low MB group bits at once (the Sylvester
       // matrix is a Kronecker product over the coordinate bits, so its
       // factors can be applied in any order and any grouping).  Output
-      // block b of group block gb lands in register group gb GA + b.
-      constexpr int GA = 1 << SH::MB, GB = G / GA;
-      float v[G][2][4];
+      // block b of group block gb lands in register group gb GA + b.  With
+      // a split tile the top group bit joins them: the wave of half hh
+      // accumulates both halves a1 of the slot's groups with the sign of
+      // H_2[hh][a1], and its register group g is group hh GW + g.
+      constexpr int GA = 1 << SH::MB, GB = GW / GA, GS = SH::GS;
+      float v[GW][2][4];
+      auto transform = [&](auto half) {
+        constexpr int HH = decltype(half)::value;
 #pragma unroll
-      for (int gb = 0; gb < GB; gb++) {
-        floatx4 acc[GA][2];
+        for (int gb = 0; gb < GB; gb++) {
+          floatx4 acc[GA][2];
 #pragma unroll
-        for (int b = 0; b < GA; b++) acc[b][0] = acc[b][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+          for (int b = 0; b < GA; b++) acc[b][0] = acc[b][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int a = 0; a < GA; a++) {
-          const bf16x8 av = *(const bf16x8 *)(ya + 256 * (gb * GA + a));
+          for (int a1 = 0; a1 < GS; a1++)
 #pragma unroll
-          for (int b = 0; b < GA; b++) {
-            const bool neg = __builtin_popcount(a & b) & 1;
-            acc[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, neg ? nhb0 : hb0, acc[b][0],
-                                                                0, 0, 0);
-            acc[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, neg ? nhb1 : hb1, acc[b][1],
-                                                                0, 0, 0);
-          }
+            for (int a = 0; a < GA; a++) {
+              const bf16x8 av = *(const bf16x8 *)(ya + 256 * (a1 * GW + gb * GA + a));
+#pragma unroll
+              for (int b = 0; b < GA; b++) {
+                const bool neg = (__builtin_popcount(a & b) & 1) ^ (a1 & HH);
+                acc[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, neg ? nhb0 : hb0, acc[b][0],
+                                                                    0, 0, 0);
+                acc[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, neg ? nhb1 : hb1, acc[b][1],
+                                                                    0, 0, 0);
+              }
+            }
+#pragma unroll
+          for (int b = 0; b < GA; b++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              v[gb * GA + b][0][i] = acc[b][0][i];
+              v[gb * GA + b][1][i] = acc[b][1][i];
+            }
         }
-#pragma unroll
-        for (int b = 0; b < GA; b++)
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            v[gb * GA + b][0][i] = acc[b][0][i];
-            v[gb * GA + b][1][i] = acc[b][1][i];
-          }
-      }
+      };
+      if (hh == 0) transform(Half<0>{});
+      else if constexpr (GS == 2) transform(Half<1>{});
       // butterfly (scaling comes later: an fma(p0, us, -p1 us) would turn an
       // exact cancellation p0 = p1 into a rounding residue of either sign,
       // and an exact zero sits on a decision threshold)
@@ -470,12 +509,12 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       };
       // register stages over the chunk bits the matrix cores did not take:
       // chunk = 4g + i, bits 0-1 are i, bits 2.. are g
-      constexpr int NCB = SH::CBITS - SH::MB;  // register chunk stages
+      constexpr int NCB = SH::CBITS - SH::MB - (GS - 1);  // register chunk stages
 #pragma unroll
       for (int st = 0; st < NCB; st++) {
         const int bit = st < 2 ? st : st + SH::MB;
 #pragma unroll
-        for (int g = 0; g < G; g++)
+        for (int g = 0; g < GW; g++)
 #pragma unroll
           for (int w = 0; w < 2; w++)
 #pragma unroll
@@ -489,7 +528,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
 #pragma unroll
       for (int x = 0; x < SH::XB; x++) {
 #pragma unroll
-        for (int g = 0; g < G; g++) {
+        for (int g = 0; g < GW; g++) {
           if (g & (1 << x)) continue;
           const int g2 = g | (1 << x);
 #pragma unroll
@@ -507,24 +546,26 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
         }
       }
       // quantize + pack + store.  Register group g holds slot jo + (g & m)
-      // and group (g & ~m) | (rl & m) of that slot, m = 2^XB - 1.
+      // and group hh GW + (g & ~m) | (rl & m) of that slot, m = 2^XB - 1.
       constexpr int XM = (1 << SH::XB) - 1;
       // tok_end: stores happen for tok < tok_end (n_tok, or 0 for rows past
       // the batch's last slot)
       const int64_t tok = b * TB + tko, tok_end = row_ok ? n_tok : 0;
-      if ((lane & 15) == 0 && (rl & XM) == 0 && jo == 0 && tok < tok_end) norms[tok] = s;
-      uint8_t *dst0 = codes + tok * row_bytes + 16 * BITS * (jo * G + (rl & XM)) + BITS * (lane & 15);
+      if ((lane & 15) == 0 && (rl & XM) == 0 && jo == 0 && hh == 0 && tok < tok_end) norms[tok] = s;
+      const int gh = hh * GW;  // first group of this wave's half
+      uint8_t *dst0 =
+          codes + tok * row_bytes + 16 * BITS * (jo * G + gh + (rl & XM)) + BITS * (lane & 15);
       // fake quantization: coordinate of register (g, w, i) is
-      // (jo + (g & XM)) S + ((g & ~XM) | (rl & XM)) 128 + 32 i + 16 w + (lane & 15)
-      uint16_t *dq0 = dq + tok * D + jo * S + (rl & XM) * 128 + (lane & 15);
+      // (jo + (g & XM)) S + (gh + (g & ~XM) | (rl & XM)) 128 + 32 i + 16 w + (lane & 15)
+      uint16_t *dq0 = dq + tok * D + jo * S + (gh + (rl & XM)) * 128 + (lane & 15);
       const float fs = s * (1.0f / __builtin_sqrtf((float)D));  // s / sqrt(d)
       if constexpr (ZO) {
         // rotated values: z = v us / sqrt(d), same coordinates as above
         const float rsd = us / __builtin_sqrtf((float)D);
-        float *z0 = zout + tok * D + jo * S + (rl & XM) * 128 + (lane & 15);
+        float *z0 = zout + tok * D + jo * S + (gh + (rl & XM)) * 128 + (lane & 15);
         if (tok < tok_end) {
 #pragma unroll
-          for (int g = 0; g < G; g++)
+          for (int g = 0; g < GW; g++)
 #pragma unroll
             for (int w = 0; w < 2; w++)
 #pragma unroll
@@ -534,7 +575,7 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
         continue;  // wave-uniform: no codes in this mode
       }
 #pragma unroll
-      for (int g = 0; g < G; g++) {
+      for (int g = 0; g < GW; g++) {
         uint32_t word = 0, word1 = 0;  // word1: codes 4-7 at 8 bits
 #pragma unroll
         for (int w = 0; w < 2; w++)

@@ -105,6 +105,21 @@ def test_partial_last_tile_token_counts(q, M, bits):
     _check_rows(q, x, wl.BF16, d, 123, bits, True, f"d=13824 M={M}")
 
 
+@pytest.mark.parametrize("M", [1, 3, 5, 260])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("d", [4096, 12288])
+def test_split_tile_token_counts(q, d, M, bits):
+    """h = 4096: each 4-slot wave tile is one Hadamard block, produced by two
+    waves that each hold half of its groups.  Token counts that leave the
+    last batch part-filled (1, 3, 5) and several batches per workgroup
+    (260), checked code by code, with norms and rotated values, against the
+    oracle, so a group handed to the wrong half or stored at the other
+    half's place fails."""
+    x = wl.custom_activations(M, d, wl.BF16, d + 3 * M + bits, n_out=max(1, d // 100),
+                              out_factor=50.0, sigma_s=1.5, zero_rows=(M - 1,) if M > 2 else ())
+    _check_rows(q, x, wl.BF16, d, 321, bits, True, f"split d={d} M={M} b={bits}")
+
+
 @pytest.mark.parametrize("d", [128, 384, 640, 1024, 1152, 2048, 4096, 8192, 16384])
 def test_other_dimensions(q, d):
     """Block sizes 128..16384 and odd block counts."""
@@ -328,18 +343,21 @@ def test_rotated_basis_tokens(q, d, bits):
 
 
 @pytest.mark.parametrize("M", [1, 3])
-def test_partial_last_tile_writes_nothing_past_the_outputs(q, M):
+@pytest.mark.parametrize("d", [13824, 12288, 4096])
+def test_partial_last_tile_writes_nothing_past_the_outputs(q, d, M):
     """d = 13824: the fourth row of each token's last wave tile works on a
-    copy and must store nothing.  Codes, fake-quantized values, rotated
+    copy and must store nothing; d = 12288 and 4096 (two waves per wave
+    tile, several tokens per batch): a part-filled last batch must store
+    nothing for its missing tokens.  Codes, fake-quantized values, rotated
     values and norms go into the front of buffers two rows longer, filled
     with a sentinel: the extra rows keep it, and the front matches a call
     into buffers of the exact size."""
     import ctypes
     import torch
-    d, seed, bits = 13824, 123, 4
+    seed, bits = 123, 4
     x = to_device(wl.custom_activations(M, d, wl.BF16, d + 7, n_out=30, out_factor=50.0,
                                         sigma_s=1.0))
-    say("guard rows", M)
+    say("guard rows", d, M)
 
     def guarded(shape, dtype):
         t = torch.empty((M + 2,) + shape, dtype=dtype, device="cuda")
