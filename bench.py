@@ -8,7 +8,9 @@ low-bit linear against weight codes prepared offline.  Weight preparation
 (rotate + quantize of the weight rows) runs once before the timed region,
 as it would when a layer is loaded, and is timed on its own.  The codebook
 and rotation plan are host-side precomputations cached by the library after
-the first call.
+the first call.  Before the W warm-up steps, untimed settle steps run for
+about --settle-ms (200 ms by default), so the timed steps see the clocks of
+a GPU under this load rather than of one just out of idle.
 
 Prints ONE JSON line with the throughput of the step (in the linear's
 FLOP-equivalent TFLOP/s), per-kernel rates, the roofline of the dominant
@@ -33,6 +35,7 @@ Other modes:
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -43,6 +46,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+# Untimed steps before the warm-up steps, in ms of load.  From idle the
+# part's clocks need tens of milliseconds of this load to settle: at
+# 9216 x 9216 x 3072 the linear's first calls took 480 us, the next ten
+# 550-600 us, and it settled at 447 us after about 50 ms.
+SETTLE_MS = 200.0
 MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, 2.5 PFLOP/s
 
 
@@ -55,6 +63,9 @@ def parse():
     p.add_argument("--linear", default=None, help="linear name inside the workload")
     p.add_argument("--bits", default=None, help="w,a bits (default: the workload's first pair)")
     p.add_argument("--sets", type=int, default=2, help="activation buffer sets cycled")
+    p.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                   help="before the warm-up steps, untimed steps for about this long, so the "
+                        "clocks settle at their loaded state (0: none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=3072,
                    help="token rows of the oracle's sample (rotate + quantize and the linear)")
@@ -390,6 +401,14 @@ def _short_kernel_name(name):
     return n.replace("void ", "").strip()
 
 
+def _step_launches(line):
+    """Activation launches of the steps one bench line ran: settle, warm-up
+    and timed steps (None for a line without step counts)."""
+    if "steps" not in line or "warmup" not in line:
+        return None
+    return int(line["steps"]) + int(line["warmup"]) + int(line.get("settle", {}).get("steps", 0))
+
+
 def _split_rotate(rows, n_prep, n_act=None):
     """Rotate-kernel rows of a rocprofv3 csv in dispatch order -> (weight
     preparation rows, activation rows): the first n_prep dispatches of the
@@ -447,10 +466,9 @@ def summarize_profiles(a):
         tr = [r for r in csv.DictReader(open(trace))
               if _short_kernel_name(r["Kernel_Name"]) == rot_name]
         n_act = None
-        if a.profile_bench_log:  # the steps' own launches: warm-up + timed steps
+        if a.profile_bench_log:  # the steps' own launches
             jl = json.loads([l for l in open(a.profile_bench_log) if l.startswith("{")][-1])
-            if "steps" in jl and "warmup" in jl:
-                n_act = int(jl["steps"]) + int(jl["warmup"])
+            n_act = _step_launches(jl)
         prep, act = _split_rotate(tr, n_prep, n_act)
         dur = lambda rs: [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
         if act:
@@ -634,12 +652,20 @@ def write_counter_summary(a, tag, lin_parts, rot_name, M, N, K, ba, bw, in_b, n_
         f.write("\n".join(lines))
 
 
-def _median_ms(fn, n_sets, iters):
+def _median_ms(fn, n_sets, iters, settle_ms=SETTLE_MS):
     """Median of per-call HIP event times (current stream), cycling buffer
-    sets, after two untimed rounds."""
+    sets, after two untimed rounds and untimed calls for about settle_ms."""
     import torch
     for i in range(2 * n_sets):
         fn(i % n_sets)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t0) * 1e3 < settle_ms and i < 5000:
+        fn(i % n_sets)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(iters)]
@@ -709,13 +735,14 @@ PREP_TIMED = 5  # timed weight-preparation launches after the first one
 BACK_TO_BACK = 20  # rotate+quantize launches timed alone after the steps
 
 
-def online_step(q, lin, cfg, bw, ba, steps, warmup, sets, calib_copy_mib=0):
+def online_step(q, lin, cfg, bw, ba, steps, warmup, sets, calib_copy_mib=0, settle_ms=0.0):
     """Times the online step of one linear: weight codes prepared once
     (offline; 1 + PREP_TIMED launches, the first untimed, before anything
-    else touches the rotate kernel), then `warmup` untimed and `steps` timed
-    steps of rotate + quantize (activation set i mod sets) followed by the
-    linear, with HIP events on the launch stream around each kernel and the
-    whole timed region bracketed by device synchronisations."""
+    else touches the rotate kernel), then untimed settle steps for about
+    `settle_ms` (the first one measures the step), `warmup` untimed and
+    `steps` timed steps of rotate + quantize (activation set i mod sets)
+    followed by the linear, with HIP events on the launch stream around each
+    kernel and the whole timed region bracketed by device synchronisations."""
     import torch
     import workloads as wl
     M, N, K = lin.act.M, lin.weight.N, lin.act.d
@@ -766,6 +793,20 @@ def online_step(q, lin, cfg, bw, ba, steps, warmup, sets, calib_copy_mib=0):
         if ev is not None:
             ev[2].record(stream)
 
+    n_settle, settle_total = 0, 0.0
+    if settle_ms > 0:
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        step(0)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        first = s0.elapsed_time(s1)
+        n_settle = 1 + min(2000, max(0, int(math.ceil((settle_ms - first) / max(first, 1e-3)))))
+        for i in range(1, n_settle):
+            step(i)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        settle_total = s0.elapsed_time(s1)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -802,6 +843,8 @@ def online_step(q, lin, cfg, bw, ba, steps, warmup, sets, calib_copy_mib=0):
         "rot_steps": np.array([e[0].elapsed_time(e[1]) for e in evs]),
         "t_prep": t_prep,
         "prep_launches": 1 + PREP_TIMED,
+        "settle_steps": n_settle,
+        "settle_ms": settle_total,
     }
     r["x0"], r["W"] = xs[0], W
     del xs[1:], ac, an, y, wc, wn
@@ -854,7 +897,8 @@ def main():
     tag = f"{cfg}_w{bw}a{ba}"
     torch.cuda.set_device(0)
 
-    r = online_step(q, lin, cfg, bw, ba, a.steps, a.warmup, a.sets, a.calib_copy_mib)
+    r = online_step(q, lin, cfg, bw, ba, a.steps, a.warmup, a.sets, a.calib_copy_mib,
+                    a.settle_ms)
     rt = step_rates(lin, bw, ba, r)
     x0, W0 = r.pop("x0"), r.pop("W")
     ref_gemm = None if a.no_ref_gemm else library_fp16_gemm(M, N, K)
@@ -867,7 +911,8 @@ def main():
     second = None
     if not a.no_second_shape and cfg != "image_qkv":
         l2 = wl.CONFIGS["image_qkv"]["linears"][0]
-        r2 = online_step(q, l2, "image_qkv", 4, 4, max(a.steps, 20), max(a.warmup, 3), 4)
+        r2 = online_step(q, l2, "image_qkv", 4, 4, max(a.steps, 20), max(a.warmup, 3), 4,
+                         settle_ms=a.settle_ms)
         r2.pop("x0"), r2.pop("W")
         rt2 = step_rates(l2, 4, 4, r2)
         second = {
@@ -894,6 +939,9 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
+        "settle": {"what": "untimed steps before the warm-up steps, so the clocks settle at "
+                           "their loaded state",
+                   "steps": r["settle_steps"], "ms": round(r["settle_ms"], 1)},
         "ms_per_step": round(r["ms_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",

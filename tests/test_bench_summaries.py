@@ -149,3 +149,11 @@ def test_split_rotate_counts_only_the_steps_launches():
     assert [int(r["Dispatch_Id"]) for r in act] == [3, 5, 7, 9]
     prep, act = bench._split_rotate(rows, 2)
     assert [int(r["Dispatch_Id"]) for r in act] == [3, 5, 7, 9, 11, 13, 15]
+
+
+def test_step_launches_count_settle_warmup_and_timed_steps():
+    """The activation launches the summaries attribute to the steps: every
+    step the bench line says it ran, settle steps included."""
+    assert bench._step_launches({"steps": 10, "warmup": 2, "settle": {"steps": 45}}) == 57
+    assert bench._step_launches({"steps": 10, "warmup": 2}) == 12
+    assert bench._step_launches({"metric": "x"}) is None
