@@ -731,7 +731,56 @@ def sweep(q, iters=20):
     return 0
 
 
+class KernelEvent:
+    """A HIP timing event recorded without the system-scope fence
+    (hipEventDisableSystemFence), for the per-kernel events inside the timed
+    steps: a default event makes the queue write back and invalidate the
+    caches when it is recorded, which after the linear's 1 GB of output put
+    about 10 us between it and the next launch (the untimed steps run back
+    to back with no gap).  Made through the HIP runtime the process already
+    uses (torch's libamdhip64, found by soname); read only after a device
+    synchronisation."""
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+    _hip = None
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            import ctypes
+            lib = ctypes.CDLL("libamdhip64.so.7")
+            P = ctypes.c_void_p
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(P), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [P, P]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+            lib.hipEventDestroy.argtypes = [P]
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self.h = ctypes.c_void_p()
+        if self.hip().hipEventCreateWithFlags(ctypes.byref(self.h), self.FLAGS) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream):
+        import ctypes
+        if self.hip().hipEventRecord(self.h, ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end):
+        import ctypes
+        ms = ctypes.c_float()
+        if self.hip().hipEventElapsedTime(ctypes.byref(ms), self.h, end.h) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        if self._hip is not None and self.h:
+            self._hip.hipEventDestroy(self.h)
+
+
 PREP_TIMED = 5  # timed weight-preparation launches after the first one
+LEAD_CYCLES = 400_000  # untimed spin before the timed region (a few hundred us)
 BACK_TO_BACK = 20  # rotate+quantize launches timed alone after the steps
 
 
@@ -741,8 +790,9 @@ def online_step(q, lin, cfg, bw, ba, steps, warmup, sets, calib_copy_mib=0, sett
     else touches the rotate kernel), then untimed settle steps for about
     `settle_ms` (the first one measures the step), `warmup` untimed and
     `steps` timed steps of rotate + quantize (activation set i mod sets)
-    followed by the linear, with HIP events on the launch stream around each
-    kernel and the whole timed region bracketed by device synchronisations."""
+    followed by the linear, with one fence-free HIP event on the launch
+    stream between consecutive kernels and the whole timed region bracketed
+    by device synchronisations."""
     import torch
     import workloads as wl
     M, N, K = lin.act.M, lin.weight.N, lin.act.d
@@ -782,16 +832,14 @@ def online_step(q, lin, cfg, bw, ba, steps, warmup, sets, calib_copy_mib=0, sett
     torch.cuda.synchronize()
     t_prep = float(np.median([e0.elapsed_time(e1) for e0, e1 in pev]))
 
-    def step(i, ev=None):
+    def step(i, mid=None, end=None):
         s = i % sets
-        if ev is not None:
-            ev[0].record(stream)
         q.rotate_quantize(xs[s], lin.seed, ba, out=ac[s], norms=an[s])
-        if ev is not None:
-            ev[1].record(stream)
+        if mid is not None:
+            mid.record(stream)
         q.linear(ac[s], an[s], ba, wc, wn, bw, K, out=y)
-        if ev is not None:
-            ev[2].record(stream)
+        if end is not None:
+            end.record(stream)
 
     n_settle, settle_total = 0, 0.0
     if settle_ms > 0:
@@ -810,13 +858,22 @@ def online_step(q, lin, cfg, bw, ba, steps, warmup, sets, calib_copy_mib=0, sett
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    # one event between consecutive kernels (each recorded event costs the
+    # queue a few microseconds): mark 2i opens step i's rotate+quantize,
+    # 2i+1 separates it from the linear, 2i+2 closes the step and opens the
+    # next
+    marks = [KernelEvent() for _ in range(2 * steps + 1)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # untimed: a short spin kernel keeps the device busy while the host
+    # queues the first steps, so the timed region starts with launches
+    # already queued instead of the host's latency for the first one
+    torch.cuda._sleep(LEAD_CYCLES)
     start.record(stream)
+    marks[0].record(stream)
     for i in range(steps):
-        step(i, evs[i])
+        step(i, marks[2 * i + 1], marks[2 * i + 2])
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
@@ -836,11 +893,14 @@ def online_step(q, lin, cfg, bw, ba, steps, warmup, sets, calib_copy_mib=0, sett
     r = {
         "t_rot_b2b": b0.elapsed_time(b1) / BACK_TO_BACK,
         "ms_step": total_ms / steps,
-        "t_rot": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
-        "t_lin": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
-        "per_step": np.array([e[0].elapsed_time(e[2]) for e in evs]),
-        "lin_steps": np.array([e[1].elapsed_time(e[2]) for e in evs]),
-        "rot_steps": np.array([e[0].elapsed_time(e[1]) for e in evs]),
+        "t_rot": float(np.mean([marks[2 * i].elapsed_time(marks[2 * i + 1])
+                                for i in range(steps)])),
+        "t_lin": float(np.mean([marks[2 * i + 1].elapsed_time(marks[2 * i + 2])
+                                for i in range(steps)])),
+        "per_step": np.array([marks[2 * i].elapsed_time(marks[2 * i + 2]) for i in range(steps)]),
+        "lin_steps": np.array([marks[2 * i + 1].elapsed_time(marks[2 * i + 2])
+                               for i in range(steps)]),
+        "rot_steps": np.array([marks[2 * i].elapsed_time(marks[2 * i + 1]) for i in range(steps)]),
         "t_prep": t_prep,
         "prep_launches": 1 + PREP_TIMED,
         "settle_steps": n_settle,
