@@ -35,7 +35,6 @@ Other modes:
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -780,7 +779,7 @@ class KernelEvent:
 
 
 PREP_TIMED = 5  # timed weight-preparation launches after the first one
-LEAD_CYCLES = 400_000  # untimed spin before the timed region (a few hundred us)
+LEAD_CYCLES = 500_000  # untimed spin before the timed region (about 200 us)
 BACK_TO_BACK = 20  # rotate+quantize launches timed alone after the steps
 
 
@@ -841,30 +840,35 @@ def online_step(q, lin, cfg, bw, ba, steps, warmup, sets, calib_copy_mib=0, sett
         if end is not None:
             end.record(stream)
 
+    # every event of the timed region is made here, before the settle steps:
+    # making them takes tens of milliseconds, and an idle device that long
+    # starts the clock transient over.  One event between consecutive
+    # kernels (each recorded event costs the queue a few microseconds):
+    # mark 2i opens step i's rotate+quantize, 2i+1 separates it from the
+    # linear, 2i+2 closes the step and opens the next
+    marks = [KernelEvent() for _ in range(2 * steps + 1)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for e in (start, stop, s0, s1):  # torch makes its events at the first record
+        e.record(stream)
+    torch.cuda.synchronize()
     n_settle, settle_total = 0, 0.0
     if settle_ms > 0:
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s0.record(stream)
-        step(0)
-        s1.record(stream)
-        torch.cuda.synchronize()
-        first = s0.elapsed_time(s1)
-        n_settle = 1 + min(2000, max(0, int(math.ceil((settle_ms - first) / max(first, 1e-3)))))
-        for i in range(1, n_settle):
-            step(i)
+        t0 = time.perf_counter()
+        while n_settle < 4000:
+            step(n_settle)
+            n_settle += 1
+            if n_settle % 4 == 0:  # a short wait, the next launches follow at once
+                torch.cuda.synchronize()
+                if (time.perf_counter() - t0) * 1e3 >= settle_ms:
+                    break
         s1.record(stream)
         torch.cuda.synchronize()
         settle_total = s0.elapsed_time(s1)
     for i in range(warmup):
         step(i)
-    torch.cuda.synchronize()
-    # one event between consecutive kernels (each recorded event costs the
-    # queue a few microseconds): mark 2i opens step i's rotate+quantize,
-    # 2i+1 separates it from the linear, 2i+2 closes the step and opens the
-    # next
-    marks = [KernelEvent() for _ in range(2 * steps + 1)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     # untimed: a short spin kernel keeps the device busy while the host
     # queues the first steps, so the timed region starts with launches
