@@ -746,7 +746,18 @@ class KernelEvent:
     def hip(cls):
         if cls._hip is None:
             import ctypes
-            lib = ctypes.CDLL("libamdhip64.so.7")
+            # the copy already mapped into this process (torch's), so the
+            # events belong to the runtime that owns the streams
+            path = "libamdhip64.so.7"
+            try:
+                with open("/proc/self/maps") as f:
+                    for line in f:
+                        if "libamdhip64.so" in line:
+                            path = line.split()[-1]
+                            break
+            except OSError:
+                pass
+            lib = ctypes.CDLL(path)
             P = ctypes.c_void_p
             lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(P), ctypes.c_uint]
             lib.hipEventRecord.argtypes = [P, P]
