@@ -120,9 +120,11 @@ struct Grid {
 //    the MFMA then applies a 2^(5+MB)-point Hadamard (the H_32 operand and
 //    the +-1 signs of H_(2^MB) over 2^MB accumulated k-blocks), 2^(2MB+1)
 //    MFMAs per 16 x 2^(5+MB) block instead of MB register butterfly stages.
-//    One bit: 8-10% faster at d = 12288 and 5120, equal at 1024, 3072 and
-//    13824, 12% slower at 4096 (more MFMA chains than the register stages
-//    they replace); two or three bits were slower everywhere.
+//    One bit: 8-10% faster at d = 5120 (and at 12288 with one wave per
+//    4096 block; equal there with the split tiles), equal at 1024, 3072 and
+//    13824, 12% slower at 4096 (6-8% with the split tiles: more MFMA chains
+//    than the register stages they replace); two or three bits were slower
+//    everywhere.
 //  * d = 5120 runs 512-coordinate slots (one permlane stage joins the two
 //    halves of each 1024 block) so that a batch of two tokens still tiles
 //    the five waves: half the staging registers, which leaves room for the
