@@ -27,7 +27,10 @@
 //    rows were permuted by pi, see oq_permute_rows) the chunk is stored as
 //    one 16-byte LDS write after the sign XOR: no scatter at all.
 //  * Norm.  The 8 bf16 of a staged chunk are an MFMA operand as they are:
-//    mfma(X, X) accumulates X X^T, whose trace is the sum of squares.
+//    mfma(X, X) accumulates X X^T, whose trace is the sum of squares.  With
+//    split roles (d = 3072, 5120) the last staging wave to deliver its
+//    partials of a batch (an LDS arrival counter; no wave waits) sums them
+//    in wave order and finishes the norms before the batch's barrier.
 //  * Walsh-Hadamard, stages 0-4.  bf16 values are exact MFMA operands and
 //    H_32 is +-1, so v_mfma_f32_16x16x32_bf16 applies the 32-point
 //    transform of every 32-element chunk with fp32 accumulation.  The 16
@@ -196,6 +199,10 @@ struct Shape {
   static constexpr int WSTG = SPLIT ? WS : W;          // waves that stage
   static constexpr int CPTS = CH / WSTG;               // staged chunks per thread per token
   static constexpr int NBUF = SPLIT ? 2 : 1;
+  // with split roles the staging waves also finish each token's norm
+  // (d = 5120: 1.5-3% faster; 3072 equal), except at d = 13824, whose
+  // 64-register budget the finishing code overflows (3 spilled, 1% slower)
+  static constexpr bool FIN = SPLIT && D != 13824;
   static constexpr int G = S / 128;                   // 128-coordinate groups per slot
   static constexpr int GW = G / GS;                   // groups of a slot one wave holds
   static constexpr int CBITS = ilog2(S) - 5;          // chunk bits (above the 32-element chunk)
@@ -211,7 +218,11 @@ struct Shape {
   // LDS layout: tables first so their offsets fit instruction immediates
   static constexpr int CT_OFF = 0;                    // cell table, offsets are immediates
   static constexpr int NP_OFF = CT_OFF + Grid<D, BITS>::CELLB;  // [NBUF][TB][WSTG] sums of squares
-  static constexpr int LV_OFF = NP_OFF + ((NBUF * TB * WSTG * 4 + 15) / 16) * 16;  // unit levels
+  // FIN: [NBUF][TB] finished {s, 1/(s sqrt(h/d))} per token, and [NBUF]
+  // arrival counters of the staging waves
+  static constexpr int FN_OFF = NP_OFF + ((NBUF * TB * WSTG * 4 + 15) / 16) * 16;
+  static constexpr int CN_OFF = FN_OFF + ((NBUF * TB * 8 + 15) / 16) * 16;
+  static constexpr int LV_OFF = CN_OFF + 16;  // unit levels
   static constexpr int YB_OFF = LV_OFF + (4 << BITS);
   static constexpr int LDS = YB_OFF + NBUF * TB * TOKB;
   // register target (waves per SIMD): 5 with staging waves (about 70
@@ -231,6 +242,20 @@ struct Shape {
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert((int)Grid<D, BITS>::MASK + 8 <= LDS, "masked offsets stay in the workgroup's LDS");
 };
+
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// s = sqrt(ss) and us = 1 / (s sqrt(h/d)) (v -> sqrt(d) z) by the hardware
+// square root and reciprocal (1 ulp each; a sum of squares below 2^-64 is
+// scaled by 2^64 first, away from the range where the square root loses
+// accuracy): a few instructions instead of the correctly rounded
+// sequences, and the codes only move inside the decision windows that
+// rounding of the transform already leaves
+__device__ __forceinline__ floatx2 token_norm(float ss, float scale_hd) {
+  const bool tiny = ss < 0x1p-64f;
+  const float s = __builtin_amdgcn_sqrtf(tiny ? ss * 0x1p64f : ss) * (tiny ? 0x1p-32f : 1.0f);
+  return floatx2{s, (s > 0.f) ? __builtin_amdgcn_rcpf(s * scale_hd) : 0.f};
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -269,6 +294,13 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
   const int swave = SH::SPLIT ? wave - W : wave;   // index among the staging waves
   const int tid = swave * 64 + lane;               // staging thread index
   float *npart = (float *)(lds + SH::NP_OFF);
+  floatx2 *fin = (floatx2 *)(lds + SH::FN_OFF);
+  uint32_t *arrived = (uint32_t *)(lds + SH::CN_OFF);
+  if constexpr (SH::FIN) {
+    // zeroed before any staging wave counts (the barrier runs in every wave)
+    if (tid0 < SH::NBUF) arrived[tid0] = 0;
+    __syncthreads();
+  }
 
   // cell table (and the levels, for fake quantization) into LDS
   if constexpr (!ZO) {
@@ -374,6 +406,23 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       const float q3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(dgi, 60));
       if (lane == 0) npart[(nb * TB + tk) * WSTG + swave] = (q0 + q1) + (q2 + q3);
     }
+    if constexpr (SH::FIN) {
+      // the last staging wave to deliver its partials of this buffer sums
+      // them (in wave order, whichever wave it is) and finishes every
+      // token's norm before the batch's barrier, so the compute waves read
+      // one value per token; nothing waits here
+      uint32_t prev = 0;
+      if (lane == 0)
+        prev = __hip_atomic_fetch_add(arrived + nb, 1u, __ATOMIC_ACQ_REL,
+                                      __HIP_MEMORY_SCOPE_WORKGROUP);
+      prev = __builtin_amdgcn_readfirstlane(prev);
+      if (prev % WSTG == WSTG - 1 && lane < TB) {
+        float ss = 0.f;
+#pragma unroll
+        for (int w = 0; w < WSTG; w++) ss += npart[(nb * TB + lane) * WSTG + w];
+        fin[nb * TB + lane] = token_norm(ss, scale_hd);
+      }
+    }
   };
   if constexpr (SH::SPLIT) {
     if (stager) {
@@ -439,17 +488,16 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
       const bool row_ok = SH::NSLOT % 4 == 0 || sig_r < SH::NSLOT;
       const int sig_o = row_ok ? sig_r : SH::NSLOT - 1;
       const int tko = sig_o / P, jo = sig_o - tko * P;
-      float ss = 0.f;
+      floatx2 nrm;
+      if constexpr (SH::FIN) {
+        nrm = fin[cur * TB + tko];  // finished by the staging waves
+      } else {
+        float ss = 0.f;
 #pragma unroll
-      for (int w = 0; w < WSTG; w++) ss += npart[(cur * TB + tko) * WSTG + w];
-      // hardware square root and reciprocal (1 ulp each; a sum of squares
-      // below 2^-64 is scaled by 2^64 first, away from the range where the
-      // square root loses accuracy): a few instructions per tile instead of
-      // the correctly rounded sequences, and the codes only move inside the
-      // decision windows that rounding of the transform already leaves
-      const bool tiny = ss < 0x1p-64f;
-      const float s = __builtin_amdgcn_sqrtf(tiny ? ss * 0x1p64f : ss) * (tiny ? 0x1p-32f : 1.0f);
-      const float us = (s > 0.f) ? __builtin_amdgcn_rcpf(s * scale_hd) : 0.f;  // v -> sqrt(d) z
+        for (int w = 0; w < WSTG; w++) ss += npart[(cur * TB + tko) * WSTG + w];
+        nrm = token_norm(ss, scale_hd);
+      }
+      const float s = nrm[0], us = nrm[1];  // us: v -> sqrt(d) z
       const float a8 = us * GR::PER_UNIT;                        // 8 bytes per cell
       constexpr float m8 = kMagic + (float)(CELLB / 2);          // middle cell at u = 0
       // input side: MFMA row r = lane & 15 -> slot r>>2, chunk (r&3) of each group
