@@ -737,8 +737,8 @@ class KernelEvent:
     caches when it is recorded, which after the linear's 1 GB of output put
     about 10 us between it and the next launch (the untimed steps run back
     to back with no gap).  Made through the HIP runtime the process already
-    uses (torch's libamdhip64, found by soname); read only after a device
-    synchronisation."""
+    uses (the libamdhip64 torch mapped, found in /proc/self/maps); read only
+    after a device synchronisation."""
     FLAGS = 0x20000000  # hipEventDisableSystemFence
     _hip = None
 
@@ -798,7 +798,7 @@ def online_step(q, lin, cfg, bw, ba, steps, warmup, sets, calib_copy_mib=0, sett
     """Times the online step of one linear: weight codes prepared once
     (offline; 1 + PREP_TIMED launches, the first untimed, before anything
     else touches the rotate kernel), then untimed settle steps for about
-    `settle_ms` (the first one measures the step), `warmup` untimed and
+    `settle_ms` of wall time, `warmup` untimed and
     `steps` timed steps of rotate + quantize (activation set i mod sets)
     followed by the linear, with one fence-free HIP event on the launch
     stream between consecutive kernels and the whole timed region bracketed
@@ -884,7 +884,8 @@ def online_step(q, lin, cfg, bw, ba, steps, warmup, sets, calib_copy_mib=0, sett
     # untimed: a short spin kernel keeps the device busy while the host
     # queues the first steps, so the timed region starts with launches
     # already queued instead of the host's latency for the first one
-    torch.cuda._sleep(LEAD_CYCLES)
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(LEAD_CYCLES)
     start.record(stream)
     marks[0].record(stream)
     for i in range(steps):
