@@ -385,3 +385,32 @@ def test_partial_last_tile_writes_nothing_past_the_outputs(q, d, M):
         assert untouched(t), "a store landed past the last row"
     assert torch.equal(codes[:M], c_ref) and torch.equal(norms[:M], n_ref)
     assert torch.equal(dq[:M], dq_ref) and torch.equal(z[:M], z_ref)
+
+
+@pytest.mark.parametrize("d", [1024, 3072, 5120, 12288, 13824])
+def test_power_of_two_scaling_is_exact(q, d):
+    """Scaling tokens by 2^k changes no code and no rotated value, and
+    scales the norm by exactly 2^k (z = H D Pi x / (s sqrt(h)) is
+    scale-free, and with power-of-two factors every product, sum, square
+    root and reciprocal of the kernel scales exactly while nothing
+    underflows).  k = -60 puts the sum of squares below 2^-64, where the
+    square root runs on a rescaled sum; k = 40 keeps it below the fp32
+    range limit even for the x50 outlier channels."""
+    import torch
+    M, seed, bits = 37, 91, 4
+    x = wl.custom_activations(M, d, wl.BF16, d + 29, n_out=max(1, d // 100), out_factor=50.0,
+                              sigma_s=1.0, zero_rows=(5,))
+    xd = to_device(x)
+    say("power-of-two scaling", d)
+    c0, n0 = q.rotate_quantize(xd, seed, bits)
+    z0, _ = q.rotate(xd, seed)
+    for k in (-60, -40, -20, 20, 40):
+        xk = (xd.float() * 2.0 ** k).to(torch.bfloat16)  # exact: bf16 keeps the mantissa
+        assert torch.equal(xk.float(), xd.float() * 2.0 ** k)
+        ck, nk = q.rotate_quantize(xk, seed, bits)
+        zk, _ = q.rotate(xk, seed)
+        torch.cuda.synchronize()
+        assert torch.equal(ck, c0), f"codes change under 2^{k}"
+        assert torch.equal(nk, n0 * 2.0 ** k), f"norms not scaled exactly by 2^{k}"
+        assert torch.equal(zk, z0), f"rotated values change under 2^{k}"
+
