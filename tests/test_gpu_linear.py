@@ -309,3 +309,29 @@ def test_maximum_k(q, ba, bw):
     ref = oracle.linear(ac, an, ba, wc, wn, bw, K)
     assert parity.rel_fro(y, ref) <= parity.LINEAR_FRO
     assert np.all(np.abs(y - ref) <= 1e-2 * np.abs(ref).max() + 1e-30)
+
+
+@pytest.mark.parametrize("M,N,K,ba,bw", [
+    (1000, 700, 256, 4, 4),    # 128 x 128 tiles
+    (1000, 700, 256, 3, 2),    # mixed widths
+    (3600, 3300, 384, 4, 4),   # 256 x 256 tiles, one partial round
+    (4352, 4096, 768, 4, 4),   # full round + leftover tiles cut into K ranges
+    (4352, 4096, 768, 8, 8),   # the same at 8 bits
+])
+def test_output_scales_exactly_with_the_norms(q, M, N, K, ba, bw):
+    """y is linear in each token norm and weight row norm, and the kernels
+    apply them as fp32 factors after the dot products: scaling the norms by
+    2^5 and 2^-3 must scale every bf16 output by exactly 4 on every launch
+    path (full tiles, small tiles, K-range pieces and their reduction)."""
+    import torch
+    ac, an = wl.random_codes(M, K, ba, M + 17)
+    wc, wn = wl.random_codes(N, K, bw, N + 19)
+    say("linear norm scaling", M, N, K, ba, bw)
+    a_c, w_c = to_device(ac), to_device(wc)
+    a_n, w_n = to_device(an), to_device(wn)
+    y0 = q.linear(a_c, a_n, ba, w_c, w_n, bw, K)
+    y1 = q.linear(a_c, a_n * 32.0, ba, w_c, w_n * 0.125, bw, K)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y0.float()).all()
+    assert torch.equal(y1.float(), y0.float() * 4.0)
+
