@@ -414,3 +414,40 @@ def test_power_of_two_scaling_is_exact(q, d):
         assert torch.equal(nk, n0 * 2.0 ** k), f"norms not scaled exactly by 2^{k}"
         assert torch.equal(zk, z0), f"rotated values change under 2^{k}"
 
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("d", [1024, 5120, 12288, 13824])
+def test_negated_tokens_take_mirrored_codes(q, d, bits):
+    """The Lloyd-Max codebook is symmetric (its thresholds come in +-
+    pairs, zero the middle one at even level counts): -x must give the same
+    norms, z -> -z up to the transform's rounding (the matrix cores' sums
+    need not round negatives as mirror images), and code (2^b - 1) - c for
+    every coordinate farther than the parity window from a threshold; an
+    exact zero sits on the middle threshold and takes the upper middle code
+    in both."""
+    import torch
+    M, seed = 29, 57
+    x = wl.custom_activations(M, d, wl.BF16, d + bits, n_out=max(1, d // 100), out_factor=50.0,
+                              sigma_s=1.0, zero_rows=(3,))
+    xd = to_device(x)
+    xd[7] = 0.5  # a constant token: exact zeros after the transform
+    say("negated tokens", d, bits)
+    c0, n0 = q.rotate_quantize(xd, seed, bits)
+    c1, n1 = q.rotate_quantize(-xd, seed, bits)
+    z0, _ = q.rotate(xd, seed)
+    z1, _ = q.rotate(-xd, seed)
+    torch.cuda.synchronize()
+    assert torch.equal(n1, n0)
+    za, zb = host(z0).astype(np.float64), host(z1).astype(np.float64)
+    assert np.abs(za + zb).max() <= 1e-6 * np.abs(za).max()
+    u0 = parity.unpack_codes(host(c0), d, bits).astype(np.int64)
+    u1 = parity.unpack_codes(host(c1), d, bits).astype(np.int64)
+    u = np.sqrt(d) * za  # unpacked codes and rotated values: coordinate order
+    tau = np.asarray(oracle.codebook_unit(bits)[1], np.float64)
+    near = (np.abs(u[..., None] - tau) <= parity.CODE_WINDOW * np.maximum(np.abs(tau), 1.0)).any(-1)
+    top = (1 << bits) - 1
+    zero = (za == 0) & (zb == 0)
+    far = ~near & ~zero
+    assert (u1[far] == top - u0[far]).all(), f"{int((u1[far] != top - u0[far]).sum())} unmirrored"
+    assert zero.any(), "the constant token must give exact zeros"
+    assert (u0[zero] == 1 << (bits - 1)).all() and (u1[zero] == 1 << (bits - 1)).all()
