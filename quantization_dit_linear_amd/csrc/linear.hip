@@ -572,7 +572,11 @@ __global__ __launch_bounds__(TL::THREADS, TL::WGS) void linear_kernel(
       if (m >= M || n >= N) continue;
       uint16_t *yp = Y + (int64_t)m * N + n;
       if (vec_store && n + 7 < N) {
-        *(u32x4 *)yp = v;
+        // non-temporal: the output is not read again by this kernel, and
+        // lines that stay dirty in the caches are written back later, in
+        // whatever runs next (the following rotate+quantize at 32760 x 5120
+        // measured 91.3 -> 88.4 us; this kernel equal or 0.3% faster)
+        __builtin_nontemporal_store(v, (u32x4 *)yp);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; e++)
@@ -611,8 +615,9 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(
   const bf16x2 p0 = {(__bf16)(acc[0] * sc * r[0]), (__bf16)(acc[1] * sc * r[1])};
   const bf16x2 p1 = {(__bf16)(acc[2] * sc * r[2]), (__bf16)(acc[3] * sc * r[3])};
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  *(u32x2 *)(Y + (int64_t)m * N + n) =
-      u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+  __builtin_nontemporal_store(
+      u32x2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)},
+      (u32x2 *)(Y + (int64_t)m * N + n));  // output, as in the tile epilogue
 }
 
 PermTab make_tab(const LevelsF16 &lv) {

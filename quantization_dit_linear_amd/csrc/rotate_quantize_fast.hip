@@ -353,13 +353,19 @@ __attribute__((amdgpu_waves_per_eu(Shape<D, BITS>::MIN_WAVES_PER_SIMD, 8))) void
     for (int i = 0; i < 4; i++) dsel[i] = (on_diag && (r & 3) == i) ? 1.f : 0.f;
   }
   u32x4 stg[TB][CPT];
+  // non-temporal loads: every token is read once, so its lines need not
+  // displace what the caches hold -- in a layer the output the previous
+  // kernel has just written (a linear's 1 GB at 32760 x 15360), whose
+  // write-back the displacement would otherwise pull into this kernel's
+  // time (32760 x 5120 after such a linear: 102.6 -> 91.3 us)
   auto load_batch = [&](int64_t b) {
 #pragma unroll
     for (int tk = 0; tk < TB; tk++) {
       const int64_t t = b * TB + tk;
 #pragma unroll
       for (int c = 0; c < CPT; c++)
-        stg[tk][c] = (t < n_tok) ? *(const u32x4 *)(x + t * D + 8 * (tid + c * WSTG * 64))
+        stg[tk][c] = (t < n_tok) ? __builtin_nontemporal_load(
+                                       (const u32x4 *)(x + t * D + 8 * (tid + c * WSTG * 64)))
                                  : u32x4{0, 0, 0, 0};
     }
   };
