@@ -55,7 +55,7 @@ def _load():
     lib.oqo_quantize_one.restype = ctypes.c_int
     lib.oqo_quantize_one.argtypes = [ctypes.c_double, P, ctypes.c_int]
     lib.oqo_slot_of.restype = ctypes.c_int64
-    lib.oqo_slot_of.argtypes = [ctypes.c_int64]
+    lib.oqo_slot_of.argtypes = [ctypes.c_int64, ctypes.c_int]
     lib.oqo_pack_row.restype = None
     lib.oqo_pack_row.argtypes = [P, ctypes.c_int, ctypes.c_int, P]
     lib.oqo_unpack_row.restype = None
@@ -190,8 +190,9 @@ def quantize_one(z, thresholds):
     return _load().oqo_quantize_one(float(z), _ptr(th), len(thresholds) + 1)
 
 
-def slot_of(i):
-    return _load().oqo_slot_of(int(i))
+def slot_of(i, d):
+    """Storage slot of coordinate i in a row of d coordinates."""
+    return _load().oqo_slot_of(int(i), int(d))
 
 
 def pack_row(codes, bits):

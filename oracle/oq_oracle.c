@@ -31,8 +31,9 @@
  *  - Hadamard in Sylvester natural order, H[a][b] = (-1)^popcount(a & b).
  *  - Gather convention y_i = s_i * u_{pi(i)}.
  *  - Ties go to the upper level: code = #{k : z >= tau_k}; -0 counts as 0.
- *  - Codes are stored in a tile-interleaved slot order inside every group of
- *    128 coordinates, then packed as a little-endian bitstream.
+ *  - Codes are stored in a tile-interleaved slot order inside every whole
+ *    group of 128 coordinates (a last, partial group of 32, 64 or 96 in
+ *    coordinate order), then packed as a little-endian bitstream.
  *  - Parity pins for each function are in the oracle test files.  The
  *    permutation itself has no value printed on any page: it is pinned only
  *    through the SplitMix64 published outputs and the bijection property.
@@ -448,11 +449,14 @@ int oqo_quantize_one(double z, const double *thresholds, int L)
     return code;
 }
 
-/* Storage slot of coordinate i: inside each group of 128 coordinates,
- * coordinate 128G + 32c + p (c < 4, p < 32) goes to slot
- * 128G + 8 (p mod 16) + 4 floor(p / 16) + c. */
-int64_t oqo_slot_of(int64_t i)
+/* Storage slot of coordinate i of a row of d coordinates: inside each
+ * whole group of 128 coordinates, coordinate 128G + 32c + p (c < 4,
+ * p < 32) goes to slot 128G + 8 (p mod 16) + 4 floor(p / 16) + c; the
+ * coordinates of a last, partial group (the d mod 128 = 32, 64 or 96 after
+ * the whole groups) keep their own index. */
+int64_t oqo_slot_of(int64_t i, int d)
 {
+    if (i >= (int64_t)(d / 128) * 128) return i;
     int64_t G = i / 128, r = i % 128;
     int64_t c = r / 32, p = r % 32;
     return 128 * G + 8 * (p % 16) + 4 * (p / 16) + c;
@@ -464,7 +468,7 @@ void oqo_pack_row(const uint8_t *codes, int d, int bits, uint8_t *out)
 {
     memset(out, 0, (size_t)d * bits / 8);
     for (int i = 0; i < d; i++) {
-        int64_t bitpos = (int64_t)bits * oqo_slot_of(i);
+        int64_t bitpos = (int64_t)bits * oqo_slot_of(i, d);
         for (int t = 0; t < bits; t++)
             if ((codes[i] >> t) & 1)
                 out[(bitpos + t) / 8] |= (uint8_t)(1u << ((bitpos + t) % 8));
@@ -474,7 +478,7 @@ void oqo_pack_row(const uint8_t *codes, int d, int bits, uint8_t *out)
 void oqo_unpack_row(const uint8_t *packed, int d, int bits, uint8_t *codes)
 {
     for (int i = 0; i < d; i++) {
-        int64_t bitpos = (int64_t)bits * oqo_slot_of(i);
+        int64_t bitpos = (int64_t)bits * oqo_slot_of(i, d);
         int c = 0;
         for (int t = 0; t < bits; t++)
             if ((packed[(bitpos + t) / 8] >> ((bitpos + t) % 8)) & 1) c |= 1 << t;
@@ -507,7 +511,7 @@ int oqo_rotate_quantize_ex(const void *x, int dtype, int64_t rows, int d, uint64
                            int use_signs, int bits, int family, uint8_t *codes, double *norms,
                            double *z)
 {
-    if (d <= 0 || d % 128 != 0 || bits < 1 || bits > 8) return -1;
+    if (d <= 0 || d % 32 != 0 || bits < 1 || bits > 8) return -1;
     const int L = 1 << bits;
     int32_t *perm = malloc(sizeof(int32_t) * d);
     int8_t *sign = malloc(d);
@@ -554,7 +558,7 @@ int oqo_linear_ex(const uint8_t *a_codes, const double *a_norms, int ba,
                   const uint8_t *w_codes, const double *w_norms, int bw, int family,
                   int64_t N, int K, const int64_t *rows, int64_t nrows, double *y)
 {
-    if (K <= 0 || K % 128 != 0) return -1;
+    if (K <= 0 || K % 32 != 0) return -1;
     double la[256], ta[256], lw[256], tw[256];
     family_codebook(family, K, ba, la, ta);
     family_codebook(family, K, bw, lw, tw);
@@ -595,7 +599,7 @@ int oqo_linear_ex(const uint8_t *a_codes, const double *a_norms, int ba,
 int oqo_fake_quantize(const void *x, int dtype, int64_t rows, int d, uint64_t seed,
                       int use_signs, int bits, double *out, double *norms)
 {
-    if (d <= 0 || d % 128 != 0 || bits < 1 || bits > 8) return -1;
+    if (d <= 0 || d % 32 != 0 || bits < 1 || bits > 8) return -1;
     const int L = 1 << bits;
     int32_t *perm = malloc(sizeof(int32_t) * d);
     int8_t *sign = malloc(d);

@@ -24,7 +24,7 @@ void oqo_rotate_token(const double *x, int d, const int32_t *perm, const int8_t 
                       int use_signs, double *z, double *norm);
 
 int oqo_quantize_one(double z, const double *thresholds, int L);
-int64_t oqo_slot_of(int64_t i);
+int64_t oqo_slot_of(int64_t i, int d);
 void oqo_pack_row(const uint8_t *codes, int d, int bits, uint8_t *out);
 void oqo_unpack_row(const uint8_t *packed, int d, int bits, uint8_t *codes);
 

@@ -23,11 +23,15 @@ DEQUANT_RTOL = 2.0 ** -8
 
 
 def slot_index(d):
-    """slot_index(d)[i] = storage slot of coordinate i."""
+    """slot_index(d)[i] = storage slot of coordinate i (whole groups of 128
+    in the group order, a last partial group in coordinate order)."""
     i = np.arange(d, dtype=np.int64)
     G, r = i // 128, i % 128
     c, p = r // 32, r % 32
-    return 128 * G + 8 * (p % 16) + 4 * (p // 16) + c
+    s = 128 * G + 8 * (p % 16) + 4 * (p // 16) + c
+    full = (d // 128) * 128
+    s[full:] = i[full:]
+    return s
 
 
 def unpack_codes(packed, d, bits):

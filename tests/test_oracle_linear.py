@@ -15,9 +15,11 @@ import oracle
 import workloads as wl
 
 
-@pytest.mark.parametrize("ba,bw", [(4, 4), (4, 2), (3, 2), (4, 3), (2, 2), (8, 8)])
-def test_linear_brute_force_tiny(ba, bw):
-    M, N, K = 3, 5, 128
+@pytest.mark.parametrize("ba,bw,K", [(4, 4, 128), (4, 2, 128), (3, 2, 128), (4, 3, 128),
+                                     (2, 2, 128), (8, 8, 128), (4, 4, 96), (3, 4, 192),
+                                     (8, 8, 160)])
+def test_linear_brute_force_tiny(ba, bw, K):
+    M, N = 3, 5
     ac, an = wl.random_codes(M, K, ba, 1)
     wc, wn = wl.random_codes(N, K, bw, 2)
     la, _ = oracle.codebook(K, ba)

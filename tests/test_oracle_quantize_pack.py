@@ -42,12 +42,25 @@ def test_ties_go_up_and_signed_zero(bits):
 
 
 def test_slot_order_is_a_bijection_inside_each_group():
-    slots = [oracle.slot_of(i) for i in range(512)]
+    slots = [oracle.slot_of(i, 512) for i in range(512)]
     for g in range(4):
         assert sorted(slots[128 * g:128 * g + 128]) == list(range(128 * g, 128 * g + 128))
     # hand-worked entries: coordinate 32c + p -> 8 (p mod 16) + 4 (p div 16) + c
-    assert [oracle.slot_of(i) for i in (0, 1, 16, 31, 32, 33, 127, 128, 161)] == \
+    assert [oracle.slot_of(i, 512) for i in (0, 1, 16, 31, 32, 33, 127, 128, 161)] == \
         [0, 8, 4, 124, 1, 9, 127, 128, 137]
+
+
+@pytest.mark.parametrize("d", [32, 64, 96, 160, 224, 352, 16352])
+def test_partial_last_group_keeps_coordinate_order(d):
+    """Rows whose length is not a multiple of 128: the whole groups keep the
+    group order, the last 32, 64 or 96 coordinates sit at their own index,
+    and the whole row is a bijection onto its d slots."""
+    slots = np.array([oracle.slot_of(i, d) for i in range(d)])
+    full = (d // 128) * 128
+    assert np.array_equal(np.sort(slots), np.arange(d))
+    assert np.array_equal(slots[full:], np.arange(full, d))
+    for i in range(0, full, 37):
+        assert slots[i] == oracle.slot_of(i, full + 128)
 
 
 def _load_pack_golden():
@@ -87,10 +100,45 @@ def test_pack_hand_built_vectors():
         assert got.tobytes() == expect, (bits, spec)
 
 
+def _hex_bytes(spec):
+    raw = bytearray()
+    for tok in spec.split():
+        if "*" in tok:
+            v, n = tok.split("*")
+            raw += bytes.fromhex(v) * int(n)
+        else:
+            raw += bytes.fromhex(tok)
+    return bytes(raw)
+
+
+def test_pack_hand_built_partial_groups():
+    """Rows of 32, 96, 160 and 224 coordinates (a partial last group of 32,
+    96, 32 and 96), worked by hand from the slot rule."""
+    n = 0
+    with open(os.path.join(GOLD, "pack_examples_partial.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            d, bits, spec, hexbytes = [t.strip() for t in line.split("|")]
+            d, bits = int(d), int(bits)
+            codes = np.zeros(d, np.uint8)
+            for tok in spec.split():
+                i, v = tok.split(":")
+                codes[int(i)] = int(v)
+            expect = _hex_bytes(hexbytes)
+            assert len(expect) == d * bits // 8
+            got = oracle.pack_row(codes, bits)
+            assert got.tobytes() == expect, (d, bits, spec)
+            assert np.array_equal(oracle.unpack_row(got, d, bits), codes)
+            n += 1
+    assert n == 5
+
+
+@pytest.mark.parametrize("d", [384, 416])
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
-def test_pack_unpack_roundtrip(bits):
+def test_pack_unpack_roundtrip(bits, d):
     rng = np.random.default_rng(bits)
-    d = 384
     codes = rng.integers(0, 1 << bits, d).astype(np.uint8)
     packed = oracle.pack_row(codes, bits)
     assert packed.shape[0] == d * bits // 8
@@ -106,7 +154,7 @@ def test_eight_bit_codes_are_whole_bytes_in_slot_order():
     packed = oracle.pack_row(codes, 8)
     assert packed.shape[0] == d
     for i in range(d):
-        assert packed[oracle.slot_of(i)] == codes[i]
+        assert packed[oracle.slot_of(i, d)] == codes[i]
 
 
 def test_eight_bit_quantize_matches_sorted_search():

@@ -44,18 +44,19 @@ def _rot_matrix(d, seed, use_signs=True):
     return R
 
 
-@pytest.mark.parametrize("d,use_signs", [(384, True), (384, False), (256, True), (640, True)])
+@pytest.mark.parametrize("d,use_signs", [(384, True), (384, False), (256, True), (640, True),
+                                          (96, True), (160, False), (224, True)])
 def test_rotation_is_orthogonal(d, use_signs):
     R = _rot_matrix(d, 5, use_signs)
     assert np.allclose(R.T @ R, np.eye(d), rtol=0, atol=1e-13)
 
 
-def test_basis_vector_spreads_over_one_block():
-    d, seed = 3072, 21
+@pytest.mark.parametrize("d,seed", [(3072, 21), (160, 4), (4160, 8)])
+def test_basis_vector_spreads_over_one_block(d, seed):
     h = oracle.block_size(d)
     perm, sign = oracle.plan(d, seed)
     inv = np.argsort(perm)
-    for m in (0, 17, 3071):
+    for m in (0, 17, d - 1):
         e = np.zeros(d)
         e[m] = 1.0
         z, _ = oracle.rotate_token(e, perm, sign)
@@ -65,7 +66,7 @@ def test_basis_vector_spreads_over_one_block():
         assert np.allclose(np.abs(z[nz]), 1 / np.sqrt(h), rtol=1e-15)
 
 
-@pytest.mark.parametrize("d", [256, 3072, 13824])
+@pytest.mark.parametrize("d", [256, 3072, 13824, 96, 4160])
 def test_norm_preserved_and_zero_token(d):
     perm, sign = oracle.plan(d, 3)
     rng = np.random.default_rng(d)
@@ -78,7 +79,8 @@ def test_norm_preserved_and_zero_token(d):
     assert n0 == 0.0 and not z0.any()
 
 
-@pytest.mark.parametrize("d,use_signs", [(384, True), (3072, True), (3072, False)])
+@pytest.mark.parametrize("d,use_signs", [(384, True), (3072, True), (3072, False), (224, True),
+                                         (4160, False)])
 def test_weight_fold_cancels_exactly(d, use_signs):
     """Unquantised, rows of W Pi^T times Pi x give W x: here each weight row
     and the token go through the oracle's own rotation (norm kept apart)."""
