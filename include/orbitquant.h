@@ -35,14 +35,17 @@
  *     unload.
  *   - The rotation seed and flags of a layer's weights and of its
  *     activations must be the same; the library cannot check this.
- *   - Code layout ("storage order"): inside each group of 128 consecutive
- *     rotated coordinates, coordinate 32c + p (c < 4, p < 32) is stored at
- *     slot 8 (p mod 16) + 4 (p div 16) + c; slot t of a row holds the code
+ *   - Code layout ("storage order"): inside each whole group of 128
+ *     consecutive rotated coordinates, coordinate 32c + p (c < 4, p < 32)
+ *     is stored at slot 8 (p mod 16) + 4 (p div 16) + c; the coordinates
+ *     of a last, partial group (d mod 128 = 32, 64 or 96 of them) are
+ *     stored at their own index; slot t of a row holds the code
  *     in bits [b t, b t + b) of the row's bytes, little-endian bit order.
  *     A row of d codes therefore takes d*b/8 bytes.  Codes are level
  *     indices 0..2^b-1 in ascending level order.
  *     At 8 bits this is plain byte addressing: byte slot(i) holds code i.
- *   - Limits: d (and K) a multiple of 128, 128 <= d <= 16384; bits in
+ *   - Limits: d a multiple of 32, 32 <= d <= 16384 (so h = d & -d >= 32);
+ *     the linear's K a multiple of 64 (whole 64-slot K steps); bits in
  *     {2, 3, 4, 8} (1..8 for oq_codebook; the exact-sphere family 1..4 and 8).
  *     Zero rows are valid (a zero token gets norm 0 and every code
  *     2^(b-1)).  NaN/Inf inputs give unspecified codes and no error.
@@ -105,7 +108,7 @@ int oq_codebook(int d, int bits, float *levels, float *thresholds);
  * sphere family is the Lloyd-Max quantizer of the density
  * c_d (1 - t^2)^((d-3)/2) of one coordinate of a uniform point on S^{d-1}
  * (pith.science: the referee's minor comment 1 asks for this closed-form
- * marginal), defined for the dimensions the kernels take (d % 128 == 0,
+ * marginal), defined for the dimensions the kernels take (d % 32 == 0,
  * d <= 16384) and bits 1..4 and 8 (else OQ_EUNSUPPORTED).  It differs from
  * the Gaussian one by 0.8% of a level at d = 256 and 0.015% at d = 13824
  * (4 bits).  Up to 4 bits the solver is Max's shooting method; at 8 bits
@@ -171,8 +174,10 @@ int oq_prepare_weights(const void *W, int dtype, int64_t n_out, int d_in, uint64
  *      overwritten), so nothing may read it concurrently.
  * a_bits, w_bits in {2, 3, 4}, any pair, or both 8 (W8A8: the codes are
  * decoded through an fp16 table of the 256 levels; a pair with only one
- * side at 8 bits is OQ_EUNSUPPORTED).  M and N up to 2^30 (OQ_EUNSUPPORTED
- * beyond).  M = 0 or N = 0 is a no-op that succeeds (the pointers may then
+ * side at 8 bits is OQ_EUNSUPPORTED).  K % 64 == 0, K <= 16384 (a K with a
+ * last partial group of 32 or 96 coordinates is OQ_EUNSUPPORTED here, though
+ * such rows can be rotated and prepared).  M and N up to 2^30
+ * (OQ_EUNSUPPORTED beyond).  M = 0 or N = 0 is a no-op that succeeds (the pointers may then
  * be NULL).  Errors:
  * OQ_EINVAL, OQ_EUNSUPPORTED, OQ_EDEVICE. */
 int oq_linear(const uint8_t *a_codes, const float *a_norms, int a_bits,
@@ -229,7 +234,7 @@ int oq_rtn4_linear(const void *x, int dtype, int64_t M, const uint8_t *q4, const
  * (paper.gecl.asia notes, Limitations: rotation and norm cost at run time).
  * The signs D cannot be folded through a nonlinearity and stay in the call.
  *   src, dst: device, caller-owned, distinct (no in-place), [rows][row_bytes]
- *   rows:     the permutation length d: 128 <= d <= 16384, d % 128 == 0
+ *   rows:     the permutation length d: 32 <= d <= 16384, d % 32 == 0
  *   row_bytes >= 1
  * rows = 0 is rejected (there is no plan of length 0).
  * Errors: OQ_EINVAL (null or equal pointers, row_bytes < 1), OQ_EUNSUPPORTED
@@ -245,7 +250,7 @@ int oq_permute_rows(const void *src, void *dst, int64_t rows, int64_t row_bytes,
  * handle pins them (the caller must ensure that no enqueued work still
  * uses them and that no other thread's call on the same (d, seed) is in
  * progress).  A later compute call with the same (d, seed) rebuilds the plan.
- *   d:     128 <= d <= 16384, d % 128 == 0   (else OQ_EUNSUPPORTED)
+ *   d:     32 <= d <= 16384, d % 32 == 0   (else OQ_EUNSUPPORTED)
  *   flags: 0 or OQ_ROT_NO_SIGNS (one plan serves both sign modes)
  *   plan:  receives an opaque handle (NULL on error)
  * Errors: OQ_EINVAL (null out pointer, bad flags, d <= 0, or a handle not

@@ -516,7 +516,7 @@ constexpr int64_t kMaxRows = (int64_t)1 << 30;
 int check_d_bits(int d, int bits) {
   if (d <= 0) return OQ_EINVAL;
   if ((bits < 2 || bits > 4) && bits != 8) return OQ_EUNSUPPORTED;
-  if (d % oq::kGroup != 0 || d > oq::kMaxD) return OQ_EUNSUPPORTED;
+  if (d % oq::kDimStep != 0 || d > oq::kMaxD) return OQ_EUNSUPPORTED;
   return OQ_OK;
 }
 
@@ -582,7 +582,7 @@ const char *oq_strerror(int status) {
   switch (status) {
     case OQ_OK: return "success";
     case OQ_EINVAL: return "invalid argument (null or misaligned pointer, bad size, dtype or flag)";
-    case OQ_EUNSUPPORTED: return "unsupported configuration (d must be a multiple of 128 in [128, 16384]; bits in {2,3,4,8}; 8 bits on both sides of a linear; the sphere codebook at 1-4 and 8 bits)";
+    case OQ_EUNSUPPORTED: return "unsupported configuration (d must be a multiple of 32 in [32, 16384], and the linear's K a multiple of 64; bits in {2,3,4,8}; 8 bits on both sides of a linear; the sphere codebook at 1-4 and 8 bits)";
     case OQ_ENOMEM: return "out of device memory for the rotation plan";
     case OQ_EDEVICE: return "HIP runtime or kernel launch failure";
     default: return "unknown status";
@@ -596,7 +596,7 @@ int oq_codebook_ex(int d, int bits, uint32_t flags, float *levels, float *thresh
   if (flags & ~OQ_CODEBOOK_SPHERE) return OQ_EINVAL;
   if (bits < 1 || bits > 8) return OQ_EUNSUPPORTED;
   const bool sphere = (flags & OQ_CODEBOOK_SPHERE) != 0;
-  if (sphere && (d % oq::kGroup != 0 || d > oq::kMaxD || (bits > 4 && bits != 8)))
+  if (sphere && (d % oq::kDimStep != 0 || d > oq::kMaxD || (bits > 4 && bits != 8)))
     return OQ_EUNSUPPORTED;
   double lv[256], th[255];
   family_codebook(d, bits, sphere, lv, th);
@@ -638,6 +638,7 @@ int oq_linear_ex(const uint8_t *a_codes, const float *a_norms, int a_bits, const
   if (rc != OQ_OK) return rc;
   rc = check_d_bits(K, w_bits);
   if (rc != OQ_OK) return rc;
+  if (K % oq::kLinearKStep != 0) return OQ_EUNSUPPORTED;  // whole 64-slot K steps
   if ((a_bits == 8) != (w_bits == 8)) return OQ_EUNSUPPORTED;  // W8A8 only, no mixed pair
   if (M > kMaxRows || N > kMaxRows) return OQ_EUNSUPPORTED;
   if (M == 0 || N == 0) return OQ_OK;  // empty output: pointers may be null
@@ -710,7 +711,7 @@ int oq_rtn4_linear(const void *x, int dtype, int64_t M, const uint8_t *q4, const
 int oq_permute_rows(const void *src, void *dst, int64_t rows, int64_t row_bytes, uint64_t seed,
                     void *stream) {
   if (!src || !dst || src == dst || row_bytes < 1 || rows <= 0) return OQ_EINVAL;
-  if (rows % oq::kGroup != 0 || rows > oq::kMaxD) return OQ_EUNSUPPORTED;
+  if (rows % oq::kDimStep != 0 || rows > oq::kMaxD) return OQ_EUNSUPPORTED;
   oq::DevicePlan plan;
   int rc = get_plan((int)rows, seed, (hipStream_t)stream, &plan);
   if (rc != OQ_OK) return rc;
@@ -734,7 +735,7 @@ int oq_plan_create(int d, uint64_t seed, uint32_t flags, void **plan) {
   *plan = nullptr;
   if (flags & ~OQ_ROT_NO_SIGNS) return OQ_EINVAL;
   if (d <= 0) return OQ_EINVAL;
-  if (d % oq::kGroup != 0 || d > oq::kMaxD) return OQ_EUNSUPPORTED;
+  if (d % oq::kDimStep != 0 || d > oq::kMaxD) return OQ_EUNSUPPORTED;
   oq::DevicePlan p;
   int rc = get_plan(d, seed, nullptr, &p);
   if (rc != OQ_OK) return rc;

@@ -25,6 +25,11 @@ inline hipError_t ensure_lds_limit(const void *fn, int bytes, std::atomic<uint64
 
 constexpr int kMaxD = 16384;
 constexpr int kGroup = 128;  // coordinates per storage-order group
+// token lengths d: multiples of kDimStep (a last partial group of 32, 64 or
+// 96 coordinates is stored in coordinate order); linear K: multiples of the
+// linear's 64-slot K step
+constexpr int kDimStep = 32;
+constexpr int kLinearKStep = 64;
 
 // Slot size of the bf16 fast rotate kernel for token size d: the Hadamard
 // block, at most 1024 coordinates (a block of 2048 or 4096 spans several

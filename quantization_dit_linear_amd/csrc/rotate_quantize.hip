@@ -130,20 +130,27 @@ __global__ __launch_bounds__(kThreads) void rq_generic_kernel(
       // unit-space value sqrt(d) z_i = y_i sqrt(d/h) / s
       const float us = s > 0.0 ? (float)(sqrt((double)d / (double)h) / s) : 0.f;
       const float fs = (float)(s / sqrt((double)d));  // dequantized value = s * level / sqrt(d)
+      // thread q packs 8 consecutive slots into one b-byte word: inside a
+      // whole 128-coordinate group (q < full) the slots 8n .. 8n+7 of group
+      // G hold coordinates 128G + 32c + 16w + n; in a last, partial group
+      // (d mod 128 = 32, 64 or 96) slot i holds coordinate i
+      const int full = (d / 128) * 16;
       for (int q = tid; q < d / 8; q += kThreads) {
+        const bool grp = q < full;
         const int G = q >> 4, n = q & 15;
         uint64_t word = 0;
 #pragma unroll
         for (int w = 0; w < 2; w++)
 #pragma unroll
           for (int c = 0; c < 4; c++) {
-            const int i = G * 128 + 32 * c + 16 * w + n;
+            const int e = 4 * w + c;  // slot 8q + e (8n + e of group G)
+            const int i = grp ? G * 128 + 32 * c + 16 * w + n : 8 * q + e;
             const float u = y[i] * us;
             const uint32_t code = code_of<BITS>(u, th, t8);
             if (dq) dq[t * d + i] = f32_to_bf16_rne(fs * level_of<BITS>(code, lv, l8));
-            word |= (uint64_t)code << (BITS * (4 * w + c));
+            word |= (uint64_t)code << (BITS * e);
           }
-        if (!dq) store_codes<BITS>(codes + t * row_bytes + 16 * BITS * G + BITS * n, word);
+        if (!dq) store_codes<BITS>(codes + t * row_bytes + BITS * q, word);
       }
     }
     __syncthreads();

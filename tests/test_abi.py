@@ -109,6 +109,14 @@ def test_rotate_validation_rejects_before_hip(q, fn):
     assert call(n=0) == q.OQ_OK
     assert call(n=0, x=None, out=None, nrm=None) == q.OQ_OK
     assert call(n=0, d=3000) == q.OQ_EUNSUPPORTED
+    # token lengths: multiples of 32 up to 16384 (a partial last group of
+    # 32, 64 or 96 coordinates is stored in coordinate order)
+    assert call(n=0, d=96) == q.OQ_OK
+    assert call(n=0, d=32) == q.OQ_OK
+    assert call(n=0, d=16352) == q.OQ_OK
+    assert call(n=0, d=16416) == q.OQ_EUNSUPPORTED
+    assert call(d=48) == q.OQ_EUNSUPPORTED
+    assert call(d=16) == q.OQ_EUNSUPPORTED
     # the two alternative outputs exclude each other
     assert call(flags=q.OQ_OUT_F32_ROTATED | q.OQ_OUT_BF16_DEQUANT) == q.OQ_EINVAL
     if fn == "oq_prepare_weights":
@@ -135,6 +143,11 @@ def test_linear_validation_rejects_before_hip(q):
     assert call(N=(1 << 30) + 1) == q.OQ_EUNSUPPORTED
     assert call(M=-1) == q.OQ_EINVAL
     assert call(K=100) == q.OQ_EUNSUPPORTED
+    # the linear takes whole 64-slot K steps: K % 64 == 0
+    assert call(K=96) == q.OQ_EUNSUPPORTED
+    assert call(K=160) == q.OQ_EUNSUPPORTED
+    assert call(K=192, M=0) == q.OQ_OK
+    assert call(K=64, N=0) == q.OQ_OK
     assert call(ba=5) == q.OQ_EUNSUPPORTED
     assert call(bw=1) == q.OQ_EUNSUPPORTED
     assert call(M=0) == q.OQ_OK
@@ -214,6 +227,7 @@ def test_permute_rows_validates_before_hip(q):
     assert f(A16, B16, 3072, 0, 1, None) == q.OQ_EINVAL
     assert f(A16, B16, 0, 16, 1, None) == q.OQ_EINVAL
     assert f(A16, B16, 3000, 16, 1, None) == q.OQ_EUNSUPPORTED
+    assert f(A16, B16, 48, 16, 1, None) == q.OQ_EUNSUPPORTED
     assert f(A16, B16, 32768, 16, 1, None) == q.OQ_EUNSUPPORTED
 
 
