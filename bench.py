@@ -98,6 +98,13 @@ def parse():
     return p.parse_args()
 
 
+# sources of the kernels whose counters profiles/traffic.json records: the
+# linear, and the bf16 fast rotate kernel that every recorded workload runs
+# (with the header of constants both share with the host)
+LIN_SRC = ("linear.hip", "oq_internal.h")
+ROT_SRC = ("rotate_quantize_fast.hip", "oq_internal.h")
+
+
 def src_digest(*names):
     """Digest of kernel sources with comments and blank lines dropped, so
     stored counter data stays valid across comment-only edits and goes
@@ -547,8 +554,8 @@ def summarize_profiles(a):
     lin_alg_w = 2 * M * N
     rot_alg_r = M * K * in_b
     rot_alg_w = M * (K * ba / 8 + 4)
-    lin_digest = src_digest("linear.hip")
-    rot_digest = src_digest("rotate_quantize.hip", "rotate_quantize_fast.hip")
+    lin_digest = src_digest(*LIN_SRC)
+    rot_digest = src_digest(*ROT_SRC)
     table = {
         "linear": {"kernel": lin_name, "source_digest": lin_digest,
                    "bytes_per_launch": int(lin_fetch + lin_write), "fetch_bytes": int(lin_fetch),
@@ -1005,8 +1012,8 @@ def main():
         }
         torch.cuda.empty_cache()
 
-    lin_digest = src_digest("linear.hip")
-    rot_digest = src_digest("rotate_quantize.hip", "rotate_quantize_fast.hip")
+    lin_digest = src_digest(*LIN_SRC)
+    rot_digest = src_digest(*ROT_SRC)
     lin_tflops, rot_gbs, prep_gbs = rt["lin_tflops"], rt["rot_gbs"], rt["prep_gbs"]
     out = {
         "metric": "rotate+quant GB/s and W4A4 linear TFLOP/s, as % of HBM / MFMA peak",

@@ -102,7 +102,7 @@ def test_traffic_per_call_and_scaling(runs, monkeypatch):
     assert lin["fetch_bytes"] == int((100000 + 8000 + 16000) * 1024 * 2.0)
     assert lin["write_bytes"] == int((170000 + 16000 + 2000) * 1024 * 1.0)
     assert lin["bytes_per_launch"] == lin["fetch_bytes"] + lin["write_bytes"]
-    assert lin["source_digest"] == bench.src_digest("linear.hip")
+    assert lin["source_digest"] == bench.src_digest(*bench.LIN_SRC)
     rot = e["rotate_quantize"]
     # the first dispatch prepared the weights: activation launches only
     assert rot["fetch_bytes"] == int(29500 * 1024 * 2.0)
