@@ -148,3 +148,47 @@ def test_end_to_end_other_lengths(q, K):
     ref = oracle.linear(host(ac), host(an).astype(np.float64), 4, host(wc),
                         host(wn).astype(np.float64), 4, K)
     assert parity.rel_fro(bf16_to_np(y), ref) <= parity.LINEAR_FRO
+
+
+@pytest.mark.parametrize("d", [384, 3072, 4096, 5120, 13824])
+def test_non_finite_tokens_leave_the_others_alone(q, d):
+    """Non-finite tokens give unspecified codes and no error; every other
+    token of the same call (same workgroup batches included) still matches
+    the oracle.  Rows 3, 7 and 11 carry a NaN, a +Inf, and a -Inf with a
+    NaN; row 15 is finite but its sum of squares overflows fp32."""
+    import torch
+    x = wl.custom_activations(20, d, wl.BF16, d + 7, n_out=2, out_factor=20.0, sigma_s=1.0)
+    x = x.copy()
+    x[3, 5] = 0x7FC0          # NaN
+    x[7, d - 1] = 0x7F80      # +Inf
+    x[11, 0] = 0xFF80         # -Inf
+    x[11, d // 2] = 0x7FC0
+    x[15, :] = wl.f32_to_bf16_bits(np.full(d, 1e30, np.float32))
+    bad = [3, 7, 11, 15]
+    good = np.array([r for r in range(20) if r not in bad])
+    say("non-finite tokens", d)
+    xd = to_device(x)
+    codes, norms = q.rotate_quantize(xd, 13, 4)
+    z, _ = q.rotate(xd, 13)
+    _sync()
+    rc, rn, rz = oracle.rotate_quantize(x[good], wl.BF16, d, 13, 4, want_z=True)
+    thr = oracle.codebook_unit(4)[1]
+    parity.assert_codes_match(host(codes)[good], rc, rz, d, 4, thr, f"d={d}")
+    parity.assert_norms_match(host(norms)[good], rn, f"d={d}")
+    parity.assert_rotated_match(host(z)[good], rz, f"d={d}")
+    # the linear: a non-finite norm spoils its own output row only -- the
+    # other rows are bit-identical to the same call with a finite norm,
+    # which itself matches the oracle
+    ac, an = wl.random_codes(6, d, 4, 3)
+    wc, wn = wl.random_codes(512, d, 4, 4)
+    an_nan = an.copy()
+    an_nan[2] = np.nan
+    y = bf16_to_np(q.linear(to_device(ac), to_device(an), 4, to_device(wc), to_device(wn), 4, d))
+    y_nan = bf16_to_np(q.linear(to_device(ac), to_device(an_nan), 4, to_device(wc),
+                                to_device(wn), 4, d))
+    torch.cuda.synchronize()
+    keep = np.array([0, 1, 3, 4, 5])
+    assert np.array_equal(y_nan[keep], y[keep])
+    assert not np.isfinite(y_nan[2]).any()
+    ref = oracle.linear(ac, an, 4, wc, wn, 4, d)
+    assert parity.rel_fro(y, ref) <= parity.LINEAR_FRO
