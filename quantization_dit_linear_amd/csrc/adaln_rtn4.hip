@@ -188,6 +188,145 @@ __global__ __launch_bounds__(256) void rtn4_linear_kernel(const void *__restrict
   }
 }
 
+// One DPP step: v from the lane CTRL selects (rows outside RMASK read 0).
+template <int CTRL, int RMASK>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, RMASK, 0xF, false));
+}
+
+// Sum of v over the 64 lanes of a wave, valid in lane 63.
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+  v += dpp_f<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]: every lane holds its quad's sum
+  v += dpp_f<0x141, 0xF>(v);  // row_half_mirror: sums of 8
+  v += dpp_f<0x140, 0xF>(v);  // row_mirror: sums of 16
+  v += dpp_f<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+  v += dpp_f<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3: lane 63 holds the total
+  return v;
+}
+
+// Small batches (M <= 4 activation rows, the AdaLN case: one modulation
+// row per sample).  Each thread owns one 32-coordinate chunk of K and keeps
+// those coordinates of every activation row in registers, so nothing is
+// re-read per output row (the general kernel above reads them from LDS for
+// every row group: 1.26 GB of LDS reads for 2 x 5120 -> 30720).  A
+// workgroup of ceil(K / 2048) waves covers all of K and walks blocks of RB
+// output rows: each thread loads its chunk's 16 code bytes of each row (a
+// wave reads 1 KB of one row, coalesced), decodes them with byte
+// conversions and accumulates the exact fp32 products x q; the RB * MB
+// partial sums of a block are reduced over each wave's lanes with DPP,
+// then over the waves through LDS, one barrier per block.
+template <int MB>
+__global__ __launch_bounds__(512) void rtn4_small_kernel(const void *__restrict__ x, int dtype,
+                                                         int M, const u32x4 *__restrict__ q4,
+                                                         const float *__restrict__ scales,
+                                                         int64_t N, int K,
+                                                         uint16_t *__restrict__ y) {
+  constexpr int RB = MB == 4 ? 4 : 8;  // output rows per block
+  constexpr int P = RB * MB;           // partial sums per block: 8 or 16, p = r MB + m
+  __shared__ float red[2][8][P];       // [block parity][wave][partial]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = (int)(blockDim.x >> 6);
+  const int chunks = K / 32;
+  const bool own = tid < chunks;
+  float xr[MB][32];
+#pragma unroll
+  for (int m = 0; m < MB; m++) {
+    if (own && m < M) {
+      // 16-byte loads of the thread's 32 coordinates (K % 32 == 0)
+      if (dtype == 1) {
+        const u32x4 *src = (const u32x4 *)((const uint16_t *)x + (int64_t)m * K + 32 * tid);
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const u32x4 a = src[u];
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            xr[m][8 * u + 2 * e] = __uint_as_float(a[e] << 16);
+            xr[m][8 * u + 2 * e + 1] = __uint_as_float(a[e] & 0xFFFF0000u);
+          }
+        }
+      } else {
+        const floatx4 *src = (const floatx4 *)((const float *)x + (int64_t)m * K + 32 * tid);
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          const floatx4 a = src[u];
+#pragma unroll
+          for (int e = 0; e < 4; e++) xr[m][4 * u + e] = a[e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; e++) xr[m][e] = 0.f;
+    }
+  }
+  const int64_t nblk = (N + RB - 1) / RB;
+  // codes of the next block are loaded while the current one is decoded
+  auto load_block = [&](int64_t b, u32x4 (&w)[RB]) {
+#pragma unroll
+    for (int r = 0; r < RB; r++) {
+      const int64_t n = b * RB + r;
+      w[r] = (own && b < nblk && n < N)
+                 ? q4[n * chunks + tid]
+                 : u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+    }
+  };
+  u32x4 wn[RB];
+  load_block(blockIdx.x, wn);
+  int par = 0;
+  for (int64_t b = blockIdx.x; b < nblk; b += gridDim.x, par ^= 1) {
+    const int64_t n0 = b * RB;
+    u32x4 w[RB];
+#pragma unroll
+    for (int r = 0; r < RB; r++) w[r] = wn[r];
+    load_block(b + gridDim.x, wn);
+    float v[P];
+#pragma unroll
+    for (int r = 0; r < RB; r++) {
+      float acc[MB];
+#pragma unroll
+      for (int m = 0; m < MB; m++) acc[m] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const uint32_t lo = w[r][e] & 0x0F0F0F0Fu, hi = (w[r][e] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int bb = 0; bb < 4; bb++) {
+          // q = nibble - 8 of coordinates 8e + 2bb (low) and 8e + 2bb + 1
+          // (high): one byte permute builds the float 2^23 + nibble (byte bb
+          // under the exponent byte 0x4B), one subtraction removes 2^23 + 8
+          // (both exact)
+          const uint32_t sel = (7u << 24) | (0x0Cu << 16) | (0x0Cu << 8) | (uint32_t)bb;
+          const float q0 = __uint_as_float(__builtin_amdgcn_perm(0x4B000000u, lo, sel)) - 8388616.0f;
+          const float q1 = __uint_as_float(__builtin_amdgcn_perm(0x4B000000u, hi, sel)) - 8388616.0f;
+#pragma unroll
+          for (int m = 0; m < MB; m++) {
+            acc[m] = fmaf(xr[m][8 * e + 2 * bb], q0, acc[m]);
+            acc[m] = fmaf(xr[m][8 * e + 2 * bb + 1], q1, acc[m]);
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MB; m++) v[r * MB + m] = acc[m];
+    }
+    // each partial summed over the wave's 64 lanes by DPP adds (quad swaps,
+    // half-row and row mirrors, then row broadcasts), which leave the total
+    // in lane 63: six VALU instructions per partial, no LDS traffic
+#pragma unroll
+    for (int i = 0; i < P; i++) {
+      const float t = wave_sum_lane63(v[i]);
+      if (lane == 63) red[par][wave][i] = t;
+    }
+    __syncthreads();  // one barrier per block: red alternates between two buffers
+    if (tid < P) {
+      float sum = 0.f;
+      for (int ww = 0; ww < nw; ww++) sum += red[par][ww][tid];
+      const int r = tid / MB, m = tid % MB;
+      const int64_t n = n0 + r;
+      if (n < N && m < M) y[(int64_t)m * N + n] = f32_to_bf16_rne(sum * scales[n]);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rtn4_prepare(const void *W, int dtype, int64_t rows, int d, uint8_t *q4,
@@ -201,6 +340,28 @@ hipError_t launch_rtn4_prepare(const void *W, int dtype, int64_t rows, int d, ui
 hipError_t launch_rtn4_linear(const void *x, int dtype, int64_t M, const uint8_t *q4,
                               const float *scales, int64_t N, int K, uint16_t *y,
                               hipStream_t stream) {
+  int dev = 0, cus = 0;
+  (void)hipGetDevice(&dev);
+  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (M <= 4) {
+    // one wave per 64 chunks of 32 coordinates (K <= 16384: at most 8 waves)
+    const int chunks = K / 32, threads = 64 * ((chunks + 63) / 64);
+    const int rb = M > 2 ? 4 : 8;
+    const int64_t nblk = (N + rb - 1) / rb;
+    const int64_t want = (int64_t)(cus > 0 ? cus : 256) * 2;
+    const unsigned grid = (unsigned)(nblk < want ? nblk : want);
+    if (threads > 512) return hipErrorInvalidValue;
+    if (M == 1)
+      hipLaunchKernelGGL(rtn4_small_kernel<1>, dim3(grid), dim3(threads), 0, stream, x, dtype,
+                         (int)M, (const u32x4 *)q4, scales, N, K, y);
+    else if (M == 2)
+      hipLaunchKernelGGL(rtn4_small_kernel<2>, dim3(grid), dim3(threads), 0, stream, x, dtype,
+                         (int)M, (const u32x4 *)q4, scales, N, K, y);
+    else
+      hipLaunchKernelGGL(rtn4_small_kernel<4>, dim3(grid), dim3(threads), 0, stream, x, dtype,
+                         (int)M, (const u32x4 *)q4, scales, N, K, y);
+    return hipGetLastError();
+  }
   int mb = kXBytes / (4 * (K / 32) * kPad);
   if (mb < 1) return hipErrorInvalidValue;
   if (mb > kMaxMB) mb = kMaxMB;
@@ -208,9 +369,6 @@ hipError_t launch_rtn4_linear(const void *x, int dtype, int64_t M, const uint8_t
   static std::atomic<uint64_t> lds_set{0};
   hipError_t e = ensure_lds_limit((const void *)rtn4_linear_kernel, kXBytes, lds_set);
   if (e != hipSuccess) return e;
-  int dev = 0, cus = 0;
-  (void)hipGetDevice(&dev);
-  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   // as many workgroups as fit two per CU, each with the same number of row
   // groups (no partial last round of groups)
   const int64_t groups = (N + kRows - 1) / kRows;
