@@ -80,3 +80,29 @@ def test_edge_rows_and_fp32(q):
     torch.cuda.synchronize()
     _check_out(y, x, wl.F32, rq, rs)
     assert np.all(y[:, 1] == 0)
+
+
+@pytest.mark.parametrize("M,K,N,dtype", [(1, 256, 1001, "bf16"), (3, 3072, 777, "bf16"),
+                                         (4, 1088, 260, "f32"), (2, 16384, 67, "f32"),
+                                         (1, 32, 9, "f32"), (4, 16384, 33, "bf16")])
+def test_small_batches(q, M, K, N, dtype):
+    """Up to 4 activation rows run on the register-resident kernel: one and
+    four rows (4-row output blocks), fp32 and bf16 input, output counts that
+    leave the last block partial, K from one chunk (32) to 512 chunks (8
+    waves per workgroup)."""
+    import torch
+    rng = np.random.default_rng(M * 100 + K + N)
+    Wf = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wf[N // 2] = 0.0
+    xf = rng.standard_normal((M, K)).astype(np.float32)
+    xf[0, K // 3] = 40.0
+    if dtype == "bf16":
+        W, x, code = wl.f32_to_bf16_bits(Wf), wl.f32_to_bf16_bits(xf), wl.BF16
+    else:
+        W, x, code = Wf, xf, wl.F32
+    q4, sc, rq, rs = _prep_check(q, W, code, K, f"small {M}x{K}->{N}")
+    say("rtn4 small batch", M, K, N, dtype)
+    y = bf16_to_np(q.rtn4_linear(to_device(x), q4, sc))
+    torch.cuda.synchronize()
+    _check_out(y, x, code, rq, rs)
+    assert np.all(y[:, N // 2] == 0)
