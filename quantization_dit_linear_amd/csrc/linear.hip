@@ -51,11 +51,11 @@
 //     every CU, with their fp32 partial sums parked in output rows that the
 //     full rounds overwrite afterwards, and a small kernel sums them.
 //
-// Throughput: 40-50% of the fp16 matrix-core peak at these shapes (about
-// 42% at 9216 x 9216 x 3072, 48-50% with 32760 tokens), on par with the
-// plain fp16 library GEMM of the same shape (which does no decoding); the
-// K loop's LDS traffic (fragment loads, table lookups, decoded stores) and
-// barriers take most of the rest.
+// Throughput: 45-50% of the fp16 matrix-core peak at these shapes (45-47%
+// at 9216 x 9216 x 3072, on par with the plain fp16 library GEMM of that
+// shape, which does no decoding; 46-50% with 32760 tokens, 0.81-0.87 of
+// it there); the K loop's LDS traffic (fragment loads, table lookups,
+// decoded stores) and barriers take most of the rest.
 //
 // 8-bit codes (W8A8) take the same path except for the decode: 256 levels do
 // not fit byte-permute tables, so each workgroup first converts the fp32
