@@ -123,6 +123,20 @@ static double std_mass(double a, double b)
  * returns iterations. */
 static int lloyd_max_newton(int L, double *levels);
 
+/* Both densities (N(0,1) and the sphere marginal) are even, so their
+ * Lloyd-Max quantizers are symmetric, c_{L-1-k} = -c_k, with the middle
+ * threshold at 0.  Newton's method on the conditions (5-8 bits) breaks
+ * that only by rounding (about 1e-13); this restores it, so a zero token
+ * takes code L/2 whatever the bit width. */
+static void symmetrize(int L, double *c)
+{
+    for (int k = 0; k < L / 2; k++) {
+        const double m = 0.5 * (c[L - 1 - k] - c[k]);
+        c[k] = -m;
+        c[L - 1 - k] = m;
+    }
+}
+
 int oqo_codebook_unit(int bits, double *levels, double *thresholds)
 {
     const int L = 1 << bits;
@@ -146,6 +160,7 @@ int oqo_codebook_unit(int bits, double *levels, double *thresholds)
         if (move < 1e-15) break;
     }
     if (bits > 4) it += lloyd_max_newton(L, levels);
+    symmetrize(L, levels);
     for (int k = 1; k < L; k++) thresholds[k - 1] = 0.5 * (levels[k - 1] + levels[k]);
     return it;
 }
@@ -388,6 +403,7 @@ int oqo_codebook_sphere(int d, int bits, double *levels, double *thresholds)
         if (move < 1e-13) break; /* the incomplete beta is good to about 1e-15 */
     }
     if (bits > 4) it += sphere_newton(d, L, levels);
+    symmetrize(L, levels);
     for (int k = 1; k < L; k++) thresholds[k - 1] = 0.5 * (levels[k - 1] + levels[k]);
     return it;
 }

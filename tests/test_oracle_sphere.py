@@ -101,3 +101,22 @@ def test_gaussian_limit_8bit_scales_like_one_over_d():
     for i in range(2):
         ratio = gaps[i] / gaps[i + 1]
         assert abs(ratio / (ds[i + 1] / ds[i]) - 1) < 0.15, (gaps, ratio)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_codebooks_are_exactly_symmetric(bits):
+    """Both densities are even, so their Lloyd-Max quantizers are symmetric:
+    c_{L-1-k} = -c_k exactly and the middle threshold is 0, so a zero token
+    takes code 2^(b-1) at every bit width (the Newton refinement above 4
+    bits must not leave a rounding asymmetry behind)."""
+    r = oracle.codebook_unit(bits)
+    lv, th = np.asarray(r[0]), np.asarray(r[1])
+    assert np.array_equal(lv, -lv[::-1]) and th[len(th) // 2] == 0.0
+    for d in (3, 96, 3072):
+        lvs, ths, _ = oracle.codebook_sphere(d, bits)
+        lvs, ths = np.asarray(lvs), np.asarray(ths)
+        assert np.array_equal(lvs, -lvs[::-1]) and ths[len(ths) // 2] == 0.0
+    x = np.zeros((2, 224), np.float32)
+    for sphere in (False, True):
+        codes, norms, _ = oracle.rotate_quantize(x, oracle.F32, 224, 5, bits, sphere=sphere)
+        assert (oracle.unpack_row(codes[0], 224, bits) == 1 << (bits - 1)).all()
