@@ -432,9 +432,10 @@ int oqo_hadamard_entry(int a, int b)
     return (__builtin_popcount((unsigned)(a & b)) & 1) ? -1 : 1;
 }
 
-/* Rotate one token: s = ||x||, u = x / s (u = 0 when s = 0),
- * y_i = D_i u_{pi(i)}, and z^(j) = H_h y^(j) / sqrt(h) for each of the
- * k = d/h blocks.  Writes z (length d) and the norm. */
+/* Rotate one token: s = ||x||, y_i = D_i x_{pi(i)}, and
+ * z^(j) = H_h y^(j) / (s sqrt(h)) for each of the k = d/h blocks (z = 0
+ * when s = 0): the rotation of u = x / s, normalised last.  Writes z
+ * (length d) and the norm. */
 void oqo_rotate_token(const double *x, int d, const int32_t *perm, const int8_t *sign,
                       int use_signs, double *z, double *norm)
 {
@@ -443,13 +444,20 @@ void oqo_rotate_token(const double *x, int d, const int32_t *perm, const int8_t 
     for (int i = 0; i < d; i++) ss += x[i] * x[i];
     const double s = sqrt(ss);
     *norm = s;
+    /* the rotation is linear, so it runs on x itself and the division by
+     * s sqrt(h) comes last: the transform of bf16 or fp32 inputs is then
+     * exact in double precision, and a coordinate that cancels exactly is
+     * an exact zero (which the tie rule sends to the upper level) instead of
+     * a rounding residue of either sign */
     for (int i = 0; i < d; i++) {
-        double u = (s > 0.0) ? x[perm[i]] / s : 0.0;
-        z[i] = (use_signs && sign[i] < 0) ? -u : u;
+        const double v = x[perm[i]];
+        z[i] = (use_signs && sign[i] < 0) ? -v : v;
     }
+    const double den = s * sqrt((double)h);
     for (int j = 0; j < d / h; j++) {
         oqo_fwht(z + (size_t)j * h, h);
-        for (int i = 0; i < h; i++) z[(size_t)j * h + i] /= sqrt((double)h);
+        for (int i = 0; i < h; i++)
+            z[(size_t)j * h + i] = (s > 0.0) ? z[(size_t)j * h + i] / den : 0.0;
     }
 }
 

@@ -192,3 +192,38 @@ def test_non_finite_tokens_leave_the_others_alone(q, d):
     assert not np.isfinite(y_nan[2]).any()
     ref = oracle.linear(ac, an, 4, wc, wn, 4, d)
     assert parity.rel_fro(y, ref) <= parity.LINEAR_FRO
+
+
+@pytest.mark.parametrize("d,bits", [(96, 4), (160, 2), (224, 8), (4160, 3)])
+def test_sphere_family_other_lengths(q, d, bits):
+    """The exact-sphere codebook family at lengths with a partial last group
+    (its thresholds depend on d), codes and norms against the oracle."""
+    x = wl.custom_activations(23, d, wl.BF16, d + 5 * bits, n_out=2, out_factor=30.0,
+                              sigma_s=1.0, zero_rows=(4,))
+    say("dims sphere", d, bits)
+    c, n = q.rotate_quantize(to_device(x), 29, bits, sphere=True)
+    _sync()
+    rc, rn, rz = oracle.rotate_quantize(x, wl.BF16, d, 29, bits, want_z=True, sphere=True)
+    _, th, _ = oracle.codebook_sphere(d, bits)
+    parity.assert_codes_match(host(c), rc, rz, d, bits, np.asarray(th) * np.sqrt(d), f"d={d}")
+    parity.assert_norms_match(host(n), rn, f"d={d}")
+
+
+@pytest.mark.parametrize("K,bw,ba", [(192, 4, 4), (1088, 2, 4), (320, 8, 8)])
+def test_sphere_linear_whole_k_steps(q, K, bw, ba):
+    """The sphere family through the linear at K % 128 == 64, end to end:
+    the library's weight and activation codes against the oracle's linear
+    of the same codes."""
+    import torch
+    M, N, seed = 70, 150, 37
+    x = wl.custom_activations(M, K, wl.BF16, K + 3, n_out=2, out_factor=20.0, sigma_s=1.0)
+    rng = np.random.default_rng(K + bw)
+    W = wl.f32_to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    say("dims sphere linear", K, bw, ba)
+    wc, wn = q.prepare_weights(to_device(W), seed, bw, sphere=True)
+    ac, an = q.rotate_quantize(to_device(x), seed, ba, sphere=True)
+    y = bf16_to_np(q.linear(ac, an, ba, wc, wn, bw, K, sphere=True))
+    torch.cuda.synchronize()
+    ref = oracle.linear(host(ac), host(an).astype(np.float64), ba, host(wc),
+                        host(wn).astype(np.float64), bw, K, sphere=True)
+    assert parity.rel_fro(y, ref) <= parity.LINEAR_FRO
