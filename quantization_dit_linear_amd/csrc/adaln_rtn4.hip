@@ -8,8 +8,9 @@
 // q_nk = rint(W_nk * (7 / amax)) in [-7, 7] (fp32, ties to even), stored
 // offset-binary (nibble q + 8), two per byte, the even coordinate in the low
 // nibble.  The projection y[m][n] = bf16(scale_n sum_k x_mk q_nk)
-// accumulates in fp32.  Both kernels are bound by HBM: the modulation input
-// is a handful of rows (one per sample), so the weights are read once.
+// accumulates in fp32 over the exact products x q.  The kernels are bound by
+// HBM and latency: the modulation input is a handful of rows (one per
+// sample), so the weights are read once.
 #include <hip/hip_runtime.h>
 
 #include "oq_internal.h"
@@ -262,7 +263,10 @@ __global__ __launch_bounds__(512) void rtn4_small_kernel(const void *__restrict_
   }
   const int64_t nblk = (N + RB - 1) / RB;
   // codes of the next block are loaded while the current one is decoded
-  auto load_block = [&](int64_t b, u32x4 (&w)[RB]) {
+  // the code words of the next block, and the scale of the output row that
+  // this thread writes (threads p < RB MB write output p), are loaded while
+  // the current block is decoded
+  auto load_block = [&](int64_t b, u32x4 (&w)[RB], float &sc) {
 #pragma unroll
     for (int r = 0; r < RB; r++) {
       const int64_t n = b * RB + r;
@@ -270,16 +274,20 @@ __global__ __launch_bounds__(512) void rtn4_small_kernel(const void *__restrict_
                  ? q4[n * chunks + tid]
                  : u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
     }
+    const int64_t ns = b * RB + tid / MB;
+    sc = (tid < P && b < nblk && ns < N) ? scales[ns] : 0.f;
   };
   u32x4 wn[RB];
-  load_block(blockIdx.x, wn);
+  float sn;
+  load_block(blockIdx.x, wn, sn);
   int par = 0;
   for (int64_t b = blockIdx.x; b < nblk; b += gridDim.x, par ^= 1) {
     const int64_t n0 = b * RB;
     u32x4 w[RB];
 #pragma unroll
     for (int r = 0; r < RB; r++) w[r] = wn[r];
-    load_block(b + gridDim.x, wn);
+    const float scale = sn;
+    load_block(b + gridDim.x, wn, sn);
     float v[P];
 #pragma unroll
     for (int r = 0; r < RB; r++) {
@@ -322,7 +330,177 @@ __global__ __launch_bounds__(512) void rtn4_small_kernel(const void *__restrict_
       for (int ww = 0; ww < nw; ww++) sum += red[par][ww][tid];
       const int r = tid / MB, m = tid % MB;
       const int64_t n = n0 + r;
-      if (n < N && m < M) y[(int64_t)m * N + n] = f32_to_bf16_rne(sum * scales[n]);
+      if (n < N && m < M) y[(int64_t)m * N + n] = f32_to_bf16_rne(sum * scale);
+    }
+  }
+}
+
+// bf16 activations (the AdaLN case) on half-precision dot products.  A
+// thread scales its 32-coordinate chunk of each activation row by a power of
+// two 2^s (largest magnitude into [2^15, 2^16)) and converts it to fp16,
+// which is exact when every nonzero bf16 value of the chunk lies within 2^29
+// of the largest (fp16 normals hold 11 significant bits, bf16 has 8).  A
+// code word's nibbles are split into the even and odd ones (one mask, one
+// shift and mask); nibbles j and j + 4 are then two bytes of one of those
+// words, and one byte permute puts them under the fp16 high byte 0x64,
+// which makes the pair (1024 + n_j, 1024 + n_j+4); one packed fp16
+// subtraction of 1032 leaves the exact q = n - 8, and v_dot2c_f32_f16 adds
+// the two exact products to an fp32 sum.  The chunk's partial sum is scaled
+// back by 2^-s (exact).  Per 8 nibbles that is 3 + 4 + 4 instructions and 4
+// dot products per activation row, against 3 + 16 and 8 products per row in
+// the fp32 decode.  A thread whose
+// chunk is not exact in fp16 (wider range, bf16 subnormals, inf or NaN)
+// decodes in fp32 instead, re-reading its chunk per output row.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+template <int MB>
+__global__ __launch_bounds__(512) void rtn4_small_h_kernel(const uint16_t *__restrict__ x, int M,
+                                                           const u32x4 *__restrict__ q4,
+                                                           const float *__restrict__ scales,
+                                                           int64_t N, int K,
+                                                           uint16_t *__restrict__ y) {
+  constexpr int RB = MB == 4 ? 4 : 8;
+  constexpr int P = RB * MB;
+  __shared__ float red[2][8][P];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = (int)(blockDim.x >> 6);
+  const int chunks = K / 32;
+  const bool own = tid < chunks;
+  half2_t xh[MB][16];  // [m][4e + j]: coordinates 8e + j and 8e + j + 4, times 2^s[m]
+  int sh[MB];
+  bool exact = true;
+#pragma unroll
+  for (int m = 0; m < MB; m++) {
+    uint32_t xb[16];
+    if (own && m < M) {
+      const u32x4 *src = (const u32x4 *)(x + (int64_t)m * K + 32 * tid);
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const u32x4 a = src[u];
+#pragma unroll
+        for (int e = 0; e < 4; e++) xb[4 * u + e] = a[e];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; i++) xb[i] = 0u;
+    }
+    // exponent fields of the nonzero values
+    int emax = 0, emin = 255;
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+      const uint32_t b = (xb[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      const int ex = (int)((b >> 7) & 0xFFu);
+      if (b & 0x7FFFu) {
+        emax = ex > emax ? ex : emax;
+        emin = ex < emin ? ex : emin;
+      }
+    }
+    if (emin == 255 && emax == 0) emin = emax = 142;  // an all-zero chunk
+    exact = exact && emax < 255 && emin > 0 && emax - emin <= 29;
+    sh[m] = 142 - emax;  // the largest value lands in [2^15, 2^16)
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int i0 = 8 * e + j, i1 = 8 * e + j + 4;
+        const float f0 = __uint_as_float(((xb[i0 >> 1] >> (16 * (i0 & 1))) & 0xFFFFu) << 16);
+        const float f1 = __uint_as_float(((xb[i1 >> 1] >> (16 * (i1 & 1))) & 0xFFFFu) << 16);
+        // both values are exact in fp16 once scaled, so the rounding mode
+        // of the conversion does not matter
+        xh[m][4 * e + j] = __builtin_bit_cast(
+            half2_t, __builtin_amdgcn_cvt_pkrtz(ldexpf(f0, sh[m]), ldexpf(f1, sh[m])));
+      }
+  }
+  const int64_t nblk = (N + RB - 1) / RB;
+  // the code words of the next block, and the scale of the output row that
+  // this thread writes (threads p < RB MB write output p), are loaded while
+  // the current block is decoded
+  auto load_block = [&](int64_t b, u32x4 (&w)[RB], float &sc) {
+#pragma unroll
+    for (int r = 0; r < RB; r++) {
+      const int64_t n = b * RB + r;
+      w[r] = (own && b < nblk && n < N)
+                 ? q4[n * chunks + tid]
+                 : u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+    }
+    const int64_t ns = b * RB + tid / MB;
+    sc = (tid < P && b < nblk && ns < N) ? scales[ns] : 0.f;
+  };
+  const half2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  u32x4 wn[RB];
+  float sn;
+  load_block(blockIdx.x, wn, sn);
+  int par = 0;
+  for (int64_t b = blockIdx.x; b < nblk; b += gridDim.x, par ^= 1) {
+    const int64_t n0 = b * RB;
+    u32x4 w[RB];
+#pragma unroll
+    for (int r = 0; r < RB; r++) w[r] = wn[r];
+    const float scale = sn;
+    load_block(b + gridDim.x, wn, sn);
+    float v[P];
+#pragma unroll
+    for (int r = 0; r < RB; r++) {
+      float acc[MB];
+#pragma unroll
+      for (int m = 0; m < MB; m++) acc[m] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const uint32_t lo = w[r][e] & 0x0F0F0F0Fu, hi = (w[r][e] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          // nibbles j and j + 4 are bytes k and k + 2 of lo (even j) or hi
+          // (odd j), k = j / 2; each goes under the fp16 high byte 0x64
+          const uint32_t k = (uint32_t)(j >> 1);
+          const uint32_t sel = (4u << 24) | ((k + 2u) << 16) | (4u << 8) | k;
+          const uint32_t p = __builtin_amdgcn_perm(0x64646464u, (j & 1) ? hi : lo, sel);
+          const half2_t qh = __builtin_bit_cast(half2_t, p) - bias;
+#pragma unroll
+          for (int m = 0; m < MB; m++)
+            acc[m] = __builtin_amdgcn_fdot2(xh[m][4 * e + j], qh, acc[m], false);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MB; m++) v[r * MB + m] = ldexpf(acc[m], -sh[m]);
+      if (!exact) {
+        // the fp32 decode of the general case, activations re-read
+#pragma unroll
+        for (int m = 0; m < MB; m++) {
+          float s = 0.f;
+          if (m < M) {
+            const u32x4 *src = (const u32x4 *)(x + (int64_t)m * K + 32 * tid);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              const u32x4 a = src[e];
+              const uint32_t lo = w[r][e] & 0x0F0F0F0Fu, hi = (w[r][e] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+              for (int bb = 0; bb < 4; bb++) {
+                const uint32_t sel = (7u << 24) | (0x0Cu << 16) | (0x0Cu << 8) | (uint32_t)bb;
+                const float q0 =
+                    __uint_as_float(__builtin_amdgcn_perm(0x4B000000u, lo, sel)) - 8388616.0f;
+                const float q1 =
+                    __uint_as_float(__builtin_amdgcn_perm(0x4B000000u, hi, sel)) - 8388616.0f;
+                s = fmaf(__uint_as_float(a[bb] << 16), q0, s);
+                s = fmaf(__uint_as_float(a[bb] & 0xFFFF0000u), q1, s);
+              }
+            }
+          }
+          v[r * MB + m] = s;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < P; i++) {
+      const float t = wave_sum_lane63(v[i]);
+      if (lane == 63) red[par][wave][i] = t;
+    }
+    __syncthreads();
+    if (tid < P) {
+      float sum = 0.f;
+      for (int ww = 0; ww < nw; ww++) sum += red[par][ww][tid];
+      const int r = tid / MB, m = tid % MB;
+      const int64_t n = n0 + r;
+      if (n < N && m < M) y[(int64_t)m * N + n] = f32_to_bf16_rne(sum * scale);
     }
   }
 }
@@ -348,9 +526,24 @@ hipError_t launch_rtn4_linear(const void *x, int dtype, int64_t M, const uint8_t
     const int chunks = K / 32, threads = 64 * ((chunks + 63) / 64);
     const int rb = M > 2 ? 4 : 8;
     const int64_t nblk = (N + rb - 1) / rb;
-    const int64_t want = (int64_t)(cus > 0 ? cus : 256) * 2;
+    // four workgroups per CU: more waves in flight measured faster than a
+    // deeper prefetch queue per wave
+    const int64_t want = (int64_t)(cus > 0 ? cus : 256) * 4;
     const unsigned grid = (unsigned)(nblk < want ? nblk : want);
     if (threads > 512) return hipErrorInvalidValue;
+    if (dtype == 1) {
+      const uint16_t *xb = (const uint16_t *)x;
+      if (M == 1)
+        hipLaunchKernelGGL(rtn4_small_h_kernel<1>, dim3(grid), dim3(threads), 0, stream, xb,
+                           (int)M, (const u32x4 *)q4, scales, N, K, y);
+      else if (M == 2)
+        hipLaunchKernelGGL(rtn4_small_h_kernel<2>, dim3(grid), dim3(threads), 0, stream, xb,
+                           (int)M, (const u32x4 *)q4, scales, N, K, y);
+      else
+        hipLaunchKernelGGL(rtn4_small_h_kernel<4>, dim3(grid), dim3(threads), 0, stream, xb,
+                           (int)M, (const u32x4 *)q4, scales, N, K, y);
+      return hipGetLastError();
+    }
     if (M == 1)
       hipLaunchKernelGGL(rtn4_small_kernel<1>, dim3(grid), dim3(threads), 0, stream, x, dtype,
                          (int)M, (const u32x4 *)q4, scales, N, K, y);

@@ -106,3 +106,31 @@ def test_small_batches(q, M, K, N, dtype):
     torch.cuda.synchronize()
     _check_out(y, x, code, rq, rs)
     assert np.all(y[:, N // 2] == 0)
+
+
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_bf16_range_fallback(q, M):
+    """bf16 activations run on fp16 dot products after a per-chunk power-of-two
+    scaling, exact while a 32-coordinate chunk spans at most 2^29; wider
+    chunks, bf16 subnormals and zero chunks take the fp32 decode or scale
+    trivially.  Chunk 0: magnitudes 2^20 and 2^-20 (fallback); chunk 1: a
+    subnormal (fallback); chunk 2: all zero; chunk 3: exponents 15 and -14,
+    the widest exact span; chunk 4: exponents 15 and -15 (fallback); the
+    rest ordinary values."""
+    import torch
+    rng = np.random.default_rng(40 + M)
+    K, N = 512, 203
+    Wf = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    xf = rng.standard_normal((M, K)).astype(np.float32)
+    for m in range(M):
+        xf[m, 0], xf[m, 5] = 2.0 ** 20, -(2.0 ** -20)
+        xf[m, 33] = np.float32(3.0 * 2.0 ** -133)
+        xf[m, 64:96] = 0.0
+        xf[m, 96], xf[m, 100] = 1.5 * 2.0 ** 15, 2.0 ** -14
+        xf[m, 128], xf[m, 130] = -1.25 * 2.0 ** 15, 2.0 ** -15
+    W, x = wl.f32_to_bf16_bits(Wf), wl.f32_to_bf16_bits(xf)
+    q4, sc, rq, rs = _prep_check(q, W, wl.BF16, K, f"range {M}")
+    say("rtn4 bf16 range fallback", M)
+    y = bf16_to_np(q.rtn4_linear(to_device(x), q4, sc))
+    torch.cuda.synchronize()
+    _check_out(y, x, wl.BF16, rq, rs)
