@@ -13,6 +13,8 @@
 // sample), so the weights are read once.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "oq_internal.h"
 
 namespace oq {
@@ -348,9 +350,10 @@ __global__ __launch_bounds__(512) void rtn4_small_kernel(const void *__restrict_
 // the two exact products to an fp32 sum.  The chunk's partial sum is scaled
 // back by 2^-s (exact).  Per 8 nibbles that is 3 + 4 + 4 instructions and 4
 // dot products per activation row, against 3 + 16 and 8 products per row in
-// the fp32 decode.  A thread whose
-// chunk is not exact in fp16 (wider range, bf16 subnormals, inf or NaN)
-// decodes in fp32 instead, re-reading its chunk per output row.
+// the fp32 decode.  A workgroup in which any chunk is not exact in fp16
+// (a wider range, bf16 subnormals, inf or NaN) decodes in fp32 instead, in
+// a loop of its own that re-reads the activations per output row, so the
+// fp16 loop holds no registers for it.
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 template <int MB>
@@ -427,82 +430,86 @@ __global__ __launch_bounds__(512) void rtn4_small_h_kernel(const uint16_t *__res
     sc = (tid < P && b < nblk && ns < N) ? scales[ns] : 0.f;
   };
   const half2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-  u32x4 wn[RB];
-  float sn;
-  load_block(blockIdx.x, wn, sn);
-  int par = 0;
-  for (int64_t b = blockIdx.x; b < nblk; b += gridDim.x, par ^= 1) {
-    const int64_t n0 = b * RB;
-    u32x4 w[RB];
+  // the workgroup takes the fp32 decode if any of its chunks is not exact in
+  // fp16 (one branch for all its waves, so both loops keep their barriers)
+  const bool all_exact = __syncthreads_and(exact ? 1 : 0) != 0;
+  auto run = [&](auto fp32_decode) {
+    u32x4 wn[RB];
+    float sn;
+    load_block(blockIdx.x, wn, sn);
+    int par = 0;
+    for (int64_t b = blockIdx.x; b < nblk; b += gridDim.x, par ^= 1) {
+      const int64_t n0 = b * RB;
+      u32x4 w[RB];
 #pragma unroll
-    for (int r = 0; r < RB; r++) w[r] = wn[r];
-    const float scale = sn;
-    load_block(b + gridDim.x, wn, sn);
-    float v[P];
+      for (int r = 0; r < RB; r++) w[r] = wn[r];
+      const float scale = sn;
+      load_block(b + gridDim.x, wn, sn);
+      float v[P];
 #pragma unroll
-    for (int r = 0; r < RB; r++) {
-      float acc[MB];
+      for (int r = 0; r < RB; r++) {
+        float acc[MB];
 #pragma unroll
-      for (int m = 0; m < MB; m++) acc[m] = 0.f;
+        for (int m = 0; m < MB; m++) acc[m] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const uint32_t lo = w[r][e] & 0x0F0F0F0Fu, hi = (w[r][e] >> 4) & 0x0F0F0F0Fu;
+        for (int e = 0; e < 4; e++) {
+          const uint32_t lo = w[r][e] & 0x0F0F0F0Fu, hi = (w[r][e] >> 4) & 0x0F0F0F0Fu;
+          if constexpr (!decltype(fp32_decode)::value) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          // nibbles j and j + 4 are bytes k and k + 2 of lo (even j) or hi
-          // (odd j), k = j / 2; each goes under the fp16 high byte 0x64
-          const uint32_t k = (uint32_t)(j >> 1);
-          const uint32_t sel = (4u << 24) | ((k + 2u) << 16) | (4u << 8) | k;
-          const uint32_t p = __builtin_amdgcn_perm(0x64646464u, (j & 1) ? hi : lo, sel);
-          const half2_t qh = __builtin_bit_cast(half2_t, p) - bias;
+            for (int j = 0; j < 4; j++) {
+              // nibbles j and j + 4 are bytes k and k + 2 of lo (even j) or
+              // hi (odd j), k = j / 2; each goes under the fp16 high byte 0x64
+              const uint32_t k = (uint32_t)(j >> 1);
+              const uint32_t sel = (4u << 24) | ((k + 2u) << 16) | (4u << 8) | k;
+              const uint32_t p = __builtin_amdgcn_perm(0x64646464u, (j & 1) ? hi : lo, sel);
+              const half2_t qh = __builtin_bit_cast(half2_t, p) - bias;
 #pragma unroll
-          for (int m = 0; m < MB; m++)
-            acc[m] = __builtin_amdgcn_fdot2(xh[m][4 * e + j], qh, acc[m], false);
-        }
-      }
+              for (int m = 0; m < MB; m++)
+                acc[m] = __builtin_amdgcn_fdot2(xh[m][4 * e + j], qh, acc[m], false);
+            }
+          } else {
+            // fp32 products, the activations re-read from memory (L1/L2)
 #pragma unroll
-      for (int m = 0; m < MB; m++) v[r * MB + m] = ldexpf(acc[m], -sh[m]);
-      if (!exact) {
-        // the fp32 decode of the general case, activations re-read
+            for (int m = 0; m < MB; m++) {
+              if (own && m < M) {
+                const u32x4 a = ((const u32x4 *)(x + (int64_t)m * K + 32 * tid))[e];
 #pragma unroll
-        for (int m = 0; m < MB; m++) {
-          float s = 0.f;
-          if (m < M) {
-            const u32x4 *src = (const u32x4 *)(x + (int64_t)m * K + 32 * tid);
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-              const u32x4 a = src[e];
-              const uint32_t lo = w[r][e] & 0x0F0F0F0Fu, hi = (w[r][e] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-              for (int bb = 0; bb < 4; bb++) {
-                const uint32_t sel = (7u << 24) | (0x0Cu << 16) | (0x0Cu << 8) | (uint32_t)bb;
-                const float q0 =
-                    __uint_as_float(__builtin_amdgcn_perm(0x4B000000u, lo, sel)) - 8388616.0f;
-                const float q1 =
-                    __uint_as_float(__builtin_amdgcn_perm(0x4B000000u, hi, sel)) - 8388616.0f;
-                s = fmaf(__uint_as_float(a[bb] << 16), q0, s);
-                s = fmaf(__uint_as_float(a[bb] & 0xFFFF0000u), q1, s);
+                for (int bb = 0; bb < 4; bb++) {
+                  const uint32_t sel = (7u << 24) | (0x0Cu << 16) | (0x0Cu << 8) | (uint32_t)bb;
+                  const float q0 =
+                      __uint_as_float(__builtin_amdgcn_perm(0x4B000000u, lo, sel)) - 8388616.0f;
+                  const float q1 =
+                      __uint_as_float(__builtin_amdgcn_perm(0x4B000000u, hi, sel)) - 8388616.0f;
+                  acc[m] = fmaf(__uint_as_float(a[bb] << 16), q0, acc[m]);
+                  acc[m] = fmaf(__uint_as_float(a[bb] & 0xFFFF0000u), q1, acc[m]);
+                }
               }
             }
           }
-          v[r * MB + m] = s;
         }
+#pragma unroll
+        for (int m = 0; m < MB; m++)
+          v[r * MB + m] = decltype(fp32_decode)::value ? acc[m] : ldexpf(acc[m], -sh[m]);
+      }
+#pragma unroll
+      for (int i = 0; i < P; i++) {
+        const float t = wave_sum_lane63(v[i]);
+        if (lane == 63) red[par][wave][i] = t;
+      }
+      __syncthreads();
+      if (tid < P) {
+        float sum = 0.f;
+        for (int ww = 0; ww < nw; ww++) sum += red[par][ww][tid];
+        const int r = tid / MB, m = tid % MB;
+        const int64_t n = n0 + r;
+        if (n < N && m < M) y[(int64_t)m * N + n] = f32_to_bf16_rne(sum * scale);
       }
     }
-#pragma unroll
-    for (int i = 0; i < P; i++) {
-      const float t = wave_sum_lane63(v[i]);
-      if (lane == 63) red[par][wave][i] = t;
-    }
-    __syncthreads();
-    if (tid < P) {
-      float sum = 0.f;
-      for (int ww = 0; ww < nw; ww++) sum += red[par][ww][tid];
-      const int r = tid / MB, m = tid % MB;
-      const int64_t n = n0 + r;
-      if (n < N && m < M) y[(int64_t)m * N + n] = f32_to_bf16_rne(sum * scale);
-    }
-  }
+  };
+  if (all_exact)
+    run(std::false_type{});
+  else
+    run(std::true_type{});
 }
 
 }  // namespace
