@@ -491,10 +491,32 @@ __global__ __launch_bounds__(512) void rtn4_small_h_kernel(const uint16_t *__res
         for (int m = 0; m < MB; m++)
           v[r * MB + m] = decltype(fp32_decode)::value ? acc[m] : ldexpf(acc[m], -sh[m]);
       }
+      // transposed reduction of the P partial sums over the wave: swapping
+      // the wave's halves (v_permlane32_swap) and adding leaves partial i in
+      // lanes 0-31 and i + P/2 in lanes 32-63 of P/2 registers; swapping
+      // odd and even 16-lane rows (v_permlane16_swap) leaves partial
+      // i + rho P/4 in row rho of P/4 registers; four DPP adds then sum each
+      // row.  3P/4 swaps and adds and P DPP adds, against 6P DPP adds.
 #pragma unroll
-      for (int i = 0; i < P; i++) {
-        const float t = wave_sum_lane63(v[i]);
-        if (lane == 63) red[par][wave][i] = t;
+      for (int i = 0; i < P / 2; i++) {
+        const auto t = __builtin_amdgcn_permlane32_swap(
+            __float_as_uint(v[i]), __float_as_uint(v[i + P / 2]), false, false);
+        v[i] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+      }
+#pragma unroll
+      for (int i = 0; i < P / 4; i++) {
+        const auto t = __builtin_amdgcn_permlane16_swap(
+            __float_as_uint(v[i]), __float_as_uint(v[i + P / 4]), false, false);
+        v[i] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+      }
+#pragma unroll
+      for (int i = 0; i < P / 4; i++) {
+        float t = v[i];
+        t += dpp_f<0xB1, 0xF>(t);   // quad_perm [1,0,3,2]
+        t += dpp_f<0x4E, 0xF>(t);   // quad_perm [2,3,0,1]
+        t += dpp_f<0x141, 0xF>(t);  // row_half_mirror
+        t += dpp_f<0x140, 0xF>(t);  // row_mirror: every lane holds its row's sum
+        if ((lane & 15) == 0) red[par][wave][i + (lane >> 4) * (P / 4)] = t;
       }
       __syncthreads();
       if (tid < P) {
