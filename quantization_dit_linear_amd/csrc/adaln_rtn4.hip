@@ -198,15 +198,38 @@ __device__ __forceinline__ float dpp_f(float v) {
                                                                CTRL, RMASK, 0xF, false));
 }
 
-// Sum of v over the 64 lanes of a wave, valid in lane 63.
-__device__ __forceinline__ float wave_sum_lane63(float v) {
-  v += dpp_f<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
-  v += dpp_f<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]: every lane holds its quad's sum
-  v += dpp_f<0x141, 0xF>(v);  // row_half_mirror: sums of 8
-  v += dpp_f<0x140, 0xF>(v);  // row_mirror: sums of 16
-  v += dpp_f<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
-  v += dpp_f<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3: lane 63 holds the total
-  return v;
+// Sums each of the P partial sums v[i] over the 64 lanes of a wave and
+// stores partial i's total to out[i] (LDS), by a transposed reduction:
+// swapping the wave's halves (v_permlane32_swap) and adding leaves partial i
+// in lanes 0-31 and i + P/2 in lanes 32-63 of P/2 registers; swapping odd
+// and even 16-lane rows (v_permlane16_swap) and adding leaves partial
+// i + rho P/4 in row rho of P/4 registers; four DPP adds then sum each row.
+// 3P/4 swaps and adds and P DPP adds, against 6P DPP adds for P separate
+// wave sums.  v is consumed.
+template <int P>
+__device__ __forceinline__ void wave_sums_to(float (&v)[P], float *out, int lane) {
+  static_assert(P % 4 == 0, "P partials in four 16-lane rows");
+#pragma unroll
+  for (int i = 0; i < P / 2; i++) {
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]),
+                                                    __float_as_uint(v[i + P / 2]), false, false);
+    v[i] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < P / 4; i++) {
+    const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]),
+                                                    __float_as_uint(v[i + P / 4]), false, false);
+    v[i] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < P / 4; i++) {
+    float t = v[i];
+    t += dpp_f<0xB1, 0xF>(t);   // quad_perm [1,0,3,2]
+    t += dpp_f<0x4E, 0xF>(t);   // quad_perm [2,3,0,1]
+    t += dpp_f<0x141, 0xF>(t);  // row_half_mirror
+    t += dpp_f<0x140, 0xF>(t);  // row_mirror: every lane holds its row's sum
+    if ((lane & 15) == 0) out[i + (lane >> 4) * (P / 4)] = t;
+  }
 }
 
 // Small batches (M <= 4 activation rows, the AdaLN case: one modulation
@@ -218,7 +241,7 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
 // output rows: each thread loads its chunk's 16 code bytes of each row (a
 // wave reads 1 KB of one row, coalesced), decodes them with byte
 // conversions and accumulates the exact fp32 products x q; the RB * MB
-// partial sums of a block are reduced over each wave's lanes with DPP,
+// partial sums of a block are reduced over each wave's lanes (wave_sums_to),
 // then over the waves through LDS, one barrier per block.
 template <int MB>
 __global__ __launch_bounds__(512) void rtn4_small_kernel(const void *__restrict__ x, int dtype,
@@ -318,14 +341,7 @@ __global__ __launch_bounds__(512) void rtn4_small_kernel(const void *__restrict_
 #pragma unroll
       for (int m = 0; m < MB; m++) v[r * MB + m] = acc[m];
     }
-    // each partial summed over the wave's 64 lanes by DPP adds (quad swaps,
-    // half-row and row mirrors, then row broadcasts), which leave the total
-    // in lane 63: six VALU instructions per partial, no LDS traffic
-#pragma unroll
-    for (int i = 0; i < P; i++) {
-      const float t = wave_sum_lane63(v[i]);
-      if (lane == 63) red[par][wave][i] = t;
-    }
+    wave_sums_to(v, red[par][wave], lane);
     __syncthreads();  // one barrier per block: red alternates between two buffers
     if (tid < P) {
       float sum = 0.f;
@@ -491,33 +507,7 @@ __global__ __launch_bounds__(512) void rtn4_small_h_kernel(const uint16_t *__res
         for (int m = 0; m < MB; m++)
           v[r * MB + m] = decltype(fp32_decode)::value ? acc[m] : ldexpf(acc[m], -sh[m]);
       }
-      // transposed reduction of the P partial sums over the wave: swapping
-      // the wave's halves (v_permlane32_swap) and adding leaves partial i in
-      // lanes 0-31 and i + P/2 in lanes 32-63 of P/2 registers; swapping
-      // odd and even 16-lane rows (v_permlane16_swap) leaves partial
-      // i + rho P/4 in row rho of P/4 registers; four DPP adds then sum each
-      // row.  3P/4 swaps and adds and P DPP adds, against 6P DPP adds.
-#pragma unroll
-      for (int i = 0; i < P / 2; i++) {
-        const auto t = __builtin_amdgcn_permlane32_swap(
-            __float_as_uint(v[i]), __float_as_uint(v[i + P / 2]), false, false);
-        v[i] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
-      }
-#pragma unroll
-      for (int i = 0; i < P / 4; i++) {
-        const auto t = __builtin_amdgcn_permlane16_swap(
-            __float_as_uint(v[i]), __float_as_uint(v[i + P / 4]), false, false);
-        v[i] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
-      }
-#pragma unroll
-      for (int i = 0; i < P / 4; i++) {
-        float t = v[i];
-        t += dpp_f<0xB1, 0xF>(t);   // quad_perm [1,0,3,2]
-        t += dpp_f<0x4E, 0xF>(t);   // quad_perm [2,3,0,1]
-        t += dpp_f<0x141, 0xF>(t);  // row_half_mirror
-        t += dpp_f<0x140, 0xF>(t);  // row_mirror: every lane holds its row's sum
-        if ((lane & 15) == 0) red[par][wave][i + (lane >> 4) * (P / 4)] = t;
-      }
+      wave_sums_to(v, red[par][wave], lane);
       __syncthreads();
       if (tid < P) {
         float sum = 0.f;
