@@ -364,9 +364,10 @@ __global__ __launch_bounds__(512) void rtn4_small_kernel(const void *__restrict_
 // which makes the pair (1024 + n_j, 1024 + n_j+4); one packed fp16
 // subtraction of 1032 leaves the exact q = n - 8, and v_dot2c_f32_f16 adds
 // the two exact products to an fp32 sum.  The chunk's partial sum is scaled
-// back by 2^-s (exact).  Per 8 nibbles that is 3 + 4 + 4 instructions and 4
-// dot products per activation row, against 3 + 16 and 8 products per row in
-// the fp32 decode.  A workgroup in which any chunk is not exact in fp16
+// back by 2^-s (exact unless the result falls below the fp32 normal range,
+// where the fp32 path would round too).  Per 8 nibbles that is 3 + 4 + 4
+// instructions and 4 dot products per activation row, against 3 + 16 and 8
+// products per row in the fp32 decode.  A workgroup in which any chunk is not exact in fp16
 // (a wider range, bf16 subnormals, inf or NaN) decodes in fp32 instead, in
 // a loop of its own that re-reads the activations per output row, so the
 // fp16 loop holds no registers for it.
