@@ -288,15 +288,15 @@ __global__ __launch_bounds__(512) void rtn4_small_kernel(const void *__restrict_
   }
   const int64_t nblk = (N + RB - 1) / RB;
   // codes of the next block are loaded while the current one is decoded
-  // the code words of the next block, and the scale of the output row that
-  // this thread writes (threads p < RB MB write output p), are loaded while
-  // the current block is decoded
+  // the code words of the next block (non-temporal: read once per launch),
+  // and the scale of the output row that this thread writes (threads
+  // p < RB MB write output p), are loaded while the current block is decoded
   auto load_block = [&](int64_t b, u32x4 (&w)[RB], float &sc) {
 #pragma unroll
     for (int r = 0; r < RB; r++) {
       const int64_t n = b * RB + r;
       w[r] = (own && b < nblk && n < N)
-                 ? q4[n * chunks + tid]
+                 ? __builtin_nontemporal_load(&q4[n * chunks + tid])
                  : u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
     }
     const int64_t ns = b * RB + tid / MB;
@@ -432,15 +432,15 @@ __global__ __launch_bounds__(512) void rtn4_small_h_kernel(const uint16_t *__res
       }
   }
   const int64_t nblk = (N + RB - 1) / RB;
-  // the code words of the next block, and the scale of the output row that
-  // this thread writes (threads p < RB MB write output p), are loaded while
-  // the current block is decoded
+  // the code words of the next block (non-temporal: read once per launch),
+  // and the scale of the output row that this thread writes (threads
+  // p < RB MB write output p), are loaded while the current block is decoded
   auto load_block = [&](int64_t b, u32x4 (&w)[RB], float &sc) {
 #pragma unroll
     for (int r = 0; r < RB; r++) {
       const int64_t n = b * RB + r;
       w[r] = (own && b < nblk && n < N)
-                 ? q4[n * chunks + tid]
+                 ? __builtin_nontemporal_load(&q4[n * chunks + tid])
                  : u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
     }
     const int64_t ns = b * RB + tid / MB;
